@@ -1,0 +1,297 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each test names what fixes the expected value: a hand derivation stored in
+tests/golden, exact rational arithmetic, a textbook special case (Sylvester
+Hadamard matrices, via scipy), a closed form, an invariant of the definition,
+or numbers printed on the pages.
+"""
+
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.linalg
+
+import oracle
+from binary_rank_gemv_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _branches_from_json(d):
+    out = []
+    for b in d["branches"]:
+        out.append({k: np.asarray(b[k], dtype=np.float64) if k in ("U", "V")
+                    else np.asarray(b[k], dtype=np.float16) for k in b})
+    return out
+
+
+def _random_layer(rng, m, n, ranks):
+    out = []
+    for r in ranks:
+        out.append({
+            "U": rng.standard_normal((m, r)).astype(np.float32),
+            "V": rng.standard_normal((n, r)).astype(np.float32),
+            "h": rng.uniform(0.5, 1.5, m).astype(np.float16),
+            "l": rng.uniform(0.5, 1.5, r).astype(np.float16),
+            "g": rng.uniform(0.5, 1.5, n).astype(np.float16),
+        })
+    return out
+
+
+# ---------------------------------------------------------------- hand example
+
+def test_hand_example_all_evaluators():
+    d = _load("hand_example_two_branch.json")
+    br = _branches_from_json(d)
+    x = np.asarray(d["x"], dtype=np.float16)
+    want = np.asarray(d["y"])
+    np.testing.assert_array_equal(oracle.linear_forward(x, br), want)
+    np.testing.assert_array_equal(oracle.factored_forward(x, br), want)
+    exact = oracle.exact_forward(x, br)
+    assert exact == [[Fraction(10), Fraction(-19)]]
+    np.testing.assert_array_equal(oracle.rows_forward(x, br, [1, 0]), want[:, ::-1])
+
+
+def test_sign_reading_zero_and_negative_zero():
+    v = np.array([-1.0, -0.0, 0.0, 1e-30, -1e-30, np.nan], dtype=np.float64)
+    np.testing.assert_array_equal(oracle.sign_matrix(v), [-1, 1, 1, 1, -1, 1])
+    v16 = np.array([-0.0, 0.0, -6e-8, 6e-8], dtype=np.float16)   # fp16 subnormals
+    np.testing.assert_array_equal(oracle.sign_matrix(v16), [1, 1, -1, 1])
+
+
+# ------------------------------------------------------------ exact arithmetic
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_float64_matches_exact_rational(seed):
+    rng = np.random.default_rng(100 + seed)
+    m, n = 11, 13
+    br = _random_layer(rng, m, n, (5, 3))
+    x = rng.standard_normal((2, n)).astype(np.float16)
+    exact = oracle.exact_forward(x, br)
+    ex = np.array([[float(v) for v in row] for row in exact])
+    scale = np.max(np.abs(ex))
+    for y in (oracle.linear_forward(x, br), oracle.factored_forward(x, br)):
+        assert np.max(np.abs(y - ex)) <= 1e-13 * scale
+
+
+# -------------------------------------------------------------- special cases
+
+@pytest.mark.parametrize("k", [1, 3, 5])
+def test_hadamard_factors_reduce_to_elementwise_scaling(k):
+    """sign(U) = sign(V) = H (Sylvester), l = 2^-k  =>  H diag(l) H^T = I,
+    so each branch is diag(h*g) and y = sum_b h_b*g_b*x."""
+    n = 2 ** k
+    H = scipy.linalg.hadamard(n).astype(np.float64)
+    rng = np.random.default_rng(k)
+    br = []
+    for _ in range(2):
+        br.append({"U": H * rng.uniform(0.1, 2.0, (n, n)),
+                   "V": H * rng.uniform(0.1, 2.0, (n, n)),
+                   "h": rng.uniform(0.5, 1.5, n).astype(np.float16),
+                   "l": np.full(n, 2.0 ** -k, dtype=np.float16),
+                   "g": rng.uniform(0.5, 1.5, n).astype(np.float16)})
+    x = rng.standard_normal((3, n)).astype(np.float16)
+    want = sum(b["h"].astype(np.float64) * b["g"].astype(np.float64) for b in br) * x.astype(np.float64)
+    np.testing.assert_allclose(oracle.linear_forward(x, br), want, rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(oracle.factored_forward(x, br), want, rtol=1e-14, atol=1e-12)
+
+
+def test_all_positive_signs_closed_form():
+    """All signs +1: W_b = h_b (sum_j l_bj) g_b^T, so
+    y_i = sum_b h_bi (sum_j l_bj) (sum_k g_bk x_k)."""
+    rng = np.random.default_rng(7)
+    m, n = 9, 6
+    br = _random_layer(rng, m, n, (4, 2))
+    for b in br:
+        b["U"] = np.abs(b["U"])
+        b["V"] = np.abs(b["V"])
+    x = rng.standard_normal((2, n)).astype(np.float16)
+    x64 = x.astype(np.float64)
+    want = np.zeros((2, m))
+    for b in br:
+        h, l, g = (b[k].astype(np.float64) for k in ("h", "l", "g"))
+        want += np.outer(x64 @ g, h) * l.sum()
+    np.testing.assert_allclose(oracle.linear_forward(x, br), want, rtol=1e-13)
+
+
+# ----------------------------------------------------------------- invariants
+
+def test_dense_and_factored_agree_tiny_config():
+    br, x = synth.make_layer(synth.TINY, batch=3, seed=0)
+    yd = oracle.linear_forward(x, br)
+    yf = oracle.factored_forward(x, br)
+    assert np.max(np.abs(yd - yf)) <= 1e-12 * np.max(np.abs(yd))
+
+
+def test_gauge_flip_of_latent_column_leaves_output_unchanged():
+    rng = np.random.default_rng(3)
+    br = _random_layer(rng, 20, 24, (6, 6))
+    x = rng.standard_normal((2, 24)).astype(np.float16)
+    y0 = oracle.linear_forward(x, br)
+    flipped = [dict(b) for b in br]
+    for j in (0, 4):
+        flipped[0]["U"] = flipped[0]["U"].copy(); flipped[0]["U"][:, j] *= -1
+        flipped[0]["V"] = flipped[0]["V"].copy(); flipped[0]["V"][:, j] *= -1
+    assert not np.array_equal(oracle.sign_matrix(br[0]["U"]), oracle.sign_matrix(flipped[0]["U"]))
+    np.testing.assert_allclose(oracle.linear_forward(x, flipped), y0, rtol=1e-13, atol=1e-12)
+
+
+def test_latent_permutation_leaves_output_unchanged():
+    rng = np.random.default_rng(4)
+    br = _random_layer(rng, 17, 15, (7,))
+    x = rng.standard_normal((2, 15)).astype(np.float16)
+    perm = rng.permutation(7)
+    pb = [{"U": br[0]["U"][:, perm], "V": br[0]["V"][:, perm], "l": br[0]["l"][perm],
+           "h": br[0]["h"], "g": br[0]["g"]}]
+    np.testing.assert_allclose(oracle.linear_forward(x, pb), oracle.linear_forward(x, br),
+                               rtol=1e-13, atol=1e-12)
+
+
+def test_branch_additivity_and_linearity():
+    rng = np.random.default_rng(5)
+    br = _random_layer(rng, 14, 10, (3, 5))
+    x1 = rng.standard_normal((2, 10)).astype(np.float16)
+    x2 = rng.standard_normal((2, 10)).astype(np.float16)
+    y = oracle.linear_forward(x1, br)
+    np.testing.assert_allclose(y, oracle.linear_forward(x1, br[:1]) + oracle.linear_forward(x1, br[1:]),
+                               rtol=1e-13, atol=1e-12)
+    xs = (x1.astype(np.float64) + x2.astype(np.float64))
+    np.testing.assert_allclose(oracle.linear_forward(xs, br),
+                               y + oracle.linear_forward(x2, br), rtol=1e-12, atol=1e-11)
+
+
+def test_rows_forward_matches_full():
+    br, x = synth.make_layer(synth.TINY, batch=2, seed=1)
+    rows = [0, 5, 511, 100]
+    np.testing.assert_allclose(oracle.rows_forward(x, br, rows),
+                               oracle.linear_forward(x, br)[:, rows], rtol=1e-12, atol=1e-9)
+
+
+def test_transposed_is_adjoint_of_forward():
+    rng = np.random.default_rng(6)
+    br = _random_layer(rng, 12, 9, (4, 3))
+    x = rng.standard_normal((1, 9))
+    d = rng.standard_normal((1, 12))
+    lhs = (oracle.linear_forward(x, br) @ d.T).item()
+    rhs = (x @ oracle.transposed_forward(d, br).T).item()
+    assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(lhs))
+    np.testing.assert_allclose(oracle.transposed_forward(d, br), d @ oracle.dense_weight(br),
+                               rtol=1e-14)
+
+
+# --------------------------------------------------------- bits per weight
+
+def test_bits_per_weight_counts_the_arrays_of_a_layer():
+    for shape in (synth.TINY, synth.LayerShape("odd", 40, 72, (9, 9))):
+        br, _ = synth.make_layer(shape, batch=1, seed=0)
+        bits = sum(b["U"].size + b["V"].size + 16 * (b["h"].size + b["l"].size + b["g"].size)
+                   for b in br)
+        assert bits / (shape.m * shape.n) == pytest.approx(
+            oracle.bits_per_weight(shape.m, shape.n, shape.ranks[0], len(shape.ranks)), rel=1e-15)
+
+
+@pytest.mark.parametrize("m,n,r,stated", [
+    (512, 512, 32, 0.38), (11008, 4096, 1472, 1.0), (5120, 5120, 688, 0.55),
+    (5120, 5120, 112, 0.1), (13824, 5120, 1008, 0.55), (5120, 13824, 168, 0.1),
+    (28672, 8192, 1728, 0.55)])
+def test_config_ranks_give_the_stated_bits_per_weight(m, n, r, stated):
+    assert oracle.bits_per_weight(m, n, r) == pytest.approx(stated, rel=0.02)
+    assert abs(oracle.rank_for_bpw(m, n, oracle.bits_per_weight(m, n, r)) - r) < 1e-9
+
+
+def test_model_footprints_match_the_pages():
+    d = _load("model_sizes.json")
+    tol = d["tolerance"]
+    for mdl in d["models"]:
+        dims = (mdl["hidden"], mdl["intermediate"], mdl["layers"], mdl["vocab"])
+        for key, gb in mdl["sizes_gb"].items():
+            got = oracle.model_footprint_bytes(*dims, bpw=None if key == "fp16" else float(key)) / 1e9
+            rel = tol["fp16"] if key == "fp16" else tol["quantised"]
+            assert got == pytest.approx(gb, rel=rel), (mdl["name"], key, got, gb)
+
+
+# -------------------------------------------------------------------- packing
+
+def test_pack_worked_examples():
+    d = _load("pack_worked_examples.json")
+    for case in d["cases"]:
+        neg = np.zeros((case["R"], case["K"]), dtype=bool)
+        for a, k in case["negative"]:
+            neg[a, k] = True
+        p = oracle.pack_factor(neg)
+        assert p.size == case["total_bytes"] == oracle.packed_factor_bytes(case["R"], case["K"])
+        want = np.zeros(p.size, dtype=np.uint8)
+        for off, val in case["nonzero_bytes"].items():
+            want[int(off)] = val
+        np.testing.assert_array_equal(p, want)
+
+
+@pytest.mark.parametrize("R,K", [(16, 64), (20, 600), (33, 1472), (7, 40), (48, 4096)])
+def test_pack_roundtrip_and_popcount(R, K):
+    rng = np.random.default_rng(R * 1000 + K)
+    neg = rng.random((R, K)) < 0.5
+    p = oracle.pack_factor(neg)
+    np.testing.assert_array_equal(oracle.unpack_factor(p, R, K), neg)
+    assert int(np.unpackbits(p).sum()) == int(neg.sum())
+
+
+def test_pack_all_negative_and_all_positive():
+    for R, K in ((16, 64), (20, 600)):
+        p1 = oracle.pack_factor(np.ones((R, K), dtype=bool))
+        assert int(np.unpackbits(p1).sum()) == R * K        # pad bits stay 0
+        p0 = oracle.pack_factor(np.zeros((R, K), dtype=bool))
+        assert not p0.any()
+    # a full 16 x 64 tile of -1 is all ones
+    assert (oracle.pack_factor(np.ones((16, 64), dtype=bool)) == 0xFF).all()
+
+
+def test_sign_bits_transpose():
+    v = np.array([[1.0, -2.0, 0.0], [-0.0, -1.0, 3.0]], dtype=np.float32)
+    np.testing.assert_array_equal(oracle.sign_bits(v), [[False, True, False], [False, True, False]])
+    np.testing.assert_array_equal(oracle.sign_bits(v, transpose=True),
+                                  [[False, False], [True, True], [False, False]])
+
+
+# ------------------------------------------------ planted mistakes are caught
+
+def _hand_case():
+    d = _load("hand_example_two_branch.json")
+    return _branches_from_json(d), np.asarray(d["x"], dtype=np.float16), np.asarray(d["y"])
+
+
+@pytest.mark.parametrize("mistake", ["drop_g", "drop_l", "l_index_reversed", "negated_u",
+                                     "sign_zero_negative", "drop_residual"])
+def test_pins_catch_planted_oracle_mistakes(mistake, monkeypatch):
+    """Each plausible slip in the definition changes the hand example's y."""
+    import oracle.littlebit_oracle as lo
+
+    def bad_bw(br):
+        su, sv = lo.sign_matrix(br["U"]), lo.sign_matrix(br["V"])
+        h, l, g = (np.asarray(br[k], dtype=np.float64) for k in ("h", "l", "g"))
+        if mistake == "drop_g":
+            return h[:, None] * ((su * l) @ sv.T)
+        if mistake == "drop_l":
+            return h[:, None] * (su @ sv.T) * g[None, :]
+        if mistake == "l_index_reversed":
+            return h[:, None] * ((su * l[::-1]) @ sv.T) * g[None, :]
+        assert mistake == "negated_u"
+        return h[:, None] * ((-su * l) @ sv.T) * g[None, :]
+
+    br, x, want = _hand_case()
+    if mistake == "sign_zero_negative":
+        monkeypatch.setattr(lo, "sign_matrix",
+                            lambda a: np.where(np.signbit(np.asarray(a, dtype=np.float64)), -1.0, 1.0))
+    elif mistake == "drop_residual":
+        br = br[:1]
+    else:
+        monkeypatch.setattr(lo, "branch_weight", bad_bw)
+    y = lo.linear_forward(x, br)
+    assert not np.array_equal(y, want), mistake
