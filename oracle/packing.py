@@ -26,7 +26,10 @@ LB16 format (one packed factor F with R rows and reduction length K)
   8 * (e mod 2) + 7 - (4 q + floor(e / 2)) of the unit.
 * Units are stored little-endian.  With NF = floor(NU / 8) and TU = NU mod 8:
   unit u < 8 NF is at tile byte 1024 * floor(u / 8) + 16 L + 2 (u mod 8);
-  unit u >= 8 NF is at tile byte 1024 NF + 128 (u - 8 NF) + 2 L.
+  for u >= 8 NF let j = u - 8 NF: if j < 2 floor(TU / 2) the unit is at
+  1024 NF + 256 floor(j / 2) + 4 L + 2 (j mod 2), otherwise (the last unit
+  when TU is odd) at 1024 NF + 256 floor(TU / 2) + 2 L.  So units 2p and
+  2p+1 of a lane are always one aligned 32-bit word.
 """
 
 from __future__ import annotations
@@ -64,8 +67,12 @@ def _unit_byte_offsets(nu: int) -> np.ndarray:
         for u in range(nu):
             if u < 8 * nf:
                 out[lane, u] = 1024 * (u // 8) + 16 * lane + 2 * (u % 8)
+                continue
+            j, tu = u - 8 * nf, nu - 8 * nf
+            if j < 2 * (tu // 2):
+                out[lane, u] = 1024 * nf + 256 * (j // 2) + 4 * lane + 2 * (j % 2)
             else:
-                out[lane, u] = 1024 * nf + 128 * (u - 8 * nf) + 2 * lane
+                out[lane, u] = 1024 * nf + 256 * (tu // 2) + 2 * lane
     return out
 
 

@@ -26,8 +26,14 @@ def _units(packed, R, K):
     for T in range(nt):
         for L in range(64):
             for u in range(nu):
-                off = T * 2 * kp + (1024 * (u // 8) + 16 * L + 2 * (u % 8) if u < 8 * nf
-                                    else 1024 * nf + 128 * (u - 8 * nf) + 2 * L)
+                j, tu = u - 8 * nf, nu - 8 * nf
+                if u < 8 * nf:
+                    rel = 1024 * (u // 8) + 16 * L + 2 * (u % 8)
+                elif j < 2 * (tu // 2):
+                    rel = 1024 * nf + 256 * (j // 2) + 4 * L + 2 * (j % 2)
+                else:
+                    rel = 1024 * nf + 256 * (tu // 2) + 2 * L
+                off = T * 2 * kp + rel
                 out[T, L, u] = int(packed[off]) | (int(packed[off + 1]) << 8)
     return out
 
