@@ -1,0 +1,194 @@
+#!/usr/bin/env python3
+"""Benchmark of the LittleBit layer's decode path on one MI355X.
+
+Workload (the headline configuration): the Llama2-7B-shaped MLP
+up-projection, 4096 -> 11008, two branches of rank 1472 (about 1.0 bit per
+weight), fp16 scales ~U[0.5, 1.5], one fp16 token ~N(0, 1) per call (batch-1
+decode GEMV).  Inputs are synthetic and seeded (binary_rank_gemv_amd.synth for
+the first copy of the layer, torch's seeded GPU generator for the others).
+
+One step = one littlebit_linear_fwd call (every step of the layer for one
+token).  To measure HBM rather than the 256 MB last-level cache, the timed
+loop cycles through distinct copies of the layer totalling >= 1 GB; the calls
+are captured once in a HIP graph and replayed.
+
+Prints one JSON line (see the keys below), including a roofline object for the
+decode kernel and a cpu_baseline object for the float64 CPU oracle timed on
+a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def algorithmic_bytes(m, n, ranks, batch):
+    """Unpadded sign bits + fp16 scales + fp16 x + fp16 y for one call."""
+    bits = sum(r * (m + n) for r in ranks)
+    scales = sum(m + n + r for r in ranks) * 2
+    return bits // 8 + scales + 2 * batch * n + 2 * batch * m
+
+
+def make_copy(lb, torch, shape, seed):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    branches = []
+    for r in shape.ranks:
+        U = torch.randn((shape.m, r), device="cuda", generator=g)
+        V = torch.randn((shape.n, r), device="cuda", generator=g)
+        h = (torch.rand(shape.m, device="cuda", generator=g) + 0.5).half()
+        l = (torch.rand(r, device="cuda", generator=g) + 0.5).half()
+        gg = (torch.rand(shape.n, device="cuda", generator=g) + 0.5).half()
+        branches.append(lb.LittleBitBranch(v_bits=lb.littlebit_pack(V, True),
+                                           u_bits=lb.littlebit_pack(U, False),
+                                           h=h, l=l, g=gg, r=r))
+        del U, V
+    return lb.LittleBitLayer(m=shape.m, n=shape.n, branches=branches)
+
+
+def cpu_baseline(shape, branches, x, budget_rows):
+    """Time the oracle's dense definition on a sample of output rows."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max(d["num_threads"] for d in threadpool_info()) if threadpool_info() else 1
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    rows = np.arange(budget_rows)
+    t0 = time.perf_counter()
+    oracle.rows_forward(x, branches, rows)
+    dt = time.perf_counter() - t0
+    frac = budget_rows / shape.m
+    return {"value": x.shape[0] * frac / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{budget_rows} of {shape.m} output rows of one batch-1 call (dense float64 "
+                      f"definition, rows of W built per call), {dt:.1f} s, scaled by {shape.m}/{budget_rows}"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3840)
+    ap.add_argument("--warmup", type=int, default=384)
+    ap.add_argument("--copies-gb", type=float, default=1.0, help="total size of distinct layer copies")
+    ap.add_argument("--cpu-rows", type=int, default=2752, help="output rows in the oracle sample (0: skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the layer is measured per GPU.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from binary_rank_gemv_amd import littlebit as lb
+    from binary_rank_gemv_amd import synth
+    import oracle
+
+    shape, batch = synth.UP7B, 1
+    branches, x_np = synth.make_layer(shape, batch=batch, seed=0)
+    torch.cuda.set_device(0)
+    x = torch.from_numpy(x_np).cuda()
+    y = torch.empty((batch, shape.m), dtype=torch.float16, device="cuda")
+
+    first = lb.LittleBitLayer.from_latents(branches)
+    per_copy = sum(b.v_bits.numel() + b.u_bits.numel() + 2 * (b.h.numel() + b.l.numel() + b.g.numel())
+                   for b in first.branches)
+    ncopies = max(1, int(np.ceil(args.copies_gb * 1e9 / per_copy)))
+    copies = [first] + [make_copy(lb, torch, shape, 1000 + i) for i in range(ncopies - 1)]
+    need = lb.littlebit_linear_workspace_bytes(first, batch)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+
+    # correctness of the measured configuration (first copy) against the oracle
+    lb.littlebit_linear_fwd(first, x, out=y, workspace=ws)
+    torch.cuda.synchronize()
+    yr = oracle.factored_forward(x_np, branches)
+    yg = y.float().cpu().numpy().astype(np.float64)
+    rel_l2 = float(np.linalg.norm(yg - yr) / np.linalg.norm(yr))
+    max_rms = float(np.max(np.abs(yg - yr)) / np.sqrt(np.mean(yr ** 2)))
+
+    # capture one cycle over the copies, plus a remainder graph
+    def capture(nc):
+        gr = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for c in copies[:nc]:
+                lb.littlebit_linear_fwd(c, x, out=y, workspace=ws)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(gr, stream=s):
+                for c in copies[:nc]:
+                    lb.littlebit_linear_fwd(c, x, out=y, workspace=ws)
+        torch.cuda.current_stream().wait_stream(s)
+        return gr
+
+    full = capture(ncopies)
+
+    def run(steps):
+        reps, rem = divmod(steps, ncopies)
+        for _ in range(reps):
+            full.replay()
+        if rem:
+            capture_rem[rem].replay()
+
+    capture_rem = {}
+    for k in {args.steps % ncopies, args.warmup % ncopies} - {0}:
+        capture_rem[k] = capture(k)
+
+    run(args.warmup)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    run(args.steps)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end)
+    ms_per_step = ms / args.steps
+
+    abytes = algorithmic_bytes(shape.m, shape.n, shape.ranks, batch)
+    achieved = abytes / (ms_per_step * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "lb_decode_vpass + lb_decode_upass (two launches per call)",
+                "algorithmic_bytes_per_call": abytes,
+                "avg_call_us": round(ms_per_step * 1e3, 3)}
+
+    cpu = None
+    if args.cpu_rows > 0:
+        cpu = cpu_baseline(shape, branches, x_np, min(args.cpu_rows, shape.m))
+
+    out = {
+        "metric": "decode tokens/s per layer",
+        "value": round(batch * args.steps / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 operands, f32 accumulate",
+        "data": "synthetic",
+        "config": {"workload": "Llama2-7B-shaped MLP up-projection 4096->11008, 2 branches r=1472 "
+                               "(~1.0 BPW), batch-1 decode",
+                   "m": shape.m, "n": shape.n, "ranks": list(shape.ranks), "batch": batch,
+                   "distinct_layer_copies": ncopies, "copies_bytes": ncopies * per_copy},
+        "parity": {"rel_l2": rel_l2, "max_err_over_rms": max_rms},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

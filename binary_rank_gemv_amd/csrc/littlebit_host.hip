@@ -1,0 +1,289 @@
+// C ABI of the LittleBit gfx950 library: argument validation, workspace
+// layout and kernel dispatch.  No allocation, no synchronisation.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "littlebit.h"
+#include "lb_common.h"
+
+hipError_t lb_launch_pack(const void* latent, int is_f16, long ld, int transpose, int R, int K,
+                          void* dst, hipStream_t stream);
+hipError_t lb_launch_decode(const LbDecodeArgs& args, int chunk_units, hipStream_t stream);
+
+namespace {
+
+thread_local std::string g_last_error;
+
+lb_status fail(lb_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+lb_status hip_fail(hipError_t e, const char* what) {
+  return fail(LB_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+constexpr int kMaxRank = 4096;
+constexpr int kMaxN = 32768;
+constexpr int kDecodeMaxBatch = 16;
+constexpr size_t kDecodeLdsBudget = 56 * 1024;
+
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Per-layer workspace: z rows (fp16, batch x zs) then the V-tile sums.
+struct LayerWs {
+  int zs;             // halves per z row
+  int zoff[2];
+  int csum_off[2];
+  size_t z_bytes, csum_bytes;
+};
+
+LayerWs layer_ws(const lb_layer& L, const int* sel, int nsel, int64_t batch) {
+  LayerWs w{};
+  int zs = 0, cs = 0;
+  for (int i = 0; i < nsel; ++i) {
+    const lb_branch& B = L.br[sel[i]];
+    w.zoff[i] = zs;
+    w.csum_off[i] = cs;
+    zs += 64 * lb16_units(B.r);
+    cs += 16 * ((B.r + 15) / 16);
+  }
+  w.zs = zs;
+  w.z_bytes = round_up((size_t)batch * zs * sizeof(uint16_t), 256);
+  w.csum_bytes = round_up((size_t)cs * sizeof(float), 256);
+  return w;
+}
+
+constexpr size_t kWsHeader = 256;  // reserved (synchronisation words)
+
+lb_status check_layer(const lb_layer* L, uint32_t mask, int* sel, int* nsel, const char* name) {
+  if (!L) return fail(LB_ERR_INVALID_ARG, "%s: layer pointer is NULL", name);
+  if (L->m < 1 || L->n < 1) return fail(LB_ERR_INVALID_ARG, "%s: m=%d n=%d must be >= 1", name, L->m, L->n);
+  if (L->n > kMaxN) return fail(LB_ERR_UNSUPPORTED, "%s: n=%d exceeds %d", name, L->n, kMaxN);
+  if (L->nbranches < 1 || L->nbranches > 2)
+    return fail(LB_ERR_INVALID_ARG, "%s: nbranches=%d must be 1 or 2", name, L->nbranches);
+  if (mask == 0 || (mask & ~3u)) return fail(LB_ERR_INVALID_ARG, "%s: branch_mask=%u must be 1, 2 or 3", name, mask);
+  *nsel = 0;
+  for (int b = 0; b < 2; ++b) {
+    if (!(mask & (1u << b))) continue;
+    if (b >= L->nbranches)
+      return fail(LB_ERR_INVALID_ARG, "%s: branch_mask selects branch %d but nbranches=%d", name, b, L->nbranches);
+    const lb_branch& B = L->br[b];
+    if (B.r < 1) return fail(LB_ERR_INVALID_ARG, "%s: branch %d rank %d must be >= 1", name, b, B.r);
+    if (B.r > kMaxRank) return fail(LB_ERR_UNSUPPORTED, "%s: branch %d rank %d exceeds %d", name, b, B.r, kMaxRank);
+    if (!B.v_bits || !B.u_bits || !B.h || !B.l || !B.g)
+      return fail(LB_ERR_INVALID_ARG, "%s: branch %d has a NULL pointer", name, b);
+    if (!aligned(B.v_bits, 16) || !aligned(B.u_bits, 16))
+      return fail(LB_ERR_INVALID_ARG, "%s: branch %d packed factors must be 16-byte aligned", name, b);
+    if (!aligned(B.h, 16) || !aligned(B.l, 16) || !aligned(B.g, 16))
+      return fail(LB_ERR_INVALID_ARG, "%s: branch %d scale vectors must be 16-byte aligned", name, b);
+    sel[(*nsel)++] = b;
+  }
+  return LB_OK;
+}
+
+int decode_chunk_units(int64_t batch, int n) {
+  const int nu = lb16_units(n);
+  int cu = (int)((kDecodeLdsBudget / sizeof(uint16_t) / batch - 8) / 64);
+  cu = cu / 8 * 8;
+  if (cu < 8) cu = 8;
+  return cu >= nu ? nu : cu;
+}
+
+void fill_layer_args(LbLayerArgs& a, const lb_layer& L, const int* sel, int nsel, const LayerWs& w,
+                     uint8_t* base, const uint16_t* x, long ldx, uint16_t* y, long ldy) {
+  memset(&a, 0, sizeof a);
+  a.nb = nsel;
+  a.m = L.m;
+  a.n = L.n;
+  a.x = x;
+  a.ldx = ldx;
+  a.y = y;
+  a.ldy = ldy;
+  a.z = reinterpret_cast<uint16_t*>(base);
+  a.csum = reinterpret_cast<float*>(base + w.z_bytes);
+  a.zs = w.zs;
+  for (int i = 0; i < nsel; ++i) {
+    const lb_branch& B = L.br[sel[i]];
+    a.br[i].vbits = static_cast<const uint8_t*>(B.v_bits);
+    a.br[i].ubits = static_cast<const uint8_t*>(B.u_bits);
+    a.br[i].h = B.h;
+    a.br[i].l = B.l;
+    a.br[i].g = B.g;
+    a.br[i].r = B.r;
+    a.br[i].zoff = w.zoff[i];
+    a.br[i].csum_off = w.csum_off[i];
+  }
+}
+
+// Launch the decode kernels for up to 16 tokens over `nl` prepared layers.
+lb_status run_decode(LbLayerArgs* layers, int nl, int batch, hipStream_t stream) {
+  LbDecodeArgs args;
+  memset(&args, 0, sizeof args);
+  args.nlayers = nl;
+  args.batch = batch;
+  int vt = 0, ut = 0, maxn = 1;
+  for (int i = 0; i < nl; ++i) {
+    args.L[i] = layers[i];
+    for (int b = 0; b < layers[i].nb; ++b) {
+      args.L[i].vt_begin[b] = vt;
+      vt += (layers[i].br[b].r + 15) / 16;
+    }
+    args.L[i].ut_begin = ut;
+    ut += (layers[i].m + 15) / 16;
+    if (layers[i].n > maxn) maxn = layers[i].n;
+  }
+  args.nvt = vt;
+  args.nut = ut;
+  const int cu = decode_chunk_units(batch, maxn);
+  hipError_t e = lb_launch_decode(args, cu, stream);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return LB_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t littlebit_packed_bytes(int64_t R, int64_t K) {
+  if (R <= 0 || K <= 0) return 0;
+  return (size_t)(16 * ((R + 15) / 16)) * (size_t)(64 * ((K + 63) / 64)) / 8;
+}
+
+lb_status littlebit_pack(const void* latent, lb_dtype dtype, int64_t rows, int64_t cols, int64_t ld,
+                         int transpose, void* dst, void* stream) {
+  if (!latent || !dst) return fail(LB_ERR_INVALID_ARG, "littlebit_pack: NULL pointer");
+  if (rows < 1 || cols < 1) return fail(LB_ERR_INVALID_ARG, "littlebit_pack: rows=%lld cols=%lld", (long long)rows, (long long)cols);
+  if (ld < cols) return fail(LB_ERR_INVALID_ARG, "littlebit_pack: ld=%lld < cols=%lld", (long long)ld, (long long)cols);
+  if (dtype != LB_F32 && dtype != LB_F16) return fail(LB_ERR_INVALID_ARG, "littlebit_pack: bad dtype %d", (int)dtype);
+  if (transpose != 0 && transpose != 1) return fail(LB_ERR_INVALID_ARG, "littlebit_pack: transpose must be 0 or 1");
+  if (!aligned(dst, 4)) return fail(LB_ERR_INVALID_ARG, "littlebit_pack: dst must be 4-byte aligned");
+  const int64_t R = transpose ? cols : rows, K = transpose ? rows : cols;
+  if (R > (1LL << 30) || K > (1LL << 24)) return fail(LB_ERR_UNSUPPORTED, "littlebit_pack: factor too large");
+  hipError_t e = lb_launch_pack(latent, dtype == LB_F16, (long)ld, transpose, (int)R, (int)K, dst,
+                                (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "littlebit_pack launch");
+  return LB_OK;
+}
+
+size_t littlebit_linear_workspace_bytes(const lb_layer* L, int64_t batch) {
+  int sel[2], nsel = 0;
+  if (batch < 1 || !L || L->nbranches < 1 || L->nbranches > 2) return 0;
+  if (check_layer(L, (1u << L->nbranches) - 1, sel, &nsel, "workspace") != LB_OK) return 0;
+  const int64_t rows = batch < kDecodeMaxBatch ? batch : kDecodeMaxBatch;
+  const LayerWs w = layer_ws(*L, sel, nsel, rows);
+  return kWsHeader + w.z_bytes + w.csum_bytes;
+}
+
+lb_status littlebit_linear_fwd(const lb_layer* L, uint32_t branch_mask, const uint16_t* x, int64_t batch,
+                               int64_t ldx, uint16_t* y, int64_t ldy, void* ws, size_t ws_bytes,
+                               uint32_t flags, void* stream) {
+  int sel[2], nsel = 0;
+  lb_status st = check_layer(L, branch_mask, sel, &nsel, "littlebit_linear_fwd");
+  if (st != LB_OK) return st;
+  if (!x || !y) return fail(LB_ERR_INVALID_ARG, "littlebit_linear_fwd: x or y is NULL");
+  if (batch < 1) return fail(LB_ERR_INVALID_ARG, "littlebit_linear_fwd: batch=%lld must be >= 1", (long long)batch);
+  if (ldx < L->n || ldy < L->m) return fail(LB_ERR_INVALID_ARG, "littlebit_linear_fwd: ldx/ldy smaller than n/m");
+  if (!aligned(x, 2) || !aligned(y, 2)) return fail(LB_ERR_INVALID_ARG, "littlebit_linear_fwd: x and y must be 2-byte aligned");
+  if (flags > LB_PATH_PREFILL) return fail(LB_ERR_INVALID_ARG, "littlebit_linear_fwd: unknown flags %u", flags);
+  if (flags == LB_PATH_DECODE && batch > kDecodeMaxBatch)
+    return fail(LB_ERR_INVALID_ARG, "littlebit_linear_fwd: decode path takes at most %d tokens", kDecodeMaxBatch);
+  if (!ws) return fail(LB_ERR_WORKSPACE, "littlebit_linear_fwd: workspace is NULL");
+  if (!aligned(ws, 256)) return fail(LB_ERR_WORKSPACE, "littlebit_linear_fwd: workspace must be 256-byte aligned");
+  const int64_t rows = batch < kDecodeMaxBatch ? batch : kDecodeMaxBatch;
+  const LayerWs w = layer_ws(*L, sel, nsel, rows);
+  const size_t need = kWsHeader + w.z_bytes + w.csum_bytes;
+  if (ws_bytes < need)
+    return fail(LB_ERR_WORKSPACE, "littlebit_linear_fwd: workspace has %zu bytes, needs %zu", ws_bytes, need);
+
+  uint8_t* base = static_cast<uint8_t*>(ws) + kWsHeader;
+  for (int64_t t0 = 0; t0 < batch; t0 += kDecodeMaxBatch) {
+    const int nb = (int)((batch - t0) < kDecodeMaxBatch ? (batch - t0) : kDecodeMaxBatch);
+    LbLayerArgs la;
+    fill_layer_args(la, *L, sel, nsel, w, base, x + t0 * ldx, (long)ldx, y + t0 * ldy, (long)ldy);
+    st = run_decode(&la, 1, nb, (hipStream_t)stream);
+    if (st != LB_OK) return st;
+  }
+  return LB_OK;
+}
+
+size_t littlebit_block_workspace_bytes(const lb_layer L[7], int64_t batch) {
+  if (!L || batch < 1) return 0;
+  const int64_t rows = batch < kDecodeMaxBatch ? batch : kDecodeMaxBatch;
+  size_t total = kWsHeader;
+  for (int i = 0; i < 7; ++i) {
+    int sel[2], nsel = 0;
+    if (L[i].nbranches < 1 || L[i].nbranches > 2) return 0;
+    if (check_layer(&L[i], (1u << L[i].nbranches) - 1, sel, &nsel, "workspace") != LB_OK) return 0;
+    const LayerWs w = layer_ws(L[i], sel, nsel, rows);
+    total += w.z_bytes + w.csum_bytes;
+  }
+  return total;
+}
+
+lb_status littlebit_block_fwd(const lb_layer L[7], const uint16_t* x_qkv, const uint16_t* x_o,
+                              const uint16_t* x_gu, const uint16_t* x_down, uint16_t* const y[7],
+                              int64_t batch, void* ws, size_t ws_bytes, void* stream) {
+  if (!L || !y) return fail(LB_ERR_INVALID_ARG, "littlebit_block_fwd: NULL layer or output array");
+  if (!x_qkv || !x_o || !x_gu || !x_down) return fail(LB_ERR_INVALID_ARG, "littlebit_block_fwd: NULL input");
+  if (batch < 1) return fail(LB_ERR_INVALID_ARG, "littlebit_block_fwd: batch must be >= 1");
+  const uint16_t* xs[7] = {x_qkv, x_qkv, x_qkv, x_o, x_gu, x_gu, x_down};
+  int sel[7][2], nsel[7];
+  LayerWs w[7];
+  const int64_t rows = batch < kDecodeMaxBatch ? batch : kDecodeMaxBatch;
+  size_t need = kWsHeader;
+  for (int i = 0; i < 7; ++i) {
+    if (L[i].nbranches < 1 || L[i].nbranches > 2)
+      return fail(LB_ERR_INVALID_ARG, "littlebit_block_fwd: layer %d nbranches=%d", i, L[i].nbranches);
+    lb_status st = check_layer(&L[i], (1u << L[i].nbranches) - 1, sel[i], &nsel[i], "littlebit_block_fwd");
+    if (st != LB_OK) return st;
+    if (!y[i]) return fail(LB_ERR_INVALID_ARG, "littlebit_block_fwd: y[%d] is NULL", i);
+    if (!aligned(xs[i], 2) || !aligned(y[i], 2))
+      return fail(LB_ERR_INVALID_ARG, "littlebit_block_fwd: inputs and outputs must be 2-byte aligned");
+    w[i] = layer_ws(L[i], sel[i], nsel[i], rows);
+    need += w[i].z_bytes + w[i].csum_bytes;
+  }
+  if (L[0].n != L[1].n || L[0].n != L[2].n || L[4].n != L[5].n)
+    return fail(LB_ERR_INVALID_ARG, "littlebit_block_fwd: q/k/v and gate/up must share their input size");
+  if (!ws) return fail(LB_ERR_WORKSPACE, "littlebit_block_fwd: workspace is NULL");
+  if (!aligned(ws, 256)) return fail(LB_ERR_WORKSPACE, "littlebit_block_fwd: workspace must be 256-byte aligned");
+  if (ws_bytes < need) return fail(LB_ERR_WORKSPACE, "littlebit_block_fwd: workspace has %zu bytes, needs %zu", ws_bytes, need);
+
+  for (int64_t t0 = 0; t0 < batch; t0 += kDecodeMaxBatch) {
+    const int nb = (int)((batch - t0) < kDecodeMaxBatch ? (batch - t0) : kDecodeMaxBatch);
+    LbLayerArgs la[7];
+    uint8_t* base = static_cast<uint8_t*>(ws) + kWsHeader;
+    for (int i = 0; i < 7; ++i) {
+      fill_layer_args(la[i], L[i], sel[i], nsel[i], w[i], base, xs[i] + t0 * L[i].n, L[i].n,
+                      y[i] + t0 * L[i].m, L[i].m);
+      base += w[i].z_bytes + w[i].csum_bytes;
+    }
+    lb_status st = run_decode(la, 7, nb, (hipStream_t)stream);
+    if (st != LB_OK) return st;
+  }
+  return LB_OK;
+}
+
+const char* littlebit_status_string(lb_status s) {
+  switch (s) {
+    case LB_OK: return "LB_OK";
+    case LB_ERR_INVALID_ARG: return "LB_ERR_INVALID_ARG: invalid argument";
+    case LB_ERR_UNSUPPORTED: return "LB_ERR_UNSUPPORTED: sizes beyond the supported range";
+    case LB_ERR_WORKSPACE: return "LB_ERR_WORKSPACE: workspace missing or too small";
+    case LB_ERR_HIP: return "LB_ERR_HIP: HIP runtime error";
+  }
+  return "unknown lb_status";
+}
+
+const char* littlebit_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,236 @@
+"""ctypes binding of ``include/littlebit.h`` (argument marshalling only).
+
+Every step of the layer runs in the HIP library ``_lib/liblittlebit.so``;
+PyTorch provides device memory and the current stream.  Importing this module
+raises if the library has not been built (``python -m
+binary_rank_gemv_amd.build``) -- there is no fallback path.
+
+The functions keep the C names:
+
+* ``littlebit_pack(latent, transpose)`` -> packed uint8 tensor
+* ``littlebit_linear_fwd(layer, x, branch_mask=3, path=LB_PATH_AUTO)`` -> y
+* ``littlebit_block_fwd(layers, x_qkv, x_o, x_gu, x_down)`` -> list of 7 y
+* ``littlebit_packed_bytes``, ``littlebit_linear_workspace_bytes``,
+  ``littlebit_block_workspace_bytes``, ``littlebit_status_string``,
+  ``littlebit_last_error``
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass, field
+from typing import List, Optional, Sequence
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "liblittlebit.so")
+
+LB_OK, LB_ERR_INVALID_ARG, LB_ERR_UNSUPPORTED, LB_ERR_WORKSPACE, LB_ERR_HIP = 0, -1, -2, -3, -4
+LB_F32, LB_F16 = 0, 1
+LB_PATH_AUTO, LB_PATH_DECODE, LB_PATH_PREFILL = 0, 1, 2
+
+EXPORTED = (
+    "littlebit_packed_bytes", "littlebit_pack", "littlebit_linear_workspace_bytes",
+    "littlebit_linear_fwd", "littlebit_block_workspace_bytes", "littlebit_block_fwd",
+    "littlebit_status_string", "littlebit_last_error",
+)
+
+
+class LittleBitError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} [status {status}]")
+        self.status = status
+
+
+class _Branch(ctypes.Structure):
+    _fields_ = [("v_bits", ctypes.c_void_p), ("u_bits", ctypes.c_void_p),
+                ("h", ctypes.c_void_p), ("l", ctypes.c_void_p), ("g", ctypes.c_void_p),
+                ("r", ctypes.c_int32)]
+
+
+class _Layer(ctypes.Structure):
+    _fields_ = [("m", ctypes.c_int32), ("n", ctypes.c_int32), ("nbranches", ctypes.c_int32),
+                ("br", _Branch * 2)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m binary_rank_gemv_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, u32, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32, ctypes.c_int, ctypes.c_size_t
+    lib.littlebit_packed_bytes.argtypes = [i64, i64]
+    lib.littlebit_packed_bytes.restype = sz
+    lib.littlebit_pack.argtypes = [vp, i32, i64, i64, i64, i32, vp, vp]
+    lib.littlebit_pack.restype = i32
+    lib.littlebit_linear_workspace_bytes.argtypes = [ctypes.POINTER(_Layer), i64]
+    lib.littlebit_linear_workspace_bytes.restype = sz
+    lib.littlebit_linear_fwd.argtypes = [ctypes.POINTER(_Layer), u32, vp, i64, i64, vp, i64, vp, sz, u32, vp]
+    lib.littlebit_linear_fwd.restype = i32
+    lib.littlebit_block_workspace_bytes.argtypes = [ctypes.POINTER(_Layer), i64]
+    lib.littlebit_block_workspace_bytes.restype = sz
+    lib.littlebit_block_fwd.argtypes = [ctypes.POINTER(_Layer), vp, vp, vp, vp, ctypes.POINTER(vp), i64, vp, sz, vp]
+    lib.littlebit_block_fwd.restype = i32
+    lib.littlebit_status_string.argtypes = [i32]
+    lib.littlebit_status_string.restype = ctypes.c_char_p
+    lib.littlebit_last_error.argtypes = []
+    lib.littlebit_last_error.restype = ctypes.c_char_p
+    return lib
+
+
+LIB = _load()
+
+
+def _check(status: int):
+    if status != LB_OK:
+        raise LittleBitError(status, LIB.littlebit_last_error().decode())
+
+
+def _stream_ptr(stream: Optional[torch.cuda.Stream] = None) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def _ptr(t: torch.Tensor) -> int:
+    return int(t.data_ptr())
+
+
+# ------------------------------------------------------------------- wrappers
+
+def littlebit_packed_bytes(R: int, K: int) -> int:
+    return int(LIB.littlebit_packed_bytes(R, K))
+
+
+def littlebit_status_string(status: int) -> str:
+    return LIB.littlebit_status_string(status).decode()
+
+
+def littlebit_last_error() -> str:
+    return LIB.littlebit_last_error().decode()
+
+
+def littlebit_pack(latent: torch.Tensor, transpose: bool, stream=None) -> torch.Tensor:
+    """Pack sign(latent) (transpose=False) or sign(latent)^T (transpose=True)."""
+    if latent.dim() != 2 or not latent.is_cuda or latent.stride(1) != 1:
+        raise ValueError("latent must be a 2-D CUDA tensor with unit column stride")
+    dtype = {torch.float32: LB_F32, torch.float16: LB_F16}.get(latent.dtype)
+    if dtype is None:
+        raise ValueError("latent must be float32 or float16")
+    rows, cols = latent.shape
+    R, K = (cols, rows) if transpose else (rows, cols)
+    out = torch.empty(littlebit_packed_bytes(R, K), dtype=torch.uint8, device=latent.device)
+    _check(LIB.littlebit_pack(_ptr(latent), dtype, rows, cols, latent.stride(0), int(transpose),
+                              _ptr(out), _stream_ptr(stream)))
+    return out
+
+
+@dataclass
+class LittleBitBranch:
+    v_bits: torch.Tensor
+    u_bits: torch.Tensor
+    h: torch.Tensor
+    l: torch.Tensor
+    g: torch.Tensor
+    r: int
+
+
+@dataclass
+class LittleBitLayer:
+    """Device-resident packed layer (keeps the tensors the C struct points to)."""
+    m: int
+    n: int
+    branches: List[LittleBitBranch] = field(default_factory=list)
+
+    @staticmethod
+    def from_latents(branches: Sequence[dict], device="cuda") -> "LittleBitLayer":
+        """branches: dicts with U (m x r), V (n x r) latents and fp16 h, l, g (numpy or torch)."""
+        out = []
+        m = n = None
+        for br in branches:
+            U = torch.as_tensor(br["U"]).to(device).contiguous()
+            V = torch.as_tensor(br["V"]).to(device).contiguous()
+            m, r = U.shape
+            n = V.shape[0]
+            scales = {k: torch.as_tensor(br[k]).to(device=device, dtype=torch.float16).contiguous()
+                      for k in ("h", "l", "g")}
+            out.append(LittleBitBranch(v_bits=littlebit_pack(V, transpose=True),
+                                       u_bits=littlebit_pack(U, transpose=False),
+                                       r=int(r), **scales))
+        return LittleBitLayer(m=int(m), n=int(n), branches=out)
+
+    def c_struct(self) -> _Layer:
+        s = _Layer()
+        s.m, s.n, s.nbranches = self.m, self.n, len(self.branches)
+        for i, b in enumerate(self.branches):
+            s.br[i] = _Branch(_ptr(b.v_bits), _ptr(b.u_bits), _ptr(b.h), _ptr(b.l), _ptr(b.g), b.r)
+        return s
+
+
+class Workspace:
+    """Zero-initialised device workspace, grown on demand (one per stream)."""
+
+    def __init__(self):
+        self._bufs = {}
+
+    def get(self, nbytes: int, device: torch.device, stream_ptr: int) -> torch.Tensor:
+        key = (str(device), stream_ptr)
+        buf = self._bufs.get(key)
+        if buf is None or buf.numel() < nbytes:
+            buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+            self._bufs[key] = buf
+        return buf
+
+
+_WS = Workspace()
+
+
+def littlebit_linear_workspace_bytes(layer: LittleBitLayer, batch: int) -> int:
+    return int(LIB.littlebit_linear_workspace_bytes(ctypes.byref(layer.c_struct()), batch))
+
+
+def littlebit_block_workspace_bytes(layers: Sequence[LittleBitLayer], batch: int) -> int:
+    arr = (_Layer * 7)(*[l.c_struct() for l in layers])
+    return int(LIB.littlebit_block_workspace_bytes(arr, batch))
+
+
+def littlebit_linear_fwd(layer: LittleBitLayer, x: torch.Tensor, branch_mask: int = 3,
+                         path: int = LB_PATH_AUTO, out: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """y = layer(x) for x of shape (batch, n) fp16 on the GPU."""
+    if x.dim() != 2 or x.dtype != torch.float16 or not x.is_cuda or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D CUDA float16 tensor with unit column stride")
+    batch = x.shape[0]
+    if branch_mask == 3 and len(layer.branches) == 1:
+        branch_mask = 1
+    y = out if out is not None else torch.empty((batch, layer.m), dtype=torch.float16, device=x.device)
+    s = layer.c_struct()
+    sp = _stream_ptr(stream)
+    need = int(LIB.littlebit_linear_workspace_bytes(ctypes.byref(s), batch))
+    ws = workspace if workspace is not None else _WS.get(need, x.device, sp)
+    _check(LIB.littlebit_linear_fwd(ctypes.byref(s), branch_mask, _ptr(x), batch, x.stride(0),
+                                    _ptr(y), y.stride(0), _ptr(ws), ws.numel(), path, sp))
+    return y
+
+
+def littlebit_block_fwd(layers: Sequence[LittleBitLayer], x_qkv: torch.Tensor, x_o: torch.Tensor,
+                        x_gu: torch.Tensor, x_down: torch.Tensor,
+                        outs: Optional[Sequence[torch.Tensor]] = None,
+                        workspace: Optional[torch.Tensor] = None, stream=None) -> List[torch.Tensor]:
+    """The seven projections (q, k, v, o, gate, up, down) of one decoder block."""
+    if len(layers) != 7:
+        raise ValueError("a block has exactly 7 projections")
+    xs = (x_qkv, x_qkv, x_qkv, x_o, x_gu, x_gu, x_down)
+    batch = x_qkv.shape[0]
+    for lay, xx in zip(layers, xs):
+        if xx.shape != (batch, lay.n) or xx.dtype != torch.float16 or not xx.is_contiguous():
+            raise ValueError("block inputs must be contiguous fp16 (batch, n) tensors")
+    ys = list(outs) if outs is not None else [
+        torch.empty((batch, lay.m), dtype=torch.float16, device=x_qkv.device) for lay in layers]
+    arr = (_Layer * 7)(*[l.c_struct() for l in layers])
+    yptrs = (ctypes.c_void_p * 7)(*[_ptr(y) for y in ys])
+    sp = _stream_ptr(stream)
+    need = int(LIB.littlebit_block_workspace_bytes(arr, batch))
+    ws = workspace if workspace is not None else _WS.get(need, x_qkv.device, sp)
+    _check(LIB.littlebit_block_fwd(arr, _ptr(x_qkv), _ptr(x_o), _ptr(x_gu), _ptr(x_down), yptrs,
+                                   batch, _ptr(ws), ws.numel(), sp))
+    return ys
