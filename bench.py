@@ -116,51 +116,54 @@ def main():
     rel_l2 = float(np.linalg.norm(yg - yr) / np.linalg.norm(yr))
     max_rms = float(np.max(np.abs(yg - yr)) / np.sqrt(np.mean(yr ** 2)))
 
-    # capture one cycle over the copies, plus a remainder graph
-    def capture(nc):
-        gr = torch.cuda.CUDAGraph()
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            for c in copies[:nc]:
-                lb.littlebit_linear_fwd(c, x, out=y, workspace=ws)
-            torch.cuda.synchronize()
-            with torch.cuda.graph(gr, stream=s):
+    def time_path(path):
+        """Capture one cycle over the copies (plus a remainder) and time `steps` calls."""
+        def capture(nc):
+            gr = torch.cuda.CUDAGraph()
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
                 for c in copies[:nc]:
-                    lb.littlebit_linear_fwd(c, x, out=y, workspace=ws)
-        torch.cuda.current_stream().wait_stream(s)
-        return gr
+                    lb.littlebit_linear_fwd(c, x, out=y, workspace=ws, path=path)
+                torch.cuda.synchronize()
+                with torch.cuda.graph(gr, stream=s):
+                    for c in copies[:nc]:
+                        lb.littlebit_linear_fwd(c, x, out=y, workspace=ws, path=path)
+            torch.cuda.current_stream().wait_stream(s)
+            return gr
 
-    full = capture(ncopies)
+        graphs = {ncopies: capture(ncopies)}
+        for k in {args.steps % ncopies, args.warmup % ncopies} - {0}:
+            graphs[k] = capture(k)
 
-    def run(steps):
-        reps, rem = divmod(steps, ncopies)
-        for _ in range(reps):
-            full.replay()
-        if rem:
-            capture_rem[rem].replay()
+        def run(steps):
+            reps, rem = divmod(steps, ncopies)
+            for _ in range(reps):
+                graphs[ncopies].replay()
+            if rem:
+                graphs[rem].replay()
 
-    capture_rem = {}
-    for k in {args.steps % ncopies, args.warmup % ncopies} - {0}:
-        capture_rem[k] = capture(k)
+        run(args.warmup)
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        run(args.steps)
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end)
 
-    run(args.warmup)
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    run(args.steps)
-    end.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end)
+    ms_two = time_path(lb.LB_DECODE_TWO_LAUNCHES)
+    ms = time_path(lb.LB_PATH_AUTO)
     ms_per_step = ms / args.steps
 
     abytes = algorithmic_bytes(shape.m, shape.n, shape.ranks, batch)
     achieved = abytes / (ms_per_step * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "lb_decode_vpass + lb_decode_upass (two launches per call)",
+                "kernel": "lb_decode_kernel<2> (one launch per call: V pass, grid barrier, U pass)",
                 "algorithmic_bytes_per_call": abytes,
-                "avg_call_us": round(ms_per_step * 1e3, 3)}
+                "avg_call_us": round(ms_per_step * 1e3, 3),
+                "two_launch_variant_us": round(ms_two / args.steps * 1e3, 3)}
 
     cpu = None
     if args.cpu_rows > 0:

@@ -2,240 +2,669 @@
 //
 // Per branch (explainx.ai explainer, "How it works" items 1-3):
 //   u = g*x (fp16), t = sign(V)^T u, z = l*t (fp16), s = sign(U) z, y = sum_b h_b*s_b.
-// Each 16-row tile of a packed factor is one 16x16x32 matrix-core operand
-// stream: tokens fill the 16 columns, 4 waves split the reduction, and the
-// signs are expanded in registers by lb16_step_operand (one shift and one mask
-// per two values).  Activations in the "negated class" (k & 2) are stored
-// negated and their per-token sum is added back (t = acc + C_u, s = acc + D).
+// Each 16-row tile of a packed factor is a stream of 16x16x32 matrix-core
+// steps: tokens fill the 16 columns, the signs are expanded in registers by
+// lb16_step_operand (one shift and one and-or per two values).  Activations
+// in the "negated class" (k & 2) are stored negated and their per-token sum
+// is added back.  Operand columns of absent tokens read the last token's
+// data; those output columns are never stored, so operand loads are
+// unconditional.
+//
+// One call = phase A (V pass over every 16-row tile of every sign(V)^T,
+// giving z) then phase B (U pass over every 16-row output tile, giving y).
+// Phase B needs all of z.  Either the phases are two launches, or one launch
+// of exactly as many 512-thread workgroups as are resident at once: then z
+// is stored as 64-bit words [32-bit call tag | two fp16 values] with
+// device-coherent stores, and phase B polls its z words until every tag
+// equals this call's tag, so there is no separate grid barrier.  The tag is
+// one more than a per-workgroup call counter in the workspace header, read at
+// kernel start and incremented by the workgroup as its last action (calls on
+// one stream run one after another, so every workgroup reads the same value).
+// Every word a call polls is written by that same call, so a stale word could
+// only pass if its address went unwritten for a multiple of 2^32 calls.  Each
+// workgroup issues the loads of its phase-B sign words and row scales during
+// phase A, so their latency overlaps phase A.
 #include "lb_common.h"
+
+#define LB_WAVES 8                    // waves per workgroup (2 per SIMD)
+#define LB_THREADS (64 * LB_WAVES)
+#define LB_MAXPV 8                    // V-pass pairs per wave held in registers
+#define LB_MAXT 3                     // phase-B tiles whose sign words are prefetched
+#define LB_MAXPW 4                    // phase-B pairs per wave held in registers
+#define LB_MAX_GRID 256               // workgroups of the single launch (one counter each)
+#define LB_SPIN_LIMIT (1 << 20)
+
+// workspace header (bytes): one 64-bit call counter per workgroup of the
+// single launch, then an error word set when a poll gives up.
+#define LB_SYNC_CTR 0  // + 8 * workgroup
+#define LB_SYNC_ERR 2048
 
 namespace {
 
-__device__ inline void find_vtile(const LbDecodeArgs& A, int t, int& li, int& b, int& tile) {
-  li = 0; b = 0; tile = 0;
-  for (int i = 0; i < A.nlayers; ++i)
-    for (int bb = 0; bb < A.L[i].nb; ++bb) {
-      const int nt = (A.L[i].br[bb].r + 15) >> 4;
-      const int beg = A.L[i].vt_begin[bb];
-      if (t >= beg && t < beg + nt) { li = i; b = bb; tile = t - beg; return; }
-    }
+__device__ inline uint32_t ld32c(const void* p) {
+  return __hip_atomic_load(reinterpret_cast<uint32_t*>(const_cast<void*>(p)), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void st32c(void* p, uint32_t v) {
+  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void st64c(void* p, uint64_t v) {
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void add64c_noret(void* p, uint64_t v) {
+  (void)__hip_atomic_fetch_add(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ inline void find_utile(const LbDecodeArgs& A, int t, int& li, int& tile) {
-  li = 0; tile = 0;
-  for (int i = 0; i < A.nlayers; ++i) {
-    const int nt = (A.L[i].m + 15) >> 4;
-    if (t >= A.L[i].ut_begin && t < A.L[i].ut_begin + nt) { li = i; tile = t - A.L[i].ut_begin; return; }
+// Raw buffer resource over `bytes` bytes (loads beyond return 0).
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+// 16 bytes (two tagged z words) with a device-coherent (sc1) load.
+__device__ inline u32x4 ld_tagged2(__amdgpu_buffer_rsrc_t rs, int byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(rs, byte_off, 0, 16 /* sc1 */);
+}
+
+// Compiler-only barrier: memory may have changed here, so loads after it are
+// neither hoisted above it nor merged with loads before it.
+__device__ inline void compiler_memory_barrier() { __asm__ volatile("" ::: "memory"); }
+
+// Index of the calling wave in its workgroup, as a wave-uniform (scalar) value.
+__device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// Hands `v` to the compiler as if modified here, so work that depends on it
+// (and the wait for the load that produced it) is not hoisted above this point.
+__device__ inline uint32_t late(uint32_t v) {
+  __asm__ volatile("" : "+v"(v));
+  return v;
+}
+// Flattened view of one layer: branch fields are selected with `b ? x1 : x0`
+// so no per-branch array is indexed at run time.
+struct LayerView {
+  const uint8_t *vb0, *vb1, *ub0, *ub1;
+  const uint16_t *h0, *h1, *l0, *l1, *g0, *g1;
+  int r0, r1, zoff0, zoff1;
+  int nb, m, n, zs;
+  const uint16_t* x;
+  long ldx;
+  uint16_t* y;
+  long ldy;
+  uint64_t* z;
+};
+
+__device__ __forceinline__ LayerView layer_view(const LbLayerArgs& L) {
+  LayerView v;
+  v.vb0 = L.br[0].vbits; v.vb1 = L.br[1].vbits;
+  v.ub0 = L.br[0].ubits; v.ub1 = L.br[1].ubits;
+  v.h0 = L.br[0].h; v.h1 = L.br[1].h;
+  v.l0 = L.br[0].l; v.l1 = L.br[1].l;
+  v.g0 = L.br[0].g; v.g1 = L.br[1].g;
+  v.r0 = L.br[0].r; v.r1 = L.br[1].r;
+  v.zoff0 = L.br[0].zoff; v.zoff1 = L.br[1].zoff;
+  v.nb = L.nb; v.m = L.m; v.n = L.n; v.zs = L.zs;
+  v.x = L.x; v.ldx = L.ldx; v.y = L.y; v.ldy = L.ldy; v.z = L.z;
+  return v;
+}
+
+// Mapping of global tile indices to layers, kept in registers.
+struct TileMap {
+  int nl;
+  int ue[LB_MAX_LAYERS];      // cumulative U-tile ends
+  int ve[2 * LB_MAX_LAYERS];  // cumulative V-tile ends per (layer, branch)
+};
+
+__device__ __forceinline__ void load_map(const LbDecodeArgs& A, TileMap& M) {
+  M.nl = A.nlayers;
+#pragma unroll
+  for (int i = 0; i < LB_MAX_LAYERS; ++i) M.ue[i] = A.ut_end[i];
+#pragma unroll
+  for (int i = 0; i < 2 * LB_MAX_LAYERS; ++i) M.ve[i] = A.vt_end[i];
+}
+
+// Layer of global U tile t (tile index inside the layer in `tile`).
+template <bool SINGLE>
+__device__ __forceinline__ int u_layer(const TileMap& M, int t, int& tile) {
+  int li = 0, beg = 0;
+  if (!SINGLE) {
+#pragma unroll
+    for (int i = 0; i < LB_MAX_LAYERS - 1; ++i)
+      if (i < M.nl - 1 && t >= M.ue[i]) { li = i + 1; beg = M.ue[i]; }
   }
+  tile = t - beg;
+  return li;
 }
 
-// Sum over the `width` consecutive lanes that share a value (width = 1..64, power of 2).
+// Slot 2*layer + branch of global V tile t.
+template <bool SINGLE>
+__device__ __forceinline__ int v_slot(const TileMap& M, int t, int& tile) {
+  int k = 0, beg = 0;
+  const int nk = SINGLE ? 2 : 2 * LB_MAX_LAYERS;
+#pragma unroll
+  for (int q = 0; q < nk - 1; ++q)
+    if (q < 2 * M.nl - 1 && t >= M.ve[q]) { k = q + 1; beg = M.ve[q]; }
+  tile = t - beg;
+  return k;
+}
+
+// Contiguous share [beg, end) of part i: q items each, one more for parts < r.
+__device__ inline void share(int q, int r, int i, int& beg, int& end) {
+  beg = i * q + min(i, r);
+  end = beg + q + (i < r ? 1 : 0);
+}
+
+// Sum over aligned groups of `width` lanes (width = power of 2 <= 64).
 __device__ inline float seg_sum(float v, int width) {
   for (int off = 1; off < width; off <<= 1) v += __shfl_xor(v, off, 64);
   return v;
 }
 
-}  // namespace
+// Phase-B role of wave `wave` (scalar): branch and pair range.
+__device__ inline void u_role(const LayerView& L, int wave, int& b, int& p0, int& p1) {
+  if (L.nb == 2) {
+    b = wave >> 2;
+    const int np = (lb16_units(b ? L.r1 : L.r0) + 1) >> 1, w = wave & 3;
+    p0 = (np * w) >> 2;
+    p1 = (np * (w + 1)) >> 2;
+  } else {
+    b = 0;
+    const int np = (lb16_units(L.r0) + 1) >> 1;
+    p0 = (np * wave) >> 3;
+    p1 = (np * (wave + 1)) >> 3;
+  }
+}
 
-// --------------------------------------------------------------------- V pass
-// One workgroup per 16-row tile of sign(V)^T of one branch; the reduction over
-// the n inputs is cut into LDS chunks of `chunk_units` * 64 columns.
-__global__ __launch_bounds__(256) void lb_decode_vpass(LbDecodeArgs A, int chunk_units) {
-  extern __shared__ __align__(16) uint16_t u_lds[];
-  __shared__ float red[4][256];
-  __shared__ float part[256];
-  __shared__ float cu[16];
-  __shared__ float cs[256];
+// Sum of the negated-class halves (dwords 1 and 3) of an operand fragment.
+__device__ inline float negated_class_sum(f16x8 v, float acc) {
+  typedef f16 h2 __attribute__((ext_vector_type(2)));
+  const h2 one = {(f16)1.0f, (f16)1.0f};
+  const u32x4 d = __builtin_bit_cast(u32x4, v);
+  // copy the elements to scalars first: bit_cast of a vector-element lvalue
+  // reads the vector's first element with this compiler
+  const uint32_t d1 = d[1], d3 = d[3];
+  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, d1), one, acc, false);
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, d3), one, acc, false);
+}
 
-  int li, b, tile;
-  find_vtile(A, blockIdx.x, li, b, tile);
-  const int batch = A.batch;
-  const int n = A.L[li].n;
-  const long ldx = A.L[li].ldx;
-  const uint16_t* __restrict__ x = A.L[li].x;
-  const uint16_t* __restrict__ g = A.L[li].br[b].g;
-  const uint16_t* __restrict__ l = A.L[li].br[b].l;
-  const int r = A.L[li].br[b].r;
-  const int nu = lb16_units(n);
-  const uint8_t* __restrict__ tile_ptr = A.L[li].br[b].vbits + (long)tile * lb16_tile_bytes(n);
+// ------------------------------------------------------------------ phase A
+// One 16-row tile of sign(V)^T of branch b of layer L: t, then
+// z = fp16(l*t), stored (negated in the negated class) as tagged words.
+// The reduction over n runs in LDS chunks of `chunk_pairs` pairs (128 inputs
+// each, at most LB_WAVES * LB_MAXPV); each wave takes a contiguous eighth of
+// a chunk and holds all its sign words in registers.
+// With HOOK, `hook` runs after the first chunk's activations are staged (its
+// loads then queue behind this tile's sign words).  The first chunk is its
+// own copy of the code, so every wait count in it is exact.
+template <bool B>
+struct BoolTag {
+  static constexpr bool value = B;
+};
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+template <bool HOOK, class Hook>
+__device__ __forceinline__ void v_tile(const LayerView& L, int batch, int b, int tile, int chunk_pairs,
+                                       uint32_t ctr, const LbSignConsts& sc, uint16_t* u_lds,
+                                       float (*red)[256], float* part, float* cu, Hook&& hook) {
+  const int n = L.n;
+  const long ldx = L.ldx;
+  const uint16_t* __restrict__ x = L.x;
+  const uint16_t* __restrict__ g = b ? L.g1 : L.g0;
+  const int r = b ? L.r1 : L.r0;
+  const int nu = lb16_units(n), np = (nu + 1) >> 1;
+  const uint8_t* __restrict__ tile_ptr = (b ? L.vb1 : L.vb0) + (long)tile * lb16_tile_bytes(n);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int tok = lane & 15, grp = lane >> 4;
+  const int trow = min(tok, batch - 1);      // operand row read by this lane
+  const int rho = tid & 15, tk = (tid >> 4) & 15;  // epilogue role (threads < 256)
+  const int j = 16 * tile + rho;
+  // fp16 bits of l[j], loaded from an always-valid index and converted at use
+  const uint32_t lj_raw = (b ? L.l1 : L.l0)[min(j, r - 1)];
 
-  // threads per token for building u (power of two, >= 16)
   int lb = 0;
   while ((1 << lb) < batch) ++lb;
-  const int tpt = 256 >> lb;
-  const int my_tok = tid / tpt, my_sub = tid % tpt;
+  const int tpt = LB_THREADS >> lb;          // threads per token building u
+  const int my_tok = tid >> (9 - lb), my_sub = tid & (tpt - 1);
+  static_assert(LB_THREADS == 512, "token split assumes 512 threads");
+  // 16-byte loads of x and g when aligned and n % 8 == 0 (then a group of 8
+  // inputs is either wholly below n or wholly at/after it)
+  const bool fast = ((((uintptr_t)x) & 15) == 0) && ((ldx & 7) == 0) && ((n & 7) == 0);
+  const uint16_t* __restrict__ xr = x + (long)min(my_tok, batch - 1) * ldx;
   float csum_u = 0.f;
 
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int u0 = 0; u0 < nu; u0 += chunk_units) {
-    const int u1 = min(nu, u0 + chunk_units);
-    const int k0 = 64 * u0, kc = 64 * (u1 - u0);
+  // x and g of inputs k..k+7 (zero at and beyond n)
+  auto load_xg = [&](int k, uint4& xv, uint4& gv) {
+    if (fast) {
+      const int kk = min(k, n - 8);  // always-valid address; zeroed below when k >= n
+      xv = *reinterpret_cast<const uint4*>(xr + kk);
+      gv = *reinterpret_cast<const uint4*>(g + kk);
+    } else {
+      uint16_t xe[8], ge[8];
+      for (int e = 0; e < 8; ++e) {
+        xe[e] = (k + e < n) ? xr[k + e] : (uint16_t)0;
+        ge[e] = (k + e < n) ? g[k + e] : (uint16_t)0;
+      }
+      xv = *reinterpret_cast<uint4*>(xe);
+      gv = *reinterpret_cast<uint4*>(ge);
+    }
+  };
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  auto chunk = [&](int cb, auto with_hook) {
+    const int cn = min(np - cb, chunk_pairs);
+    const int pb = cb + ((cn * wave) >> 3), pe = cb + ((cn * (wave + 1)) >> 3);
+    const int k0 = 128 * cb, kc = 128 * cn;
     const int rowh = kc + 8;
-    __syncthreads();
-    // u = fp16(g*x), negated class stored negated, zero beyond n
+    // this thread's first group of activations is loaded before the sign
+    // words, so waiting for it leaves the words in flight (loads complete in
+    // issue order)
+    uint4 xv0, gv0;
+    load_xg(k0 + 8 * min(my_sub, (kc >> 3) - 1), xv0, gv0);
+    // unconditional loads (clamped to a valid pair) keep the wait counts
+    // exact; pairs beyond pe are never used
+    uint32_t words[LB_MAXPV];
+    const int plast = max(pe - 1, 0);
+#pragma unroll
+    for (int i = 0; i < LB_MAXPV; ++i) words[i] = lb16_load_pair(tile_ptr, min(pb + i, plast), lane, nu);
+
+    __syncthreads();  // previous users of u_lds are done
     if (my_tok < batch) {
+      uint4 xv = xv0, gv = gv0;
       for (int k8 = my_sub; k8 < (kc >> 3); k8 += tpt) {
         const int k = k0 + 8 * k8;
+        if (k8 != my_sub) load_xg(k, xv, gv);
+        if (fast && k >= n) xv = gv = make_uint4(0u, 0u, 0u, 0u);
+        const uint16_t* xe = reinterpret_cast<const uint16_t*>(&xv);
+        const uint16_t* ge = reinterpret_cast<const uint16_t*>(&gv);
         uint16_t vals[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const int kk = k + e;
-          float v = 0.f;
-          if (kk < n) v = h2f(g[kk]) * h2f(x[(long)my_tok * ldx + kk]);
-          const f16 hv = (f16)v;
-          if (lb16_negated_class(kk)) {
+          const f16 hv = (f16)(h2f(ge[e]) * h2f(xe[e]));
+          if (lb16_negated_class(e)) {  // k is a multiple of 8
             csum_u += (float)hv;
             vals[e] = __builtin_bit_cast(uint16_t, (f16)(-hv));
           } else {
             vals[e] = __builtin_bit_cast(uint16_t, hv);
           }
         }
-        uint16_t* dst = u_lds + my_tok * rowh + 8 * k8;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) dst[e] = vals[e];
+        *reinterpret_cast<uint4*>(u_lds + my_tok * rowh + 8 * k8) = *reinterpret_cast<uint4*>(vals);
       }
     }
+    if constexpr (decltype(with_hook)::value) hook();
     __syncthreads();
-    // this wave's pairs of the chunk
-    const int pb = u0 >> 1, pe = (u1 + 1) >> 1, np = pe - pb;
-    const int p0 = pb + (wave * np) / 4, p1 = pb + ((wave + 1) * np) / 4;
-    for (int p = p0; p < p1; ++p) {
-      const uint32_t reg = lb16_reg_word(lb16_load_pair(tile_ptr, p, lane, nu));
-      const int nsteps = (2 * p + 1 < nu) ? 4 : 2;
-      for (int st = 0; st < nsteps; ++st) {
-        const f16x8 av = lb16_step_operand(reg, st);
-        f16x8 bv = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (tok < batch)
-          bv = *reinterpret_cast<const f16x8*>(u_lds + tok * rowh + (32 * (4 * p + st) - k0) + 8 * grp);
-        acc = mfma16(av, bv, acc);
+
+    // inputs beyond n are zero in LDS, so the odd last unit's two missing
+    // steps contribute nothing and every pair runs all 4 steps; the next
+    // pair's operands are read from LDS while the current pair computes
+    const uint16_t* ub = u_lds + trow * rowh + 8 * grp - k0;
+    f16x8 bv[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) bv[st] = *reinterpret_cast<const f16x8*>(ub + 32 * (4 * pb + st));
+#pragma unroll
+    for (int i = 0; i < LB_MAXPV; ++i) {
+      const int p = pb + i;
+      if (p < pe) {
+        f16x8 bn[4];
+        const int pn = (p + 1 < pe) ? p + 1 : p;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) bn[st] = *reinterpret_cast<const f16x8*>(ub + 32 * (4 * pn + st));
+        const uint32_t reg = lb16_reg_word(words[i], lb16_pair_sel(p, lane, nu));
+        acc = mfma16(lb16_step_operand(reg, 0, sc), bv[0], acc);
+        acc1 = mfma16(lb16_step_operand(reg, 1, sc), bv[1], acc1);
+        acc = mfma16(lb16_step_operand(reg, 2, sc), bv[2], acc);
+        acc1 = mfma16(lb16_step_operand(reg, 3, sc), bv[3], acc1);
+#pragma unroll
+        for (int st = 0; st < 4; ++st) bv[st] = bn[st];
       }
     }
+  };
+  int cb0 = 0;
+  if constexpr (HOOK) {
+    chunk(0, BoolTag<true>());
+    cb0 = chunk_pairs;
   }
-  // per-token sum of the negated-class u values (deterministic tree)
+  for (int cb = cb0; cb < np; cb += chunk_pairs) chunk(cb, BoolTag<false>());
+  acc += acc1;
+
+  // per-token sum of the negated-class u (deterministic)
   part[tid] = seg_sum(csum_u, min(tpt, 64));
-  __syncthreads();
-  if (tid < 16) {
-    float s = 0.f;
-    if (tid < batch) {
-      const int first = tid * tpt;
-      for (int w = 0; w < tpt; w += 64) s += part[first + w];
-    }
-    cu[tid] = s;
-  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) red[wave][(4 * grp + i) * 16 + tok] = acc[i];
   __syncthreads();
-
-  // thread -> (row rho, token tk); rho fastest for contiguous z rows
-  const int rho = tid & 15, tk = tid >> 4;
-  const int j = 16 * tile + rho;
-  const float t = red[0][rho * 16 + tk] + red[1][rho * 16 + tk] + red[2][rho * 16 + tk] +
-                  red[3][rho * 16 + tk] + cu[tk];
-  f16 zv = (f16)0.f;
-  if (j < r) zv = (f16)(h2f(l[j]) * t);
-  uint16_t* __restrict__ z = A.L[li].z;
-  const int zs = A.L[li].zs, zoff = A.L[li].br[b].zoff;
-  if (tk < batch)
-    z[(long)tk * zs + zoff + j] = __builtin_bit_cast(uint16_t, lb16_negated_class(j) ? (f16)(-zv) : zv);
-  cs[tk * 16 + rho] = (j < r && lb16_negated_class(j)) ? (float)zv : 0.f;
-  __syncthreads();
   if (tid < 16) {
     float s = 0.f;
-    for (int q = 0; q < 16; ++q) s += cs[tid * 16 + q];
-    A.L[li].csum[A.L[li].br[b].csum_off + tile * 16 + tid] = s;
+    if (tid < batch)
+      for (int w = 0; w < tpt; w += 64) s += part[tid * tpt + w];
+    cu[tid] = s;
   }
-  // the last tile also clears the z columns between 16*ceil(r/16) and 64*ceil(r/64)
+  __syncthreads();
+
+  if (tid < 256) {
+    const int e = rho * 16 + tk;
+    float t = cu[tk];
+#pragma unroll
+    for (int w = 0; w < LB_WAVES; ++w) t += red[w][e];
+    const f16 zv = (j < r) ? (f16)(h2f((uint16_t)late(lj_raw)) * t) : (f16)0.f;
+    const f16 zst = lb16_negated_class(j) ? (f16)(-zv) : zv;
+    reinterpret_cast<uint16_t*>(part)[tk * 16 + rho] = __builtin_bit_cast(uint16_t, zst);
+  }
+  __syncthreads();
+  // tagged words: [tag | z(2q) | z(2q+1)], 8 words per token for the 16 rows
+  uint64_t* __restrict__ zw = L.z;
+  const int zrow = L.zs >> 1, zoff = (b ? L.zoff1 : L.zoff0) >> 1;
+  const uint32_t tag = late(ctr) + 1u;
+  if (tid < 8 * batch) {
+    const int q = tid & 7, tt = tid >> 3;
+    const uint32_t v = reinterpret_cast<const uint32_t*>(part)[tt * 8 + q];
+    st64c(zw + (long)tt * zrow + zoff + 8 * tile + q, (uint64_t)tag | ((uint64_t)v << 32));
+  }
+  // the last tile also writes the zero words between 16*ceil(r/16) and 64*ceil(r/64)
   const int ntv = (r + 15) >> 4;
   if (tile == ntv - 1) {
-    const int rp = 16 * ntv, kpu = 64 * lb16_units(r);
-    const int cnt = (kpu - rp) * batch;
-    for (int e = tid; e < cnt; e += 256) {
-      const int tt = e / (kpu - rp), jj = rp + e % (kpu - rp);
-      z[(long)tt * zs + zoff + jj] = 0;
+    const int w0 = 8 * ntv, w1 = 32 * lb16_units(r);
+    const int nw = w1 - w0;
+    for (int i = tid; i < nw * batch; i += LB_THREADS) {
+      const int tt = i / nw, ww = w0 + i % nw;
+      st64c(zw + (long)tt * zrow + zoff + ww, (uint64_t)tag);
     }
   }
 }
 
-// --------------------------------------------------------------------- U pass
-// One workgroup per 16-row tile of the outputs of one layer; waves 0-1 take
-// the primary branch and waves 2-3 the residual one (all four with one branch).
-__global__ __launch_bounds__(256) void lb_decode_upass(LbDecodeArgs A) {
-  __shared__ float red[4][256];
-  __shared__ float dsum[2][16];
+// ------------------------------------------------------------------ phase B
+// Prefetched per-tile data: this wave's sign words and the epilogue thread's
+// row scales (h of both branches).
+struct UTilePre {
+  uint32_t w[LB_MAXPW];
+  uint32_t h0, h1;  // fp16 bits: converting here would wait for the load
+};
 
-  int li, tile;
-  find_utile(A, blockIdx.x, li, tile);
-  const int batch = A.batch;
-  const int nb = A.L[li].nb;
-  const int m = A.L[li].m;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int tok = lane & 15, grp = lane >> 4;
-  const uint16_t* __restrict__ z = A.L[li].z;
-  const int zs = A.L[li].zs;
-
-  // D_b[tok] = sum of the negated-class z of branch b (from the V-pass tile sums)
-  if (wave == 0) {
-    for (int bb = 0; bb < nb; ++bb) {
-      const int ntv = (A.L[li].br[bb].r + 15) >> 4;
-      const float* cs = A.L[li].csum + A.L[li].br[bb].csum_off;
-      float s = 0.f;
-      for (int T = grp; T < ntv; T += 4) s += cs[T * 16 + tok];
-      s += __shfl_xor(s, 16, 64);
-      s += __shfl_xor(s, 32, 64);
-      if (lane < 16) dsum[bb][lane] = s;
-    }
-  }
-
-  const int b = (nb == 2) ? (wave >> 1) : 0;
-  const int wsub = (nb == 2) ? (wave & 1) : wave;
-  const int nsub = (nb == 2) ? 2 : 4;
-  const int r = A.L[li].br[b].r;
+__device__ __forceinline__ void u_prefetch(const LayerView& L, int tile, UTilePre& P) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  int b, p0, p1;
+  u_role(L, wave, b, p0, p1);
+  const int r = b ? L.r1 : L.r0;
   const int nu = lb16_units(r);
-  const int np = (nu + 1) >> 1;
-  const int p0 = (wsub * np) / nsub, p1 = ((wsub + 1) * np) / nsub;
-  const uint8_t* __restrict__ tile_ptr = A.L[li].br[b].ubits + (long)tile * lb16_tile_bytes(r);
-  const uint16_t* __restrict__ zrow = z + (long)tok * zs + A.L[li].br[b].zoff + 8 * grp;
+  const uint8_t* tp = (b ? L.ub1 : L.ub0) + (long)tile * lb16_tile_bytes(r);
+  const int plast = max(p1 - 1, 0);
+#pragma unroll
+  for (int i = 0; i < LB_MAXPW; ++i) P.w[i] = lb16_load_pair(tp, min(p0 + i, plast), lane, nu);
+  // loaded from always-valid indices (rows >= m are never stored)
+  const int i = min(16 * tile + (tid & 15), L.m - 1);
+  P.h0 = L.h0[i];
+  P.h1 = (L.nb == 2 ? L.h1 : L.h0)[i];
+}
 
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int p = p0; p < p1; ++p) {
-    const uint32_t reg = lb16_reg_word(lb16_load_pair(tile_ptr, p, lane, nu));
-    const int nsteps = (2 * p + 1 < nu) ? 4 : 2;
-    for (int st = 0; st < nsteps; ++st) {
-      const f16x8 av = lb16_step_operand(reg, st);
-      f16x8 bv = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (tok < batch) bv = *reinterpret_cast<const f16x8*>(zrow + 32 * (4 * p + st));
-      acc = mfma16(av, bv, acc);
+struct UState {
+  int li;              // layer whose z fragments are in registers (-1: none)
+  int b, p0, p1, nu;
+  float dw;            // this wave's share of the branch's negated-class z sum (per token)
+  f16x8 bfr[LB_MAXPW * 4];
+};
+
+// Loads this wave's z fragments for layer L (index li).  With check, polls
+// until every tagged word of the wave's range carries `tag`.
+__device__ __forceinline__ void u_enter_layer(const LayerView& L, int li, int batch, uint32_t ctr, bool check,
+                                              uint8_t* sync, UState& S) {
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const uint32_t tag = late(ctr) + 1u;
+  const int tok = lane & 15, grp = lane >> 4;
+  S.li = li;
+  u_role(L, wave, S.b, S.p0, S.p1);
+  S.nu = lb16_units(S.b ? L.r1 : L.r0);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(L.z, batch * L.zs * 4);
+  const int zb = 4 * (min(tok, batch - 1) * L.zs + (S.b ? L.zoff1 : L.zoff0) + 8 * grp);
+  const int s1 = min(4 * S.p1, 2 * S.nu);
+  // every load is issued (steps clamped to a valid one) before any result is
+  // examined, so one poll costs one memory round trip
+  const int slast = max(s1 - 1, 0);
+  int spins = 0;
+  for (;;) {
+    compiler_memory_barrier();  // every pass re-reads the words
+    bool ok = true;
+#pragma unroll
+    for (int i = 0; i < LB_MAXPW * 4; ++i) {
+      const int step = 4 * S.p0 + i;
+      const int sc = min(step, slast);
+      const u32x4 q0 = ld_tagged2(rs, zb + 128 * sc);
+      const u32x4 q1 = ld_tagged2(rs, zb + 128 * sc + 16);
+      const bool in = step < s1;
+      ok = ok & (!in | ((q0[0] == tag) & (q0[2] == tag) & (q1[0] == tag) & (q1[2] == tag)));
+      u32x4 d;
+      d[0] = in ? q0[1] : 0u;
+      d[1] = in ? q0[3] : 0u;
+      d[2] = in ? q1[1] : 0u;
+      d[3] = in ? q1[3] : 0u;
+      S.bfr[i] = __builtin_bit_cast(f16x8, d);
+    }
+    // steps beyond the register window are read later by u_tile: wait for them too
+    for (int step = 4 * S.p0 + 4 * LB_MAXPW; step < s1; ++step) {
+      const u32x4 q0 = ld_tagged2(rs, zb + 128 * step);
+      const u32x4 q1 = ld_tagged2(rs, zb + 128 * step + 16);
+      ok = ok & (q0[0] == tag) & (q0[2] == tag) & (q1[0] == tag) & (q1[2] == tag);
+    }
+    if (!check || __all(ok)) break;
+    if (++spins > LB_SPIN_LIMIT) {
+      st32c(sync + LB_SYNC_ERR, 1u);
+      break;
     }
   }
+  float d = 0.f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) red[wave][(4 * grp + i) * 16 + tok] = acc[i];
+  for (int i = 0; i < LB_MAXPW * 4; ++i) d = negated_class_sum(S.bfr[i], d);
+  d += __shfl_xor(d, 16, 64);
+  d += __shfl_xor(d, 32, 64);
+  S.dw = -d;  // fragments hold the negated-class values negated
+}
+
+__device__ __forceinline__ void u_tile(const LayerView& L, int li, int batch, int tile, const UTilePre& P,
+                                       uint32_t ctr, bool check, uint8_t* sync, const LbSignConsts& sc,
+                                       UState& S, float (*red)[256]) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int tok = lane & 15, grp = lane >> 4;
+  if (li != S.li) u_enter_layer(L, li, batch, ctr, check, sync, S);
+
+  // fragments beyond the branch's steps are zero, so every pair runs 4 steps
+  f32x4 acc = {S.dw, S.dw, S.dw, S.dw}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < LB_MAXPW; ++i) {
+    if (S.p0 + i < S.p1) {
+      const uint32_t reg = lb16_reg_word(P.w[i], lb16_pair_sel(S.p0 + i, lane, S.nu));
+      acc = mfma16(lb16_step_operand(reg, 0, sc), S.bfr[4 * i + 0], acc);
+      acc1 = mfma16(lb16_step_operand(reg, 1, sc), S.bfr[4 * i + 1], acc1);
+      acc = mfma16(lb16_step_operand(reg, 2, sc), S.bfr[4 * i + 2], acc);
+      acc1 = mfma16(lb16_step_operand(reg, 3, sc), S.bfr[4 * i + 3], acc1);
+    }
+  }
+  acc += acc1;
+  // pairs beyond the register window (ranks above 64 * 4 * LB_MAXPW per wave)
+  if (S.p1 > S.p0 + LB_MAXPW) {
+    const int r = S.b ? L.r1 : L.r0;
+    const uint8_t* tp = (S.b ? L.ub1 : L.ub0) + (long)tile * lb16_tile_bytes(r);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(L.z, batch * L.zs * 4);
+    const int zb = 4 * (min(tok, batch - 1) * L.zs + (S.b ? L.zoff1 : L.zoff0) + 8 * grp);
+    float d = 0.f;
+    for (int p = S.p0 + LB_MAXPW; p < S.p1; ++p) {
+      const uint32_t reg = lb16_reg_word(lb16_load_pair(tp, p, lane, S.nu), lb16_pair_sel(p, lane, S.nu));
+      const int nsteps = (2 * p + 1 < S.nu) ? 4 : 2;
+      for (int st = 0; st < nsteps; ++st) {
+        const int step = 4 * p + st;
+        const u32x4 q0 = ld_tagged2(rs, zb + 128 * step);
+        const u32x4 q1 = ld_tagged2(rs, zb + 128 * step + 16);
+        u32x4 dd;
+        dd[0] = q0[1]; dd[1] = q0[3]; dd[2] = q1[1]; dd[3] = q1[3];
+        const f16x8 bv = __builtin_bit_cast(f16x8, dd);
+        d = negated_class_sum(bv, d);
+        acc = mfma16(lb16_step_operand(reg, st, sc), bv, acc);
+      }
+    }
+    d += __shfl_xor(d, 16, 64);
+    d += __shfl_xor(d, 32, 64);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] -= d;
+  }
+  __syncthreads();  // previous epilogue done with red
+#pragma unroll
+  for (int q = 0; q < 4; ++q) red[wave][(4 * grp + q) * 16 + tok] = acc[q];
   __syncthreads();
 
   const int rho = tid & 15, tk = tid >> 4;
   const int i = 16 * tile + rho;
-  if (tk < batch && i < m) {
+  if (tid < 256 && tk < batch && i < L.m) {
     const int e = rho * 16 + tk;
     float y;
-    if (nb == 2) {
-      const float s0 = red[0][e] + red[1][e] + dsum[0][tk];
-      const float s1 = red[2][e] + red[3][e] + dsum[1][tk];
-      y = h2f(A.L[li].br[0].h[i]) * s0 + h2f(A.L[li].br[1].h[i]) * s1;
+    if (L.nb == 2) {
+      float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+      for (int w = 0; w < LB_WAVES / 2; ++w) {
+        s0 += red[w][e];
+        s1 += red[w + LB_WAVES / 2][e];
+      }
+      y = h2f((uint16_t)late(P.h0)) * s0 + h2f((uint16_t)late(P.h1)) * s1;
     } else {
-      const float s0 = red[0][e] + red[1][e] + red[2][e] + red[3][e] + dsum[0][tk];
-      y = h2f(A.L[li].br[0].h[i]) * s0;
+      float s0 = 0.f;
+#pragma unroll
+      for (int w = 0; w < LB_WAVES; ++w) s0 += red[w][e];
+      y = h2f((uint16_t)late(P.h0)) * s0;
     }
-    A.L[li].y[(long)tk * A.L[li].ldy + i] = f2h(y);
+    L.y[(long)tk * L.ldy + i] = f2h(y);
   }
 }
 
-hipError_t lb_launch_decode(const LbDecodeArgs& args, int chunk_units, hipStream_t stream) {
-  const size_t lds = (size_t)args.batch * (64 * chunk_units + 8) * sizeof(uint16_t);
-  hipLaunchKernelGGL(lb_decode_vpass, dim3(args.nvt), dim3(256), lds, stream, args, chunk_units);
-  hipError_t e = hipGetLastError();
+}  // namespace
+
+// -------------------------------------------------------------- kernels
+
+// MODE 0: phase A only; 1: phase B only; 2: both in one launch (z tagged and
+// polled).  SINGLE: one layer, whose fields are loaded once at kernel start.
+// Workgroup w takes a contiguous range of the V tiles and of the U tiles.
+template <int MODE, bool SINGLE>
+__global__ __launch_bounds__(LB_THREADS) void lb_decode_kernel(LbDecodeArgs A, int chunk_pairs, uint8_t* sync) {
+  extern __shared__ __align__(16) uint16_t u_lds[];
+  __shared__ __align__(16) float red[LB_WAVES][256];
+  __shared__ __align__(16) float part[LB_THREADS];
+  __shared__ __align__(16) float cu[16];
+
+  const int wg = blockIdx.x;
+  const int batch = A.batch;
+  const LbSignConsts sc = lb16_sign_consts();
+  TileMap M;
+  load_map(A, M);
+  LayerView V0;
+  if (SINGLE) {
+    V0 = layer_view(A.L[0]);
+  }
+
+  // this workgroup's call counter (single launch only): the tag is its value + 1
+  uint32_t ctr = 0;
+  if (MODE == 2) ctr = ld32c(sync + LB_SYNC_CTR + 8 * wg);
+
+  int ut0, ut1, vt0, vt1;
+  share(A.uq, A.ur, wg, ut0, ut1);
+  share(A.vq, A.vr, wg, vt0, vt1);
+  if (MODE == 1) vt1 = vt0;
+  if (MODE == 0) ut1 = ut0;
+  UTilePre pre[LB_MAXT];
+  // every load is issued (tiles clamped to a valid one), which keeps the
+  // wait counts exact; tiles beyond ut1 are never used
+  auto prefetch = [&]() {
+    const int nut = A.nut;
+#pragma unroll
+    for (int k = 0; k < LB_MAXT; ++k) {
+      int tile;
+      const int li = u_layer<SINGLE>(M, min(ut0 + k, nut - 1), tile);
+      u_prefetch(SINGLE ? V0 : layer_view(A.L[li]), tile, pre[k]);
+    }
+  };
+  // phase-B loads are issued during phase A: after the first V tile's sign
+  // words and activations, or at once by a workgroup without V tiles
+  if (vt0 < vt1) {
+    int tile;
+    const int k = v_slot<SINGLE>(M, vt0, tile);
+    v_tile<MODE == 2>(SINGLE ? V0 : layer_view(A.L[k >> 1]), batch, k & 1, tile, chunk_pairs, ctr, sc, u_lds,
+                      red, part, cu, prefetch);
+    __syncthreads();
+  } else if (MODE == 2) {
+    prefetch();
+  }
+  for (int t = vt0 + 1; t < vt1; ++t) {
+    int tile;
+    const int k = v_slot<SINGLE>(M, t, tile);
+    v_tile<false>(SINGLE ? V0 : layer_view(A.L[k >> 1]), batch, k & 1, tile, chunk_pairs, ctr, sc, u_lds, red,
+                  part, cu, prefetch);
+    __syncthreads();
+  }
+  if (MODE != 0) {
+    const bool check = MODE == 2;
+    UState S;
+    S.li = -1;
+#pragma unroll
+    for (int k = 0; k < LB_MAXT; ++k) {
+      const int t = ut0 + k;
+      if (t < ut1) {
+        int tile;
+        const int li = u_layer<SINGLE>(M, t, tile);
+        const LayerView L = SINGLE ? V0 : layer_view(A.L[li]);
+        if (MODE != 2) u_prefetch(L, tile, pre[k]);
+        u_tile(L, li, batch, tile, pre[k], ctr, check, sync, sc, S, red);
+      }
+    }
+    for (int t = ut0 + LB_MAXT; t < ut1; ++t) {
+      int tile;
+      const int li = u_layer<SINGLE>(M, t, tile);
+      const LayerView L = SINGLE ? V0 : layer_view(A.L[li]);
+      UTilePre p;
+      u_prefetch(L, tile, p);
+      u_tile(L, li, batch, tile, p, ctr, check, sync, sc, S, red);
+    }
+  }
+  // this workgroup's call is done: the next call's tag is one higher
+  if (MODE == 2 && threadIdx.x == 0) add64c_noret(sync + LB_SYNC_CTR + 8 * wg, 1ull);
+}
+
+static int g_fused_grid[64];  // per device: workgroups of the single-launch kernel (0: unknown, -1: none)
+
+template <bool SINGLE>
+static hipError_t launch_decode_t(const LbDecodeArgs& args, int chunk_pairs, void* sync, int allow_fused,
+                                  hipStream_t stream) {
+  const size_t lds = (size_t)args.batch * (128 * chunk_pairs + 8) * sizeof(uint16_t);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(lb_decode_upass, dim3(args.nut), dim3(256), 0, stream, args);
+  if (allow_fused && dev >= 0 && dev < 64) {
+    if (g_fused_grid[dev] == 0) {
+      int ncu = 0, occ1 = 0, occ7 = 0;
+      e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+      if (e != hipSuccess) return e;
+      // every workgroup of the single launch must be resident at once: size
+      // the grid for the largest dynamic LDS the host may request (56 KB)
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ1, lb_decode_kernel<2, true>, LB_THREADS, 56 * 1024);
+      if (e != hipSuccess) return e;
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ7, lb_decode_kernel<2, false>, LB_THREADS, 56 * 1024);
+      if (e != hipSuccess) return e;
+      g_fused_grid[dev] = (occ1 >= 1 && occ7 >= 1) ? (ncu < LB_MAX_GRID ? ncu : LB_MAX_GRID) : -1;
+    }
+    const int G = g_fused_grid[dev];
+    if (G > 0) {
+      LbDecodeArgs a = args;
+      a.vq = a.nvt / G; a.vr = a.nvt % G;
+      a.uq = a.nut / G; a.ur = a.nut % G;
+      hipLaunchKernelGGL((lb_decode_kernel<2, SINGLE>), dim3(G), dim3(LB_THREADS), lds, stream, a, chunk_pairs,
+                         (uint8_t*)sync);
+      return hipGetLastError();
+    }
+  }
+  LbDecodeArgs a = args;
+  a.vq = 1; a.vr = 0;
+  hipLaunchKernelGGL((lb_decode_kernel<0, SINGLE>), dim3(a.nvt), dim3(LB_THREADS), lds, stream, a, chunk_pairs,
+                     (uint8_t*)sync);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int gb = a.nut < 1024 ? a.nut : 1024;
+  a.uq = a.nut / gb; a.ur = a.nut % gb;
+  hipLaunchKernelGGL((lb_decode_kernel<1, SINGLE>), dim3(gb), dim3(LB_THREADS), 0, stream, a, chunk_pairs,
+                     (uint8_t*)sync);
   return hipGetLastError();
+}
+
+hipError_t lb_launch_decode(const LbDecodeArgs& args, int chunk_pairs, void* sync, int allow_fused,
+                            hipStream_t stream) {
+  return args.nlayers == 1 ? launch_decode_t<true>(args, chunk_pairs, sync, allow_fused, stream)
+                           : launch_decode_t<false>(args, chunk_pairs, sync, allow_fused, stream);
 }

@@ -10,53 +10,68 @@ typedef f16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-#define LB_WAVE 64
 #define LB_MAX_LAYERS 7
 
 // ---------------------------------------------------------------- LB16 layout
 // A packed factor with R rows and reduction length K is a sequence of tiles of
 // 16 rows; a tile holds 64 lanes x NU 16-bit units, NU = ceil(K/64).  Units
-// 2p and 2p+1 of a lane form one aligned 32-bit word ("pair p"), except the
-// last unit when NU is odd.
+// 2p and 2p+1 of lane L ("pair p") are the aligned 32-bit word at tile byte
+// 256p + 4L; when NU is odd the last unit is alone at 256*(NU/2) + 2L.
 
 __host__ __device__ inline int lb16_units(int K) { return (K + 63) >> 6; }
 __host__ __device__ inline long lb16_tile_bytes(int K) { return 128L * lb16_units(K); }
 
-// Byte offset, inside a tile, of lane `lane`'s pair p (or of its odd last unit).
-__device__ inline int lb16_pair_offset(int p, int lane, int nu) {
-  const int nf = nu >> 3;
-  if (2 * p < 8 * nf) return 1024 * (p >> 2) + 16 * lane + 4 * (p & 3);
-  const int j = 2 * p - 8 * nf, tu = nu - 8 * nf;
-  if (j + 1 < tu) return 1024 * nf + 256 * (j >> 1) + 4 * lane;
-  return 1024 * nf + 256 * (tu >> 1) + 2 * lane;  // odd last unit (16 bits)
-}
-
-// Load lane `lane`'s pair p of a tile as a 32-bit word in memory order (the
-// odd last unit is zero-extended).
+// Lane `lane`'s pair p of a tile as one aligned 32-bit load: units 2p, 2p+1,
+// or, for an odd last unit, the word holding the lane's unit and its
+// neighbour's (lb16_pair_sel picks the right half).  p must be wave-uniform.
 __device__ inline uint32_t lb16_load_pair(const uint8_t* tile, int p, int lane, int nu) {
-  const int off = lb16_pair_offset(p, lane, nu);
-  if (2 * p + 1 < nu) return *reinterpret_cast<const uint32_t*>(tile + off);
-  return (uint32_t)(*reinterpret_cast<const uint16_t*>(tile + off));
+  const int off = (2 * p + 1 < nu) ? 4 * lane : 4 * (lane >> 1);
+  return *reinterpret_cast<const uint32_t*>(tile + 256 * p + off);
 }
 
-// Memory bytes [m0 m1 m2 m3] (units 2p, 2p+1) -> register word [m2 m0 m3 m1]:
-// bit 15-q holds the low element and bit 31-q the high element of operand
-// dword q = 4*step + d (step 0..3 of the pair, d = 0..3).
-__device__ inline uint32_t lb16_reg_word(uint32_t mem) {
-  return __builtin_amdgcn_perm(mem, mem, 0x01030002u);
+// Byte selector of lb16_reg_word for pair p.  Memory bytes [m0 m1 m2 m3] of a
+// full pair give the register word [m2 m0 m3 m1] (byte 0 first); an odd last
+// unit stands in for unit 2p with unit 2p+1 = 0: [0 m0 0 m1] for an even lane
+// (its unit is bytes m0 m1), [0 m2 0 m3] for an odd lane.  Selector byte 0x0C
+// yields 0x00.
+__device__ inline uint32_t lb16_pair_sel(int p, int lane, int nu) {
+  return (2 * p + 1 < nu) ? 0x01030002u : ((lane & 1) ? 0x030C020Cu : 0x010C000Cu);
+}
+
+// Register word of a pair: bit 15-q holds the low element and bit 31-q the
+// high element of operand dword q = 4*step + d (step 0..3 of the pair, d = 0..3).
+__device__ inline uint32_t lb16_reg_word(uint32_t mem, uint32_t sel) {
+  return __builtin_amdgcn_perm(mem, mem, sel);
+}
+
+// Constants of the sign expansion, held in registers so that the compiler
+// can use one and-or per value pair (a 3-operand instruction takes no
+// literals on this architecture).
+struct LbSignConsts {
+  uint32_t sign_mask;  // 0x80008000 (scalar register)
+  uint32_t one_pair;   // 0x3C003C00 = (1.0, 1.0) in fp16 (vector register)
+};
+
+__device__ inline LbSignConsts lb16_sign_consts() {
+  LbSignConsts c;
+  c.sign_mask = 0x80008000u;
+  c.one_pair = 0x3C003C00u;
+  __asm__ volatile("" : "+s"(c.sign_mask));
+  __asm__ volatile("" : "+v"(c.one_pair));
+  return c;
 }
 
 // The four operand dwords (8 fp16 values) of step `st` (0..3) of a register
 // word.  Even q: bits 15/31 after the shift are signs -> +-1.0 (0x3C00).
 // Odd q: bits 14/30 -> 0.0 or 2.0; the matching activations are stored
 // negated and their sum is added back, so  A.B' + sum = sum_k sign_k * act_k.
-__device__ inline f16x8 lb16_step_operand(uint32_t reg, int st) {
+__device__ inline f16x8 lb16_step_operand(uint32_t reg, int st, const LbSignConsts& c) {
   const uint32_t w0 = reg << (4 * st);
   const uint32_t w1 = reg << (4 * st + 2);
   u32x4 d;
-  d[0] = (w0 & 0x80008000u) | 0x3C003C00u;
+  d[0] = (w0 & c.sign_mask) | c.one_pair;
   d[1] = w0 & 0x40004000u;
-  d[2] = (w1 & 0x80008000u) | 0x3C003C00u;
+  d[2] = (w1 & c.sign_mask) | c.one_pair;
   d[3] = w1 & 0x40004000u;
   return __builtin_bit_cast(f16x8, d);
 }
@@ -80,7 +95,6 @@ struct LbBranchArgs {
   const uint16_t* g;
   int r;
   int zoff;               // offset of this branch's z inside a z row (halves)
-  int csum_off;           // offset (floats) of this branch's tile sums
 };
 
 struct LbLayerArgs {
@@ -89,17 +103,22 @@ struct LbLayerArgs {
   int m, n;
   const uint16_t* x; long ldx;
   uint16_t* y; long ldy;
-  uint16_t* z;            // workspace: [batch][zs] fp16 (negated class stored negated)
-  float* csum;            // workspace: per branch [ceil(r/16)][16] floats
-  int zs;                 // z row stride (halves)
-  int vt_begin[2];        // first global V-tile index of each branch
-  int ut_begin;           // first global U-tile index
+  uint64_t* z;            // workspace: [batch][zs/2] tagged words (see decode.hip)
+  int zs;                 // z row length (halves; a multiple of 64)
 };
 
+// Kernel arguments of the decode kernels.  The header (first 128 bytes) holds
+// everything needed to map a global tile index to its layer without further
+// memory traffic; tiles are numbered layer by layer (V tiles branch by branch).
 struct LbDecodeArgs {
-  LbLayerArgs L[LB_MAX_LAYERS];
   int nlayers;
   int batch;
-  int nvt;                // total V tiles
-  int nut;                // total U tiles
+  int nvt;                          // total V tiles
+  int nut;                          // total U tiles
+  int ut_end[LB_MAX_LAYERS];        // cumulative U-tile count after layer i
+  int vt_end[2 * LB_MAX_LAYERS];    // cumulative V-tile count after (layer i, branch b) = 2i+b
+  int vq, vr;                       // V tiles of workgroup w: vq + (w < vr), contiguous
+  int uq, ur;                       // U tiles likewise
+  int pad_[3];
+  LbLayerArgs L[LB_MAX_LAYERS];
 };

@@ -11,7 +11,8 @@
 
 hipError_t lb_launch_pack(const void* latent, int is_f16, long ld, int transpose, int R, int K,
                           void* dst, hipStream_t stream);
-hipError_t lb_launch_decode(const LbDecodeArgs& args, int chunk_units, hipStream_t stream);
+hipError_t lb_launch_decode(const LbDecodeArgs& args, int chunk_pairs, void* sync, int allow_fused,
+                            hipStream_t stream);
 
 namespace {
 
@@ -35,35 +36,31 @@ constexpr int kMaxRank = 4096;
 constexpr int kMaxN = 32768;
 constexpr int kDecodeMaxBatch = 16;
 constexpr size_t kDecodeLdsBudget = 56 * 1024;
+constexpr int kDecodeMaxChunkPairs = 64;  // 8 waves x 8 register-held pairs
 
 inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Per-layer workspace: z rows (fp16, batch x zs) then the V-tile sums.
+// Per-layer workspace: z rows of batch x zs/2 tagged 64-bit words (two fp16 values each).
 struct LayerWs {
   int zs;             // halves per z row
   int zoff[2];
-  int csum_off[2];
-  size_t z_bytes, csum_bytes;
+  size_t z_bytes;
 };
 
 LayerWs layer_ws(const lb_layer& L, const int* sel, int nsel, int64_t batch) {
   LayerWs w{};
-  int zs = 0, cs = 0;
+  int zs = 0;
   for (int i = 0; i < nsel; ++i) {
-    const lb_branch& B = L.br[sel[i]];
     w.zoff[i] = zs;
-    w.csum_off[i] = cs;
-    zs += 64 * lb16_units(B.r);
-    cs += 16 * ((B.r + 15) / 16);
+    zs += 64 * lb16_units(L.br[sel[i]].r);
   }
   w.zs = zs;
-  w.z_bytes = round_up((size_t)batch * zs * sizeof(uint16_t), 256);
-  w.csum_bytes = round_up((size_t)cs * sizeof(float), 256);
+  w.z_bytes = round_up((size_t)batch * zs * 4, 256);
   return w;
 }
 
-constexpr size_t kWsHeader = 256;  // reserved (synchronisation words)
+constexpr size_t kWsHeader = 4096;  // call counters and error word of the single-launch decode kernel
 
 lb_status check_layer(const lb_layer* L, uint32_t mask, int* sel, int* nsel, const char* name) {
   if (!L) return fail(LB_ERR_INVALID_ARG, "%s: layer pointer is NULL", name);
@@ -91,12 +88,14 @@ lb_status check_layer(const lb_layer* L, uint32_t mask, int* sel, int* nsel, con
   return LB_OK;
 }
 
-int decode_chunk_units(int64_t batch, int n) {
-  const int nu = lb16_units(n);
-  int cu = (int)((kDecodeLdsBudget / sizeof(uint16_t) / batch - 8) / 64);
-  cu = cu / 8 * 8;
-  if (cu < 8) cu = 8;
-  return cu >= nu ? nu : cu;
+// Pairs (128 inputs each) of the decode V pass staged in LDS at once.
+int decode_chunk_pairs(int64_t batch, int n) {
+  const int np = (lb16_units(n) + 1) / 2;
+  int cp = (int)((kDecodeLdsBudget / sizeof(uint16_t) / batch - 8) / 128);
+  cp = cp / 4 * 4;
+  if (cp > kDecodeMaxChunkPairs) cp = kDecodeMaxChunkPairs;
+  if (cp < 4) cp = 4;
+  return cp >= np ? np : cp;
 }
 
 void fill_layer_args(LbLayerArgs& a, const lb_layer& L, const int* sel, int nsel, const LayerWs& w,
@@ -109,8 +108,7 @@ void fill_layer_args(LbLayerArgs& a, const lb_layer& L, const int* sel, int nsel
   a.ldx = ldx;
   a.y = y;
   a.ldy = ldy;
-  a.z = reinterpret_cast<uint16_t*>(base);
-  a.csum = reinterpret_cast<float*>(base + w.z_bytes);
+  a.z = reinterpret_cast<uint64_t*>(base);
   a.zs = w.zs;
   for (int i = 0; i < nsel; ++i) {
     const lb_branch& B = L.br[sel[i]];
@@ -121,12 +119,11 @@ void fill_layer_args(LbLayerArgs& a, const lb_layer& L, const int* sel, int nsel
     a.br[i].g = B.g;
     a.br[i].r = B.r;
     a.br[i].zoff = w.zoff[i];
-    a.br[i].csum_off = w.csum_off[i];
   }
 }
 
 // Launch the decode kernels for up to 16 tokens over `nl` prepared layers.
-lb_status run_decode(LbLayerArgs* layers, int nl, int batch, hipStream_t stream) {
+lb_status run_decode(LbLayerArgs* layers, int nl, int batch, void* sync, int allow_fused, hipStream_t stream) {
   LbDecodeArgs args;
   memset(&args, 0, sizeof args);
   args.nlayers = nl;
@@ -134,18 +131,18 @@ lb_status run_decode(LbLayerArgs* layers, int nl, int batch, hipStream_t stream)
   int vt = 0, ut = 0, maxn = 1;
   for (int i = 0; i < nl; ++i) {
     args.L[i] = layers[i];
-    for (int b = 0; b < layers[i].nb; ++b) {
-      args.L[i].vt_begin[b] = vt;
-      vt += (layers[i].br[b].r + 15) / 16;
+    for (int b = 0; b < 2; ++b) {
+      if (b < layers[i].nb) vt += (layers[i].br[b].r + 15) / 16;
+      args.vt_end[2 * i + b] = vt;
     }
-    args.L[i].ut_begin = ut;
     ut += (layers[i].m + 15) / 16;
+    args.ut_end[i] = ut;
     if (layers[i].n > maxn) maxn = layers[i].n;
   }
   args.nvt = vt;
   args.nut = ut;
-  const int cu = decode_chunk_units(batch, maxn);
-  hipError_t e = lb_launch_decode(args, cu, stream);
+  const int cp = decode_chunk_pairs(batch, maxn);
+  hipError_t e = lb_launch_decode(args, cp, sync, allow_fused, stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return LB_OK;
 }
@@ -181,7 +178,7 @@ size_t littlebit_linear_workspace_bytes(const lb_layer* L, int64_t batch) {
   if (check_layer(L, (1u << L->nbranches) - 1, sel, &nsel, "workspace") != LB_OK) return 0;
   const int64_t rows = batch < kDecodeMaxBatch ? batch : kDecodeMaxBatch;
   const LayerWs w = layer_ws(*L, sel, nsel, rows);
-  return kWsHeader + w.z_bytes + w.csum_bytes;
+  return kWsHeader + w.z_bytes;
 }
 
 lb_status littlebit_linear_fwd(const lb_layer* L, uint32_t branch_mask, const uint16_t* x, int64_t batch,
@@ -194,14 +191,15 @@ lb_status littlebit_linear_fwd(const lb_layer* L, uint32_t branch_mask, const ui
   if (batch < 1) return fail(LB_ERR_INVALID_ARG, "littlebit_linear_fwd: batch=%lld must be >= 1", (long long)batch);
   if (ldx < L->n || ldy < L->m) return fail(LB_ERR_INVALID_ARG, "littlebit_linear_fwd: ldx/ldy smaller than n/m");
   if (!aligned(x, 2) || !aligned(y, 2)) return fail(LB_ERR_INVALID_ARG, "littlebit_linear_fwd: x and y must be 2-byte aligned");
-  if (flags > LB_PATH_PREFILL) return fail(LB_ERR_INVALID_ARG, "littlebit_linear_fwd: unknown flags %u", flags);
-  if (flags == LB_PATH_DECODE && batch > kDecodeMaxBatch)
+  if ((flags & 3u) == 3u || (flags & ~(3u | LB_DECODE_TWO_LAUNCHES)))
+    return fail(LB_ERR_INVALID_ARG, "littlebit_linear_fwd: unknown flags %u", flags);
+  if ((flags & 3u) == LB_PATH_DECODE && batch > kDecodeMaxBatch)
     return fail(LB_ERR_INVALID_ARG, "littlebit_linear_fwd: decode path takes at most %d tokens", kDecodeMaxBatch);
   if (!ws) return fail(LB_ERR_WORKSPACE, "littlebit_linear_fwd: workspace is NULL");
   if (!aligned(ws, 256)) return fail(LB_ERR_WORKSPACE, "littlebit_linear_fwd: workspace must be 256-byte aligned");
   const int64_t rows = batch < kDecodeMaxBatch ? batch : kDecodeMaxBatch;
   const LayerWs w = layer_ws(*L, sel, nsel, rows);
-  const size_t need = kWsHeader + w.z_bytes + w.csum_bytes;
+  const size_t need = kWsHeader + w.z_bytes;
   if (ws_bytes < need)
     return fail(LB_ERR_WORKSPACE, "littlebit_linear_fwd: workspace has %zu bytes, needs %zu", ws_bytes, need);
 
@@ -210,7 +208,7 @@ lb_status littlebit_linear_fwd(const lb_layer* L, uint32_t branch_mask, const ui
     const int nb = (int)((batch - t0) < kDecodeMaxBatch ? (batch - t0) : kDecodeMaxBatch);
     LbLayerArgs la;
     fill_layer_args(la, *L, sel, nsel, w, base, x + t0 * ldx, (long)ldx, y + t0 * ldy, (long)ldy);
-    st = run_decode(&la, 1, nb, (hipStream_t)stream);
+    st = run_decode(&la, 1, nb, ws, !(flags & LB_DECODE_TWO_LAUNCHES), (hipStream_t)stream);
     if (st != LB_OK) return st;
   }
   return LB_OK;
@@ -225,7 +223,7 @@ size_t littlebit_block_workspace_bytes(const lb_layer L[7], int64_t batch) {
     if (L[i].nbranches < 1 || L[i].nbranches > 2) return 0;
     if (check_layer(&L[i], (1u << L[i].nbranches) - 1, sel, &nsel, "workspace") != LB_OK) return 0;
     const LayerWs w = layer_ws(L[i], sel, nsel, rows);
-    total += w.z_bytes + w.csum_bytes;
+    total += w.z_bytes;
   }
   return total;
 }
@@ -250,7 +248,7 @@ lb_status littlebit_block_fwd(const lb_layer L[7], const uint16_t* x_qkv, const 
     if (!aligned(xs[i], 2) || !aligned(y[i], 2))
       return fail(LB_ERR_INVALID_ARG, "littlebit_block_fwd: inputs and outputs must be 2-byte aligned");
     w[i] = layer_ws(L[i], sel[i], nsel[i], rows);
-    need += w[i].z_bytes + w[i].csum_bytes;
+    need += w[i].z_bytes;
   }
   if (L[0].n != L[1].n || L[0].n != L[2].n || L[4].n != L[5].n)
     return fail(LB_ERR_INVALID_ARG, "littlebit_block_fwd: q/k/v and gate/up must share their input size");
@@ -265,9 +263,9 @@ lb_status littlebit_block_fwd(const lb_layer L[7], const uint16_t* x_qkv, const 
     for (int i = 0; i < 7; ++i) {
       fill_layer_args(la[i], L[i], sel[i], nsel[i], w[i], base, xs[i] + t0 * L[i].n, L[i].n,
                       y[i] + t0 * L[i].m, L[i].m);
-      base += w[i].z_bytes + w[i].csum_bytes;
+      base += w[i].z_bytes;
     }
-    lb_status st = run_decode(la, 7, nb, (hipStream_t)stream);
+    lb_status st = run_decode(la, 7, nb, ws, 1, (hipStream_t)stream);
     if (st != LB_OK) return st;
   }
   return LB_OK;

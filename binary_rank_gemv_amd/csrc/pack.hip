@@ -46,7 +46,7 @@ __global__ __launch_bounds__(256) void lb_pack_kernel(const T* __restrict__ late
     word |= unit << (16 * half);
   }
   uint8_t* tile_ptr = dst + (long)tile * lb16_tile_bytes(K);
-  const int off = lb16_pair_offset(p, lane, nu);
+  const int off = 256 * p + (nunits == 2 ? 4 : 2) * lane;
   if (nunits == 2)
     *reinterpret_cast<uint32_t*>(tile_ptr + off) = word;
   else

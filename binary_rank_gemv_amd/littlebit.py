@@ -29,6 +29,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "lib
 LB_OK, LB_ERR_INVALID_ARG, LB_ERR_UNSUPPORTED, LB_ERR_WORKSPACE, LB_ERR_HIP = 0, -1, -2, -3, -4
 LB_F32, LB_F16 = 0, 1
 LB_PATH_AUTO, LB_PATH_DECODE, LB_PATH_PREFILL = 0, 1, 2
+LB_DECODE_TWO_LAUNCHES = 4
 
 EXPORTED = (
     "littlebit_packed_bytes", "littlebit_pack", "littlebit_linear_workspace_bytes",

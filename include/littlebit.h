@@ -52,6 +52,10 @@ typedef enum lb_dtype { LB_F32 = 0, LB_F16 = 1 } lb_dtype;
 #define LB_PATH_AUTO 0u    /* decode kernels for batch <= 16, else prefill  */
 #define LB_PATH_DECODE 1u  /* force the decode kernels (batch must be <= 16)*/
 #define LB_PATH_PREFILL 2u /* force the prefill (matrix-core GEMM) kernels  */
+/* OR-able: run the decode path as two launches (V pass, then U pass) instead
+ * of one launch whose workgroups exchange the rank-space intermediate through
+ * the workspace.  Same results; for measurement. */
+#define LB_DECODE_TWO_LAUNCHES 4u
 
 /*
  * LB16 packed sign format.  A packed factor F has R rows and reduction
@@ -67,10 +71,9 @@ typedef enum lb_dtype { LB_F32 = 0, LB_F16 = 1 } lb_dtype;
  *     e = 0..7.
  *   - 16-bit unit u (0 <= u < NU = Kp/64) of a lane holds steps 2u, 2u+1;
  *     element (step 2u+q, e) is bit 8*(e%2) + 7 - (4q + e/2).
- *   - NF = NU/8, TU = NU%8.  Unit u < 8NF sits at tile byte
- *     1024*(u/8) + 16L + 2*(u%8).  Otherwise j = u - 8NF: if j < 2*(TU/2)
- *     at 1024NF + 256*(j/2) + 4L + 2*(j%2), else (odd last unit) at
- *     1024NF + 256*(TU/2) + 2L.  Units are little-endian.
+ *   - Units are little-endian.  Units 2p and 2p+1 of lane L are the aligned
+ *     32-bit word at tile byte 256p + 4L (unit 2p in the low half); when NU
+ *     is odd the last unit sits alone at tile byte 256*(NU/2) + 2L.
  * sign(V_b)^T is packed with R = r_b, K = n; sign(U_b) with R = m, K = r_b.
  */
 
@@ -112,8 +115,9 @@ typedef struct lb_layer {
 /*
  * Workspace bytes littlebit_linear_fwd needs for this layer and batch
  * (0 on invalid arguments).  The workspace must be zero-filled once before
- * its first use; the library leaves it reusable after every call.  Calls
- * that run concurrently must not share a workspace.
+ * its first use; the library leaves it reusable after every call.  It holds
+ * per-workspace call counters, so calls that run concurrently must not share
+ * a workspace, and a workspace stays with the device it was first used on.
  */
 size_t littlebit_linear_workspace_bytes(const lb_layer *L, int64_t batch);
 
@@ -129,7 +133,7 @@ size_t littlebit_linear_workspace_bytes(const lb_layer *L, int64_t batch);
  *   ws, ws_bytes device workspace of at least
  *                littlebit_linear_workspace_bytes(L, batch) bytes, 256-byte
  *                aligned.
- *   flags        LB_PATH_*.
+ *   flags        LB_PATH_* optionally OR-ed with LB_DECODE_TWO_LAUNCHES.
  * Intermediates: g*x and l*t are rounded to fp16 before the sign
  * contractions; accumulation is fp32; y is rounded to fp16 once.
  */

@@ -24,12 +24,9 @@ LB16 format (one packed factor F with R rows and reduction length K)
 * A lane's elements form 16-bit units.  Unit u (0 <= u < NU = Kp / 64) holds
   steps 2u and 2u+1; element (step 2u + q, e), q in {0, 1}, is bit
   8 * (e mod 2) + 7 - (4 q + floor(e / 2)) of the unit.
-* Units are stored little-endian.  With NF = floor(NU / 8) and TU = NU mod 8:
-  unit u < 8 NF is at tile byte 1024 * floor(u / 8) + 16 L + 2 (u mod 8);
-  for u >= 8 NF let j = u - 8 NF: if j < 2 floor(TU / 2) the unit is at
-  1024 NF + 256 floor(j / 2) + 4 L + 2 (j mod 2), otherwise (the last unit
-  when TU is odd) at 1024 NF + 256 floor(TU / 2) + 2 L.  So units 2p and
-  2p+1 of a lane are always one aligned 32-bit word.
+* Units are stored little-endian.  Units 2p and 2p+1 of lane L form the
+  aligned 32-bit word at tile byte 256 p + 4 L (unit 2p in the low half);
+  when NU is odd the last unit sits alone at tile byte 256 floor(NU / 2) + 2 L.
 """
 
 from __future__ import annotations
@@ -62,17 +59,13 @@ def _unit_bit_position(q: int, e: int) -> int:
 
 def _unit_byte_offsets(nu: int) -> np.ndarray:
     """offsets[L, u] = byte offset of lane L's unit u inside a tile."""
-    nf, out = nu // 8, np.zeros((64, nu), dtype=np.int64)
+    out = np.zeros((64, nu), dtype=np.int64)
     for lane in range(64):
         for u in range(nu):
-            if u < 8 * nf:
-                out[lane, u] = 1024 * (u // 8) + 16 * lane + 2 * (u % 8)
-                continue
-            j, tu = u - 8 * nf, nu - 8 * nf
-            if j < 2 * (tu // 2):
-                out[lane, u] = 1024 * nf + 256 * (j // 2) + 4 * lane + 2 * (j % 2)
+            if u < 2 * (nu // 2):
+                out[lane, u] = 256 * (u // 2) + 4 * lane + 2 * (u % 2)
             else:
-                out[lane, u] = 1024 * nf + 256 * (tu // 2) + 2 * lane
+                out[lane, u] = 256 * (nu // 2) + 2 * lane
     return out
 
 

@@ -73,7 +73,8 @@ def _fwd(layer, mask=3, x=FAKE, batch=1, ldx=64, y=FAKE, ldy=64, ws=FAKE, ws_byt
     (dict(ldx=32), lb.LB_ERR_INVALID_ARG),
     (dict(ldy=60), lb.LB_ERR_INVALID_ARG),
     (dict(x=FAKE + 1), lb.LB_ERR_INVALID_ARG),
-    (dict(flags=7), lb.LB_ERR_INVALID_ARG),
+    (dict(flags=3), lb.LB_ERR_INVALID_ARG),
+    (dict(flags=8), lb.LB_ERR_INVALID_ARG),
     (dict(flags=1, batch=17), lb.LB_ERR_INVALID_ARG),
     (dict(ws=None), lb.LB_ERR_WORKSPACE),
     (dict(ws=FAKE + 16), lb.LB_ERR_WORKSPACE),

@@ -1,8 +1,9 @@
 """The LB16 bit order supports an exact shift-and-mask sign unpack.
 
 These CPU tests model, in plain Python, how a 64-lane matrix-core fragment is
-formed from LB16 bytes (packed here by the oracle's packer): a lane joins two
-16-bit units into a 32-bit word with a byte permutation, then for q = 0..15
+formed from LB16 bytes (packed here by the oracle's packer): a lane loads one
+aligned 32-bit word per pair of 16-bit units (an odd last unit comes with its
+neighbour lane's unit) and rearranges its bytes with a byte permutation, then for q = 0..15
 shifts the word left by 2*floor(q/2) and masks either bits 15/31 (q even,
 giving fp16 +-1 after OR-ing in 1.0) or bits 14/30 (q odd, giving fp16 0 or
 2).  Element k lands in the q-odd class exactly when (k & 2) != 0, so a
@@ -17,46 +18,49 @@ import pytest
 import oracle
 
 
-def _units(packed, R, K):
-    """units[T, L, u] read back from the bytes with the placement rule."""
-    rp, kp = 16 * ((R + 15) // 16), 64 * ((K + 63) // 64)
-    nt, nu = rp // 16, kp // 64
-    nf = nu // 8
-    out = np.zeros((nt, 64, nu), dtype=np.uint32)
-    for T in range(nt):
-        for L in range(64):
-            for u in range(nu):
-                j, tu = u - 8 * nf, nu - 8 * nf
-                if u < 8 * nf:
-                    rel = 1024 * (u // 8) + 16 * L + 2 * (u % 8)
-                elif j < 2 * (tu // 2):
-                    rel = 1024 * nf + 256 * (j // 2) + 4 * L + 2 * (j % 2)
-                else:
-                    rel = 1024 * nf + 256 * (tu // 2) + 2 * L
-                off = T * 2 * kp + rel
-                out[T, L, u] = int(packed[off]) | (int(packed[off + 1]) << 8)
+def _perm(mem, sel):
+    """Byte permutation of one 32-bit word: selector byte 0..3 (or 4..7) picks
+    that byte of the word, 0x0C gives 0x00."""
+    out = 0
+    for i in range(4):
+        b = (sel >> (8 * i)) & 0xFF
+        v = (mem >> (8 * (b & 3))) & 0xFF if b < 8 else 0
+        assert b < 8 or b == 0x0C
+        out |= v << (8 * i)
     return out
+
+
+def _pair_reg(packed, T, L, p, R, K):
+    """The register word a lane forms for pair p: one aligned 32-bit load
+    (units 2p, 2p+1 at 256p + 4L; an odd last unit through the aligned word
+    at 256p + 4*(L//2) that it shares with its neighbour) and a byte
+    selection that puts the lane's units in place."""
+    rp, kp = 16 * ((R + 15) // 16), 64 * ((K + 63) // 64)
+    nu = kp // 64
+    full = 2 * p + 1 < nu
+    rel = 256 * p + (4 * L if full else 4 * (L // 2))
+    off = T * 2 * kp + rel
+    assert off + 4 <= len(packed) and rel + 4 <= 2 * kp   # stays inside the tile
+    mem = int.from_bytes(bytes(packed[off:off + 4]), "little")
+    sel = 0x01030002 if full else (0x030C020C if L & 1 else 0x010C000C)
+    return _perm(mem, sel)
 
 
 def _fp16_bits_to_float(bits16):
     return float(np.array([bits16], dtype=np.uint16).view(np.float16)[0])
 
 
-def _fragment_values(units, R, K):
+def _fragment_values(packed, R, K):
     """A[a, k] as the lanes would build them; cls[k] = True for the q-odd class."""
-    nt, _, nu = units.shape
-    kp = 64 * nu
+    rp, kp = 16 * ((R + 15) // 16), 64 * ((K + 63) // 64)
+    nt, nu = rp // 16, kp // 64
     A = np.full((nt * 16, kp), np.nan)
     cls = np.zeros(kp, dtype=bool)
     for T in range(nt):
         for L in range(64):
             row, c = 16 * T + L % 16, L // 16
             for p in range((nu + 1) // 2):
-                u0 = units[T, L, 2 * p]
-                u1 = units[T, L, 2 * p + 1] if 2 * p + 1 < nu else 0
-                mem = u0 | (u1 << 16)
-                mb = [(mem >> (8 * i)) & 0xFF for i in range(4)]
-                reg = mb[2] | (mb[0] << 8) | (mb[3] << 16) | (mb[1] << 24)
+                reg = _pair_reg(packed, T, L, p, R, K)
                 for q in range(16):
                     step = 4 * p + q // 4
                     if 32 * step >= kp:
@@ -71,12 +75,11 @@ def _fragment_values(units, R, K):
     return A, cls
 
 
-@pytest.mark.parametrize("R,K", [(16, 64), (16, 128), (20, 600), (32, 1472)])
+@pytest.mark.parametrize("R,K", [(16, 64), (16, 128), (16, 192), (20, 600), (40, 320), (32, 1472)])
 def test_fragment_unpack_reproduces_signs(R, K):
     rng = np.random.default_rng(R + K)
     neg = rng.random((R, K)) < 0.5
-    units = _units(oracle.pack_factor(neg), R, K)
-    A, cls = _fragment_values(units, R, K)
+    A, cls = _fragment_values(oracle.pack_factor(neg), R, K)
     kk = np.arange(A.shape[1])
     np.testing.assert_array_equal(cls, (kk & 2) != 0)
     s = np.where(neg, -1.0, 1.0)

@@ -76,13 +76,15 @@ def test_pack_f16_and_strided(lb):
 
 # --------------------------------------------------------------- small layers
 
+@pytest.mark.parametrize("two_launches", [False, True])
 @pytest.mark.parametrize("batch", [1, 2, 5, 16])
-def test_tiny_config_full_oracle(lb, batch):
-    print(f"[case] tiny batch={batch}", flush=True)
+def test_tiny_config_full_oracle(lb, batch, two_launches):
+    print(f"[case] tiny batch={batch} two_launches={two_launches}", flush=True)
     br, x = synth.make_layer(synth.TINY, batch=batch, seed=0)
     layer = _layer(lb, br)
-    y = lb.littlebit_linear_fwd(layer, torch.from_numpy(x).cuda())
-    _assert_parity(y, oracle.linear_forward(x, br), f"tiny b={batch}")
+    path = lb.LB_DECODE_TWO_LAUNCHES if two_launches else lb.LB_PATH_AUTO
+    y = lb.littlebit_linear_fwd(layer, torch.from_numpy(x).cuda(), path=path)
+    _assert_parity(y, oracle.linear_forward(x, br), f"tiny b={batch} two={two_launches}")
 
 
 @pytest.mark.parametrize("m,n,ranks,batch", [
@@ -140,12 +142,25 @@ def test_determinism_and_poisoned_buffers(lb):
     layer = _layer(lb, br)
     xt = torch.from_numpy(x).cuda()
     need = lb.littlebit_linear_workspace_bytes(layer, 3)
-    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda")   # garbage workspace
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda")   # garbage data region
+    ws[:4096] = 0                                                       # zeroed sync header
     out = torch.full((3, 700), float("nan"), dtype=torch.float16, device="cuda")
     y_a = lb.littlebit_linear_fwd(layer, xt, out=out, workspace=ws).clone()
     y_b = lb.littlebit_linear_fwd(layer, xt).clone()
-    assert torch.equal(y_a, y_b)
+    y_c = lb.littlebit_linear_fwd(layer, xt, path=lb.LB_DECODE_TWO_LAUNCHES).clone()
+    for _ in range(5):
+        lb.littlebit_linear_fwd(layer, xt, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y_a, y_b) and torch.equal(y_a, y_c) and torch.equal(out, y_a)
     _assert_parity(y_a, oracle.linear_forward(x, br), "poisoned")
+    # header: one 64-bit call counter per workgroup of the single launch
+    # (bytes 8*w, at most 256 workgroups), error word at byte 2048.  Six
+    # single-launch calls ran on this workspace.
+    hdr = ws[:4096].cpu()
+    counters = hdr[:2048].view(torch.int64).tolist()
+    grid = min(torch.cuda.get_device_properties(0).multi_processor_count, 256)
+    assert int(hdr[2048:2052].view(torch.int32)) == 0, "z poll spin limit hit"
+    assert counters[:grid] == [6] * grid and not any(counters[grid:]), counters
 
 
 def test_strided_rows(lb):
@@ -175,10 +190,12 @@ def _full_size_check(lb, br, x, what, nrows=64, path=None):
     return layer, xt, y
 
 
-def test_llama2_7b_up_batch1(lb):
-    print("[case] 7b up batch 1", flush=True)
+@pytest.mark.parametrize("two_launches", [False, True])
+def test_llama2_7b_up_batch1(lb, two_launches):
+    print(f"[case] 7b up batch 1 two_launches={two_launches}", flush=True)
     br, x = synth.make_layer(synth.UP7B, batch=1, seed=0)
-    _full_size_check(lb, br, x, "7B up b=1")
+    _full_size_check(lb, br, x, f"7B up b=1 two={two_launches}",
+                     path=lb.LB_DECODE_TWO_LAUNCHES if two_launches else None)
 
 
 @pytest.mark.parametrize("batch", [1, 16])
