@@ -58,22 +58,60 @@ def make_copy(lb, torch, shape, seed):
     return lb.LittleBitLayer(m=shape.m, n=shape.n, branches=branches)
 
 
-def cpu_baseline(shape, branches, x, budget_rows):
-    """Time the oracle's dense definition on a sample of output rows."""
-    import oracle
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "lb_decode_7b_up_b1_pmc.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "binary_rank_gemv_amd", "csrc", f) for f in ("decode.hip", "lb_common.h")]
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed counter summary, or None when
+    the decode kernel's sources have changed since the counters were taken."""
+    import hashlib
+    import re
+    try:
+        text = open(PMC_SUMMARY).read()
+        h = hashlib.sha256(b"".join(open(f, "rb").read() for f in KERNEL_SOURCES)).hexdigest()
+    except OSError:
+        return None
+    mt = re.search(r"traffic_bytes_per_launch:\s*(\d+)", text)
+    mh = re.search(r"kernel_sources_sha256:\s*([0-9a-f]{64})", text)
+    if not (mt and mh) or mh.group(1) != h:
+        return None
+    return int(mt.group(1))
+
+
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max(d["num_threads"] for d in threadpool_info()) if threadpool_info() else 1
+        info = threadpool_info()
+        if info:
+            return max(d["num_threads"] for d in info)
     except Exception:
-        threads = len(os.sched_getaffinity(0))
-    rows = np.arange(budget_rows)
-    t0 = time.perf_counter()
-    oracle.rows_forward(x, branches, rows)
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(shape, branches, x, seconds):
+    """Time the float64 oracle on the host: whole batch-1 calls of its factored
+    form, repeated for about `seconds`, plus a sample of output rows of its
+    dense definition (rows of W built per call) for about a third of that."""
+    import oracle
+    calls, t0 = 0, time.perf_counter()
+    while calls < 3 or time.perf_counter() - t0 < seconds:
+        oracle.factored_forward(x, branches)
+        calls += 1
     dt = time.perf_counter() - t0
-    frac = budget_rows / shape.m
-    return {"value": x.shape[0] * frac / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{budget_rows} of {shape.m} output rows of one batch-1 call (dense float64 "
-                      f"definition, rows of W built per call), {dt:.1f} s, scaled by {shape.m}/{budget_rows}"}
+    rows, t1 = 0, time.perf_counter()
+    while rows < shape.m and (rows == 0 or time.perf_counter() - t1 < seconds / 3):
+        blk = np.arange(rows, min(rows + 344, shape.m))
+        oracle.rows_forward(x, branches, blk)
+        rows += len(blk)
+    dtd = time.perf_counter() - t1
+    return {"value": round(x.shape[0] * calls / dt, 3), "unit": "tokens/s", "cores": int(_blas_threads()),
+            "kind": "oracle",
+            "sample": f"{calls} whole batch-1 calls of the float64 factored oracle in {dt:.1f} s",
+            "dense_definition": {"value": round(x.shape[0] * (rows / shape.m) / dtd, 4), "unit": "tokens/s",
+                                 "sample": f"{rows} of {shape.m} output rows of the dense float64 definition "
+                                           f"in {dtd:.1f} s, scaled by {shape.m}/{rows}"}}
 
 
 def main():
@@ -82,7 +120,10 @@ def main():
     ap.add_argument("--steps", type=int, default=3840)
     ap.add_argument("--warmup", type=int, default=384)
     ap.add_argument("--copies-gb", type=float, default=1.0, help="total size of distinct layer copies")
-    ap.add_argument("--cpu-rows", type=int, default=2752, help="output rows in the oracle sample (0: skip)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="host time for the oracle baseline (0: skip)")
+    ap.add_argument("--pmc-pass", action="store_true",
+                    help="no timing: one call per layer copy plus a 256 MiB device copy, for hardware counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the layer is measured per GPU.",
@@ -107,6 +148,18 @@ def main():
     copies = [first] + [make_copy(lb, torch, shape, 1000 + i) for i in range(ncopies - 1)]
     need = lb.littlebit_linear_workspace_bytes(first, batch)
     ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+
+    if args.pmc_pass:
+        # counter pass: every copy once (cold in the caches), then a plain
+        # device copy of known size that calibrates the byte counters
+        for c in copies:
+            lb.littlebit_linear_fwd(c, x, out=y, workspace=ws)
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"pmc_pass": True, "decode_calls": len(copies), "copy_bytes": src.numel()}))
+        return
 
     # correctness of the measured configuration (first copy) against the oracle
     lb.littlebit_linear_fwd(first, x, out=y, workspace=ws)
@@ -159,15 +212,15 @@ def main():
     abytes = algorithmic_bytes(shape.m, shape.n, shape.ranks, batch)
     achieved = abytes / (ms_per_step * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "lb_decode_kernel<2> (one launch per call: V pass, grid barrier, U pass)",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                "kernel": "lb_decode_kernel<2, true> (one launch per call: V pass, tagged z exchange, U pass)",
                 "algorithmic_bytes_per_call": abytes,
                 "avg_call_us": round(ms_per_step * 1e3, 3),
                 "two_launch_variant_us": round(ms_two / args.steps * 1e3, 3)}
 
     cpu = None
-    if args.cpu_rows > 0:
-        cpu = cpu_baseline(shape, branches, x_np, min(args.cpu_rows, shape.m))
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(shape, branches, x_np, args.cpu_seconds)
 
     out = {
         "metric": "decode tokens/s per layer",
