@@ -76,6 +76,20 @@ __device__ inline f16x8 lb16_step_operand(uint32_t reg, int st, const LbSignCons
   return __builtin_bit_cast(f16x8, d);
 }
 
+// The same step with every value exactly +-v, where `vpair` holds the fp16
+// bits of v >= 0 in both halves (v = 1.0: 0x3C003C00).  For odd q the sign
+// bit sits one position lower, so the word is shifted one further.  Two
+// instructions per value pair.  (A negative scale is applied by inverting
+// every bit of the register word first: all values of a lane share one row.)
+__device__ inline f16x8 lb16_step_operand_val(uint32_t reg, int st, uint32_t sign_mask, uint32_t vpair) {
+  u32x4 d;
+  d[0] = ((reg << (4 * st)) & sign_mask) | vpair;
+  d[1] = ((reg << (4 * st + 1)) & sign_mask) | vpair;
+  d[2] = ((reg << (4 * st + 2)) & sign_mask) | vpair;
+  d[3] = ((reg << (4 * st + 3)) & sign_mask) | vpair;
+  return __builtin_bit_cast(f16x8, d);
+}
+
 // Activation index k belongs to the "odd q" operand class iff (k & 2) != 0.
 __host__ __device__ inline bool lb16_negated_class(int k) { return (k & 2) != 0; }
 
@@ -121,4 +135,19 @@ struct LbDecodeArgs {
   int uq, ur;                       // U tiles likewise
   int pad_[3];
   LbLayerArgs L[LB_MAX_LAYERS];
+};
+
+// Kernel arguments of the prefill (matrix-core GEMM) kernels for one layer
+// and up to LB_PREFILL_MAX_TOKENS tokens.  z: [M][zs] fp16, branch b's
+// latent values at zoff (halves), zero-padded to 64*ceil(r/64).
+#define LB_PREFILL_MAX_TOKENS 8192
+struct LbPrefillArgs {
+  LbBranchArgs br[2];
+  int nb;
+  int m, n;
+  int M;                  // tokens
+  const uint16_t* x; long ldx;
+  uint16_t* y; long ldy;
+  uint16_t* z;
+  int zs;                 // z row length (halves; a multiple of 64)
 };

@@ -11,6 +11,7 @@
 
 hipError_t lb_launch_pack(const void* latent, int is_f16, long ld, int transpose, int R, int K,
                           void* dst, hipStream_t stream);
+hipError_t lb_launch_prefill(const LbPrefillArgs& args, hipStream_t stream);
 hipError_t lb_launch_decode(const LbDecodeArgs& args, int chunk_pairs, void* sync, int allow_fused,
                             hipStream_t stream);
 
@@ -41,12 +42,20 @@ constexpr int kDecodeMaxChunkPairs = 64;  // 8 waves x 8 register-held pairs
 inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Per-layer workspace: z rows of batch x zs/2 tagged 64-bit words (two fp16 values each).
+// Workspace layout: [header | decode z of every layer | prefill z].  Decode
+// z: 16 rows of zs/2 tagged 64-bit words (two fp16 values each) per layer,
+// reserved whatever the batch.  Prefill z: up to 8192 rows of zs fp16 values,
+// in a region of its own, so a decode poll never meets plain prefill values.
 struct LayerWs {
   int zs;             // halves per z row
   int zoff[2];
-  size_t z_bytes;
+  size_t z_bytes;     // decode region (16 rows)
 };
+
+inline size_t prefill_z_bytes(int zs, int64_t tokens) {
+  const int64_t t = tokens < LB_PREFILL_MAX_TOKENS ? tokens : LB_PREFILL_MAX_TOKENS;
+  return round_up((size_t)t * zs * sizeof(uint16_t), 256);
+}
 
 LayerWs layer_ws(const lb_layer& L, const int* sel, int nsel, int64_t batch) {
   LayerWs w{};
@@ -56,7 +65,7 @@ LayerWs layer_ws(const lb_layer& L, const int* sel, int nsel, int64_t batch) {
     zs += 64 * lb16_units(L.br[sel[i]].r);
   }
   w.zs = zs;
-  w.z_bytes = round_up((size_t)batch * zs * 4, 256);
+  w.z_bytes = round_up((size_t)batch * zs * 4, 256);  // batch = 16: the reserved decode rows
   return w;
 }
 
@@ -109,6 +118,31 @@ void fill_layer_args(LbLayerArgs& a, const lb_layer& L, const int* sel, int nsel
   a.y = y;
   a.ldy = ldy;
   a.z = reinterpret_cast<uint64_t*>(base);
+  a.zs = w.zs;
+  for (int i = 0; i < nsel; ++i) {
+    const lb_branch& B = L.br[sel[i]];
+    a.br[i].vbits = static_cast<const uint8_t*>(B.v_bits);
+    a.br[i].ubits = static_cast<const uint8_t*>(B.u_bits);
+    a.br[i].h = B.h;
+    a.br[i].l = B.l;
+    a.br[i].g = B.g;
+    a.br[i].r = B.r;
+    a.br[i].zoff = w.zoff[i];
+  }
+}
+
+void fill_prefill_args(LbPrefillArgs& a, const lb_layer& L, const int* sel, int nsel, const LayerWs& w,
+                       uint8_t* base, const uint16_t* x, long ldx, uint16_t* y, long ldy, int tokens) {
+  memset(&a, 0, sizeof a);
+  a.nb = nsel;
+  a.m = L.m;
+  a.n = L.n;
+  a.M = tokens;
+  a.x = x;
+  a.ldx = ldx;
+  a.y = y;
+  a.ldy = ldy;
+  a.z = reinterpret_cast<uint16_t*>(base);
   a.zs = w.zs;
   for (int i = 0; i < nsel; ++i) {
     const lb_branch& B = L.br[sel[i]];
@@ -176,9 +210,8 @@ size_t littlebit_linear_workspace_bytes(const lb_layer* L, int64_t batch) {
   int sel[2], nsel = 0;
   if (batch < 1 || !L || L->nbranches < 1 || L->nbranches > 2) return 0;
   if (check_layer(L, (1u << L->nbranches) - 1, sel, &nsel, "workspace") != LB_OK) return 0;
-  const int64_t rows = batch < kDecodeMaxBatch ? batch : kDecodeMaxBatch;
-  const LayerWs w = layer_ws(*L, sel, nsel, rows);
-  return kWsHeader + w.z_bytes;
+  const LayerWs w = layer_ws(*L, sel, nsel, kDecodeMaxBatch);
+  return kWsHeader + w.z_bytes + prefill_z_bytes(w.zs, batch);
 }
 
 lb_status littlebit_linear_fwd(const lb_layer* L, uint32_t branch_mask, const uint16_t* x, int64_t batch,
@@ -197,13 +230,25 @@ lb_status littlebit_linear_fwd(const lb_layer* L, uint32_t branch_mask, const ui
     return fail(LB_ERR_INVALID_ARG, "littlebit_linear_fwd: decode path takes at most %d tokens", kDecodeMaxBatch);
   if (!ws) return fail(LB_ERR_WORKSPACE, "littlebit_linear_fwd: workspace is NULL");
   if (!aligned(ws, 256)) return fail(LB_ERR_WORKSPACE, "littlebit_linear_fwd: workspace must be 256-byte aligned");
-  const int64_t rows = batch < kDecodeMaxBatch ? batch : kDecodeMaxBatch;
-  const LayerWs w = layer_ws(*L, sel, nsel, rows);
-  const size_t need = kWsHeader + w.z_bytes;
+  const LayerWs w = layer_ws(*L, sel, nsel, kDecodeMaxBatch);
+  const uint32_t path = flags & 3u;
+  const bool prefill = path == LB_PATH_PREFILL || (path == LB_PATH_AUTO && batch > kDecodeMaxBatch);
+  const size_t need = kWsHeader + w.z_bytes + (prefill ? prefill_z_bytes(w.zs, batch) : 0);
   if (ws_bytes < need)
     return fail(LB_ERR_WORKSPACE, "littlebit_linear_fwd: workspace has %zu bytes, needs %zu", ws_bytes, need);
 
   uint8_t* base = static_cast<uint8_t*>(ws) + kWsHeader;
+  if (prefill) {
+    for (int64_t t0 = 0; t0 < batch; t0 += LB_PREFILL_MAX_TOKENS) {
+      const int nt = (int)((batch - t0) < LB_PREFILL_MAX_TOKENS ? (batch - t0) : LB_PREFILL_MAX_TOKENS);
+      LbPrefillArgs pa;
+      fill_prefill_args(pa, *L, sel, nsel, w, base + w.z_bytes, x + t0 * ldx, (long)ldx, y + t0 * ldy,
+                        (long)ldy, nt);
+      hipError_t e = lb_launch_prefill(pa, (hipStream_t)stream);
+      if (e != hipSuccess) return hip_fail(e, "prefill launch");
+    }
+    return LB_OK;
+  }
   for (int64_t t0 = 0; t0 < batch; t0 += kDecodeMaxBatch) {
     const int nb = (int)((batch - t0) < kDecodeMaxBatch ? (batch - t0) : kDecodeMaxBatch);
     LbLayerArgs la;
@@ -216,16 +261,17 @@ lb_status littlebit_linear_fwd(const lb_layer* L, uint32_t branch_mask, const ui
 
 size_t littlebit_block_workspace_bytes(const lb_layer L[7], int64_t batch) {
   if (!L || batch < 1) return 0;
-  const int64_t rows = batch < kDecodeMaxBatch ? batch : kDecodeMaxBatch;
-  size_t total = kWsHeader;
+  size_t total = 0, zp = 0;
   for (int i = 0; i < 7; ++i) {
     int sel[2], nsel = 0;
     if (L[i].nbranches < 1 || L[i].nbranches > 2) return 0;
     if (check_layer(&L[i], (1u << L[i].nbranches) - 1, sel, &nsel, "workspace") != LB_OK) return 0;
-    const LayerWs w = layer_ws(L[i], sel, nsel, rows);
+    const LayerWs w = layer_ws(L[i], sel, nsel, kDecodeMaxBatch);
     total += w.z_bytes;
+    const size_t p = prefill_z_bytes(w.zs, batch);
+    if (p > zp) zp = p;
   }
-  return total;
+  return kWsHeader + total + (batch > kDecodeMaxBatch ? zp : 0);
 }
 
 lb_status littlebit_block_fwd(const lb_layer L[7], const uint16_t* x_qkv, const uint16_t* x_o,
@@ -237,8 +283,7 @@ lb_status littlebit_block_fwd(const lb_layer L[7], const uint16_t* x_qkv, const 
   const uint16_t* xs[7] = {x_qkv, x_qkv, x_qkv, x_o, x_gu, x_gu, x_down};
   int sel[7][2], nsel[7];
   LayerWs w[7];
-  const int64_t rows = batch < kDecodeMaxBatch ? batch : kDecodeMaxBatch;
-  size_t need = kWsHeader;
+  size_t need = kWsHeader, zp = 0;
   for (int i = 0; i < 7; ++i) {
     if (L[i].nbranches < 1 || L[i].nbranches > 2)
       return fail(LB_ERR_INVALID_ARG, "littlebit_block_fwd: layer %d nbranches=%d", i, L[i].nbranches);
@@ -247,15 +292,35 @@ lb_status littlebit_block_fwd(const lb_layer L[7], const uint16_t* x_qkv, const 
     if (!y[i]) return fail(LB_ERR_INVALID_ARG, "littlebit_block_fwd: y[%d] is NULL", i);
     if (!aligned(xs[i], 2) || !aligned(y[i], 2))
       return fail(LB_ERR_INVALID_ARG, "littlebit_block_fwd: inputs and outputs must be 2-byte aligned");
-    w[i] = layer_ws(L[i], sel[i], nsel[i], rows);
+    w[i] = layer_ws(L[i], sel[i], nsel[i], kDecodeMaxBatch);
     need += w[i].z_bytes;
+    const size_t p = prefill_z_bytes(w[i].zs, batch);
+    if (p > zp) zp = p;
   }
+  const bool prefill = batch > kDecodeMaxBatch;
+  const size_t decode_bytes = need - kWsHeader;
+  if (prefill) need += zp;
   if (L[0].n != L[1].n || L[0].n != L[2].n || L[4].n != L[5].n)
     return fail(LB_ERR_INVALID_ARG, "littlebit_block_fwd: q/k/v and gate/up must share their input size");
   if (!ws) return fail(LB_ERR_WORKSPACE, "littlebit_block_fwd: workspace is NULL");
   if (!aligned(ws, 256)) return fail(LB_ERR_WORKSPACE, "littlebit_block_fwd: workspace must be 256-byte aligned");
   if (ws_bytes < need) return fail(LB_ERR_WORKSPACE, "littlebit_block_fwd: workspace has %zu bytes, needs %zu", ws_bytes, need);
 
+  if (prefill) {
+    // the projections one after another, each as two matrix-core GEMMs
+    uint8_t* base = static_cast<uint8_t*>(ws) + kWsHeader + decode_bytes;
+    for (int i = 0; i < 7; ++i) {
+      for (int64_t t0 = 0; t0 < batch; t0 += LB_PREFILL_MAX_TOKENS) {
+        const int nt = (int)((batch - t0) < LB_PREFILL_MAX_TOKENS ? (batch - t0) : LB_PREFILL_MAX_TOKENS);
+        LbPrefillArgs pa;
+        fill_prefill_args(pa, L[i], sel[i], nsel[i], w[i], base, xs[i] + t0 * L[i].n, L[i].n,
+                          y[i] + t0 * L[i].m, L[i].m, nt);
+        hipError_t e = lb_launch_prefill(pa, (hipStream_t)stream);
+        if (e != hipSuccess) return hip_fail(e, "prefill launch");
+      }
+    }
+    return LB_OK;
+  }
   for (int64_t t0 = 0; t0 < batch; t0 += kDecodeMaxBatch) {
     const int nb = (int)((batch - t0) < kDecodeMaxBatch ? (batch - t0) : kDecodeMaxBatch);
     LbLayerArgs la[7];
