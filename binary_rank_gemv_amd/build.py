@@ -19,7 +19,11 @@ LIB = os.path.join(LIBDIR, "liblittlebit.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops keeps the compiler from emitting packed fp32 VALU forms.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# -amdgpu-kernarg-preload-count: the dispatch preloads up to 14 leading
+# kernel-argument dwords into scalar registers (the decode kernel puts its
+# phase-A fields there).
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mllvm", "-amdgpu-kernarg-preload-count=14"]
 
 
 def sources():

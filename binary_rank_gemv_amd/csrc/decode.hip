@@ -3,12 +3,10 @@
 // Per branch (explainx.ai explainer, "How it works" items 1-3):
 //   u = g*x (fp16), t = sign(V)^T u, z = l*t (fp16), s = sign(U) z, y = sum_b h_b*s_b.
 // Each 16-row tile of a packed factor is a stream of 16x16x32 matrix-core
-// steps: tokens fill the 16 columns, the signs are expanded in registers by
-// lb16_step_operand (one shift and one and-or per two values).  Activations
-// in the "negated class" (k & 2) are stored negated and their per-token sum
-// is added back.  Operand columns of absent tokens read the last token's
-// data; those output columns are never stored, so operand loads are
-// unconditional.
+// steps: tokens fill the 16 columns, the signs are expanded in registers to
+// exact +-1.0 by lb16_step_operand_val (one shift and one and-or per two
+// values).  Operand columns of absent tokens read the last token's data;
+// those output columns are never stored, so operand loads are unconditional.
 //
 // One call = phase A (V pass over every 16-row tile of every sign(V)^T,
 // giving z) then phase B (U pass over every 16-row output tile, giving y).
@@ -30,7 +28,7 @@
 #define LB_THREADS (64 * LB_WAVES)
 #define LB_MAXPV 8                    // V-pass pairs per wave held in registers
 #define LB_MAXT 3                     // phase-B tiles whose sign words are prefetched
-#define LB_MAXPW 4                    // phase-B pairs per wave held in registers
+#define LB_MAXPW 3                    // phase-B pairs per wave held in registers
 #define LB_MAX_GRID 256               // workgroups of the single launch (one counter each)
 #define LB_SPIN_LIMIT (1 << 20)
 
@@ -133,13 +131,18 @@ __device__ __forceinline__ int u_layer(const TileMap& M, int t, int& tile) {
   return li;
 }
 
-// Slot 2*layer + branch of global V tile t.
+// Slot 2*layer + branch of global V tile t (one layer: `vsplit` = tiles of
+// branch 0).
 template <bool SINGLE>
-__device__ __forceinline__ int v_slot(const TileMap& M, int t, int& tile) {
+__device__ __forceinline__ int v_slot(const TileMap& M, int vsplit, int t, int& tile) {
+  if (SINGLE) {
+    const int k = t >= vsplit ? 1 : 0;
+    tile = t - (k ? vsplit : 0);
+    return k;
+  }
   int k = 0, beg = 0;
-  const int nk = SINGLE ? 2 : 2 * LB_MAX_LAYERS;
 #pragma unroll
-  for (int q = 0; q < nk - 1; ++q)
+  for (int q = 0; q < 2 * LB_MAX_LAYERS - 1; ++q)
     if (q < 2 * M.nl - 1 && t >= M.ve[q]) { k = q + 1; beg = M.ve[q]; }
   tile = t - beg;
   return k;
@@ -149,12 +152,6 @@ __device__ __forceinline__ int v_slot(const TileMap& M, int t, int& tile) {
 __device__ inline void share(int q, int r, int i, int& beg, int& end) {
   beg = i * q + min(i, r);
   end = beg + q + (i < r ? 1 : 0);
-}
-
-// Sum over aligned groups of `width` lanes (width = power of 2 <= 64).
-__device__ inline float seg_sum(float v, int width) {
-  for (int off = 1; off < width; off <<= 1) v += __shfl_xor(v, off, 64);
-  return v;
 }
 
 // Phase-B role of wave `wave` (scalar): branch and pair range.
@@ -172,21 +169,9 @@ __device__ inline void u_role(const LayerView& L, int wave, int& b, int& p0, int
   }
 }
 
-// Sum of the negated-class halves (dwords 1 and 3) of an operand fragment.
-__device__ inline float negated_class_sum(f16x8 v, float acc) {
-  typedef f16 h2 __attribute__((ext_vector_type(2)));
-  const h2 one = {(f16)1.0f, (f16)1.0f};
-  const u32x4 d = __builtin_bit_cast(u32x4, v);
-  // copy the elements to scalars first: bit_cast of a vector-element lvalue
-  // reads the vector's first element with this compiler
-  const uint32_t d1 = d[1], d3 = d[3];
-  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, d1), one, acc, false);
-  return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, d3), one, acc, false);
-}
-
 // ------------------------------------------------------------------ phase A
 // One 16-row tile of sign(V)^T of branch b of layer L: t, then
-// z = fp16(l*t), stored (negated in the negated class) as tagged words.
+// z = fp16(l*t), stored as tagged words.
 // The reduction over n runs in LDS chunks of `chunk_pairs` pairs (128 inputs
 // each, at most LB_WAVES * LB_MAXPV); each wave takes a contiguous eighth of
 // a chunk and holds all its sign words in registers.
@@ -200,8 +185,8 @@ struct BoolTag {
 
 template <bool HOOK, class Hook>
 __device__ __forceinline__ void v_tile(const LayerView& L, int batch, int b, int tile, int chunk_pairs,
-                                       uint32_t ctr, const LbSignConsts& sc, uint16_t* u_lds,
-                                       float (*red)[256], float* part, float* cu, Hook&& hook) {
+                                       const uint32_t& ctr, const LbSignConsts& sc, uint16_t* u_lds,
+                                       float (*red)[256], uint32_t* zstage, Hook&& hook) {
   const int n = L.n;
   const long ldx = L.ldx;
   const uint16_t* __restrict__ x = L.x;
@@ -215,8 +200,7 @@ __device__ __forceinline__ void v_tile(const LayerView& L, int batch, int b, int
   const int trow = min(tok, batch - 1);      // operand row read by this lane
   const int rho = tid & 15, tk = (tid >> 4) & 15;  // epilogue role (threads < 256)
   const int j = 16 * tile + rho;
-  // fp16 bits of l[j], loaded from an always-valid index and converted at use
-  const uint32_t lj_raw = (b ? L.l1 : L.l0)[min(j, r - 1)];
+  uint32_t lj_raw = 0;  // fp16 bits of l[j], loaded after the first sign words
 
   int lb = 0;
   while ((1 << lb) < batch) ++lb;
@@ -227,7 +211,6 @@ __device__ __forceinline__ void v_tile(const LayerView& L, int batch, int b, int
   // inputs is either wholly below n or wholly at/after it)
   const bool fast = ((((uintptr_t)x) & 15) == 0) && ((ldx & 7) == 0) && ((n & 7) == 0);
   const uint16_t* __restrict__ xr = x + (long)min(my_tok, batch - 1) * ldx;
-  float csum_u = 0.f;
 
   // x and g of inputs k..k+7 (zero at and beyond n)
   auto load_xg = [&](int k, uint4& xv, uint4& gv) {
@@ -263,6 +246,9 @@ __device__ __forceinline__ void v_tile(const LayerView& L, int batch, int b, int
     const int plast = max(pe - 1, 0);
 #pragma unroll
     for (int i = 0; i < LB_MAXPV; ++i) words[i] = lb16_load_pair(tile_ptr, min(pb + i, plast), lane, nu);
+    // l[j] (from an always-valid index; converted at use) needs fields that
+    // arrive with the kernel arguments, so its load comes after the words
+    if (cb == 0) lj_raw = (b ? L.l1 : L.l0)[min(j, r - 1)];
 
     __syncthreads();  // previous users of u_lds are done
     if (my_tok < batch) {
@@ -275,15 +261,7 @@ __device__ __forceinline__ void v_tile(const LayerView& L, int batch, int b, int
         const uint16_t* ge = reinterpret_cast<const uint16_t*>(&gv);
         uint16_t vals[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const f16 hv = (f16)(h2f(ge[e]) * h2f(xe[e]));
-          if (lb16_negated_class(e)) {  // k is a multiple of 8
-            csum_u += (float)hv;
-            vals[e] = __builtin_bit_cast(uint16_t, (f16)(-hv));
-          } else {
-            vals[e] = __builtin_bit_cast(uint16_t, hv);
-          }
-        }
+        for (int e = 0; e < 8; ++e) vals[e] = f2h(h2f(ge[e]) * h2f(xe[e]));
         *reinterpret_cast<uint4*>(u_lds + my_tok * rowh + 8 * k8) = *reinterpret_cast<uint4*>(vals);
       }
     }
@@ -305,11 +283,13 @@ __device__ __forceinline__ void v_tile(const LayerView& L, int batch, int b, int
         const int pn = (p + 1 < pe) ? p + 1 : p;
 #pragma unroll
         for (int st = 0; st < 4; ++st) bn[st] = *reinterpret_cast<const f16x8*>(ub + 32 * (4 * pn + st));
-        const uint32_t reg = lb16_reg_word(words[i], lb16_pair_sel(p, lane, nu));
-        acc = mfma16(lb16_step_operand(reg, 0, sc), bv[0], acc);
-        acc1 = mfma16(lb16_step_operand(reg, 1, sc), bv[1], acc1);
-        acc = mfma16(lb16_step_operand(reg, 2, sc), bv[2], acc);
-        acc1 = mfma16(lb16_step_operand(reg, 3, sc), bv[3], acc1);
+        // late(): the expansion is not hoisted above this point (it would hold
+        // registers and wait for the load early)
+        const uint32_t reg = lb16_reg_word(late(words[i]), lb16_pair_sel(p, lane, nu));
+        acc = mfma16(lb16_step_operand_val(reg, 0, sc.sign_mask, sc.one_pair), bv[0], acc);
+        acc1 = mfma16(lb16_step_operand_val(reg, 1, sc.sign_mask, sc.one_pair), bv[1], acc1);
+        acc = mfma16(lb16_step_operand_val(reg, 2, sc.sign_mask, sc.one_pair), bv[2], acc);
+        acc1 = mfma16(lb16_step_operand_val(reg, 3, sc.sign_mask, sc.one_pair), bv[3], acc1);
 #pragma unroll
         for (int st = 0; st < 4; ++st) bv[st] = bn[st];
       }
@@ -323,27 +303,17 @@ __device__ __forceinline__ void v_tile(const LayerView& L, int batch, int b, int
   for (int cb = cb0; cb < np; cb += chunk_pairs) chunk(cb, BoolTag<false>());
   acc += acc1;
 
-  // per-token sum of the negated-class u (deterministic)
-  part[tid] = seg_sum(csum_u, min(tpt, 64));
 #pragma unroll
   for (int i = 0; i < 4; ++i) red[wave][(4 * grp + i) * 16 + tok] = acc[i];
-  __syncthreads();
-  if (tid < 16) {
-    float s = 0.f;
-    if (tid < batch)
-      for (int w = 0; w < tpt; w += 64) s += part[tid * tpt + w];
-    cu[tid] = s;
-  }
   __syncthreads();
 
   if (tid < 256) {
     const int e = rho * 16 + tk;
-    float t = cu[tk];
+    float t = 0.f;
 #pragma unroll
     for (int w = 0; w < LB_WAVES; ++w) t += red[w][e];
     const f16 zv = (j < r) ? (f16)(h2f((uint16_t)late(lj_raw)) * t) : (f16)0.f;
-    const f16 zst = lb16_negated_class(j) ? (f16)(-zv) : zv;
-    reinterpret_cast<uint16_t*>(part)[tk * 16 + rho] = __builtin_bit_cast(uint16_t, zst);
+    reinterpret_cast<uint16_t*>(zstage)[tk * 16 + rho] = __builtin_bit_cast(uint16_t, zv);
   }
   __syncthreads();
   // tagged words: [tag | z(2q) | z(2q+1)], 8 words per token for the 16 rows
@@ -352,7 +322,7 @@ __device__ __forceinline__ void v_tile(const LayerView& L, int batch, int b, int
   const uint32_t tag = late(ctr) + 1u;
   if (tid < 8 * batch) {
     const int q = tid & 7, tt = tid >> 3;
-    const uint32_t v = reinterpret_cast<const uint32_t*>(part)[tt * 8 + q];
+    const uint32_t v = zstage[tt * 8 + q];
     st64c(zw + (long)tt * zrow + zoff + 8 * tile + q, (uint64_t)tag | ((uint64_t)v << 32));
   }
   // the last tile also writes the zero words between 16*ceil(r/16) and 64*ceil(r/64)
@@ -394,7 +364,6 @@ __device__ __forceinline__ void u_prefetch(const LayerView& L, int tile, UTilePr
 struct UState {
   int li;              // layer whose z fragments are in registers (-1: none)
   int b, p0, p1, nu;
-  float dw;            // this wave's share of the branch's negated-class z sum (per token)
   f16x8 bfr[LB_MAXPW * 4];
 };
 
@@ -445,12 +414,6 @@ __device__ __forceinline__ void u_enter_layer(const LayerView& L, int li, int ba
       break;
     }
   }
-  float d = 0.f;
-#pragma unroll
-  for (int i = 0; i < LB_MAXPW * 4; ++i) d = negated_class_sum(S.bfr[i], d);
-  d += __shfl_xor(d, 16, 64);
-  d += __shfl_xor(d, 32, 64);
-  S.dw = -d;  // fragments hold the negated-class values negated
 }
 
 __device__ __forceinline__ void u_tile(const LayerView& L, int li, int batch, int tile, const UTilePre& P,
@@ -461,15 +424,15 @@ __device__ __forceinline__ void u_tile(const LayerView& L, int li, int batch, in
   if (li != S.li) u_enter_layer(L, li, batch, ctr, check, sync, S);
 
   // fragments beyond the branch's steps are zero, so every pair runs 4 steps
-  f32x4 acc = {S.dw, S.dw, S.dw, S.dw}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < LB_MAXPW; ++i) {
     if (S.p0 + i < S.p1) {
-      const uint32_t reg = lb16_reg_word(P.w[i], lb16_pair_sel(S.p0 + i, lane, S.nu));
-      acc = mfma16(lb16_step_operand(reg, 0, sc), S.bfr[4 * i + 0], acc);
-      acc1 = mfma16(lb16_step_operand(reg, 1, sc), S.bfr[4 * i + 1], acc1);
-      acc = mfma16(lb16_step_operand(reg, 2, sc), S.bfr[4 * i + 2], acc);
-      acc1 = mfma16(lb16_step_operand(reg, 3, sc), S.bfr[4 * i + 3], acc1);
+      const uint32_t reg = lb16_reg_word(late(P.w[i]), lb16_pair_sel(S.p0 + i, lane, S.nu));
+      acc = mfma16(lb16_step_operand_val(reg, 0, sc.sign_mask, sc.one_pair), S.bfr[4 * i + 0], acc);
+      acc1 = mfma16(lb16_step_operand_val(reg, 1, sc.sign_mask, sc.one_pair), S.bfr[4 * i + 1], acc1);
+      acc = mfma16(lb16_step_operand_val(reg, 2, sc.sign_mask, sc.one_pair), S.bfr[4 * i + 2], acc);
+      acc1 = mfma16(lb16_step_operand_val(reg, 3, sc.sign_mask, sc.one_pair), S.bfr[4 * i + 3], acc1);
     }
   }
   acc += acc1;
@@ -479,7 +442,6 @@ __device__ __forceinline__ void u_tile(const LayerView& L, int li, int batch, in
     const uint8_t* tp = (S.b ? L.ub1 : L.ub0) + (long)tile * lb16_tile_bytes(r);
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(L.z, batch * L.zs * 4);
     const int zb = 4 * (min(tok, batch - 1) * L.zs + (S.b ? L.zoff1 : L.zoff0) + 8 * grp);
-    float d = 0.f;
     for (int p = S.p0 + LB_MAXPW; p < S.p1; ++p) {
       const uint32_t reg = lb16_reg_word(lb16_load_pair(tp, p, lane, S.nu), lb16_pair_sel(p, lane, S.nu));
       const int nsteps = (2 * p + 1 < S.nu) ? 4 : 2;
@@ -490,14 +452,9 @@ __device__ __forceinline__ void u_tile(const LayerView& L, int li, int batch, in
         u32x4 dd;
         dd[0] = q0[1]; dd[1] = q0[3]; dd[2] = q1[1]; dd[3] = q1[3];
         const f16x8 bv = __builtin_bit_cast(f16x8, dd);
-        d = negated_class_sum(bv, d);
-        acc = mfma16(lb16_step_operand(reg, st, sc), bv, acc);
+        acc = mfma16(lb16_step_operand_val(reg, st, sc.sign_mask, sc.one_pair), bv, acc);
       }
     }
-    d += __shfl_xor(d, 16, 64);
-    d += __shfl_xor(d, 32, 64);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) acc[q] -= d;
   }
   __syncthreads();  // previous epilogue done with red
 #pragma unroll
@@ -532,38 +489,57 @@ __device__ __forceinline__ void u_tile(const LayerView& L, int li, int batch, in
 // -------------------------------------------------------------- kernels
 
 // MODE 0: phase A only; 1: phase B only; 2: both in one launch (z tagged and
-// polled).  SINGLE: one layer, whose fields are loaded once at kernel start.
-// Workgroup w takes a contiguous range of the V tiles and of the U tiles.
+// polled).  SINGLE: one layer.  Workgroup w takes a contiguous range of the V
+// tiles and of the U tiles.
+//
+// The leading arguments are preloaded into scalar registers by the dispatch
+// (kernel-argument preloading), so a single-layer kernel issues its first
+// sign-word and activation loads without waiting for a kernel-argument fetch.
+// They repeat fields of A.L[0]; the multi-layer kernel ignores them.
+//   misc = vq | vr << 8 | batch << 16 | chunk_pairs << 21  (V tiles of
+//          workgroup w: vq + (w < vr), contiguous)
 template <int MODE, bool SINGLE>
-__global__ __launch_bounds__(LB_THREADS) void lb_decode_kernel(LbDecodeArgs A, int chunk_pairs, uint8_t* sync) {
+__global__ __launch_bounds__(LB_THREADS) void lb_decode_kernel(
+    const uint8_t* pre_vb0, const uint8_t* pre_vb1, const uint16_t* pre_x, const uint16_t* pre_g0,
+    const uint16_t* pre_g1, int pre_n, int pre_ldx, int pre_vsplit, uint32_t pre_misc,
+    LbDecodeArgs A, int chunk_pairs_arg, uint8_t* sync) {
   extern __shared__ __align__(16) uint16_t u_lds[];
   __shared__ __align__(16) float red[LB_WAVES][256];
-  __shared__ __align__(16) float part[LB_THREADS];
-  __shared__ __align__(16) float cu[16];
+  __shared__ __align__(16) uint32_t zstage[128];  // one tile's z (16 tokens x 16 rows of fp16)
 
   const int wg = blockIdx.x;
-  const int batch = A.batch;
+  const int batch = SINGLE ? (int)((pre_misc >> 16) & 31u) : A.batch;
+  const int chunk_pairs = SINGLE ? (int)(pre_misc >> 21) : chunk_pairs_arg;
   const LbSignConsts sc = lb16_sign_consts();
   TileMap M;
   load_map(A, M);
   LayerView V0;
   if (SINGLE) {
     V0 = layer_view(A.L[0]);
+    V0.vb0 = pre_vb0;
+    V0.vb1 = pre_vb1;
+    V0.x = pre_x;
+    V0.g0 = pre_g0;
+    V0.g1 = pre_g1;
+    V0.n = pre_n;
+    V0.ldx = pre_ldx;
   }
 
-  // this workgroup's call counter (single launch only): the tag is its value + 1
-  uint32_t ctr = 0;
-  if (MODE == 2) ctr = ld32c(sync + LB_SYNC_CTR + 8 * wg);
-
-  int ut0, ut1, vt0, vt1;
-  share(A.uq, A.ur, wg, ut0, ut1);
-  share(A.vq, A.vr, wg, vt0, vt1);
+  int ut0 = 0, ut1 = 0, vt0, vt1;
+  if (SINGLE)
+    share((int)(pre_misc & 255u), (int)((pre_misc >> 8) & 255u), wg, vt0, vt1);
+  else
+    share(A.vq, A.vr, wg, vt0, vt1);
   if (MODE == 1) vt1 = vt0;
-  if (MODE == 0) ut1 = ut0;
+  // this workgroup's call counter (single launch only): the tag is its value
+  // + 1.  Loaded with the phase-B prefetch, after the first V-tile loads.
+  uint32_t ctr = 0;
   UTilePre pre[LB_MAXT];
   // every load is issued (tiles clamped to a valid one), which keeps the
   // wait counts exact; tiles beyond ut1 are never used
   auto prefetch = [&]() {
+    if (MODE == 2) ctr = ld32c(sync + LB_SYNC_CTR + 8 * wg);
+    share(A.uq, A.ur, wg, ut0, ut1);
     const int nut = A.nut;
 #pragma unroll
     for (int k = 0; k < LB_MAXT; ++k) {
@@ -576,20 +552,24 @@ __global__ __launch_bounds__(LB_THREADS) void lb_decode_kernel(LbDecodeArgs A, i
   // words and activations, or at once by a workgroup without V tiles
   if (vt0 < vt1) {
     int tile;
-    const int k = v_slot<SINGLE>(M, vt0, tile);
+    const int k = v_slot<SINGLE>(M, pre_vsplit, vt0, tile);
     v_tile<MODE == 2>(SINGLE ? V0 : layer_view(A.L[k >> 1]), batch, k & 1, tile, chunk_pairs, ctr, sc, u_lds,
-                      red, part, cu, prefetch);
+                      red, zstage, prefetch);
     __syncthreads();
   } else if (MODE == 2) {
+    // no V tile here: let the V-tile workgroups' sign words go to memory
+    // first, then fetch this workgroup's phase-B data
+    __builtin_amdgcn_s_sleep(24);
     prefetch();
   }
   for (int t = vt0 + 1; t < vt1; ++t) {
     int tile;
-    const int k = v_slot<SINGLE>(M, t, tile);
+    const int k = v_slot<SINGLE>(M, pre_vsplit, t, tile);
     v_tile<false>(SINGLE ? V0 : layer_view(A.L[k >> 1]), batch, k & 1, tile, chunk_pairs, ctr, sc, u_lds, red,
-                  part, cu, prefetch);
+                  zstage, prefetch);
     __syncthreads();
   }
+  if (MODE == 1) share(A.uq, A.ur, wg, ut0, ut1);
   if (MODE != 0) {
     const bool check = MODE == 2;
     UState S;
@@ -627,6 +607,17 @@ static hipError_t launch_decode_t(const LbDecodeArgs& args, int chunk_pairs, voi
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
+  // preloaded copies of layer 0's phase-A fields (single-layer kernels)
+  const LbLayerArgs& L0 = args.L[0];
+  const uint8_t* vb0 = SINGLE ? L0.br[0].vbits : nullptr;
+  const uint8_t* vb1 = SINGLE ? L0.br[1].vbits : nullptr;
+  const uint16_t* px = SINGLE ? L0.x : nullptr;
+  const uint16_t* g0 = SINGLE ? L0.br[0].g : nullptr;
+  const uint16_t* g1 = SINGLE ? L0.br[1].g : nullptr;
+  const int pn = SINGLE ? L0.n : 0, pldx = SINGLE ? (int)L0.ldx : 0, vsplit = SINGLE ? args.vt_end[0] : 0;
+  auto misc = [&](const LbDecodeArgs& a) {
+    return (uint32_t)a.vq | ((uint32_t)a.vr << 8) | ((uint32_t)a.batch << 16) | ((uint32_t)chunk_pairs << 21);
+  };
   if (allow_fused && dev >= 0 && dev < 64) {
     if (g_fused_grid[dev] == 0) {
       int ncu = 0, occ1 = 0, occ7 = 0;
@@ -645,21 +636,21 @@ static hipError_t launch_decode_t(const LbDecodeArgs& args, int chunk_pairs, voi
       LbDecodeArgs a = args;
       a.vq = a.nvt / G; a.vr = a.nvt % G;
       a.uq = a.nut / G; a.ur = a.nut % G;
-      hipLaunchKernelGGL((lb_decode_kernel<2, SINGLE>), dim3(G), dim3(LB_THREADS), lds, stream, a, chunk_pairs,
-                         (uint8_t*)sync);
+      hipLaunchKernelGGL((lb_decode_kernel<2, SINGLE>), dim3(G), dim3(LB_THREADS), lds, stream, vb0, vb1, px, g0,
+                         g1, pn, pldx, vsplit, misc(a), a, chunk_pairs, (uint8_t*)sync);
       return hipGetLastError();
     }
   }
   LbDecodeArgs a = args;
   a.vq = 1; a.vr = 0;
-  hipLaunchKernelGGL((lb_decode_kernel<0, SINGLE>), dim3(a.nvt), dim3(LB_THREADS), lds, stream, a, chunk_pairs,
-                     (uint8_t*)sync);
+  hipLaunchKernelGGL((lb_decode_kernel<0, SINGLE>), dim3(a.nvt), dim3(LB_THREADS), lds, stream, vb0, vb1, px, g0,
+                     g1, pn, pldx, vsplit, misc(a), a, chunk_pairs, (uint8_t*)sync);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int gb = a.nut < 1024 ? a.nut : 1024;
   a.uq = a.nut / gb; a.ur = a.nut % gb;
-  hipLaunchKernelGGL((lb_decode_kernel<1, SINGLE>), dim3(gb), dim3(LB_THREADS), 0, stream, a, chunk_pairs,
-                     (uint8_t*)sync);
+  hipLaunchKernelGGL((lb_decode_kernel<1, SINGLE>), dim3(gb), dim3(LB_THREADS), 0, stream, vb0, vb1, px, g0, g1,
+                     pn, pldx, vsplit, misc(a), a, chunk_pairs, (uint8_t*)sync);
   return hipGetLastError();
 }
 

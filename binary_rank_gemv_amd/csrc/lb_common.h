@@ -61,25 +61,11 @@ __device__ inline LbSignConsts lb16_sign_consts() {
   return c;
 }
 
-// The four operand dwords (8 fp16 values) of step `st` (0..3) of a register
-// word.  Even q: bits 15/31 after the shift are signs -> +-1.0 (0x3C00).
-// Odd q: bits 14/30 -> 0.0 or 2.0; the matching activations are stored
-// negated and their sum is added back, so  A.B' + sum = sum_k sign_k * act_k.
-__device__ inline f16x8 lb16_step_operand(uint32_t reg, int st, const LbSignConsts& c) {
-  const uint32_t w0 = reg << (4 * st);
-  const uint32_t w1 = reg << (4 * st + 2);
-  u32x4 d;
-  d[0] = (w0 & c.sign_mask) | c.one_pair;
-  d[1] = w0 & 0x40004000u;
-  d[2] = (w1 & c.sign_mask) | c.one_pair;
-  d[3] = w1 & 0x40004000u;
-  return __builtin_bit_cast(f16x8, d);
-}
-
-// The same step with every value exactly +-v, where `vpair` holds the fp16
-// bits of v >= 0 in both halves (v = 1.0: 0x3C003C00).  For odd q the sign
-// bit sits one position lower, so the word is shifted one further.  Two
-// instructions per value pair.  (A negative scale is applied by inverting
+// The four operand dwords (8 fp16 values) of step `st` (0..3) of a pair's
+// register word, every value exactly +-v, where `vpair` holds the fp16 bits
+// of v >= 0 in both halves (v = 1.0: 0x3C003C00).  Dword q's two signs sit
+// at bits 15-(4st+q) and 31-(4st+q): a left shift by 4st+q brings them to
+// the fp16 sign positions.  Two instructions per value pair.  (A negative scale is applied by inverting
 // every bit of the register word first: all values of a lane share one row.)
 __device__ inline f16x8 lb16_step_operand_val(uint32_t reg, int st, uint32_t sign_mask, uint32_t vpair) {
   u32x4 d;
@@ -89,9 +75,6 @@ __device__ inline f16x8 lb16_step_operand_val(uint32_t reg, int st, uint32_t sig
   d[3] = ((reg << (4 * st + 3)) & sign_mask) | vpair;
   return __builtin_bit_cast(f16x8, d);
 }
-
-// Activation index k belongs to the "odd q" operand class iff (k & 2) != 0.
-__host__ __device__ inline bool lb16_negated_class(int k) { return (k & 2) != 0; }
 
 __device__ inline f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);

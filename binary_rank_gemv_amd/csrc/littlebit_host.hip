@@ -223,6 +223,8 @@ lb_status littlebit_linear_fwd(const lb_layer* L, uint32_t branch_mask, const ui
   if (!x || !y) return fail(LB_ERR_INVALID_ARG, "littlebit_linear_fwd: x or y is NULL");
   if (batch < 1) return fail(LB_ERR_INVALID_ARG, "littlebit_linear_fwd: batch=%lld must be >= 1", (long long)batch);
   if (ldx < L->n || ldy < L->m) return fail(LB_ERR_INVALID_ARG, "littlebit_linear_fwd: ldx/ldy smaller than n/m");
+  if (ldx > INT32_MAX || ldy > INT32_MAX)
+    return fail(LB_ERR_UNSUPPORTED, "littlebit_linear_fwd: row strides above 2^31-1 elements");
   if (!aligned(x, 2) || !aligned(y, 2)) return fail(LB_ERR_INVALID_ARG, "littlebit_linear_fwd: x and y must be 2-byte aligned");
   if ((flags & 3u) == 3u || (flags & ~(3u | LB_DECODE_TWO_LAUNCHES)))
     return fail(LB_ERR_INVALID_ARG, "littlebit_linear_fwd: unknown flags %u", flags);

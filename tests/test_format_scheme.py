@@ -3,13 +3,12 @@
 These CPU tests model, in plain Python, how a 64-lane matrix-core fragment is
 formed from LB16 bytes (packed here by the oracle's packer): a lane loads one
 aligned 32-bit word per pair of 16-bit units (an odd last unit comes with its
-neighbour lane's unit) and rearranges its bytes with a byte permutation, then for q = 0..15
-shifts the word left by 2*floor(q/2) and masks either bits 15/31 (q even,
-giving fp16 +-1 after OR-ing in 1.0) or bits 14/30 (q odd, giving fp16 0 or
-2).  Element k lands in the q-odd class exactly when (k & 2) != 0, so a
-contraction with the q-odd operand entries negated, plus the sum of those
-operand entries, equals the signed contraction.  Nothing here is the GPU
-code; it checks that the format makes that scheme exact.
+neighbour lane's unit) and rearranges its bytes with a byte permutation; then
+operand dword q (q = 4*step + d, two fp16 values) is the word shifted left by
+q, masked to bits 15 and 31, and OR-ed with the bits of 1.0 in both halves.
+Every fragment entry must come out as exactly the sign, +1.0 or -1.0, at the
+row and input index the fragment layout assigns to it.  Nothing here is the
+GPU code; it checks that the format makes that scheme exact.
 """
 
 import numpy as np
@@ -51,11 +50,10 @@ def _fp16_bits_to_float(bits16):
 
 
 def _fragment_values(packed, R, K):
-    """A[a, k] as the lanes would build them; cls[k] = True for the q-odd class."""
+    """A[a, k] as the lanes would build them (NaN where no lane writes)."""
     rp, kp = 16 * ((R + 15) // 16), 64 * ((K + 63) // 64)
     nt, nu = rp // 16, kp // 64
     A = np.full((nt * 16, kp), np.nan)
-    cls = np.zeros(kp, dtype=bool)
     for T in range(nt):
         for L in range(64):
             row, c = 16 * T + L % 16, L // 16
@@ -65,31 +63,26 @@ def _fragment_values(packed, R, K):
                     step = 4 * p + q // 4
                     if 32 * step >= kp:
                         continue
-                    ws = (reg << (2 * (q // 2))) & 0xFFFFFFFF
-                    dw = ((ws & 0x80008000) | 0x3C003C00) if q % 2 == 0 else (ws & 0x40004000)
+                    dw = (((reg << q) & 0xFFFFFFFF) & 0x80008000) | 0x3C003C00
                     d = q % 4
                     for half, e in ((0, 2 * d), (1, 2 * d + 1)):
                         k = 32 * step + 8 * c + e
+                        assert np.isnan(A[row, k]), "two lanes write one entry"
                         A[row, k] = _fp16_bits_to_float((dw >> (16 * half)) & 0xFFFF)
-                        cls[k] = (q % 2 == 1)
-    return A, cls
+    return A
 
 
 @pytest.mark.parametrize("R,K", [(16, 64), (16, 128), (16, 192), (20, 600), (40, 320), (32, 1472)])
 def test_fragment_unpack_reproduces_signs(R, K):
     rng = np.random.default_rng(R + K)
     neg = rng.random((R, K)) < 0.5
-    A, cls = _fragment_values(oracle.pack_factor(neg), R, K)
-    kk = np.arange(A.shape[1])
-    np.testing.assert_array_equal(cls, (kk & 2) != 0)
+    A = _fragment_values(oracle.pack_factor(neg), R, K)
     s = np.where(neg, -1.0, 1.0)
-    for k in range(K):
-        if cls[k]:
-            np.testing.assert_array_equal(A[:R, k], np.where(neg[:, k], 2.0, 0.0))
-        else:
-            np.testing.assert_array_equal(A[:R, k], s[:, k])
-    # exact signed contraction through the class rule
+    np.testing.assert_array_equal(A[:R, :K], s)
+    # padding (rows >= R, inputs >= K) unpacks to +1: the kernels pair it with
+    # zero activations and never store padded rows
+    assert not np.isnan(A).any()
+    assert (A[R:, :] == 1.0).all() and (A[:, K:] == 1.0).all()
+    # exact signed contraction
     u = rng.standard_normal(K)
-    Bp = np.where(cls[:K], -u, u)
-    got = A[:R, :K] @ Bp + u[cls[:K]].sum()
-    np.testing.assert_allclose(got, s @ u, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(A[:R, :K] @ u, s @ u, rtol=1e-12, atol=1e-12)
