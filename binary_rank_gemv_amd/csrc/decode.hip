@@ -131,6 +131,16 @@ __device__ __forceinline__ int u_layer(const TileMap& M, int t, int& tile) {
   return li;
 }
 
+// End (exclusive) of layer li's global U tiles, without indexing the
+// register array by a run-time value.
+__device__ __forceinline__ int layer_u_end(const TileMap& M, int li) {
+  int e = M.ue[0];
+#pragma unroll
+  for (int i = 1; i < LB_MAX_LAYERS; ++i)
+    if (li == i) e = M.ue[i];
+  return e;
+}
+
 // Slot 2*layer + branch of global V tile t (one layer: `vsplit` = tiles of
 // branch 0).
 template <bool SINGLE>
@@ -175,8 +185,9 @@ __device__ inline void u_role(const LayerView& L, int wave, int& b, int& p0, int
 // The reduction over n runs in LDS chunks of `chunk_pairs` pairs (128 inputs
 // each, at most LB_WAVES * LB_MAXPV); each wave takes a contiguous eighth of
 // a chunk and holds all its sign words in registers.
-// With HOOK, `hook` runs after the first chunk's activations are staged (its
-// loads then queue behind this tile's sign words).  The first chunk is its
+// With HOOK, `hook` runs after the first chunk's matrix steps are issued, i.e.
+// once this tile's sign words have arrived, so its loads do not compete with
+// them for memory.  The first chunk is its
 // own copy of the code, so every wait count in it is exact.
 template <bool B>
 struct BoolTag {
@@ -265,7 +276,6 @@ __device__ __forceinline__ void v_tile(const LayerView& L, int batch, int b, int
         *reinterpret_cast<uint4*>(u_lds + my_tok * rowh + 8 * k8) = *reinterpret_cast<uint4*>(vals);
       }
     }
-    if constexpr (decltype(with_hook)::value) hook();
     __syncthreads();
 
     // inputs beyond n are zero in LDS, so the odd last unit's two missing
@@ -294,6 +304,7 @@ __device__ __forceinline__ void v_tile(const LayerView& L, int batch, int b, int
         for (int st = 0; st < 4; ++st) bv[st] = bn[st];
       }
     }
+    if constexpr (decltype(with_hook)::value) hook();
   };
   int cb0 = 0;
   if constexpr (HOOK) {
@@ -338,12 +349,25 @@ __device__ __forceinline__ void v_tile(const LayerView& L, int batch, int b, int
 }
 
 // ------------------------------------------------------------------ phase B
-// Prefetched per-tile data: this wave's sign words and the epilogue thread's
-// row scales (h of both branches).
+// Prefetched per-tile data: this wave's sign words.
 struct UTilePre {
   uint32_t w[LB_MAXPW];
-  uint32_t h0, h1;  // fp16 bits: converting here would wait for the load
 };
+
+// Row scales (h of both branches, fp16 bits: converting here would wait for
+// the load) of the two epilogue entries of a thread in a tile group: entry j
+// belongs to tile (wave >> 2) + 2 j of the group and row (tid & 15).
+struct HPre {
+  uint32_t h0[2], h1[2];
+};
+
+// Loads entry j's row scales: row 16*tile + (tid & 15) of layer L (a row
+// beyond m loads row m - 1; such entries are never stored).
+__device__ __forceinline__ void load_h(const LayerView& L, int tile, HPre& H, int j) {
+  const int i = min(16 * tile + (int)(threadIdx.x & 15), L.m - 1);
+  H.h0[j] = L.h0[i];
+  H.h1[j] = (L.nb == 2 ? L.h1 : L.h0)[i];
+}
 
 __device__ __forceinline__ void u_prefetch(const LayerView& L, int tile, UTilePre& P) {
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
@@ -355,133 +379,192 @@ __device__ __forceinline__ void u_prefetch(const LayerView& L, int tile, UTilePr
   const int plast = max(p1 - 1, 0);
 #pragma unroll
   for (int i = 0; i < LB_MAXPW; ++i) P.w[i] = lb16_load_pair(tp, min(p0 + i, plast), lane, nu);
-  // loaded from always-valid indices (rows >= m are never stored)
-  const int i = min(16 * tile + (tid & 15), L.m - 1);
-  P.h0 = L.h0[i];
-  P.h1 = (L.nb == 2 ? L.h1 : L.h0)[i];
 }
 
+// Phase-B role of a wave for the layer whose z is staged in LDS.
 struct UState {
-  int li;              // layer whose z fragments are in registers (-1: none)
+  int li;              // layer whose z is in LDS (-1: none)
   int b, p0, p1, nu;
-  f16x8 bfr[LB_MAXPW * 4];
 };
 
-// Loads this wave's z fragments for layer L (index li).  With check, polls
-// until every tagged word of the wave's range carries `tag`.
+#define LB_POLL_STEPS (4 * LB_MAXPW)  // z steps polled per memory round trip
+
+// Copies this wave's range of layer L's z into LDS (zl: [token][zs + 8] fp16),
+// polling (check) until every word carries this call's tag.  The steps go in
+// batches of LB_POLL_STEPS; every load of a batch is issued before any result
+// is examined, so a batch costs one memory round trip.  A wave later reads
+// only the range it copied, so no barrier follows the copy; the barrier in
+// front keeps the previous layer's readers safe.
 __device__ __forceinline__ void u_enter_layer(const LayerView& L, int li, int batch, uint32_t ctr, bool check,
-                                              uint8_t* sync, UState& S) {
+                                              uint8_t* sync, UState& S, uint16_t* zl) {
   const int lane = threadIdx.x & 63, wave = wave_id();
   const uint32_t tag = late(ctr) + 1u;
   const int tok = lane & 15, grp = lane >> 4;
+  __syncthreads();  // earlier readers of zl (previous layer, or phase A's u) are done
   S.li = li;
   u_role(L, wave, S.b, S.p0, S.p1);
   S.nu = lb16_units(S.b ? L.r1 : L.r0);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(L.z, batch * L.zs * 4);
   const int zb = 4 * (min(tok, batch - 1) * L.zs + (S.b ? L.zoff1 : L.zoff0) + 8 * grp);
-  const int s1 = min(4 * S.p1, 2 * S.nu);
-  // every load is issued (steps clamped to a valid one) before any result is
-  // examined, so one poll costs one memory round trip
-  const int slast = max(s1 - 1, 0);
-  int spins = 0;
-  for (;;) {
-    compiler_memory_barrier();  // every pass re-reads the words
-    bool ok = true;
+  uint16_t* zdst = zl + tok * (L.zs + 8) + (S.b ? L.zoff1 : L.zoff0) + 8 * grp;
+  const int s1 = min(4 * S.p1, 2 * S.nu);  // steps of this wave's range that hold data
+  for (int sb = 4 * S.p0; sb < s1; sb += LB_POLL_STEPS) {
+    int spins = 0;
+    for (;;) {
+      compiler_memory_barrier();  // every pass re-reads the words
+      u32x4 q0[LB_POLL_STEPS], q1[LB_POLL_STEPS];
 #pragma unroll
-    for (int i = 0; i < LB_MAXPW * 4; ++i) {
-      const int step = 4 * S.p0 + i;
-      const int sc = min(step, slast);
-      const u32x4 q0 = ld_tagged2(rs, zb + 128 * sc);
-      const u32x4 q1 = ld_tagged2(rs, zb + 128 * sc + 16);
-      const bool in = step < s1;
-      ok = ok & (!in | ((q0[0] == tag) & (q0[2] == tag) & (q1[0] == tag) & (q1[2] == tag)));
-      u32x4 d;
-      d[0] = in ? q0[1] : 0u;
-      d[1] = in ? q0[3] : 0u;
-      d[2] = in ? q1[1] : 0u;
-      d[3] = in ? q1[3] : 0u;
-      S.bfr[i] = __builtin_bit_cast(f16x8, d);
-    }
-    // steps beyond the register window are read later by u_tile: wait for them too
-    for (int step = 4 * S.p0 + 4 * LB_MAXPW; step < s1; ++step) {
-      const u32x4 q0 = ld_tagged2(rs, zb + 128 * step);
-      const u32x4 q1 = ld_tagged2(rs, zb + 128 * step + 16);
-      ok = ok & (q0[0] == tag) & (q0[2] == tag) & (q1[0] == tag) & (q1[2] == tag);
-    }
-    if (!check || __all(ok)) break;
-    if (++spins > LB_SPIN_LIMIT) {
-      st32c(sync + LB_SYNC_ERR, 1u);
-      break;
+      for (int i = 0; i < LB_POLL_STEPS; ++i) {
+        const int st = min(sb + i, s1 - 1);
+        q0[i] = ld_tagged2(rs, zb + 128 * st);
+        q1[i] = ld_tagged2(rs, zb + 128 * st + 16);
+      }
+      bool ok = true;
+#pragma unroll
+      for (int i = 0; i < LB_POLL_STEPS; ++i)
+        ok = ok & ((q0[i][0] == tag) & (q0[i][2] == tag) & (q1[i][0] == tag) & (q1[i][2] == tag));
+      if (!check || __all(ok)) {
+        if (tok < batch) {
+#pragma unroll
+          for (int i = 0; i < LB_POLL_STEPS; ++i) {
+            if (sb + i < s1) {
+              u32x4 d;
+              d[0] = q0[i][1]; d[1] = q0[i][3]; d[2] = q1[i][1]; d[3] = q1[i][3];
+              *reinterpret_cast<u32x4*>(zdst + 32 * (sb + i)) = d;
+            }
+          }
+        }
+        break;
+      }
+      if (++spins > LB_SPIN_LIMIT) {
+        st32c(sync + LB_SYNC_ERR, 1u);
+        break;
+      }
     }
   }
 }
 
-__device__ __forceinline__ void u_tile(const LayerView& L, int li, int batch, int tile, const UTilePre& P,
-                                       uint32_t ctr, bool check, uint8_t* sync, const LbSignConsts& sc,
-                                       UState& S, float (*red)[256]) {
+// The fp16 outputs an epilogue thread still has to store (p == nullptr: none).
+// Stores are held back until the next group's sign words are requested: a
+// store counts in the same in-order counter as the loads, so a wait for a
+// later load would also wait for the store to reach memory.
+struct YOut {
+  uint16_t* p[2];
+  uint16_t v[2];
+};
+
+__device__ __forceinline__ void store_y(const YOut& o) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    if (o.p[j]) *o.p[j] = o.v[j];
+}
+
+// Phase B for nt <= LB_MAXT consecutive U tiles (from tile0) of layer L, whose
+// sign words and row scales are in P[0..nt): the matrix steps of all tiles
+// run interleaved, then one epilogue (one pair of barriers) finishes them all.
+__device__ __forceinline__ YOut u_group(const LayerView& L, int li, int batch, int tile0, int nt,
+                                        const UTilePre (&P)[LB_MAXT], const HPre& H, uint32_t ctr, bool check,
+                                        uint8_t* sync,
+                                        const LbSignConsts& sc, UState& S, uint16_t* zl,
+                                        float (*red)[LB_WAVES][256]) {
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int tok = lane & 15, grp = lane >> 4;
-  if (li != S.li) u_enter_layer(L, li, batch, ctr, check, sync, S);
+  if (li != S.li) u_enter_layer(L, li, batch, ctr, check, sync, S, zl);
+  // operand rows: absent tokens read the last token's row (never stored)
+  const uint16_t* zb = zl + min(tok, batch - 1) * (L.zs + 8) + (S.b ? L.zoff1 : L.zoff0) + 8 * grp;
+  const int s1 = 2 * S.nu;  // steps of the branch that hold data
 
-  // fragments beyond the branch's steps are zero, so every pair runs 4 steps
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[LB_MAXT];
+#pragma unroll
+  for (int k = 0; k < LB_MAXT; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < LB_MAXPW; ++i) {
-    if (S.p0 + i < S.p1) {
-      const uint32_t reg = lb16_reg_word(late(P.w[i]), lb16_pair_sel(S.p0 + i, lane, S.nu));
-      acc = mfma16(lb16_step_operand_val(reg, 0, sc.sign_mask, sc.one_pair), S.bfr[4 * i + 0], acc);
-      acc1 = mfma16(lb16_step_operand_val(reg, 1, sc.sign_mask, sc.one_pair), S.bfr[4 * i + 1], acc1);
-      acc = mfma16(lb16_step_operand_val(reg, 2, sc.sign_mask, sc.one_pair), S.bfr[4 * i + 2], acc);
-      acc1 = mfma16(lb16_step_operand_val(reg, 3, sc.sign_mask, sc.one_pair), S.bfr[4 * i + 3], acc1);
+    const int p = S.p0 + i;
+    if (p < S.p1) {
+      const uint32_t sel = lb16_pair_sel(p, lane, S.nu);
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        if (4 * p + st < s1) {  // an odd last unit has two steps
+          const f16x8 bv = *reinterpret_cast<const f16x8*>(zb + 32 * (4 * p + st));
+#pragma unroll
+          for (int k = 0; k < LB_MAXT; ++k) {
+            if (k < nt) {
+              // late(): the expansion is not hoisted above this point
+              const uint32_t reg = lb16_reg_word(late(P[k].w[i]), sel);
+              acc[k] = mfma16(lb16_step_operand_val(reg, st, sc.sign_mask, sc.one_pair), bv, acc[k]);
+            }
+          }
+        }
+      }
     }
   }
-  acc += acc1;
   // pairs beyond the register window (ranks above 64 * 4 * LB_MAXPW per wave)
   if (S.p1 > S.p0 + LB_MAXPW) {
     const int r = S.b ? L.r1 : L.r0;
-    const uint8_t* tp = (S.b ? L.ub1 : L.ub0) + (long)tile * lb16_tile_bytes(r);
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(L.z, batch * L.zs * 4);
-    const int zb = 4 * (min(tok, batch - 1) * L.zs + (S.b ? L.zoff1 : L.zoff0) + 8 * grp);
     for (int p = S.p0 + LB_MAXPW; p < S.p1; ++p) {
-      const uint32_t reg = lb16_reg_word(lb16_load_pair(tp, p, lane, S.nu), lb16_pair_sel(p, lane, S.nu));
-      const int nsteps = (2 * p + 1 < S.nu) ? 4 : 2;
-      for (int st = 0; st < nsteps; ++st) {
-        const int step = 4 * p + st;
-        const u32x4 q0 = ld_tagged2(rs, zb + 128 * step);
-        const u32x4 q1 = ld_tagged2(rs, zb + 128 * step + 16);
-        u32x4 dd;
-        dd[0] = q0[1]; dd[1] = q0[3]; dd[2] = q1[1]; dd[3] = q1[3];
-        const f16x8 bv = __builtin_bit_cast(f16x8, dd);
-        acc = mfma16(lb16_step_operand_val(reg, st, sc.sign_mask, sc.one_pair), bv, acc);
+      const uint32_t sel = lb16_pair_sel(p, lane, S.nu);
+      uint32_t w[LB_MAXT];
+#pragma unroll
+      for (int k = 0; k < LB_MAXT; ++k) {
+        const uint8_t* tp = (S.b ? L.ub1 : L.ub0) + (long)(tile0 + min(k, nt - 1)) * lb16_tile_bytes(r);
+        w[k] = lb16_load_pair(tp, p, lane, S.nu);
+      }
+      for (int st = 0; st < 4; ++st) {
+        if (4 * p + st < s1) {
+          const f16x8 bv = *reinterpret_cast<const f16x8*>(zb + 32 * (4 * p + st));
+#pragma unroll
+          for (int k = 0; k < LB_MAXT; ++k) {
+            if (k < nt) {
+              const uint32_t reg = lb16_reg_word(w[k], sel);
+              acc[k] = mfma16(lb16_step_operand_val(reg, st, sc.sign_mask, sc.one_pair), bv, acc[k]);
+            }
+          }
+        }
       }
     }
   }
-  __syncthreads();  // previous epilogue done with red
+  __syncthreads();  // previous users of red are done
 #pragma unroll
-  for (int q = 0; q < 4; ++q) red[wave][(4 * grp + q) * 16 + tok] = acc[q];
+  for (int k = 0; k < LB_MAXT; ++k)
+    if (k < nt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) red[k][wave][(4 * grp + q) * 16 + tok] = acc[k][q];
   __syncthreads();
 
-  const int rho = tid & 15, tk = tid >> 4;
-  const int i = 16 * tile + rho;
-  if (tid < 256 && tk < batch && i < L.m) {
-    const int e = rho * 16 + tk;
-    float y;
-    if (L.nb == 2) {
-      float s0 = 0.f, s1 = 0.f;
+  // thread tid finishes entries tid and tid + 512 of (tile, row, token); its
+  // row 16*tile + (tid & 15) is the one whose scales it prefetched
+  static_assert(LB_MAXT == 3 && LB_THREADS == 512, "epilogue mapping");
+  const int rho = tid & 15, tk = (tid >> 4) & 15;
+  YOut out;
 #pragma unroll
-      for (int w = 0; w < LB_WAVES / 2; ++w) {
-        s0 += red[w][e];
-        s1 += red[w + LB_WAVES / 2][e];
+  for (int j = 0; j < 2; ++j) {
+    out.p[j] = nullptr;
+    out.v[j] = 0;
+    const int k = (wave >> 2) + 2 * j;  // tile of entry tid + 512 j (wave-uniform)
+    const int i = 16 * (tile0 + k) + rho;
+    if (k < nt && tk < batch && i < L.m) {
+      const int e = rho * 16 + tk;
+      const uint32_t h0 = H.h0[j], h1 = H.h1[j];
+      float y;
+      if (L.nb == 2) {
+        float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+        for (int w = 0; w < LB_WAVES / 2; ++w) {
+          s0 += red[k][w][e];
+          s1 += red[k][w + LB_WAVES / 2][e];
+        }
+        y = h2f((uint16_t)late(h0)) * s0 + h2f((uint16_t)late(h1)) * s1;
+      } else {
+        float s0 = 0.f;
+#pragma unroll
+        for (int w = 0; w < LB_WAVES; ++w) s0 += red[k][w][e];
+        y = h2f((uint16_t)late(h0)) * s0;
       }
-      y = h2f((uint16_t)late(P.h0)) * s0 + h2f((uint16_t)late(P.h1)) * s1;
-    } else {
-      float s0 = 0.f;
-#pragma unroll
-      for (int w = 0; w < LB_WAVES; ++w) s0 += red[w][e];
-      y = h2f((uint16_t)late(P.h0)) * s0;
+      out.p[j] = L.y + (long)tk * L.ldy + i;
+      out.v[j] = f2h(y);
     }
-    L.y[(long)tk * L.ldy + i] = f2h(y);
   }
+  return out;
 }
 
 }  // namespace
@@ -504,7 +587,7 @@ __global__ __launch_bounds__(LB_THREADS) void lb_decode_kernel(
     const uint16_t* pre_g1, int pre_n, int pre_ldx, int pre_vsplit, uint32_t pre_misc,
     LbDecodeArgs A, int chunk_pairs_arg, uint8_t* sync) {
   extern __shared__ __align__(16) uint16_t u_lds[];
-  __shared__ __align__(16) float red[LB_WAVES][256];
+  __shared__ __align__(16) float red[LB_MAXT][LB_WAVES][256];  // cross-wave partial sums
   __shared__ __align__(16) uint32_t zstage[128];  // one tile's z (16 tokens x 16 rows of fp16)
 
   const int wg = blockIdx.x;
@@ -535,6 +618,7 @@ __global__ __launch_bounds__(LB_THREADS) void lb_decode_kernel(
   // + 1.  Loaded with the phase-B prefetch, after the first V-tile loads.
   uint32_t ctr = 0;
   UTilePre pre[LB_MAXT];
+  HPre hpre;
   // every load is issued (tiles clamped to a valid one), which keeps the
   // wait counts exact; tiles beyond ut1 are never used
   auto prefetch = [&]() {
@@ -547,6 +631,12 @@ __global__ __launch_bounds__(LB_THREADS) void lb_decode_kernel(
       const int li = u_layer<SINGLE>(M, min(ut0 + k, nut - 1), tile);
       u_prefetch(SINGLE ? V0 : layer_view(A.L[li]), tile, pre[k]);
     }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      int tile;
+      const int li = u_layer<SINGLE>(M, min(ut0 + (wave_id() >> 2) + 2 * j, nut - 1), tile);
+      load_h(SINGLE ? V0 : layer_view(A.L[li]), tile, hpre, j);
+    }
   };
   // phase-B loads are issued during phase A: after the first V tile's sign
   // words and activations, or at once by a workgroup without V tiles
@@ -554,18 +644,18 @@ __global__ __launch_bounds__(LB_THREADS) void lb_decode_kernel(
     int tile;
     const int k = v_slot<SINGLE>(M, pre_vsplit, vt0, tile);
     v_tile<MODE == 2>(SINGLE ? V0 : layer_view(A.L[k >> 1]), batch, k & 1, tile, chunk_pairs, ctr, sc, u_lds,
-                      red, zstage, prefetch);
+                      red[0], zstage, prefetch);
     __syncthreads();
   } else if (MODE == 2) {
     // no V tile here: let the V-tile workgroups' sign words go to memory
-    // first, then fetch this workgroup's phase-B data
-    __builtin_amdgcn_s_sleep(24);
+    // first (about 1.3 us), then fetch this workgroup's phase-B data
+    for (int i = 0; i < 2; ++i) __builtin_amdgcn_s_sleep(24);
     prefetch();
   }
   for (int t = vt0 + 1; t < vt1; ++t) {
     int tile;
     const int k = v_slot<SINGLE>(M, pre_vsplit, t, tile);
-    v_tile<false>(SINGLE ? V0 : layer_view(A.L[k >> 1]), batch, k & 1, tile, chunk_pairs, ctr, sc, u_lds, red,
+    v_tile<false>(SINGLE ? V0 : layer_view(A.L[k >> 1]), batch, k & 1, tile, chunk_pairs, ctr, sc, u_lds, red[0],
                   zstage, prefetch);
     __syncthreads();
   }
@@ -574,25 +664,38 @@ __global__ __launch_bounds__(LB_THREADS) void lb_decode_kernel(
     const bool check = MODE == 2;
     UState S;
     S.li = -1;
-#pragma unroll
-    for (int k = 0; k < LB_MAXT; ++k) {
-      const int t = ut0 + k;
-      if (t < ut1) {
-        int tile;
-        const int li = u_layer<SINGLE>(M, t, tile);
-        const LayerView L = SINGLE ? V0 : layer_view(A.L[li]);
-        if (MODE != 2) u_prefetch(L, tile, pre[k]);
-        u_tile(L, li, batch, tile, pre[k], ctr, check, sync, sc, S, red);
-      }
-    }
-    for (int t = ut0 + LB_MAXT; t < ut1; ++t) {
+    // U tiles in groups of up to LB_MAXT tiles of one layer; the first group
+    // uses the sign words prefetched during phase A (single launch)
+    YOut yo;
+    yo.p[0] = yo.p[1] = nullptr;
+    yo.v[0] = yo.v[1] = 0;
+    int t = ut0;
+    if (MODE == 2 && t < ut1) {
       int tile;
       const int li = u_layer<SINGLE>(M, t, tile);
-      const LayerView L = SINGLE ? V0 : layer_view(A.L[li]);
-      UTilePre p;
-      u_prefetch(L, tile, p);
-      u_tile(L, li, batch, tile, p, ctr, check, sync, sc, S, red);
+      const int lend = SINGLE ? ut1 : min(ut1, layer_u_end(M, li));
+      const int nt = min(LB_MAXT, lend - t);
+      yo = u_group(SINGLE ? V0 : layer_view(A.L[li]), li, batch, tile, nt, pre, hpre, ctr, check, sync, sc, S, u_lds,
+                   red);
+      t += nt;
     }
+    while (t < ut1) {
+      int tile;
+      const int li = u_layer<SINGLE>(M, t, tile);
+      const int lend = SINGLE ? ut1 : min(ut1, layer_u_end(M, li));
+      const int nt = min(LB_MAXT, lend - t);
+      const LayerView L = SINGLE ? V0 : layer_view(A.L[li]);
+      UTilePre p[LB_MAXT];
+#pragma unroll
+      for (int k = 0; k < LB_MAXT; ++k) u_prefetch(L, tile + min(k, nt - 1), p[k]);
+      HPre h;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) load_h(L, tile + min((wave_id() >> 2) + 2 * j, nt - 1), h, j);
+      store_y(yo);
+      yo = u_group(L, li, batch, tile, nt, p, h, ctr, check, sync, sc, S, u_lds, red);
+      t += nt;
+    }
+    store_y(yo);
   }
   // this workgroup's call is done: the next call's tag is one higher
   if (MODE == 2 && threadIdx.x == 0) add64c_noret(sync + LB_SYNC_CTR + 8 * wg, 1ull);
@@ -600,10 +703,21 @@ __global__ __launch_bounds__(LB_THREADS) void lb_decode_kernel(
 
 static int g_fused_grid[64];  // per device: workgroups of the single-launch kernel (0: unknown, -1: none)
 
+// Dynamic LDS of a decode launch: phase A stages g*x (chunks of 128*chunk_pairs
+// inputs per token), phase B stages z (zs + 8 halves per token) in the same
+// space.
+size_t lb_decode_lds_bytes(const LbDecodeArgs& a, int chunk_pairs) {
+  int zs = 0;
+  for (int i = 0; i < a.nlayers; ++i) zs = a.L[i].zs > zs ? a.L[i].zs : zs;
+  const size_t pa = (size_t)a.batch * (128 * chunk_pairs + 8), pb = (size_t)a.batch * (zs + 8);
+  return (pa > pb ? pa : pb) * sizeof(uint16_t);
+}
+
 template <bool SINGLE>
 static hipError_t launch_decode_t(const LbDecodeArgs& args, int chunk_pairs, void* sync, int allow_fused,
                                   hipStream_t stream) {
-  const size_t lds = (size_t)args.batch * (128 * chunk_pairs + 8) * sizeof(uint16_t);
+  const size_t lds = lb_decode_lds_bytes(args, chunk_pairs);
+  if (lds > LB_DECODE_LDS_MAX) return hipErrorInvalidValue;  // the host routes such calls elsewhere
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
@@ -624,10 +738,12 @@ static hipError_t launch_decode_t(const LbDecodeArgs& args, int chunk_pairs, voi
       e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
       if (e != hipSuccess) return e;
       // every workgroup of the single launch must be resident at once: size
-      // the grid for the largest dynamic LDS the host may request (56 KB)
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ1, lb_decode_kernel<2, true>, LB_THREADS, 56 * 1024);
+      // the grid for the largest dynamic LDS a launch may request
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ1, lb_decode_kernel<2, true>, LB_THREADS,
+                                                       LB_DECODE_LDS_MAX);
       if (e != hipSuccess) return e;
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ7, lb_decode_kernel<2, false>, LB_THREADS, 56 * 1024);
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ7, lb_decode_kernel<2, false>, LB_THREADS,
+                                                       LB_DECODE_LDS_MAX);
       if (e != hipSuccess) return e;
       g_fused_grid[dev] = (occ1 >= 1 && occ7 >= 1) ? (ncu < LB_MAX_GRID ? ncu : LB_MAX_GRID) : -1;
     }
@@ -649,7 +765,7 @@ static hipError_t launch_decode_t(const LbDecodeArgs& args, int chunk_pairs, voi
   if (e != hipSuccess) return e;
   const int gb = a.nut < 1024 ? a.nut : 1024;
   a.uq = a.nut / gb; a.ur = a.nut % gb;
-  hipLaunchKernelGGL((lb_decode_kernel<1, SINGLE>), dim3(gb), dim3(LB_THREADS), 0, stream, vb0, vb1, px, g0, g1,
+  hipLaunchKernelGGL((lb_decode_kernel<1, SINGLE>), dim3(gb), dim3(LB_THREADS), lds, stream, vb0, vb1, px, g0, g1,
                      pn, pldx, vsplit, misc(a), a, chunk_pairs, (uint8_t*)sync);
   return hipGetLastError();
 }

@@ -11,6 +11,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 #define LB_MAX_LAYERS 7
+#define LB_DECODE_LDS_MAX (120 * 1024)  // dynamic LDS limit of a decode launch (bytes)
 
 // ---------------------------------------------------------------- LB16 layout
 // A packed factor with R rows and reduction length K is a sequence of tiles of

@@ -52,6 +52,12 @@ struct LayerWs {
   size_t z_bytes;     // decode region (16 rows)
 };
 
+// The decode kernels stage a token-major copy of z in LDS (zs + 8 halves per
+// token); larger products of batch and rank go to the prefill kernels.
+inline bool decode_fits(int zs, int64_t batch) {
+  return (size_t)batch * (zs + 8) * sizeof(uint16_t) <= LB_DECODE_LDS_MAX;
+}
+
 inline size_t prefill_z_bytes(int zs, int64_t tokens) {
   const int64_t t = tokens < LB_PREFILL_MAX_TOKENS ? tokens : LB_PREFILL_MAX_TOKENS;
   return round_up((size_t)t * zs * sizeof(uint16_t), 256);
@@ -234,7 +240,11 @@ lb_status littlebit_linear_fwd(const lb_layer* L, uint32_t branch_mask, const ui
   if (!aligned(ws, 256)) return fail(LB_ERR_WORKSPACE, "littlebit_linear_fwd: workspace must be 256-byte aligned");
   const LayerWs w = layer_ws(*L, sel, nsel, kDecodeMaxBatch);
   const uint32_t path = flags & 3u;
-  const bool prefill = path == LB_PATH_PREFILL || (path == LB_PATH_AUTO && batch > kDecodeMaxBatch);
+  const bool fits = decode_fits(w.zs, batch < kDecodeMaxBatch ? batch : kDecodeMaxBatch);
+  if (path == LB_PATH_DECODE && !fits)
+    return fail(LB_ERR_UNSUPPORTED, "littlebit_linear_fwd: batch %lld x rank %d exceeds the decode kernels' LDS",
+                (long long)batch, w.zs);
+  const bool prefill = path == LB_PATH_PREFILL || (path == LB_PATH_AUTO && (batch > kDecodeMaxBatch || !fits));
   const size_t need = kWsHeader + w.z_bytes + (prefill ? prefill_z_bytes(w.zs, batch) : 0);
   if (ws_bytes < need)
     return fail(LB_ERR_WORKSPACE, "littlebit_linear_fwd: workspace has %zu bytes, needs %zu", ws_bytes, need);
@@ -264,6 +274,7 @@ lb_status littlebit_linear_fwd(const lb_layer* L, uint32_t branch_mask, const ui
 size_t littlebit_block_workspace_bytes(const lb_layer L[7], int64_t batch) {
   if (!L || batch < 1) return 0;
   size_t total = 0, zp = 0;
+  bool prefill = batch > kDecodeMaxBatch;
   for (int i = 0; i < 7; ++i) {
     int sel[2], nsel = 0;
     if (L[i].nbranches < 1 || L[i].nbranches > 2) return 0;
@@ -272,8 +283,9 @@ size_t littlebit_block_workspace_bytes(const lb_layer L[7], int64_t batch) {
     total += w.z_bytes;
     const size_t p = prefill_z_bytes(w.zs, batch);
     if (p > zp) zp = p;
+    prefill = prefill || !decode_fits(w.zs, batch);
   }
-  return kWsHeader + total + (batch > kDecodeMaxBatch ? zp : 0);
+  return kWsHeader + total + (prefill ? zp : 0);
 }
 
 lb_status littlebit_block_fwd(const lb_layer L[7], const uint16_t* x_qkv, const uint16_t* x_o,
@@ -299,7 +311,8 @@ lb_status littlebit_block_fwd(const lb_layer L[7], const uint16_t* x_qkv, const 
     const size_t p = prefill_z_bytes(w[i].zs, batch);
     if (p > zp) zp = p;
   }
-  const bool prefill = batch > kDecodeMaxBatch;
+  bool prefill = batch > kDecodeMaxBatch;
+  for (int i = 0; i < 7; ++i) prefill = prefill || !decode_fits(w[i].zs, batch);
   const size_t decode_bytes = need - kWsHeader;
   if (prefill) need += zp;
   if (L[0].n != L[1].n || L[0].n != L[2].n || L[4].n != L[5].n)
