@@ -32,6 +32,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+FP16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 matrix-core peak
 
 
 def algorithmic_bytes(m, n, ranks, batch):
@@ -39,6 +40,113 @@ def algorithmic_bytes(m, n, ranks, batch):
     bits = sum(r * (m + n) for r in ranks)
     scales = sum(m + n + r for r in ranks) * 2
     return bits // 8 + scales + 2 * batch * n + 2 * batch * m
+
+
+def time_graph(torch, calls, steps, warmup):
+    """Capture a HIP graph over one cycle of `calls` (plus remainders) and
+    return milliseconds per call over `steps` timed calls."""
+    n = len(calls)
+
+    def capture(k):
+        gr = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for c in calls[:k]:
+                c()
+            torch.cuda.synchronize()
+            with torch.cuda.graph(gr, stream=s):
+                for c in calls[:k]:
+                    c()
+        torch.cuda.current_stream().wait_stream(s)
+        return gr
+
+    graphs = {n: capture(n)}
+    for k in {steps % n, warmup % n} - {0}:
+        graphs[k] = capture(k)
+
+    def run(k_steps):
+        reps, rem = divmod(k_steps, n)
+        for _ in range(reps):
+            graphs[n].replay()
+        if rem:
+            graphs[rem].replay()
+
+    run(warmup)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    run(steps)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def copies_for(bytes_per_copy, total_bytes):
+    return max(1, int(np.ceil(total_bytes / bytes_per_copy)))
+
+
+def layer_bytes(layer):
+    return sum(b.v_bits.numel() + b.u_bits.numel() + 2 * (b.h.numel() + b.l.numel() + b.g.numel())
+               for b in layer.branches)
+
+
+def extra_measurements(lb, torch, synth, args):
+    """The other configurations of the metric: the 13B block at batch 1 (time
+    per block), the 70B up-projection at batch 1 and 16, and the 2048-token
+    prefill of the 7B up-projection (matrix-core utilisation)."""
+    out = {}
+    # 13B-shaped block, one call = the 7 projections for one token
+    for setting in ("0.55", "0.1"):
+        shapes = synth.block13b_shapes(setting)
+        one = [make_copy(lb, torch, sh, 5000 + i) for i, sh in enumerate(shapes)]
+        per_block = sum(layer_bytes(l) for l in one)
+        nb = copies_for(per_block, args.copies_gb * 1e9)
+        blocks = [one] + [[make_copy(lb, torch, sh, 6000 + 7 * j + i) for i, sh in enumerate(shapes)]
+                          for j in range(nb - 1)]
+        xs = [torch.randn((1, n), device="cuda").half() for n in (5120, 5120, 5120, 13824)]
+        ys = [torch.empty((1, sh.m), dtype=torch.float16, device="cuda") for sh in shapes]
+        ws = torch.zeros(lb.littlebit_block_workspace_bytes(one, 1), dtype=torch.uint8, device="cuda")
+        calls = [lambda b=b: lb.littlebit_block_fwd(b, *xs, outs=ys, workspace=ws) for b in blocks]
+        ms = time_graph(torch, calls, max(4 * nb, 400), 2 * nb)
+        abytes = sum(algorithmic_bytes(sh.m, sh.n, sh.ranks, 1) for sh in shapes)
+        out[f"block13b_{setting}bpw_b1"] = {"us_per_block": round(ms * 1e3, 3), "tokens_per_s": round(1e3 / ms, 1),
+                                             "algorithmic_bytes": abytes,
+                                             "hbm_gbs": round(abytes / (ms * 1e-3) / 1e9, 1),
+                                             "distinct_copies": nb}
+        del blocks, one
+        torch.cuda.empty_cache()
+    # 70B-shaped up-projection
+    sh = synth.UP70B
+    one = make_copy(lb, torch, sh, 7000)
+    nc = copies_for(layer_bytes(one), args.copies_gb * 1e9)
+    lays = [one] + [make_copy(lb, torch, sh, 7001 + i) for i in range(nc - 1)]
+    for batch in (1, 16):
+        x = torch.randn((batch, sh.n), device="cuda").half()
+        y = torch.empty((batch, sh.m), dtype=torch.float16, device="cuda")
+        ws = torch.zeros(lb.littlebit_linear_workspace_bytes(one, batch), dtype=torch.uint8, device="cuda")
+        calls = [lambda l=l: lb.littlebit_linear_fwd(l, x, out=y, workspace=ws) for l in lays]
+        ms = time_graph(torch, calls, max(8 * nc, 800), 2 * nc)
+        abytes = algorithmic_bytes(sh.m, sh.n, sh.ranks, batch)
+        out[f"up70b_b{batch}"] = {"us_per_call": round(ms * 1e3, 3), "tokens_per_s": round(batch * 1e3 / ms, 1),
+                                  "algorithmic_bytes": abytes, "hbm_gbs": round(abytes / (ms * 1e-3) / 1e9, 1),
+                                  "distinct_copies": nc}
+    del lays, one
+    torch.cuda.empty_cache()
+    # prefill: 2048 tokens of the 7B up-projection (compute-bound; one copy)
+    sh, M = synth.UP7B, synth.PREFILL_TOKENS
+    lay = make_copy(lb, torch, sh, 8000)
+    x = torch.randn((M, sh.n), device="cuda").half()
+    y = torch.empty((M, sh.m), dtype=torch.float16, device="cuda")
+    ws = torch.zeros(lb.littlebit_linear_workspace_bytes(lay, M), dtype=torch.uint8, device="cuda")
+    ms = time_graph(torch, [lambda: lb.littlebit_linear_fwd(lay, x, out=y, workspace=ws)], 50, 5)
+    flops = 2 * M * sum(r * (sh.m + sh.n) for r in sh.ranks)
+    tflops = flops / (ms * 1e-3) / 1e12
+    out["prefill_7b_up_2048"] = {"us_per_call": round(ms * 1e3, 2), "tokens_per_s": round(M * 1e3 / ms, 1),
+                                 "flops": flops, "tflops": round(tflops, 1),
+                                 "mfma_util": round(tflops / FP16_MFMA_PEAK_TFLOPS, 4),
+                                 "peak_tflops": FP16_MFMA_PEAK_TFLOPS}
+    return out
 
 
 def make_copy(lb, torch, shape, seed):
@@ -122,6 +230,8 @@ def main():
     ap.add_argument("--copies-gb", type=float, default=1.0, help="total size of distinct layer copies")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="host time for the oracle baseline (0: skip)")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the 13B-block, 70B and prefill measurements")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="no timing: one call per layer copy plus a 256 MiB device copy, for hardware counters")
     args = ap.parse_args()
@@ -170,40 +280,9 @@ def main():
     max_rms = float(np.max(np.abs(yg - yr)) / np.sqrt(np.mean(yr ** 2)))
 
     def time_path(path):
-        """Capture one cycle over the copies (plus a remainder) and time `steps` calls."""
-        def capture(nc):
-            gr = torch.cuda.CUDAGraph()
-            s = torch.cuda.Stream()
-            s.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(s):
-                for c in copies[:nc]:
-                    lb.littlebit_linear_fwd(c, x, out=y, workspace=ws, path=path)
-                torch.cuda.synchronize()
-                with torch.cuda.graph(gr, stream=s):
-                    for c in copies[:nc]:
-                        lb.littlebit_linear_fwd(c, x, out=y, workspace=ws, path=path)
-            torch.cuda.current_stream().wait_stream(s)
-            return gr
-
-        graphs = {ncopies: capture(ncopies)}
-        for k in {args.steps % ncopies, args.warmup % ncopies} - {0}:
-            graphs[k] = capture(k)
-
-        def run(steps):
-            reps, rem = divmod(steps, ncopies)
-            for _ in range(reps):
-                graphs[ncopies].replay()
-            if rem:
-                graphs[rem].replay()
-
-        run(args.warmup)
-        torch.cuda.synchronize()
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        start.record()
-        run(args.steps)
-        end.record()
-        torch.cuda.synchronize()
-        return start.elapsed_time(end)
+        """Milliseconds for `steps` calls cycling over the copies (HIP graph)."""
+        calls = [lambda c=c: lb.littlebit_linear_fwd(c, x, out=y, workspace=ws, path=path) for c in copies]
+        return time_graph(torch, calls, args.steps, args.warmup) * args.steps
 
     ms_two = time_path(lb.LB_DECODE_TWO_LAUNCHES)
     ms = time_path(lb.LB_PATH_AUTO)
@@ -217,6 +296,8 @@ def main():
                 "algorithmic_bytes_per_call": abytes,
                 "avg_call_us": round(ms_per_step * 1e3, 3),
                 "two_launch_variant_us": round(ms_two / args.steps * 1e3, 3)}
+
+    extra = None if args.no_extra else extra_measurements(lb, torch, synth, args)
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -242,6 +323,7 @@ def main():
         "parity": {"rel_l2": rel_l2, "max_err_over_rms": max_rms},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "extra": extra,
     }
     print(json.dumps(out))
 

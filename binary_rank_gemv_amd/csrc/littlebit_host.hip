@@ -47,9 +47,11 @@ inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // reserved whatever the batch.  Prefill z: up to 8192 rows of zs fp16 values,
 // in a region of its own, so a decode poll never meets plain prefill values.
 struct LayerWs {
-  int zs;             // halves per z row
+  int zs;             // halves per decode z row (branch regions of 64*ceil(r/64))
   int zoff[2];
   size_t z_bytes;     // decode region (16 rows)
+  int zs_p;           // halves per prefill z row (branch regions of 128*ceil(r/128), zero-padded)
+  int zoff_p[2];
 };
 
 // The decode kernels stage a token-major copy of z in LDS (zs + 8 halves per
@@ -65,12 +67,15 @@ inline size_t prefill_z_bytes(int zs, int64_t tokens) {
 
 LayerWs layer_ws(const lb_layer& L, const int* sel, int nsel, int64_t batch) {
   LayerWs w{};
-  int zs = 0;
+  int zs = 0, zsp = 0;
   for (int i = 0; i < nsel; ++i) {
     w.zoff[i] = zs;
     zs += 64 * lb16_units(L.br[sel[i]].r);
+    w.zoff_p[i] = zsp;
+    zsp += 128 * ((L.br[sel[i]].r + 127) / 128);
   }
   w.zs = zs;
+  w.zs_p = zsp;
   w.z_bytes = round_up((size_t)batch * zs * 4, 256);  // batch = 16: the reserved decode rows
   return w;
 }
@@ -149,7 +154,7 @@ void fill_prefill_args(LbPrefillArgs& a, const lb_layer& L, const int* sel, int 
   a.y = y;
   a.ldy = ldy;
   a.z = reinterpret_cast<uint16_t*>(base);
-  a.zs = w.zs;
+  a.zs = w.zs_p;
   for (int i = 0; i < nsel; ++i) {
     const lb_branch& B = L.br[sel[i]];
     a.br[i].vbits = static_cast<const uint8_t*>(B.v_bits);
@@ -158,7 +163,7 @@ void fill_prefill_args(LbPrefillArgs& a, const lb_layer& L, const int* sel, int 
     a.br[i].l = B.l;
     a.br[i].g = B.g;
     a.br[i].r = B.r;
-    a.br[i].zoff = w.zoff[i];
+    a.br[i].zoff = w.zoff_p[i];
   }
 }
 
@@ -217,7 +222,7 @@ size_t littlebit_linear_workspace_bytes(const lb_layer* L, int64_t batch) {
   if (batch < 1 || !L || L->nbranches < 1 || L->nbranches > 2) return 0;
   if (check_layer(L, (1u << L->nbranches) - 1, sel, &nsel, "workspace") != LB_OK) return 0;
   const LayerWs w = layer_ws(*L, sel, nsel, kDecodeMaxBatch);
-  return kWsHeader + w.z_bytes + prefill_z_bytes(w.zs, batch);
+  return kWsHeader + w.z_bytes + prefill_z_bytes(w.zs_p, batch);
 }
 
 lb_status littlebit_linear_fwd(const lb_layer* L, uint32_t branch_mask, const uint16_t* x, int64_t batch,
@@ -245,7 +250,7 @@ lb_status littlebit_linear_fwd(const lb_layer* L, uint32_t branch_mask, const ui
     return fail(LB_ERR_UNSUPPORTED, "littlebit_linear_fwd: batch %lld x rank %d exceeds the decode kernels' LDS",
                 (long long)batch, w.zs);
   const bool prefill = path == LB_PATH_PREFILL || (path == LB_PATH_AUTO && (batch > kDecodeMaxBatch || !fits));
-  const size_t need = kWsHeader + w.z_bytes + (prefill ? prefill_z_bytes(w.zs, batch) : 0);
+  const size_t need = kWsHeader + w.z_bytes + (prefill ? prefill_z_bytes(w.zs_p, batch) : 0);
   if (ws_bytes < need)
     return fail(LB_ERR_WORKSPACE, "littlebit_linear_fwd: workspace has %zu bytes, needs %zu", ws_bytes, need);
 
@@ -281,7 +286,7 @@ size_t littlebit_block_workspace_bytes(const lb_layer L[7], int64_t batch) {
     if (check_layer(&L[i], (1u << L[i].nbranches) - 1, sel, &nsel, "workspace") != LB_OK) return 0;
     const LayerWs w = layer_ws(L[i], sel, nsel, kDecodeMaxBatch);
     total += w.z_bytes;
-    const size_t p = prefill_z_bytes(w.zs, batch);
+    const size_t p = prefill_z_bytes(w.zs_p, batch);
     if (p > zp) zp = p;
     prefill = prefill || !decode_fits(w.zs, batch);
   }
@@ -308,7 +313,7 @@ lb_status littlebit_block_fwd(const lb_layer L[7], const uint16_t* x_qkv, const 
       return fail(LB_ERR_INVALID_ARG, "littlebit_block_fwd: inputs and outputs must be 2-byte aligned");
     w[i] = layer_ws(L[i], sel[i], nsel[i], kDecodeMaxBatch);
     need += w[i].z_bytes;
-    const size_t p = prefill_z_bytes(w[i].zs, batch);
+    const size_t p = prefill_z_bytes(w[i].zs_p, batch);
     if (p > zp) zp = p;
   }
   bool prefill = batch > kDecodeMaxBatch;

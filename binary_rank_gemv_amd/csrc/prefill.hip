@@ -14,6 +14,8 @@
 //
 // Workgroup = 4 waves, 128 rows x 128 tokens; wave (wr, wc) owns 64 rows
 // (4 tiles) x 64 tokens (4 tiles) = 16 accumulators of 16x16.
+#include <type_traits>
+
 #include "lb_common.h"
 
 #define PF_THREADS 256
@@ -213,9 +215,9 @@ __global__ __launch_bounds__(PF_THREADS, 2) void lb_prefill_kernel(LbPrefillArgs
       }
     }
     // the block holding the last row tile also zeroes this token block's
-    // z entries between 16*ceil(r/16) and 64*ceil(r/64)
+    // z entries between 16*ceil(r/16) and 128*ceil(r/128)
     if ((int)blockIdx.x == (ntiles - 1) >> 3) {
-      const int j0 = 16 * ntiles, nz = 64 * lb16_units(B.r) - j0;  // a multiple of 16
+      const int j0 = 16 * ntiles, nz = 128 * ((B.r + 127) / 128) - j0;  // a multiple of 16
       const int per_tok = nz >> 2;                                 // 8-byte stores per token
       for (int e = threadIdx.x; e < per_tok * PF_BN; e += PF_THREADS) {
         const int tok = tok0 + e / per_tok;
@@ -261,19 +263,360 @@ __global__ __launch_bounds__(PF_THREADS, 2) void lb_prefill_kernel(LbPrefillArgs
   }
 }
 
+// ------------------------------------------------------------------ v2
+// The main prefill kernels, for n % 128 == 0 and 16-byte aligned x rows.
+// Workgroup tile: 256 rows x 128 tokens, 8 waves, two on each SIMD.  Wave w
+// owns the 64 rows of row group w % 4 (4 tiles) and all 128 tokens (8
+// tiles), so each expanded sign fragment feeds 8 matrix-core steps; the two
+// waves of a SIMD (w and w + 4) take the two halves of every 128-input chunk
+// (steps 0-1 and 2-3), so one issues while the other waits, and their
+// accumulators are summed through LDS at the end.  Activation chunks (128
+// inputs x 128 tokens = 32 KB) go from memory straight to LDS with 16-byte
+// global-to-LDS loads, no registers involved.  In LDS the 8 inputs q (of 16)
+// of token t sit in 16-byte slot 16 t + (q ^ (t & 15)): the 16 lanes reading
+// one fragment row (same q, 16 tokens) then hit 16 distinct bank groups, and
+// the 16 lanes loading one token still read one contiguous 256-byte row
+// segment.  GEMM 1 folds g into the sign operand (exact +-g_k, by XOR of the
+// sign bit), GEMM 2 folds h (exact +-h_i).  Tokens beyond M load the last
+// token's row (outputs never stored).
+// Three stages, so a chunk's loads are started two chunks ahead.  Each stage
+// is a __shared__ array of its own: the compiler tells the arrays'
+// global-to-LDS writes apart and adds no wait of its own before reads of the
+// stage being consumed; the waits that order the stages are explicit.
+#define P2_WAVES 8
+#define P2_STAGES 3
+#define P2_CHUNK 32768
+// stage layout: activations, then the sign bytes of the chunk's pair
+// [row group][row tile][256 bytes], then g (256 bytes used of 1 KB)
+#define P2_WORDS_OFF P2_CHUNK
+#define P2_G_OFF (P2_CHUNK + 4 * 4 * 256)
+#define P2_STAGE_BYTES (P2_G_OFF + 1024)
+
+template <int MODE>
+__global__ __launch_bounds__(64 * P2_WAVES, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+lb_prefill2_kernel(LbPrefillArgs A) {
+  // global-to-LDS loads per chunk of a loading (first-half) wave: 8 x 1 KB
+  // of activations, the sign bytes of its row group, (GEMM 1) g
+  constexpr int kOps = MODE == 1 ? 10 : 9;
+  __shared__ __align__(16) uint8_t stage0[P2_STAGE_BYTES];
+  __shared__ __align__(16) uint8_t stage1[P2_STAGE_BYTES];
+  __shared__ __align__(16) uint8_t stage2[P2_STAGE_BYTES];
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int rg = wave & 3, kh = wave >> 2;  // row group, half of each chunk
+  const int grp = lane >> 4, col = lane & 15;
+  const int tok0 = blockIdx.y * PF_BN;
+  const int tile0 = 16 * blockIdx.x + 4 * rg;  // first row tile of this wave
+  const int M = A.M;
+  const LbSignConsts sc = lb16_sign_consts();
+
+  // the reduction as a sequence of 128-input chunks over one or two segments
+  const int b1 = MODE == 1 ? (int)blockIdx.z : 0;
+  const LbBranchArgs& B0 = A.br[b1];
+  const LbBranchArgs& B1 = A.br[MODE == 2 && A.nb == 2 ? 1 : b1];
+  const int ntiles = MODE == 1 ? (B0.r + 15) >> 4 : (A.m + 15) >> 4;
+  if (16 * (int)blockIdx.x >= ntiles) return;  // rows beyond this branch (uniform)
+  const int K0 = MODE == 1 ? A.n : B0.r, K1 = MODE == 1 ? A.n : B1.r;
+  const int nu0 = lb16_units(K0), nu1 = lb16_units(K1);
+  const int np0 = MODE == 1 ? A.n / 128 : (nu0 + 1) >> 1;
+  const int np1 = MODE == 2 && A.nb == 2 ? (nu1 + 1) >> 1 : 0;
+  const int C = np0 + np1;
+  const uint8_t* bits0 = MODE == 1 ? B0.vbits : B0.ubits;
+  const uint8_t* bits1 = MODE == 1 ? B1.vbits : B1.ubits;
+  const uint16_t* src0 = MODE == 1 ? A.x : A.z + B0.zoff;
+  const uint16_t* src1 = MODE == 1 ? A.x : A.z + B1.zoff;
+  const long ld = MODE == 1 ? A.ldx : A.zs;
+  const uint16_t* gsrc = B0.g;
+
+  // GEMM 2: h_b[i] of the lane's row i of each tile, branch 0 in the low and
+  // branch 1 in the high half
+  uint32_t hraw[4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    hraw[rt] = 0u;
+    if (MODE == 2) {
+      const int i = min(16 * (tile0 + rt) + col, A.m - 1);
+      hraw[rt] = (uint32_t)B0.h[i] | ((uint32_t)B1.h[i] << 16);
+    }
+  }
+
+  // per-lane byte offsets of the loads, the same for every chunk (the launch
+  // guarantees that they fit 32 bits): activation slot i; sign bytes of row
+  // tile lane/16 of the row group for segment sg, 16 per lane, for a full
+  // pair (256 bytes per tile) and for a pair of one unit (128 bytes, each
+  // half-row loaded twice so that the LDS copy keeps the full pair's
+  // addressing: byte 4j of a lane's word sits at 4*(lane/2)); g
+  // (slot i + 4 is 16 tokens further than slot i; past the last token it
+  // repeats slot i)
+  uint32_t aoff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int u = (rg * 8 + i) * 64 + lane;
+    const int t = u >> 4, q = (u & 15) ^ (t & 15);
+    aoff[i] = (uint32_t)(((long)min(tok0 + t, M - 1) * ld + 8 * q) * 2);
+  }
+  const uint32_t aoff_step = (uint32_t)(32 * ld), aoff_end = (uint32_t)((long)M * ld * 2);
+  const uint32_t row0 = (uint32_t)(min(tile0 + (lane >> 4), ntiles - 1) * lb16_tile_bytes(K0));
+  const uint32_t row1 = (uint32_t)(min(tile0 + (lane >> 4), ntiles - 1) * lb16_tile_bytes(K1));
+
+  // loads of chunk c into stage S (all global-to-LDS), by the first-half
+  // waves only, so that while one wave of a SIMD waits on a full memory
+  // queue the other keeps the matrix core busy: activation slots
+  // 8rg..8rg+7, the sign bytes of row group rg, and (GEMM 1) g (lanes 16..
+  // repeat lanes 0..15; every loading wave writes the same bytes)
+  auto issue = [&](int c, uint8_t* S) {
+    const int sg = c >= np0 ? 1 : 0;
+    const int p = c - (sg ? np0 : 0);
+    const uint8_t* src = reinterpret_cast<const uint8_t*>(sg ? src1 : src0) + 256 * p;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_global_load_lds(src + (i < 4 ? aoff[i] : aoff[i - 4] + aoff_step < aoff_end ? aoff[i - 4] + aoff_step : aoff[i - 4]),
+                                       (__attribute__((address_space(3))) void*)(S + (rg * 8 + i) * 1024), 16, 0, 0);
+    const bool full = 2 * p + 1 < (sg ? nu1 : nu0);
+    const uint8_t* wsrc = (sg ? bits1 : bits0) + 256 * p + (sg ? row1 : row0) + 16 * (lane & (full ? 15 : 7));
+    __builtin_amdgcn_global_load_lds(wsrc, (__attribute__((address_space(3))) void*)(S + P2_WORDS_OFF + rg * 1024), 16, 0, 0);
+    if (MODE == 1)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(gsrc) + 256 * p + 16 * (lane & 15),
+                                       (__attribute__((address_space(3))) void*)(S + P2_G_OFF), 16, 0, 0);
+  };
+
+  f32x4 acc[4][8];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) acc[rt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // this wave's two matrix steps (2kh, 2kh+1) of chunk c from stage S; the
+  // second half of a pair made of one unit has none.  The B fragments of the
+  // second step are read while the first step's products run.
+  // The matrix steps of chunk c from stage S: steps 2kh and 2kh+1, or, for
+  // a pair made of one unit (2 steps), step kh alone.  The loads of chunk
+  // c + 2 into stage `ahead` are issued between the first step's products,
+  // where a wave stalled on a full memory queue leaves the matrix core to
+  // the other wave of its SIMD; no branch separates them from the waits
+  // that guard their stage.
+  auto compute = [&](int c, const uint8_t* S, uint8_t* ahead, auto loads) __attribute__((always_inline)) {
+    constexpr bool LOADS = decltype(loads)::value;
+    const int sg = c >= np0 ? 1 : 0;
+    const int p = c - (sg ? np0 : 0);
+    const bool full = 2 * p + 1 < (sg ? nu1 : nu0);
+    const int st0 = full ? 2 * kh : kh;
+    const uint32_t sel = lb16_pair_sel(p, lane, sg ? nu1 : nu0);
+    const uint32_t* words = reinterpret_cast<const uint32_t*>(S + P2_WORDS_OFF) + rg * 256 + (full ? lane : lane >> 1);
+    f16x8 b[2][8];
+    // the lane's column, opaque here so that the fragment addresses are
+    // formed per chunk instead of being held in registers across the loop
+    int colx = col;
+    __asm__ volatile("" : "+v"(colx));
+    auto read_b = [&](int st, f16x8* dst) {
+      const int q = 4 * st + grp;
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt)
+        dst[tt] = *reinterpret_cast<const f16x8*>(S + 16 * (16 * (16 * tt + colx) + (q ^ colx)));
+    };
+    read_b(st0, b[0]);
+    // GEMM 2 operand values +-h_b[i]: the sign is folded into the word here,
+    // the magnitude pair is formed at each use
+    auto hbits = [&](int rt) { return sg ? hraw[rt] >> 16 : hraw[rt] & 0xFFFFu; };
+    uint32_t reg[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+      reg[rt] = lb16_reg_word(words[64 * rt], sel) ^ (MODE == 2 && (hbits(rt) & 0x8000u) ? 0xFFFFFFFFu : 0u);
+    auto mstep = [&](int st, const f16x8* bb, bool with_loads) {
+      if (with_loads) issue(min(c + 2, C - 1), ahead);
+      u32x4 gq = u32x4{0u, 0u, 0u, 0u};
+      if (MODE == 1) gq = *reinterpret_cast<const u32x4*>(S + P2_G_OFF + 2 * (32 * st + 8 * grp));
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        f16x8 a;
+        if (MODE == 1) {
+          u32x4 d;
+#pragma unroll
+          for (int dd = 0; dd < 4; ++dd) d[dd] = ((reg[rt] << (4 * st + dd)) & sc.sign_mask) ^ gq[dd];
+          a = __builtin_bit_cast(f16x8, d);
+        } else {
+          a = lb16_step_operand_val(reg[rt], st, sc.sign_mask, (hbits(rt) & 0x7FFFu) * 0x10001u);
+        }
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt) acc[rt][tt] = mfma16(a, bb[tt], acc[rt][tt]);
+      }
+      // issue order: the first operand, then each later operand's ALU work
+      // (and the loads) spread between the products of the one before
+      __builtin_amdgcn_sched_group_barrier(0x2, 8, 0);
+#pragma unroll
+      for (int i = 0; i < 24; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x8, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x2, 1, 0);
+        if (with_loads && (i & 3) == 3 && i < 20) __builtin_amdgcn_sched_group_barrier(0x10, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x8, 8, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    read_b(st0 + 1, b[1]);
+    __builtin_amdgcn_sched_barrier(0);  // keep those reads ahead of the first step's products
+    mstep(st0, b[0], LOADS);
+    if (full) mstep(st0 + 1, b[1], false);
+  };
+
+  // chunk c: a loading wave waits until its loads of it have landed (those
+  // of chunk c + 1 may still be in flight), then every wave waits until all
+  // have (a plain barrier; the empty asm keeps LDS reads below it).  The
+  // stage of chunk c - 1 is then free for chunk c + 2: every wave has
+  // consumed its reads.  Every step of a loading wave issues loads, past the
+  // end as repeats of the last chunk into a stage nobody reads again, so the
+  // wait count is a constant; the loading and the other waves run separate
+  // copies of the loop, so that no branch separates a load from its waits.
+  auto run = [&](auto loads) __attribute__((always_inline)) {
+    constexpr bool LOADS = decltype(loads)::value;
+    auto step = [&](int c, const uint8_t* cur, uint8_t* ahead) __attribute__((always_inline)) {
+      if (LOADS) __builtin_amdgcn_s_waitcnt(kOps | (7 << 4) | (15 << 8));
+      __builtin_amdgcn_s_barrier();
+      __asm__ volatile("" ::: "memory");
+      compute(c, cur, ahead, loads);
+    };
+    if (LOADS) {
+      issue(0, stage0);
+      issue(min(1, C - 1), stage1);
+    }
+    int c = 0;
+    for (; c + P2_STAGES <= C; c += P2_STAGES) {
+      step(c, stage0, stage2);
+      step(c + 1, stage1, stage0);
+      step(c + 2, stage2, stage1);
+    }
+    if (c < C) step(c, stage0, stage2);
+    if (c + 1 < C) step(c + 1, stage1, stage0);
+  };
+  if (kh == 0)
+    run(std::integral_constant<bool, true>());
+  else
+    run(std::integral_constant<bool, false>());
+  // every load has landed and every wave is past its reads: the stages are free
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+  __syncthreads();
+
+  // the second-half waves hand their sums to the first-half waves: row tiles
+  // 0..2 through the three stages, then row tile 3 through the first
+  {
+    f32x4* red0 = reinterpret_cast<f32x4*>(stage0) + rg * 512 + lane;
+    f32x4* red1 = reinterpret_cast<f32x4*>(stage1) + rg * 512 + lane;
+    f32x4* red2 = reinterpret_cast<f32x4*>(stage2) + rg * 512 + lane;
+    if (kh == 1) {
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt) {
+        red0[64 * tt] = acc[0][tt];
+        red1[64 * tt] = acc[1][tt];
+        red2[64 * tt] = acc[2][tt];
+      }
+    }
+    __syncthreads();
+    if (kh == 0) {
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt) {
+        acc[0][tt] += red0[64 * tt];
+        acc[1][tt] += red1[64 * tt];
+        acc[2][tt] += red2[64 * tt];
+      }
+    }
+    __syncthreads();
+    if (kh == 1) {
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt) red0[64 * tt] = acc[3][tt];
+    }
+    __syncthreads();
+    if (kh == 0) {
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt) acc[3][tt] += red0[64 * tt];
+    }
+  }
+
+  if (MODE == 1) {
+    const LbBranchArgs& B = B0;
+    if (kh == 0) {
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const int tile = tile0 + rt;
+        if (tile >= ntiles) continue;
+        const int j0 = 16 * tile + 4 * grp;
+        float lq[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) lq[q] = (j0 + q < B.r) ? h2f(B.l[j0 + q]) : 0.f;
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt) {
+          const int tok = tok0 + 16 * tt + col;
+          if (tok >= M) continue;
+          uint16_t zq[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) zq[q] = f2h(lq[q] * acc[rt][tt][q]);
+          *reinterpret_cast<uint2*>(A.z + (long)tok * A.zs + B.zoff + j0) = *reinterpret_cast<uint2*>(zq);
+        }
+      }
+    }
+    // the block holding the last row tile also zeroes this token block's
+    // z entries between 16*ceil(r/16) and 128*ceil(r/128)
+    if ((int)blockIdx.x == (ntiles - 1) >> 4) {
+      const int j0 = 16 * ntiles, nz = 128 * ((B.r + 127) / 128) - j0;
+      const int per_tok = nz >> 2;
+      for (int e = threadIdx.x; e < per_tok * PF_BN; e += 64 * P2_WAVES) {
+        const int tok = tok0 + e / per_tok;
+        if (tok < M)
+          *reinterpret_cast<uint2*>(A.z + (long)tok * A.zs + B.zoff + j0 + 4 * (e % per_tok)) = make_uint2(0u, 0u);
+      }
+    }
+  } else if (kh == 0) {
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const int tile = tile0 + rt;
+      if (tile >= ntiles) continue;
+      const int i0 = 16 * tile + 4 * grp;
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt) {
+        const int tok = tok0 + 16 * tt + col;
+        if (tok >= M) continue;
+        uint16_t* yp = A.y + (long)tok * A.ldy + i0;
+        uint16_t yq[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) yq[q] = f2h(acc[rt][tt][q]);
+        if (i0 + 3 < A.m && ((uintptr_t)yp & 7) == 0) {
+          *reinterpret_cast<uint2*>(yp) = *reinterpret_cast<uint2*>(yq);
+        } else {
+          for (int q = 0; q < 4; ++q)
+            if (i0 + q < A.m) yp[q] = yq[q];
+        }
+      }
+    }
+  }
+}
+
 hipError_t lb_launch_prefill(const LbPrefillArgs& a, hipStream_t stream) {
   const unsigned tb = (unsigned)((a.M + PF_BN - 1) / PF_BN);
   int maxt = 0;
   for (int b = 0; b < a.nb; ++b) maxt = max(maxt, (a.br[b].r + 15) >> 4);
-  const bool fast = (a.n % 8 == 0) && (((uintptr_t)a.x & 15) == 0) && (a.ldx % 8 == 0);
-  const dim3 g1((unsigned)((maxt + 7) / 8), tb, (unsigned)a.nb);
-  if (fast)
-    hipLaunchKernelGGL((lb_prefill_kernel<1, true>), g1, dim3(PF_THREADS), 0, stream, a);
-  else
-    hipLaunchKernelGGL((lb_prefill_kernel<1, false>), g1, dim3(PF_THREADS), 0, stream, a);
-  hipError_t e = hipGetLastError();
+  const bool aligned_x = (((uintptr_t)a.x & 15) == 0) && (a.ldx % 8 == 0);
+  // v2 addresses a token row by a 32-bit byte offset
+  // (with 16 rows of slack: a slot offset is formed 16 rows ahead before its
+  // range check)
+  auto fits32 = [&](long ld, long width) { return ((long)(a.M + 16) * ld + width) * 2 < (1l << 32); };
+  hipError_t e;
+  if (aligned_x && a.n % 128 == 0 && fits32(a.ldx, a.n)) {
+    // v2: GEMM 1 over both branches (blockIdx.z), then GEMM 2
+    hipLaunchKernelGGL((lb_prefill2_kernel<1>), dim3((unsigned)((maxt + 15) / 16), tb, (unsigned)a.nb),
+                       dim3(64 * P2_WAVES), 0, stream, a);
+  } else {
+    const dim3 g1((unsigned)((maxt + 7) / 8), tb, (unsigned)a.nb);
+    if (a.n % 8 == 0 && aligned_x)
+      hipLaunchKernelGGL((lb_prefill_kernel<1, true>), g1, dim3(PF_THREADS), 0, stream, a);
+    else
+      hipLaunchKernelGGL((lb_prefill_kernel<1, false>), g1, dim3(PF_THREADS), 0, stream, a);
+  }
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 g2((unsigned)((((a.m + 15) >> 4) + 7) / 8), tb, 1);
-  hipLaunchKernelGGL((lb_prefill_kernel<2, true>), g2, dim3(PF_THREADS), 0, stream, a);
+  // GEMM 2 reads z (always 16-byte aligned, zero-padded to whole chunks)
+  const int mt = (a.m + 15) >> 4;
+  if (fits32(a.zs, a.zs))
+    hipLaunchKernelGGL((lb_prefill2_kernel<2>), dim3((unsigned)((mt + 15) / 16), tb, 1), dim3(64 * P2_WAVES), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL((lb_prefill_kernel<2, true>), dim3((unsigned)((mt + 7) / 8), tb, 1), dim3(PF_THREADS), 0,
+                       stream, a);
   return hipGetLastError();
 }
