@@ -30,6 +30,12 @@
 #define LB_MAXT 3                     // phase-B tiles whose sign words are prefetched
 #define LB_MAXPW 3                    // phase-B pairs per wave held in registers
 #define LB_MAX_GRID 256               // workgroups of the single launch (one counter each)
+#define LB_UPRE_BYTES (64 * 1024)     // LDS for a workgroup's phase-B sign bytes (single launch)
+#define LB_UPRE_OPS 8                 // 1 KB global-to-LDS loads per wave filling it
+#define LB_UPRE_HROWS 512             // row scales of the copied tiles (an LDS table)
+// dynamic LDS a launch of that variant may take: what the static arrays
+// (partial sums 24 KB, z tile 512 B, the copy, the row-scale table) leave of 160 KB
+#define LB_UPRE_DYN_MAX (160 * 1024 - LB_MAXT * LB_WAVES * 256 * 4 - 512 - LB_UPRE_BYTES - 2 * LB_UPRE_HROWS)
 #define LB_SPIN_LIMIT (1 << 20)
 
 // workspace header (bytes): one 64-bit call counter per workgroup of the
@@ -444,6 +450,86 @@ __device__ __forceinline__ void u_enter_layer(const LayerView& L, int li, int ba
   }
 }
 
+// ---------------------------------------------- phase-B sign bytes in LDS
+// A workgroup's U tiles [ut0, ut1) are, per layer and branch, one contiguous
+// run of packed bytes.  The single launch copies the runs of (at most) its
+// first two layers into LDS while phase A runs: a stream of up to
+// LB_UPRE_BYTES, cut into 1 KB global-to-LDS loads, LB_UPRE_OPS per wave, a
+// fixed count (loads past the stream's end repeat its last 16 bytes into
+// unused LDS), so the compiler's wait counts stay exact.  Tiles [ut0, cover)
+// are in LDS; a tile's bytes keep the global layout (pair p at 256 p, an odd
+// last unit alone at 256 (NU/2), 2 bytes per lane).
+struct UPrePlan {
+  int split;    // first global tile of the second layer (ut1 when none)
+  int cover;    // tiles [ut0, cover) are in LDS
+  int off[4];   // LDS byte offset of run (layer slot s, branch b) = 2 s + b
+};
+
+__device__ __forceinline__ int tile_bytes_b(const LayerView& L, int b) {
+  return (int)lb16_tile_bytes(b ? L.r1 : L.r0);
+}
+
+// Plans and issues the copy (all values wave-uniform but the addresses), and
+// loads this thread's row scale for the LDS table of the covered tiles:
+// thread (local tile tid / 32, branch (tid / 16) % 2, row tid % 16).
+template <bool SINGLE>
+__device__ __forceinline__ void upre_issue(const LbDecodeArgs& A, const TileMap& M, int ut0, int ut1,
+                                           int max_tiles, uint8_t* lds, UPrePlan& P, uint32_t& hval) {
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  int tile0;
+  const int li0 = u_layer<SINGLE>(M, min(ut0, A.nut - 1), tile0);
+  const int end0 = SINGLE ? ut1 : min(ut1, layer_u_end(M, li0));
+  const int li1 = SINGLE ? li0 : min(li0 + 1, M.nl - 1);
+  const int end1 = SINGLE ? ut1 : min(ut1, layer_u_end(M, li1));
+  const LayerView L0 = layer_view(A.L[li0]);
+  const LayerView L1 = layer_view(A.L[li1]);
+  const int n0 = max(end0 - ut0, 0), n1 = (SINGLE || li1 == li0) ? 0 : max(end1 - end0, 0);
+  const int b00 = n0 * tile_bytes_b(L0, 0), b01 = L0.nb == 2 ? n0 * tile_bytes_b(L0, 1) : 0;
+  const int b10 = n1 * tile_bytes_b(L1, 0), b11 = L1.nb == 2 ? n1 * tile_bytes_b(L1, 1) : 0;
+  int total = b00 + b01 + b10 + b11;
+  P.split = end0;
+  P.cover = SINGLE ? end0 : end1;
+  if (total > LB_UPRE_BYTES) {  // the second layer does not fit: first layer only
+    total = b00 + b01;
+    P.cover = end0;
+  }
+  if (total > LB_UPRE_BYTES) {  // nothing fits: phase B reads its sign words from memory
+    total = 0;
+    P.cover = ut0;
+  }
+  P.cover = min(P.cover, ut0 + max_tiles);  // the row-scale table and the partial sums hold these
+  P.off[0] = 0;
+  P.off[1] = b00;
+  P.off[2] = b00 + b01;
+  P.off[3] = b00 + b01 + b10;
+  const uint8_t* src0 = L0.ub0 + (long)tile0 * tile_bytes_b(L0, 0);
+  const uint8_t* src1 = (L0.nb == 2 ? L0.ub1 : L0.ub0) + (long)tile0 * tile_bytes_b(L0, L0.nb == 2 ? 1 : 0);
+  const uint8_t* src2 = L1.ub0;
+  const uint8_t* src3 = L1.nb == 2 ? L1.ub1 : L1.ub0;
+#pragma unroll
+  for (int j = 0; j < LB_UPRE_OPS; ++j) {
+    const int i = wave * LB_UPRE_OPS + j;
+    // stream offset of this lane's 16 bytes (past the end: the last 16)
+    const int o = min(1024 * i + 16 * lane, max(total - 16, 0));
+    const uint8_t* src = o >= P.off[3] && P.off[3] < total ? src3 + (o - P.off[3])
+                         : o >= P.off[2] && P.off[2] < total ? src2 + (o - P.off[2])
+                         : o >= P.off[1] && P.off[1] < total ? src1 + (o - P.off[1])
+                                                              : src0 + o;
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(lds + 1024 * i), 16, 0, 0);
+  }
+  {
+    // row scale (an always-valid row: tiles past the covered ones load row 0)
+    const int tid = threadIdx.x;
+    const int t = ut0 + (tid >> 5), hb = (tid >> 4) & 1;
+    const bool in = t < P.cover;
+    const bool second = t >= P.split;
+    const LayerView& L = second ? L1 : L0;
+    const int tl = in ? (second ? t - P.split : tile0 + t - ut0) : 0;
+    const uint16_t* h = (hb && L.nb == 2) ? L.h1 : L.h0;
+    hval = h[min(16 * tl + (tid & 15), L.m - 1)];
+  }
+}
+
 // The fp16 outputs an epilogue thread still has to store (p == nullptr: none).
 // Stores are held back until the next group's sign words are requested: a
 // store counts in the same in-order counter as the loads, so a wait for a
@@ -458,6 +544,57 @@ __device__ __forceinline__ void store_y(const YOut& o) {
   for (int j = 0; j < 2; ++j)
     if (o.p[j]) *o.p[j] = o.v[j];
 }
+
+// Cross-wave sums of nt <= LB_MAXT tiles' accumulators and the epilogue:
+// y = sum_b h_b * s_b for the entries of this thread (stores held back).
+__device__ __forceinline__ YOut u_finish(const LayerView& L, int batch, int tile0, int nt, const f32x4 (&acc)[LB_MAXT],
+                                         const HPre& H, float (*red)[LB_WAVES][256]) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int tok = lane & 15, grp = lane >> 4;
+  __syncthreads();  // previous users of red are done
+#pragma unroll
+  for (int k = 0; k < LB_MAXT; ++k)
+    if (k < nt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) red[k][wave][(4 * grp + q) * 16 + tok] = acc[k][q];
+  __syncthreads();
+
+  // thread tid finishes entries tid and tid + 512 of (tile, row, token); its
+  // row 16*tile + (tid & 15) is the one whose scales it prefetched
+  static_assert(LB_MAXT == 3 && LB_THREADS == 512, "epilogue mapping");
+  const int rho = tid & 15, tk = (tid >> 4) & 15;
+  YOut out;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    out.p[j] = nullptr;
+    out.v[j] = 0;
+    const int k = (wave >> 2) + 2 * j;  // tile of entry tid + 512 j (wave-uniform)
+    const int i = 16 * (tile0 + k) + rho;
+    if (k < nt && tk < batch && i < L.m) {
+      const int e = rho * 16 + tk;
+      const uint32_t h0 = H.h0[j], h1 = H.h1[j];
+      float y;
+      if (L.nb == 2) {
+        float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+        for (int w = 0; w < LB_WAVES / 2; ++w) {
+          s0 += red[k][w][e];
+          s1 += red[k][w + LB_WAVES / 2][e];
+        }
+        y = fmaf(h2f((uint16_t)late(h0)), s0, h2f((uint16_t)late(h1)) * s1);  // one rounding order in every path
+      } else {
+        float s0 = 0.f;
+#pragma unroll
+        for (int w = 0; w < LB_WAVES; ++w) s0 += red[k][w][e];
+        y = h2f((uint16_t)late(h0)) * s0;
+      }
+      out.p[j] = L.y + (long)tk * L.ldy + i;
+      out.v[j] = f2h(y);
+    }
+  }
+  return out;
+}
+
 
 // Phase B for nt <= LB_MAXT consecutive U tiles (from tile0) of layer L, whose
 // sign words and row scales are in P[0..nt): the matrix steps of all tiles
@@ -523,48 +660,82 @@ __device__ __forceinline__ YOut u_group(const LayerView& L, int li, int batch, i
       }
     }
   }
-  __syncthreads();  // previous users of red are done
-#pragma unroll
-  for (int k = 0; k < LB_MAXT; ++k)
-    if (k < nt)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) red[k][wave][(4 * grp + q) * 16 + tok] = acc[k][q];
-  __syncthreads();
+  return u_finish(L, batch, tile0, nt, acc, H, red);
+}
 
-  // thread tid finishes entries tid and tid + 512 of (tile, row, token); its
-  // row 16*tile + (tid & 15) is the one whose scales it prefetched
-  static_assert(LB_MAXT == 3 && LB_THREADS == 512, "epilogue mapping");
-  const int rho = tid & 15, tk = (tid >> 4) & 15;
-  YOut out;
+// Phase B for the copied tiles [tile0, tile0 + T) of layer L (T <= span_max,
+// their sign bytes in LDS: w0/w1 = tile tile0's bytes of branch 0/1, tb0/tb1
+// = bytes per tile; their row scales in hl: 32 per tile, branch 0 then 1).
+// Each wave runs its pair range (u_role) over every tile, four tiles at a
+// time, and leaves its sums in `part` ([wave][tile][row][token], no barrier);
+// one barrier, then every output is y = h_0 * (sum over branch-0 waves) +
+// h_1 * (sum over branch-1 waves), the sums taken in wave order as in u_group.
+__device__ __forceinline__ void u_span_lds(const LayerView& L, int li, int batch, int tile0, int T, int span_max,
+                                           const uint8_t* w0, const uint8_t* w1, int tb0, int tb1, const uint16_t* hl,
+                                           uint32_t ctr, bool check, uint8_t* sync, const LbSignConsts& sc, UState& S,
+                                           uint16_t* zl, float* part) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int tok = lane & 15, grp = lane >> 4;
+  if (li != S.li) u_enter_layer(L, li, batch, ctr, check, sync, S, zl);
+  const uint16_t* zb = zl + min(tok, batch - 1) * (L.zs + 8) + (S.b ? L.zoff1 : L.zoff0) + 8 * grp;
+  const int s1 = 2 * S.nu;  // steps of the branch that hold data
+  const uint8_t* wb = S.b ? w1 : w0;
+  const int tb = S.b ? tb1 : tb0;
+  for (int k0 = 0; k0 < T; k0 += 4) {
+    f32x4 acc[4];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    out.p[j] = nullptr;
-    out.v[j] = 0;
-    const int k = (wave >> 2) + 2 * j;  // tile of entry tid + 512 j (wave-uniform)
-    const int i = 16 * (tile0 + k) + rho;
-    if (k < nt && tk < batch && i < L.m) {
-      const int e = rho * 16 + tk;
-      const uint32_t h0 = H.h0[j], h1 = H.h1[j];
-      float y;
-      if (L.nb == 2) {
-        float s0 = 0.f, s1 = 0.f;
+    for (int kk = 0; kk < 4; ++kk) acc[kk] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int p = S.p0; p < S.p1; ++p) {
+      const uint32_t sel = lb16_pair_sel(p, lane, S.nu);
+      const int woff = 256 * p + ((2 * p + 1 < S.nu) ? 4 * lane : 4 * (lane >> 1));
+      uint32_t reg[4];
 #pragma unroll
-        for (int w = 0; w < LB_WAVES / 2; ++w) {
-          s0 += red[k][w][e];
-          s1 += red[k][w + LB_WAVES / 2][e];
+      for (int kk = 0; kk < 4; ++kk)
+        reg[kk] = lb16_reg_word(*reinterpret_cast<const uint32_t*>(wb + min(k0 + kk, T - 1) * tb + woff), sel);
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        if (4 * p + st < s1) {  // an odd last unit has two steps
+          const f16x8 bv = *reinterpret_cast<const f16x8*>(zb + 32 * (4 * p + st));
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk)
+            if (k0 + kk < T)
+              acc[kk] = mfma16(lb16_step_operand_val(reg[kk], st, sc.sign_mask, sc.one_pair), bv, acc[kk]);
         }
-        y = h2f((uint16_t)late(h0)) * s0 + h2f((uint16_t)late(h1)) * s1;
-      } else {
-        float s0 = 0.f;
-#pragma unroll
-        for (int w = 0; w < LB_WAVES; ++w) s0 += red[k][w][e];
-        y = h2f((uint16_t)late(h0)) * s0;
       }
-      out.p[j] = L.y + (long)tk * L.ldy + i;
-      out.v[j] = f2h(y);
+    }
+    if (tok < batch) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        if (k0 + kk < T)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) part[((wave * span_max + k0 + kk) * 16 + 4 * grp + q) * batch + tok] = acc[kk][q];
     }
   }
-  return out;
+  __syncthreads();
+  const int nout = T * 16 * batch;
+  for (int e = tid; e < nout; e += LB_THREADS) {
+    const int k = e / (16 * batch), rem = e - k * 16 * batch;
+    const int row = rem / batch, tk = rem - row * batch;
+    const int i = 16 * (tile0 + k) + row;
+    if (i >= L.m) continue;
+    const int o = (k * 16 + row) * batch + tk, ws = span_max * 16 * batch;
+    float y;
+    if (L.nb == 2) {
+      float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+      for (int w = 0; w < LB_WAVES / 2; ++w) {
+        a0 += part[w * ws + o];
+        a1 += part[(w + LB_WAVES / 2) * ws + o];
+      }
+      y = fmaf(h2f(hl[32 * k + row]), a0, h2f(hl[32 * k + 16 + row]) * a1);
+    } else {
+      float a0 = 0.f;
+#pragma unroll
+      for (int w = 0; w < LB_WAVES; ++w) a0 += part[w * ws + o];
+      y = h2f(hl[32 * k + row]) * a0;
+    }
+    L.y[(long)tk * L.ldy + i] = f2h(y);
+  }
 }
 
 }  // namespace
@@ -581,7 +752,7 @@ __device__ __forceinline__ YOut u_group(const LayerView& L, int li, int batch, i
 // They repeat fields of A.L[0]; the multi-layer kernel ignores them.
 //   misc = vq | vr << 8 | batch << 16 | chunk_pairs << 21  (V tiles of
 //          workgroup w: vq + (w < vr), contiguous)
-template <int MODE, bool SINGLE>
+template <int MODE, bool SINGLE, bool UPRE>
 __global__ __launch_bounds__(LB_THREADS) void lb_decode_kernel(
     const uint8_t* pre_vb0, const uint8_t* pre_vb1, const uint16_t* pre_x, const uint16_t* pre_g0,
     const uint16_t* pre_g1, int pre_n, int pre_ldx, int pre_vsplit, uint32_t pre_misc,
@@ -589,6 +760,9 @@ __global__ __launch_bounds__(LB_THREADS) void lb_decode_kernel(
   extern __shared__ __align__(16) uint16_t u_lds[];
   __shared__ __align__(16) float red[LB_MAXT][LB_WAVES][256];  // cross-wave partial sums
   __shared__ __align__(16) uint32_t zstage[128];  // one tile's z (16 tokens x 16 rows of fp16)
+  __shared__ __align__(16) uint8_t upre_lds[UPRE ? LB_UPRE_BYTES : 16];  // phase-B sign bytes
+  __shared__ uint16_t hl_lds[UPRE ? LB_UPRE_HROWS : 1];                  // and row scales
+  static_assert(!UPRE || MODE == 2, "the sign-byte copy belongs to the single launch");
 
   const int wg = blockIdx.x;
   const int batch = SINGLE ? (int)((pre_misc >> 16) & 31u) : A.batch;
@@ -619,17 +793,27 @@ __global__ __launch_bounds__(LB_THREADS) void lb_decode_kernel(
   uint32_t ctr = 0;
   UTilePre pre[LB_MAXT];
   HPre hpre;
+  UPrePlan plan;
+  plan.split = plan.cover = 0;
+  uint32_t hval = 0;
+  // copied tiles per workgroup: the row-scale table's 16, and partial sums
+  // [wave][tile][row][token] within the 6144 floats of red
+  const int span_max = min(LB_UPRE_HROWS / 32, (LB_MAXT * LB_WAVES * 256) / (LB_WAVES * 16 * batch));
   // every load is issued (tiles clamped to a valid one), which keeps the
   // wait counts exact; tiles beyond ut1 are never used
   auto prefetch = [&]() {
     if (MODE == 2) ctr = ld32c(sync + LB_SYNC_CTR + 8 * wg);
     share(A.uq, A.ur, wg, ut0, ut1);
     const int nut = A.nut;
+    if (UPRE) {
+      upre_issue<SINGLE>(A, M, ut0, ut1, span_max, upre_lds, plan, hval);
+    } else {
 #pragma unroll
-    for (int k = 0; k < LB_MAXT; ++k) {
-      int tile;
-      const int li = u_layer<SINGLE>(M, min(ut0 + k, nut - 1), tile);
-      u_prefetch(SINGLE ? V0 : layer_view(A.L[li]), tile, pre[k]);
+      for (int k = 0; k < LB_MAXT; ++k) {
+        int tile;
+        const int li = u_layer<SINGLE>(M, min(ut0 + k, nut - 1), tile);
+        u_prefetch(SINGLE ? V0 : layer_view(A.L[li]), tile, pre[k]);
+      }
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -670,7 +854,33 @@ __global__ __launch_bounds__(LB_THREADS) void lb_decode_kernel(
     yo.p[0] = yo.p[1] = nullptr;
     yo.v[0] = yo.v[1] = 0;
     int t = ut0;
-    if (MODE == 2 && t < ut1) {
+    // sign bytes copied to LDS: every wave's copies have landed (a wait for
+    // all of this wave's loads, then the barrier in front of the z copy)
+    if (UPRE) {
+      __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+      hl_lds[threadIdx.x] = (uint16_t)hval;
+      __syncthreads();
+    }
+    if (UPRE) {
+      // the copied prefix [ut0, cover), one span per layer, then the rest
+      // from memory (separate loops: no register of one path waits on the
+      // other's loads)
+      while (t < plan.cover) {
+        int tile;
+        const int li = u_layer<SINGLE>(M, t, tile);
+        const int lend = SINGLE ? ut1 : min(ut1, layer_u_end(M, li));
+        const int T = min(lend, plan.cover) - t;
+        const LayerView L = SINGLE ? V0 : layer_view(A.L[li]);
+        const int slot = t >= plan.split ? 1 : 0;
+        const int first = slot ? plan.split : ut0;
+        const int tb0 = tile_bytes_b(L, 0), tb1 = tile_bytes_b(L, L.nb == 2 ? 1 : 0);
+        const uint8_t* w0 = upre_lds + (slot ? plan.off[2] : plan.off[0]) + (t - first) * tb0;
+        const uint8_t* w1 = upre_lds + (slot ? plan.off[3] : plan.off[1]) + (t - first) * tb1;
+        u_span_lds(L, li, batch, tile, T, span_max, w0, w1, tb0, tb1, hl_lds + 32 * (t - ut0), ctr, check, sync, sc, S,
+                   u_lds, &red[0][0][0]);
+        t += T;
+      }
+    } else if (MODE == 2 && t < ut1) {
       int tile;
       const int li = u_layer<SINGLE>(M, t, tile);
       const int lend = SINGLE ? ut1 : min(ut1, layer_u_end(M, li));
@@ -739,33 +949,54 @@ static hipError_t launch_decode_t(const LbDecodeArgs& args, int chunk_pairs, voi
       if (e != hipSuccess) return e;
       // every workgroup of the single launch must be resident at once: size
       // the grid for the largest dynamic LDS a launch may request
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ1, lb_decode_kernel<2, true>, LB_THREADS,
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ1, lb_decode_kernel<2, true, false>, LB_THREADS,
                                                        LB_DECODE_LDS_MAX);
       if (e != hipSuccess) return e;
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ7, lb_decode_kernel<2, false>, LB_THREADS,
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ7, lb_decode_kernel<2, false, false>, LB_THREADS,
                                                        LB_DECODE_LDS_MAX);
       if (e != hipSuccess) return e;
-      g_fused_grid[dev] = (occ1 >= 1 && occ7 >= 1) ? (ncu < LB_MAX_GRID ? ncu : LB_MAX_GRID) : -1;
+      int occ1p = 0, occ7p = 0;
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ1p, lb_decode_kernel<2, true, true>, LB_THREADS,
+                                                       LB_UPRE_DYN_MAX);
+      if (e != hipSuccess) return e;
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ7p, lb_decode_kernel<2, false, true>, LB_THREADS,
+                                                       LB_UPRE_DYN_MAX);
+      if (e != hipSuccess) return e;
+      g_fused_grid[dev] = (occ1 >= 1 && occ7 >= 1 && occ1p >= 1 && occ7p >= 1) ? (ncu < LB_MAX_GRID ? ncu : LB_MAX_GRID)
+                                                                                : -1;
     }
     const int G = g_fused_grid[dev];
     if (G > 0) {
       LbDecodeArgs a = args;
       a.vq = a.nvt / G; a.vr = a.nvt % G;
       a.uq = a.nut / G; a.ur = a.nut % G;
-      hipLaunchKernelGGL((lb_decode_kernel<2, SINGLE>), dim3(G), dim3(LB_THREADS), lds, stream, vb0, vb1, px, g0,
-                         g1, pn, pldx, vsplit, misc(a), a, chunk_pairs, (uint8_t*)sync);
+      // the variant that copies phase B's sign bytes to LDS during phase A,
+      // when the dynamic LDS leaves room for the copy and a workgroup's U
+      // tiles are more than the register prefetch holds (one group of
+      // LB_MAXT tiles of one layer, LB_MAXPW pairs per wave)
+      bool regs_hold = SINGLE && (a.nut + G - 1) / G <= LB_MAXT;
+      for (int b = 0; b < args.L[0].nb && regs_hold; ++b) {
+        const int np = (lb16_units(args.L[0].br[b].r) + 1) >> 1;
+        regs_hold = (np + (args.L[0].nb == 2 ? 3 : 7)) / (args.L[0].nb == 2 ? 4 : 8) <= LB_MAXPW;
+      }
+      if (lds <= LB_UPRE_DYN_MAX && !regs_hold)
+        hipLaunchKernelGGL((lb_decode_kernel<2, SINGLE, true>), dim3(G), dim3(LB_THREADS), lds, stream, vb0, vb1, px,
+                           g0, g1, pn, pldx, vsplit, misc(a), a, chunk_pairs, (uint8_t*)sync);
+      else
+        hipLaunchKernelGGL((lb_decode_kernel<2, SINGLE, false>), dim3(G), dim3(LB_THREADS), lds, stream, vb0, vb1, px,
+                           g0, g1, pn, pldx, vsplit, misc(a), a, chunk_pairs, (uint8_t*)sync);
       return hipGetLastError();
     }
   }
   LbDecodeArgs a = args;
   a.vq = 1; a.vr = 0;
-  hipLaunchKernelGGL((lb_decode_kernel<0, SINGLE>), dim3(a.nvt), dim3(LB_THREADS), lds, stream, vb0, vb1, px, g0,
+  hipLaunchKernelGGL((lb_decode_kernel<0, SINGLE, false>), dim3(a.nvt), dim3(LB_THREADS), lds, stream, vb0, vb1, px, g0,
                      g1, pn, pldx, vsplit, misc(a), a, chunk_pairs, (uint8_t*)sync);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int gb = a.nut < 1024 ? a.nut : 1024;
   a.uq = a.nut / gb; a.ur = a.nut % gb;
-  hipLaunchKernelGGL((lb_decode_kernel<1, SINGLE>), dim3(gb), dim3(LB_THREADS), lds, stream, vb0, vb1, px, g0, g1,
+  hipLaunchKernelGGL((lb_decode_kernel<1, SINGLE, false>), dim3(gb), dim3(LB_THREADS), lds, stream, vb0, vb1, px, g0, g1,
                      pn, pldx, vsplit, misc(a), a, chunk_pairs, (uint8_t*)sync);
   return hipGetLastError();
 }

@@ -93,14 +93,22 @@ def test_tiny_config_full_oracle(lb, batch, two_launches):
     (1000, 1000, (130, 70), 7),   # several tiles, tails of 2 and 1 units
     (16, 8, (1, 1), 2),           # rank 1, n smaller than a step
     (520, 4104, (264, 264), 16),  # n not a multiple of 64, full batch
+    # single launch with phase B's sign bytes copied to LDS during phase A:
+    (81920, 64, (64, 64), 1),      # 20 tiles per workgroup: 16 copied, 4 read from memory
+    (40960, 256, (1728, 1728), 1),  # 10 tiles of 6912 bytes: too big to copy, all from memory
+    (20000, 512, (1600,), 2),      # one branch, 5 tiles per workgroup
+    (40000, 128, (96, 96), 5),     # batch 5: 9 tiles copied per workgroup, the rest from memory
 ])
 def test_ragged_shapes(lb, m, n, ranks, batch):
     print(f"[case] ragged m={m} n={n} r={ranks} batch={batch}", flush=True)
     shape = synth.LayerShape("ragged", m, n, ranks)
     br, x = synth.make_layer(shape, batch=batch, seed=m + n)
     layer = _layer(lb, br)
-    y = lb.littlebit_linear_fwd(layer, torch.from_numpy(x).cuda())
+    xt = torch.from_numpy(x).cuda()
+    y = lb.littlebit_linear_fwd(layer, xt)
     _assert_parity(y, oracle.linear_forward(x, br), f"ragged {m}x{n} r={ranks} b={batch}")
+    # the single launch and the two-launch path sum in the same order
+    assert torch.equal(y, lb.littlebit_linear_fwd(layer, xt, path=lb.LB_DECODE_TWO_LAUNCHES))
 
 
 def test_branch_masks_and_additivity(lb):
