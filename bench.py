@@ -198,16 +198,19 @@ def _blas_threads():
     return len(os.sched_getaffinity(0))
 
 
-def cpu_baseline(shape, branches, x, seconds):
+def cpu_baseline(shape, branches, x, seconds, y_gpu):
     """Time the float64 oracle on the host: whole batch-1 calls of its factored
     form, repeated for about `seconds`, plus a sample of output rows of its
-    dense definition (rows of W built per call) for about a third of that."""
+    dense definition (rows of W built per call) for about a third of that.
+    The oracle's result is also compared with the GPU's on the same input."""
     import oracle
     calls, t0 = 0, time.perf_counter()
     while calls < 3 or time.perf_counter() - t0 < seconds:
-        oracle.factored_forward(x, branches)
+        yr = oracle.factored_forward(x, branches)
         calls += 1
     dt = time.perf_counter() - t0
+    agreement = {"rel_l2": float(np.linalg.norm(y_gpu - yr) / np.linalg.norm(yr)),
+                 "max_err_over_rms": float(np.max(np.abs(y_gpu - yr)) / np.sqrt(np.mean(yr ** 2)))}
     rows, t1 = 0, time.perf_counter()
     while rows < shape.m and (rows == 0 or time.perf_counter() - t1 < seconds / 3):
         blk = np.arange(rows, min(rows + 344, shape.m))
@@ -219,7 +222,52 @@ def cpu_baseline(shape, branches, x, seconds):
             "sample": f"{calls} whole batch-1 calls of the float64 factored oracle in {dt:.1f} s",
             "dense_definition": {"value": round(x.shape[0] * (rows / shape.m) / dtd, 4), "unit": "tokens/s",
                                  "sample": f"{rows} of {shape.m} output rows of the dense float64 definition "
-                                           f"in {dtd:.1f} s, scaled by {shape.m}/{rows}"}}
+                                           f"in {dtd:.1f} s, scaled by {shape.m}/{rows}"},
+            "gpu_agreement": agreement}
+
+
+def bpw_sweep(lb, torch, synth, args):
+    """Decode time of the 70B-shaped up-projection (8192 -> 28672, two
+    branches) at 1.0, 0.8, 0.55, 0.3 and 0.1 bits per weight, batch 1 and 16,
+    beside torch's fp16 dense product y = x W^T on the same shape (context)."""
+    rows = []
+    for bpw in sorted(synth.UP70B_BPW_SWEEP, reverse=True):
+        sh = synth.up70b_at_bpw(bpw)
+        one = make_copy(lb, torch, sh, 9000)
+        nc = copies_for(layer_bytes(one), args.copies_gb * 1e9)
+        lays = [one] + [make_copy(lb, torch, sh, 9001 + i) for i in range(nc - 1)]
+        row = {"bpw": bpw, "rank": sh.ranks[0], "weight_bytes": layer_bytes(one), "distinct_copies": nc}
+        for batch in (1, 16):
+            x = torch.randn((batch, sh.n), device="cuda").half()
+            y = torch.empty((batch, sh.m), dtype=torch.float16, device="cuda")
+            ws = torch.zeros(lb.littlebit_linear_workspace_bytes(one, batch), dtype=torch.uint8, device="cuda")
+            calls = [lambda l=l: lb.littlebit_linear_fwd(l, x, out=y, workspace=ws) for l in lays]
+            ms = time_graph(torch, calls, max(8 * nc, 400), 2 * nc)
+            abytes = algorithmic_bytes(sh.m, sh.n, sh.ranks, batch)
+            row[f"b{batch}"] = {"us_per_call": round(ms * 1e3, 3), "tokens_per_s": round(batch * 1e3 / ms, 1),
+                                "hbm_gbs": round(abytes / (ms * 1e-3) / 1e9, 1)}
+        rows.append(row)
+        del lays, one
+        torch.cuda.empty_cache()
+    # fp16 dense baseline: W^T stored [n, m] (no transposed view), copies > 1 GB
+    m, n = synth.UP70B.m, synth.UP70B.n
+    nw = max(2, int(np.ceil(args.copies_gb * 1e9 / (2 * m * n))))
+    wts = [torch.randn((n, m), device="cuda", dtype=torch.float16) for _ in range(nw)]
+    dense = {"distinct_copies": nw, "weight_bytes": 2 * m * n}
+    for batch in (1, 16):
+        x = torch.randn((batch, n), device="cuda").half()
+        y = torch.empty((batch, m), dtype=torch.float16, device="cuda")
+        calls = [lambda w=w: torch.matmul(x, w, out=y) for w in wts]
+        ms = time_graph(torch, calls, max(8 * nw, 200), 2 * nw)
+        dense[f"b{batch}"] = {"us_per_call": round(ms * 1e3, 3), "hbm_gbs": round((2 * m * n) / (ms * 1e-3) / 1e9, 1)}
+    for row in rows:
+        for batch in (1, 16):
+            row[f"b{batch}"]["speedup_vs_fp16_dense"] = round(dense[f"b{batch}"]["us_per_call"] /
+                                                              row[f"b{batch}"]["us_per_call"], 2)
+    del wts
+    torch.cuda.empty_cache()
+    return {"bpw_sweep": rows, "fp16_dense": dense,
+            "shape": {"m": m, "n": n, "branches": 2}, "data": "synthetic"}
 
 
 def main():
@@ -232,6 +280,8 @@ def main():
                     help="host time for the oracle baseline (0: skip)")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the 13B-block, 70B and prefill measurements")
+    ap.add_argument("--bpw-sweep", action="store_true",
+                    help="only the bits-per-weight sweep of the 70B up-projection against fp16 dense")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="no timing: one call per layer copy plus a 256 MiB device copy, for hardware counters")
     args = ap.parse_args()
@@ -243,7 +293,11 @@ def main():
     import torch
     from binary_rank_gemv_amd import littlebit as lb
     from binary_rank_gemv_amd import synth
-    import oracle
+
+    if args.bpw_sweep:
+        torch.cuda.set_device(0)
+        print(json.dumps(bpw_sweep(lb, torch, synth, args)))
+        return
 
     shape, batch = synth.UP7B, 1
     branches, x_np = synth.make_layer(shape, batch=batch, seed=0)
@@ -271,13 +325,11 @@ def main():
         print(json.dumps({"pmc_pass": True, "decode_calls": len(copies), "copy_bytes": src.numel()}))
         return
 
-    # correctness of the measured configuration (first copy) against the oracle
+    # the measured configuration's output (first copy), compared with the
+    # oracle in the cpu_baseline leg
     lb.littlebit_linear_fwd(first, x, out=y, workspace=ws)
     torch.cuda.synchronize()
-    yr = oracle.factored_forward(x_np, branches)
     yg = y.float().cpu().numpy().astype(np.float64)
-    rel_l2 = float(np.linalg.norm(yg - yr) / np.linalg.norm(yr))
-    max_rms = float(np.max(np.abs(yg - yr)) / np.sqrt(np.mean(yr ** 2)))
 
     def time_path(path):
         """Milliseconds for `steps` calls cycling over the copies (HIP graph)."""
@@ -301,7 +353,7 @@ def main():
 
     cpu = None
     if args.cpu_seconds > 0:
-        cpu = cpu_baseline(shape, branches, x_np, args.cpu_seconds)
+        cpu = cpu_baseline(shape, branches, x_np, args.cpu_seconds, yg)
 
     out = {
         "metric": "decode tokens/s per layer",
@@ -320,7 +372,6 @@ def main():
                                "(~1.0 BPW), batch-1 decode",
                    "m": shape.m, "n": shape.n, "ranks": list(shape.ranks), "batch": batch,
                    "distinct_layer_copies": ncopies, "copies_bytes": ncopies * per_copy},
-        "parity": {"rel_l2": rel_l2, "max_err_over_rms": max_rms},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "extra": extra,

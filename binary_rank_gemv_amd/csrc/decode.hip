@@ -483,21 +483,17 @@ __device__ __forceinline__ void upre_issue(const LbDecodeArgs& A, const TileMap&
   const int end1 = SINGLE ? ut1 : min(ut1, layer_u_end(M, li1));
   const LayerView L0 = layer_view(A.L[li0]);
   const LayerView L1 = layer_view(A.L[li1]);
-  const int n0 = max(end0 - ut0, 0), n1 = (SINGLE || li1 == li0) ? 0 : max(end1 - end0, 0);
+  // whole tiles, as many as fit: the first layer's, then the second's
+  const int pt0 = tile_bytes_b(L0, 0) + (L0.nb == 2 ? tile_bytes_b(L0, 1) : 0);
+  const int pt1 = tile_bytes_b(L1, 0) + (L1.nb == 2 ? tile_bytes_b(L1, 1) : 0);
+  const int n0a = max(end0 - ut0, 0), n1a = (SINGLE || li1 == li0) ? 0 : max(end1 - end0, 0);
+  const int n0 = min(min(n0a, max_tiles), LB_UPRE_BYTES / pt0);
+  const int n1 = n0 < n0a ? 0 : min(min(n1a, max_tiles - n0), (LB_UPRE_BYTES - n0 * pt0) / pt1);
   const int b00 = n0 * tile_bytes_b(L0, 0), b01 = L0.nb == 2 ? n0 * tile_bytes_b(L0, 1) : 0;
   const int b10 = n1 * tile_bytes_b(L1, 0), b11 = L1.nb == 2 ? n1 * tile_bytes_b(L1, 1) : 0;
-  int total = b00 + b01 + b10 + b11;
+  const int total = b00 + b01 + b10 + b11;
   P.split = end0;
-  P.cover = SINGLE ? end0 : end1;
-  if (total > LB_UPRE_BYTES) {  // the second layer does not fit: first layer only
-    total = b00 + b01;
-    P.cover = end0;
-  }
-  if (total > LB_UPRE_BYTES) {  // nothing fits: phase B reads its sign words from memory
-    total = 0;
-    P.cover = ut0;
-  }
-  P.cover = min(P.cover, ut0 + max_tiles);  // the row-scale table and the partial sums hold these
+  P.cover = n1 > 0 ? end0 + n1 : ut0 + n0;
   P.off[0] = 0;
   P.off[1] = b00;
   P.off[2] = b00 + b01;

@@ -60,6 +60,15 @@ inline bool decode_fits(int zs, int64_t batch) {
   return (size_t)batch * (zs + 8) * sizeof(uint16_t) <= LB_DECODE_LDS_MAX;
 }
 
+// Tokens per decode launch: up to 16, fewer when z of 16 tokens exceeds the
+// LDS (then a call of up to 16 tokens runs as several launches); 0 when not
+// even one token fits.
+inline int decode_chunk_tokens(int zs) {
+  int t = 16;
+  while (t > 0 && !decode_fits(zs, t)) --t;
+  return t;
+}
+
 inline size_t prefill_z_bytes(int zs, int64_t tokens) {
   const int64_t t = tokens < LB_PREFILL_MAX_TOKENS ? tokens : LB_PREFILL_MAX_TOKENS;
   return round_up((size_t)t * zs * sizeof(uint16_t), 256);
@@ -245,11 +254,10 @@ lb_status littlebit_linear_fwd(const lb_layer* L, uint32_t branch_mask, const ui
   if (!aligned(ws, 256)) return fail(LB_ERR_WORKSPACE, "littlebit_linear_fwd: workspace must be 256-byte aligned");
   const LayerWs w = layer_ws(*L, sel, nsel, kDecodeMaxBatch);
   const uint32_t path = flags & 3u;
-  const bool fits = decode_fits(w.zs, batch < kDecodeMaxBatch ? batch : kDecodeMaxBatch);
-  if (path == LB_PATH_DECODE && !fits)
-    return fail(LB_ERR_UNSUPPORTED, "littlebit_linear_fwd: batch %lld x rank %d exceeds the decode kernels' LDS",
-                (long long)batch, w.zs);
-  const bool prefill = path == LB_PATH_PREFILL || (path == LB_PATH_AUTO && (batch > kDecodeMaxBatch || !fits));
+  const int chunk = decode_chunk_tokens(w.zs);
+  if (path == LB_PATH_DECODE && chunk == 0)
+    return fail(LB_ERR_UNSUPPORTED, "littlebit_linear_fwd: rank %d exceeds the decode kernels' LDS", w.zs);
+  const bool prefill = path == LB_PATH_PREFILL || (path == LB_PATH_AUTO && (batch > kDecodeMaxBatch || chunk == 0));
   const size_t need = kWsHeader + w.z_bytes + (prefill ? prefill_z_bytes(w.zs_p, batch) : 0);
   if (ws_bytes < need)
     return fail(LB_ERR_WORKSPACE, "littlebit_linear_fwd: workspace has %zu bytes, needs %zu", ws_bytes, need);
@@ -266,8 +274,8 @@ lb_status littlebit_linear_fwd(const lb_layer* L, uint32_t branch_mask, const ui
     }
     return LB_OK;
   }
-  for (int64_t t0 = 0; t0 < batch; t0 += kDecodeMaxBatch) {
-    const int nb = (int)((batch - t0) < kDecodeMaxBatch ? (batch - t0) : kDecodeMaxBatch);
+  for (int64_t t0 = 0; t0 < batch; t0 += chunk) {
+    const int nb = (int)((batch - t0) < chunk ? (batch - t0) : chunk);
     LbLayerArgs la;
     fill_layer_args(la, *L, sel, nsel, w, base, x + t0 * ldx, (long)ldx, y + t0 * ldy, (long)ldy);
     st = run_decode(&la, 1, nb, ws, !(flags & LB_DECODE_TWO_LAUNCHES), (hipStream_t)stream);
@@ -288,7 +296,7 @@ size_t littlebit_block_workspace_bytes(const lb_layer L[7], int64_t batch) {
     total += w.z_bytes;
     const size_t p = prefill_z_bytes(w.zs_p, batch);
     if (p > zp) zp = p;
-    prefill = prefill || !decode_fits(w.zs, batch);
+    prefill = prefill || decode_chunk_tokens(w.zs) == 0;
   }
   return kWsHeader + total + (prefill ? zp : 0);
 }
@@ -316,8 +324,12 @@ lb_status littlebit_block_fwd(const lb_layer L[7], const uint16_t* x_qkv, const 
     const size_t p = prefill_z_bytes(w[i].zs_p, batch);
     if (p > zp) zp = p;
   }
-  bool prefill = batch > kDecodeMaxBatch;
-  for (int i = 0; i < 7; ++i) prefill = prefill || !decode_fits(w[i].zs, batch);
+  int chunk = kDecodeMaxBatch;
+  for (int i = 0; i < 7; ++i) {
+    const int c = decode_chunk_tokens(w[i].zs);
+    chunk = c < chunk ? c : chunk;
+  }
+  const bool prefill = batch > kDecodeMaxBatch || chunk == 0;
   const size_t decode_bytes = need - kWsHeader;
   if (prefill) need += zp;
   if (L[0].n != L[1].n || L[0].n != L[2].n || L[4].n != L[5].n)
@@ -341,8 +353,8 @@ lb_status littlebit_block_fwd(const lb_layer L[7], const uint16_t* x_qkv, const 
     }
     return LB_OK;
   }
-  for (int64_t t0 = 0; t0 < batch; t0 += kDecodeMaxBatch) {
-    const int nb = (int)((batch - t0) < kDecodeMaxBatch ? (batch - t0) : kDecodeMaxBatch);
+  for (int64_t t0 = 0; t0 < batch; t0 += chunk) {
+    const int nb = (int)((batch - t0) < chunk ? (batch - t0) : chunk);
     LbLayerArgs la[7];
     uint8_t* base = static_cast<uint8_t*>(ws) + kWsHeader;
     for (int i = 0; i < 7; ++i) {

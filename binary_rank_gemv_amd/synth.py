@@ -61,6 +61,16 @@ def block13b_shapes(setting: str) -> List[LayerShape]:
 TINY = LayerShape("tiny_512x512_r32", 512, 512, (32, 32))
 UP7B = LayerShape("llama2_7b_up_4096x11008_r1472", 11008, 4096, (1472, 1472))
 UP70B = LayerShape("llama2_70b_up_8192x28672_r1728", 28672, 8192, (1728, 1728))
+# The bits-per-weight sweep on the 70B-shaped up-projection: per target BPW,
+# the rank (a multiple of 16) whose stored bits per weight come nearest to it
+# with two branches (1.0 -> 0.9999, 0.8 -> 0.7989, 0.55 -> 0.5477, 0.3 ->
+# 0.3015, 0.1 -> 0.1005; a CPU test recomputes these from the closed form).
+UP70B_BPW_SWEEP = {1.0: 3168, 0.8: 2528, 0.55: 1728, 0.3: 944, 0.1: 304}
+
+
+def up70b_at_bpw(bpw: float) -> LayerShape:
+    r = UP70B_BPW_SWEEP[bpw]
+    return LayerShape(f"llama2_70b_up_8192x28672_r{r}_{bpw}bpw", 28672, 8192, (r, r))
 PREFILL_TOKENS = 2048
 
 

@@ -51,6 +51,10 @@ typedef enum lb_dtype { LB_F32 = 0, LB_F16 = 1 } lb_dtype;
 /* Path selection for littlebit_linear_fwd (flags argument). */
 #define LB_PATH_AUTO 0u    /* decode kernels for batch <= 16, else prefill  */
 #define LB_PATH_DECODE 1u  /* force the decode kernels (batch must be <= 16)*/
+/* The decode kernels hold z of their tokens in LDS: when 16 tokens of a
+ * layer's rank do not fit, a decode call runs as several launches of fewer
+ * tokens each (LB_ERR_UNSUPPORTED, or prefill under LB_PATH_AUTO, only when
+ * not even one token fits). */
 #define LB_PATH_PREFILL 2u /* force the prefill (matrix-core GEMM) kernels  */
 /* OR-able: run the decode path as two launches (V pass, then U pass) instead
  * of one launch whose workgroups exchange the rank-space intermediate through

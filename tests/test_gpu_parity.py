@@ -95,9 +95,10 @@ def test_tiny_config_full_oracle(lb, batch, two_launches):
     (520, 4104, (264, 264), 16),  # n not a multiple of 64, full batch
     # single launch with phase B's sign bytes copied to LDS during phase A:
     (81920, 64, (64, 64), 1),      # 20 tiles per workgroup: 16 copied, 4 read from memory
-    (40960, 256, (1728, 1728), 1),  # 10 tiles of 6912 bytes: too big to copy, all from memory
+    (40960, 256, (1728, 1728), 1),  # 10 tiles of 6912 bytes: 9 fit the copy, 1 from memory
     (20000, 512, (1600,), 2),      # one branch, 5 tiles per workgroup
     (40000, 128, (96, 96), 5),     # batch 5: 9 tiles copied per workgroup, the rest from memory
+    (600, 300, (3000, 3000), 13),  # z of 13 tokens exceeds the LDS: launches of 9 and 4 tokens
 ])
 def test_ragged_shapes(lb, m, n, ranks, batch):
     print(f"[case] ragged m={m} n={n} r={ranks} batch={batch}", flush=True)
@@ -211,6 +212,14 @@ def test_llama2_70b_up(lb, batch):
     print(f"[case] 70b up batch {batch}", flush=True)
     br, x = synth.make_layer(synth.UP70B, batch=batch, seed=0)
     _full_size_check(lb, br, x, f"70B up b={batch}")
+
+
+@pytest.mark.parametrize("bpw,batch", [(1.0, 1), (0.8, 1), (0.3, 1), (0.1, 1), (0.1, 16), (1.0, 16)])
+def test_70b_bpw_sweep_ranks(lb, bpw, batch):
+    """The ranks of the bits-per-weight sweep (0.55 is the 70B case above)."""
+    print(f"[case] 70b up {bpw} bpw batch {batch}", flush=True)
+    br, x = synth.make_layer(synth.up70b_at_bpw(bpw), batch=batch, seed=1)
+    _full_size_check(lb, br, x, f"70B up {bpw} BPW b={batch}")
 
 
 @pytest.mark.parametrize("setting", ["0.55", "0.1"])

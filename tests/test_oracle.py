@@ -207,6 +207,17 @@ def test_config_ranks_give_the_stated_bits_per_weight(m, n, r, stated):
     assert abs(oracle.rank_for_bpw(m, n, oracle.bits_per_weight(m, n, r)) - r) < 1e-9
 
 
+@pytest.mark.parametrize("bpw", sorted(synth.UP70B_BPW_SWEEP))
+def test_bpw_sweep_ranks_are_the_nearest_multiples_of_16(bpw):
+    """Each sweep rank is the multiple of 16 nearest the closed-form rank, and
+    its stored bits per weight are within 1.2% of the target."""
+    r = synth.UP70B_BPW_SWEEP[bpw]
+    assert r % 16 == 0
+    exact = oracle.rank_for_bpw(28672, 8192, bpw)
+    assert abs(r - exact) <= 8
+    assert oracle.bits_per_weight(28672, 8192, r) == pytest.approx(bpw, rel=0.012)
+
+
 def test_model_footprints_match_the_pages():
     d = _load("model_sizes.json")
     tol = d["tolerance"]
