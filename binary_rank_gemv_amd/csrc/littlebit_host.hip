@@ -12,6 +12,7 @@
 hipError_t lb_launch_pack(const void* latent, int is_f16, long ld, int transpose, int R, int K,
                           void* dst, hipStream_t stream);
 hipError_t lb_launch_prefill(const LbPrefillArgs& args, hipStream_t stream);
+hipError_t lb_launch_transpose_packed(const void* src, int R, int K, void* dst, hipStream_t stream);
 hipError_t lb_launch_decode(const LbDecodeArgs& args, int chunk_pairs, void* sync, int allow_fused,
                             hipStream_t stream);
 
@@ -223,6 +224,18 @@ lb_status littlebit_pack(const void* latent, lb_dtype dtype, int64_t rows, int64
   hipError_t e = lb_launch_pack(latent, dtype == LB_F16, (long)ld, transpose, (int)R, (int)K, dst,
                                 (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "littlebit_pack launch");
+  return LB_OK;
+}
+
+lb_status littlebit_transpose_packed(const void* src, int64_t R, int64_t K, void* dst, void* stream) {
+  if (!src || !dst) return fail(LB_ERR_INVALID_ARG, "littlebit_transpose_packed: NULL pointer");
+  if (R < 1 || K < 1) return fail(LB_ERR_INVALID_ARG, "littlebit_transpose_packed: R=%lld K=%lld", (long long)R, (long long)K);
+  if (!aligned(src, 4) || !aligned(dst, 4))
+    return fail(LB_ERR_INVALID_ARG, "littlebit_transpose_packed: src and dst must be 4-byte aligned");
+  if (R > (1LL << 24) || K > (1LL << 24)) return fail(LB_ERR_UNSUPPORTED, "littlebit_transpose_packed: factor too large");
+  if (src == dst) return fail(LB_ERR_INVALID_ARG, "littlebit_transpose_packed: src and dst must not be the same buffer");
+  hipError_t e = lb_launch_transpose_packed(src, (int)R, (int)K, dst, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "littlebit_transpose_packed launch");
   return LB_OK;
 }
 

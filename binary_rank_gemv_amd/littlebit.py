@@ -8,6 +8,8 @@ binary_rank_gemv_amd.build``) -- there is no fallback path.
 The functions keep the C names:
 
 * ``littlebit_pack(latent, transpose)`` -> packed uint8 tensor
+* ``littlebit_transpose_packed(bits, R, K)`` -> packing of the K x R transpose
+  (``LittleBitLayer.transposed()`` builds the layer of W^T from it)
 * ``littlebit_linear_fwd(layer, x, branch_mask=3, path=LB_PATH_AUTO)`` -> y
 * ``littlebit_block_fwd(layers, x_qkv, x_o, x_gu, x_down)`` -> list of 7 y
 * ``littlebit_packed_bytes``, ``littlebit_linear_workspace_bytes``,
@@ -34,7 +36,7 @@ LB_DECODE_TWO_LAUNCHES = 4
 EXPORTED = (
     "littlebit_packed_bytes", "littlebit_pack", "littlebit_linear_workspace_bytes",
     "littlebit_linear_fwd", "littlebit_block_workspace_bytes", "littlebit_block_fwd",
-    "littlebit_status_string", "littlebit_last_error",
+    "littlebit_status_string", "littlebit_last_error", "littlebit_transpose_packed",
 )
 
 
@@ -64,6 +66,8 @@ def _load():
     lib.littlebit_packed_bytes.restype = sz
     lib.littlebit_pack.argtypes = [vp, i32, i64, i64, i64, i32, vp, vp]
     lib.littlebit_pack.restype = i32
+    lib.littlebit_transpose_packed.argtypes = [vp, i64, i64, vp, vp]
+    lib.littlebit_transpose_packed.restype = i32
     lib.littlebit_linear_workspace_bytes.argtypes = [ctypes.POINTER(_Layer), i64]
     lib.littlebit_linear_workspace_bytes.restype = sz
     lib.littlebit_linear_fwd.argtypes = [ctypes.POINTER(_Layer), u32, vp, i64, i64, vp, i64, vp, sz, u32, vp]
@@ -125,6 +129,15 @@ def littlebit_pack(latent: torch.Tensor, transpose: bool, stream=None) -> torch.
     return out
 
 
+def littlebit_transpose_packed(bits: torch.Tensor, R: int, K: int, stream=None) -> torch.Tensor:
+    """The packing of the K x R transpose of the packed R x K factor ``bits``."""
+    if bits.dtype != torch.uint8 or not bits.is_cuda or bits.numel() != littlebit_packed_bytes(R, K):
+        raise ValueError("bits must be the uint8 CUDA packing of an R x K factor")
+    out = torch.empty(littlebit_packed_bytes(K, R), dtype=torch.uint8, device=bits.device)
+    _check(LIB.littlebit_transpose_packed(_ptr(bits), R, K, _ptr(out), _stream_ptr(stream)))
+    return out
+
+
 @dataclass
 class LittleBitBranch:
     v_bits: torch.Tensor
@@ -158,6 +171,17 @@ class LittleBitLayer:
                                        u_bits=littlebit_pack(U, transpose=False),
                                        r=int(r), **scales))
         return LittleBitLayer(m=int(m), n=int(n), branches=out)
+
+    def transposed(self, stream=None) -> "LittleBitLayer":
+        """The layer of W^T (m' = n, n' = m): sign(U) takes the V role and
+        sign(V) the U role, h and g swap; littlebit_linear_fwd on it gives
+        dx = W^T dy, the backward-input product of quantization-aware training."""
+        out = []
+        for b in self.branches:
+            out.append(LittleBitBranch(v_bits=littlebit_transpose_packed(b.u_bits, self.m, b.r, stream),
+                                       u_bits=littlebit_transpose_packed(b.v_bits, b.r, self.n, stream),
+                                       h=b.g, l=b.l, g=b.h, r=b.r))
+        return LittleBitLayer(m=self.n, n=self.m, branches=out)
 
     def c_struct(self) -> _Layer:
         s = _Layer()

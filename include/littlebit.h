@@ -100,6 +100,22 @@ lb_status littlebit_pack(const void *latent, lb_dtype dtype, int64_t rows,
                          int64_t cols, int64_t ld, int transpose, void *dst,
                          void *stream);
 
+/*
+ * The packing of the transpose of a packed factor: src holds an R x K factor
+ * (littlebit_packed_bytes(R, K) bytes), dst receives the K x R factor with the
+ * same bits (littlebit_packed_bytes(K, R) bytes, every byte written, pad bits
+ * 0).  For the backward-input product of quantization-aware training
+ * (explainx.ai explainer, "How it works" item 3: the model trains through
+ * the binarized forward pass), dx = W^T dy, which is the layer with
+ *   v_bits' = transpose(u_bits)  (R = r, K = m),
+ *   u_bits' = transpose(v_bits)  (R = n, K = r),
+ *   h' = g, l' = l, g' = h, m' = n, n' = m,
+ * run through littlebit_linear_fwd.  src and dst: device, 4-byte aligned,
+ * distinct.  Asynchronous on `stream`.
+ */
+lb_status littlebit_transpose_packed(const void *src, int64_t R, int64_t K,
+                                     void *dst, void *stream);
+
 typedef struct lb_branch {
   const void *v_bits; /* device, LB16 sign(V)^T: R = r, K = n               */
   const void *u_bits; /* device, LB16 sign(U):   R = m, K = r               */
