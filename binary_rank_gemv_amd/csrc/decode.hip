@@ -393,61 +393,120 @@ struct UState {
   int b, p0, p1, nu;
 };
 
-#define LB_POLL_STEPS (4 * LB_MAXPW)  // z steps polled per memory round trip
+// 16-byte loads per lane in flight per pass of the z poll: 24 at larger
+// batches, 8 (fewer registers to set up) when the range is at most that
+#define LB_POLL_LOADS 24
+#define LB_POLL_LOADS_SMALL 8
 
-// Copies this wave's range of layer L's z into LDS (zl: [token][zs + 8] fp16),
-// polling (check) until every word carries this call's tag.  The steps go in
-// batches of LB_POLL_STEPS; every load of a batch is issued before any result
-// is examined, so a batch costs one memory round trip.  A wave later reads
-// only the range it copied, so no barrier follows the copy; the barrier in
-// front keeps the previous layer's readers safe.
-__device__ __forceinline__ void u_enter_layer(const LayerView& L, int li, int batch, uint32_t ctr, bool check,
-                                              uint8_t* sync, UState& S, uint16_t* zl) {
-  const int lane = threadIdx.x & 63, wave = wave_id();
-  const uint32_t tag = late(ctr) + 1u;
-  const int tok = lane & 15, grp = lane >> 4;
-  __syncthreads();  // earlier readers of zl (previous layer, or phase A's u) are done
-  S.li = li;
-  u_role(L, wave, S.b, S.p0, S.p1);
-  S.nu = lb16_units(S.b ? L.r1 : L.r0);
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(L.z, batch * L.zs * 4);
-  const int zb = 4 * (min(tok, batch - 1) * L.zs + (S.b ? L.zoff1 : L.zoff0) + 8 * grp);
-  uint16_t* zdst = zl + tok * (L.zs + 8) + (S.b ? L.zoff1 : L.zoff0) + 8 * grp;
-  const int s1 = min(4 * S.p1, 2 * S.nu);  // steps of this wave's range that hold data
-  for (int sb = 4 * S.p0; sb < s1; sb += LB_POLL_STEPS) {
+// Copies the steps [s0, s1) of a wave's range of layer L's z into LDS (zl:
+// [token][zs + 8] fp16), polling (check) until every word carries this call's
+// tag.  The range (128 bytes per step and token) is cut into 16-byte chunks
+// (two tagged words, four values) dealt to the lanes in order: chunk
+// lane + 64 j is load j of the lane, so no two lanes load the same bytes (at
+// batch 1 a range of 12 steps is two loads per lane).  Up to NL loads per
+// lane are issued before any result is examined, so a pass costs one
+// memory round trip; a later pass re-reads only the loads whose chunks were
+// not all tagged.  A wave later reads only the range it copied, so no barrier
+// follows the copy; the barrier in front keeps the previous layer's readers
+// safe.
+template <int NL>
+__device__ __forceinline__ void u_copy_z(const LayerView& L, int batch, uint32_t tag, bool check, uint8_t* sync,
+                                         const UState& S, uint16_t* zl, int s0, int s1) {
+  const int lane = threadIdx.x & 63;
+  const int zoff = S.b ? L.zoff1 : L.zoff0;
+  const int oob = batch * L.zs * 4;  // a load at this offset returns zeros and marks an idle lane
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(L.z, oob);
+  const int per_tok = 8 * (s1 - s0);              // chunks per token
+  const int nload = (batch * per_tok + 63) >> 6;  // loads per lane
+  // position of this lane's next chunk: token t, chunk w of the token, and
+  // its byte offset in z (g) and element offset in zl (l).  A load moves 64
+  // chunks on: dq tokens and dr chunks, with a carry into the next token when
+  // the chunk index passes per_tok.
+  int t = 0, w = lane;
+  while (w >= per_tok) {
+    w -= per_tok;
+    ++t;
+  }
+  const int dq = 64 / per_tok, dr = 64 - dq * per_tok;
+  const int zsb = 4 * L.zs, zsl = L.zs + 8;
+  int g = t * zsb + 4 * zoff + 128 * s0 + 16 * w;
+  int l = t * zsl + zoff + 32 * s0 + 4 * w;
+  const int dg = dq * zsb + 16 * dr, dl = dq * zsl + 4 * dr;
+  const int cg = zsb - 16 * per_tok, cl = zsl - 4 * per_tok;  // the carry's offset changes
+  for (int jb = 0; jb < nload; jb += NL) {
+    const int nj = min(NL, nload - jb);
+    int goff[NL], loff[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      if (i < nj) {
+        goff[i] = t < batch ? g : oob;
+        loff[i] = l;
+        w += dr;
+        t += dq;
+        g += dg;
+        l += dl;
+        if (w >= per_tok) {
+          w -= per_tok;
+          ++t;
+          g += cg;
+          l += cl;
+        }
+      }
+    }
+    uint32_t todo = (1u << nj) - 1u;  // loads of this batch still to read
+    u32x4 q[NL];
     int spins = 0;
     for (;;) {
       compiler_memory_barrier();  // every pass re-reads the words
-      u32x4 q0[LB_POLL_STEPS], q1[LB_POLL_STEPS];
 #pragma unroll
-      for (int i = 0; i < LB_POLL_STEPS; ++i) {
-        const int st = min(sb + i, s1 - 1);
-        q0[i] = ld_tagged2(rs, zb + 128 * st);
-        q1[i] = ld_tagged2(rs, zb + 128 * st + 16);
-      }
-      bool ok = true;
+      for (int i = 0; i < NL; ++i)
+        if (todo & (1u << i)) q[i] = ld_tagged2(rs, goff[i]);
+      if (check) {
 #pragma unroll
-      for (int i = 0; i < LB_POLL_STEPS; ++i)
-        ok = ok & ((q0[i][0] == tag) & (q0[i][2] == tag) & (q1[i][0] == tag) & (q1[i][2] == tag));
-      if (!check || __all(ok)) {
-        if (tok < batch) {
-#pragma unroll
-          for (int i = 0; i < LB_POLL_STEPS; ++i) {
-            if (sb + i < s1) {
-              u32x4 d;
-              d[0] = q0[i][1]; d[1] = q0[i][3]; d[2] = q1[i][1]; d[3] = q1[i][3];
-              *reinterpret_cast<u32x4*>(zdst + 32 * (sb + i)) = d;
-            }
+        for (int i = 0; i < NL; ++i) {
+          if (todo & (1u << i)) {
+            const bool ok = (goff[i] == oob) | ((q[i][0] == tag) & (q[i][2] == tag));
+            if (__all(ok)) todo &= ~(1u << i);
           }
         }
-        break;
+      } else {
+        todo = 0;
       }
+      if (todo == 0) break;
       if (++spins > LB_SPIN_LIMIT) {
         st32c(sync + LB_SYNC_ERR, 1u);
         break;
       }
     }
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      if (i < nj && goff[i] != oob) {
+        uint2 d;
+        d.x = q[i][1];
+        d.y = q[i][3];
+        *reinterpret_cast<uint2*>(zl + loff[i]) = d;
+      }
+    }
   }
+}
+
+// Copies this wave's range of layer L's z into LDS (u_copy_z), after taking
+// the wave's phase-B role for the layer.
+__device__ __forceinline__ void u_enter_layer(const LayerView& L, int li, int batch, uint32_t ctr, bool check,
+                                              uint8_t* sync, UState& S, uint16_t* zl) {
+  const int wave = wave_id();
+  const uint32_t tag = late(ctr) + 1u;
+  __syncthreads();  // earlier readers of zl (previous layer, or phase A's u) are done
+  S.li = li;
+  u_role(L, wave, S.b, S.p0, S.p1);
+  S.nu = lb16_units(S.b ? L.r1 : L.r0);
+  const int s0 = 4 * S.p0;
+  const int s1 = min(4 * S.p1, 2 * S.nu);  // steps of this wave's range that hold data
+  if (s1 <= s0) return;
+  if (batch * 8 * (s1 - s0) <= 64 * LB_POLL_LOADS_SMALL)
+    u_copy_z<LB_POLL_LOADS_SMALL>(L, batch, tag, check, sync, S, zl, s0, s1);
+  else
+    u_copy_z<LB_POLL_LOADS>(L, batch, tag, check, sync, S, zl, s0, s1);
 }
 
 // ---------------------------------------------- phase-B sign bytes in LDS
