@@ -81,6 +81,29 @@ __device__ inline uint32_t late(uint32_t v) {
   __asm__ volatile("" : "+v"(v));
   return v;
 }
+// The decode kernel's explicit arguments in order, as laid out in the kernel
+// argument segment (each at its natural alignment, as in a struct).
+struct LbDecodeKernargs {
+  const uint8_t *pre_vb0, *pre_vb1;
+  const uint16_t *pre_x, *pre_g0, *pre_g1;
+  int pre_n, pre_ldx, pre_vsplit;
+  uint32_t pre_misc;
+  LbDecodeArgs A;
+  int chunk_pairs;
+  uint8_t* sync;
+};
+
+// The argument block A of the decode kernel, read through a pointer the
+// compiler cannot see through, so no load of its fields is placed above the
+// call.  (Taking the parameter's address instead would copy it to scratch.)
+__device__ __forceinline__ const LbDecodeArgs& kernarg_barrier() {
+  typedef const __attribute__((address_space(4))) char* KBytes;
+  typedef const __attribute__((address_space(4))) LbDecodeArgs* KPtr;
+  KPtr p = (KPtr)((KBytes)__builtin_amdgcn_kernarg_segment_ptr() + offsetof(LbDecodeKernargs, A));
+  __asm__ volatile("" : "+s"(p));
+  return *(const LbDecodeArgs*)p;
+}
+
 // Flattened view of one layer: branch fields are selected with `b ? x1 : x0`
 // so no per-branch array is indexed at run time.
 struct LayerView {
@@ -200,17 +223,90 @@ struct BoolTag {
   static constexpr bool value = B;
 };
 
-template <bool HOOK, class Hook>
+// Geometry of this thread's part of the V pass over one 16-row tile of
+// branch b of layer L.
+struct VGeom {
+  const uint16_t* xr;       // x row of this thread's token (building u)
+  const uint16_t* g;
+  const uint8_t* tile_ptr;  // the tile's packed sign words
+  int n, nu, np;
+  int tpt, my_tok, my_sub;  // threads per token building u, and this thread's token and share
+  bool fast;                // 16-byte loads of x and g
+};
+
+// Reads only the fields a caller may know before the rest of the arguments:
+// the factor's sign words (vb0, vb1), x, ldx, g0, g1 and n.
+__device__ __forceinline__ VGeom v_geom(const LayerView& L, int batch, int b, int tile) {
+  VGeom G;
+  const int tid = threadIdx.x;
+  G.n = L.n;
+  G.g = b ? L.g1 : L.g0;
+  G.nu = lb16_units(G.n);
+  G.np = (G.nu + 1) >> 1;
+  G.tile_ptr = (b ? L.vb1 : L.vb0) + (long)tile * lb16_tile_bytes(G.n);
+  int lb = 0;
+  while ((1 << lb) < batch) ++lb;
+  static_assert(LB_THREADS == 512, "token split assumes 512 threads");
+  G.tpt = LB_THREADS >> lb;
+  G.my_tok = tid >> (9 - lb);
+  G.my_sub = tid & (G.tpt - 1);
+  // 16-byte loads of x and g when aligned and n % 8 == 0 (then a group of 8
+  // inputs is either wholly below n or wholly at/after it)
+  G.fast = ((((uintptr_t)L.x) & 15) == 0) && ((L.ldx & 7) == 0) && ((G.n & 7) == 0);
+  G.xr = L.x + (long)min(G.my_tok, batch - 1) * L.ldx;
+  return G;
+}
+
+// x and g of inputs k..k+7 (zero at and beyond n)
+__device__ __forceinline__ void v_load_xg(const VGeom& G, int k, uint4& xv, uint4& gv) {
+  if (G.fast) {
+    const int kk = min(k, G.n - 8);  // always-valid address; zeroed by the caller when k >= n
+    xv = *reinterpret_cast<const uint4*>(G.xr + kk);
+    gv = *reinterpret_cast<const uint4*>(G.g + kk);
+  } else {
+    uint16_t xe[8], ge[8];
+    for (int e = 0; e < 8; ++e) {
+      xe[e] = (k + e < G.n) ? G.xr[k + e] : (uint16_t)0;
+      ge[e] = (k + e < G.n) ? G.g[k + e] : (uint16_t)0;
+    }
+    xv = *reinterpret_cast<uint4*>(xe);
+    gv = *reinterpret_cast<uint4*>(ge);
+  }
+}
+
+// The loads that open a chunk of V pairs [cb, cb + chunk_pairs) of a tile:
+// this thread's first group of activations, then the wave's sign words (the
+// activations come first, so waiting for them leaves the words in flight).
+struct VLoads {
+  uint4 xv0, gv0;
+  uint32_t words[LB_MAXPV];
+};
+
+__device__ __forceinline__ void v_issue(const VGeom& G, int cb, int chunk_pairs, VLoads& R) {
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int cn = min(G.np - cb, chunk_pairs);
+  const int pb = cb + ((cn * wave) >> 3), pe = cb + ((cn * (wave + 1)) >> 3);
+  const int kc = 128 * cn;
+  v_load_xg(G, 128 * cb + 8 * min(G.my_sub, (kc >> 3) - 1), R.xv0, R.gv0);
+  // unconditional loads (clamped to a valid pair) keep the wait counts
+  // exact; pairs beyond pe are never used
+  const int plast = max(pe - 1, 0);
+#pragma unroll
+  for (int i = 0; i < LB_MAXPV; ++i) R.words[i] = lb16_load_pair(G.tile_ptr, min(pb + i, plast), lane, G.nu);
+}
+
+// V pass over one 16-row tile of branch b of layer L (all its pairs, in
+// chunks of chunk_pairs whose u = g*x is staged in u_lds), then z = l*t of
+// the tile's rows stored as tagged words.  HOOK: hook() runs once the first
+// chunk's loads have landed, before its matrix steps.  EARLY: the first chunk's loads were
+// issued by the caller (`early`, from v_issue with the same geometry).
+template <bool HOOK, bool EARLY, class Hook>
 __device__ __forceinline__ void v_tile(const LayerView& L, int batch, int b, int tile, int chunk_pairs,
                                        const uint32_t& ctr, const LbSignConsts& sc, uint16_t* u_lds,
-                                       float (*red)[256], uint32_t* zstage, Hook&& hook) {
-  const int n = L.n;
-  const long ldx = L.ldx;
-  const uint16_t* __restrict__ x = L.x;
-  const uint16_t* __restrict__ g = b ? L.g1 : L.g0;
+                                       float (*red)[256], uint32_t* zstage, Hook&& hook, const VLoads& early) {
+  const VGeom G = v_geom(L, batch, b, tile);
+  const int n = G.n, nu = G.nu, np = G.np;
   const int r = b ? L.r1 : L.r0;
-  const int nu = lb16_units(n), np = (nu + 1) >> 1;
-  const uint8_t* __restrict__ tile_ptr = (b ? L.vb1 : L.vb0) + (long)tile * lb16_tile_bytes(n);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int tok = lane & 15, grp = lane >> 4;
@@ -219,71 +315,39 @@ __device__ __forceinline__ void v_tile(const LayerView& L, int batch, int b, int
   const int j = 16 * tile + rho;
   uint32_t lj_raw = 0;  // fp16 bits of l[j], loaded after the first sign words
 
-  int lb = 0;
-  while ((1 << lb) < batch) ++lb;
-  const int tpt = LB_THREADS >> lb;          // threads per token building u
-  const int my_tok = tid >> (9 - lb), my_sub = tid & (tpt - 1);
-  static_assert(LB_THREADS == 512, "token split assumes 512 threads");
-  // 16-byte loads of x and g when aligned and n % 8 == 0 (then a group of 8
-  // inputs is either wholly below n or wholly at/after it)
-  const bool fast = ((((uintptr_t)x) & 15) == 0) && ((ldx & 7) == 0) && ((n & 7) == 0);
-  const uint16_t* __restrict__ xr = x + (long)min(my_tok, batch - 1) * ldx;
-
-  // x and g of inputs k..k+7 (zero at and beyond n)
-  auto load_xg = [&](int k, uint4& xv, uint4& gv) {
-    if (fast) {
-      const int kk = min(k, n - 8);  // always-valid address; zeroed below when k >= n
-      xv = *reinterpret_cast<const uint4*>(xr + kk);
-      gv = *reinterpret_cast<const uint4*>(g + kk);
-    } else {
-      uint16_t xe[8], ge[8];
-      for (int e = 0; e < 8; ++e) {
-        xe[e] = (k + e < n) ? xr[k + e] : (uint16_t)0;
-        ge[e] = (k + e < n) ? g[k + e] : (uint16_t)0;
-      }
-      xv = *reinterpret_cast<uint4*>(xe);
-      gv = *reinterpret_cast<uint4*>(ge);
-    }
-  };
-
   f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  auto chunk = [&](int cb, auto with_hook) {
+  auto chunk = [&](int cb, const VLoads& R, auto with_hook) {
     const int cn = min(np - cb, chunk_pairs);
     const int pb = cb + ((cn * wave) >> 3), pe = cb + ((cn * (wave + 1)) >> 3);
     const int k0 = 128 * cb, kc = 128 * cn;
     const int rowh = kc + 8;
-    // this thread's first group of activations is loaded before the sign
-    // words, so waiting for it leaves the words in flight (loads complete in
-    // issue order)
-    uint4 xv0, gv0;
-    load_xg(k0 + 8 * min(my_sub, (kc >> 3) - 1), xv0, gv0);
-    // unconditional loads (clamped to a valid pair) keep the wait counts
-    // exact; pairs beyond pe are never used
-    uint32_t words[LB_MAXPV];
-    const int plast = max(pe - 1, 0);
-#pragma unroll
-    for (int i = 0; i < LB_MAXPV; ++i) words[i] = lb16_load_pair(tile_ptr, min(pb + i, plast), lane, nu);
     // l[j] (from an always-valid index; converted at use) needs fields that
     // arrive with the kernel arguments, so its load comes after the words
     if (cb == 0) lj_raw = (b ? L.l1 : L.l0)[min(j, r - 1)];
 
     __syncthreads();  // previous users of u_lds are done
-    if (my_tok < batch) {
-      uint4 xv = xv0, gv = gv0;
-      for (int k8 = my_sub; k8 < (kc >> 3); k8 += tpt) {
+    if (G.my_tok < batch) {
+      uint4 xv = R.xv0, gv = R.gv0;
+      for (int k8 = G.my_sub; k8 < (kc >> 3); k8 += G.tpt) {
         const int k = k0 + 8 * k8;
-        if (k8 != my_sub) load_xg(k, xv, gv);
-        if (fast && k >= n) xv = gv = make_uint4(0u, 0u, 0u, 0u);
+        if (k8 != G.my_sub) v_load_xg(G, k, xv, gv);
+        if (G.fast && k >= n) xv = gv = make_uint4(0u, 0u, 0u, 0u);
         const uint16_t* xe = reinterpret_cast<const uint16_t*>(&xv);
         const uint16_t* ge = reinterpret_cast<const uint16_t*>(&gv);
         uint16_t vals[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) vals[e] = f2h(h2f(ge[e]) * h2f(xe[e]));
-        *reinterpret_cast<uint4*>(u_lds + my_tok * rowh + 8 * k8) = *reinterpret_cast<uint4*>(vals);
+        *reinterpret_cast<uint4*>(u_lds + G.my_tok * rowh + 8 * k8) = *reinterpret_cast<uint4*>(vals);
       }
     }
     __syncthreads();
 
+    // the phase-B loads (hook) go out once this chunk's sign words are in, so
+    // they do not compete with them, and arrive while the matrix steps run
+    if constexpr (decltype(with_hook)::value) {
+      __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
+      hook();
+    }
     // inputs beyond n are zero in LDS, so the odd last unit's two missing
     // steps contribute nothing and every pair runs all 4 steps; the next
     // pair's operands are read from LDS while the current pair computes
@@ -301,7 +365,7 @@ __device__ __forceinline__ void v_tile(const LayerView& L, int batch, int b, int
         for (int st = 0; st < 4; ++st) bn[st] = *reinterpret_cast<const f16x8*>(ub + 32 * (4 * pn + st));
         // late(): the expansion is not hoisted above this point (it would hold
         // registers and wait for the load early)
-        const uint32_t reg = lb16_reg_word(late(words[i]), lb16_pair_sel(p, lane, nu));
+        const uint32_t reg = lb16_reg_word(late(R.words[i]), lb16_pair_sel(p, lane, nu));
         acc = mfma16(lb16_step_operand_val(reg, 0, sc.sign_mask, sc.one_pair), bv[0], acc);
         acc1 = mfma16(lb16_step_operand_val(reg, 1, sc.sign_mask, sc.one_pair), bv[1], acc1);
         acc = mfma16(lb16_step_operand_val(reg, 2, sc.sign_mask, sc.one_pair), bv[2], acc);
@@ -310,14 +374,22 @@ __device__ __forceinline__ void v_tile(const LayerView& L, int batch, int b, int
         for (int st = 0; st < 4; ++st) bv[st] = bn[st];
       }
     }
-    if constexpr (decltype(with_hook)::value) hook();
   };
   int cb0 = 0;
-  if constexpr (HOOK) {
-    chunk(0, BoolTag<true>());
+  if constexpr (EARLY) {
+    chunk(0, early, BoolTag<HOOK>());
+    cb0 = chunk_pairs;
+  } else if constexpr (HOOK) {
+    VLoads R;
+    v_issue(G, 0, chunk_pairs, R);
+    chunk(0, R, BoolTag<true>());
     cb0 = chunk_pairs;
   }
-  for (int cb = cb0; cb < np; cb += chunk_pairs) chunk(cb, BoolTag<false>());
+  for (int cb = cb0; cb < np; cb += chunk_pairs) {
+    VLoads R;
+    v_issue(G, cb, chunk_pairs, R);
+    chunk(cb, R, BoolTag<false>());
+  }
   acc += acc1;
 
 #pragma unroll
@@ -811,7 +883,7 @@ template <int MODE, bool SINGLE, bool UPRE>
 __global__ __launch_bounds__(LB_THREADS) void lb_decode_kernel(
     const uint8_t* pre_vb0, const uint8_t* pre_vb1, const uint16_t* pre_x, const uint16_t* pre_g0,
     const uint16_t* pre_g1, int pre_n, int pre_ldx, int pre_vsplit, uint32_t pre_misc,
-    LbDecodeArgs A, int chunk_pairs_arg, uint8_t* sync) {
+    LbDecodeArgs, int chunk_pairs_arg, uint8_t* sync) {
   extern __shared__ __align__(16) uint16_t u_lds[];
   __shared__ __align__(16) float red[LB_MAXT][LB_WAVES][256];  // cross-wave partial sums
   __shared__ __align__(16) uint32_t zstage[128];  // one tile's z (16 tokens x 16 rows of fp16)
@@ -820,6 +892,30 @@ __global__ __launch_bounds__(LB_THREADS) void lb_decode_kernel(
   static_assert(!UPRE || MODE == 2, "the sign-byte copy belongs to the single launch");
 
   const int wg = blockIdx.x;
+  // single launch of one layer: the first V tile's first loads need only the
+  // preloaded arguments, so they are issued before anything else
+  constexpr bool EARLY = SINGLE && MODE == 2;
+  VLoads early;
+  int vt0 = 0, vt1 = 0;
+  if (SINGLE) {
+    share((int)(pre_misc & 255u), (int)((pre_misc >> 8) & 255u), wg, vt0, vt1);
+    if (EARLY && vt0 < vt1) {
+      LayerView P;  // the fields v_geom reads
+      P.vb0 = pre_vb0;
+      P.vb1 = pre_vb1;
+      P.x = pre_x;
+      P.g0 = pre_g0;
+      P.g1 = pre_g1;
+      P.n = pre_n;
+      P.ldx = pre_ldx;
+      const int b = vt0 >= pre_vsplit ? 1 : 0;
+      v_issue(v_geom(P, (int)((pre_misc >> 16) & 31u), b, vt0 - (b ? pre_vsplit : 0)), 0, (int)(pre_misc >> 21),
+              early);
+    }
+  }
+  // the remaining arguments are read from here on (their loads, and register
+  // spills that wait for them, stay behind the loads above)
+  const LbDecodeArgs& A = kernarg_barrier();
   const int batch = SINGLE ? (int)((pre_misc >> 16) & 31u) : A.batch;
   const int chunk_pairs = SINGLE ? (int)(pre_misc >> 21) : chunk_pairs_arg;
   const LbSignConsts sc = lb16_sign_consts();
@@ -837,11 +933,8 @@ __global__ __launch_bounds__(LB_THREADS) void lb_decode_kernel(
     V0.ldx = pre_ldx;
   }
 
-  int ut0 = 0, ut1 = 0, vt0, vt1;
-  if (SINGLE)
-    share((int)(pre_misc & 255u), (int)((pre_misc >> 8) & 255u), wg, vt0, vt1);
-  else
-    share(A.vq, A.vr, wg, vt0, vt1);
+  int ut0 = 0, ut1 = 0;
+  if (!SINGLE) share(A.vq, A.vr, wg, vt0, vt1);
   if (MODE == 1) vt1 = vt0;
   // this workgroup's call counter (single launch only): the tag is its value
   // + 1.  Loaded with the phase-B prefetch, after the first V-tile loads.
@@ -882,20 +975,20 @@ __global__ __launch_bounds__(LB_THREADS) void lb_decode_kernel(
   if (vt0 < vt1) {
     int tile;
     const int k = v_slot<SINGLE>(M, pre_vsplit, vt0, tile);
-    v_tile<MODE == 2>(SINGLE ? V0 : layer_view(A.L[k >> 1]), batch, k & 1, tile, chunk_pairs, ctr, sc, u_lds,
-                      red[0], zstage, prefetch);
+    v_tile<MODE == 2, EARLY>(SINGLE ? V0 : layer_view(A.L[k >> 1]), batch, k & 1, tile, chunk_pairs, ctr, sc, u_lds,
+                             red[0], zstage, prefetch, early);
     __syncthreads();
   } else if (MODE == 2) {
     // no V tile here: let the V-tile workgroups' sign words go to memory
-    // first (about 1.3 us), then fetch this workgroup's phase-B data
-    for (int i = 0; i < 2; ++i) __builtin_amdgcn_s_sleep(24);
+    // first (about 2 us), then fetch this workgroup's phase-B data
+    for (int i = 0; i < 3; ++i) __builtin_amdgcn_s_sleep(24);
     prefetch();
   }
   for (int t = vt0 + 1; t < vt1; ++t) {
     int tile;
     const int k = v_slot<SINGLE>(M, pre_vsplit, t, tile);
-    v_tile<false>(SINGLE ? V0 : layer_view(A.L[k >> 1]), batch, k & 1, tile, chunk_pairs, ctr, sc, u_lds, red[0],
-                  zstage, prefetch);
+    v_tile<false, false>(SINGLE ? V0 : layer_view(A.L[k >> 1]), batch, k & 1, tile, chunk_pairs, ctr, sc, u_lds,
+                         red[0], zstage, prefetch, early);
     __syncthreads();
   }
   if (MODE == 1) share(A.uq, A.ur, wg, ut0, ut1);
