@@ -24,12 +24,13 @@
 // phase A, so their latency overlaps phase A.
 #include "lb_common.h"
 
+#include <vector>
+
 #define LB_WAVES 8                    // waves per workgroup (2 per SIMD)
 #define LB_THREADS (64 * LB_WAVES)
 #define LB_MAXPV 8                    // V-pass pairs per wave held in registers
 #define LB_MAXT 3                     // phase-B tiles whose sign words are prefetched
 #define LB_MAXPW 3                    // phase-B pairs per wave held in registers
-#define LB_MAX_GRID 256               // workgroups of the single launch (one counter each)
 #define LB_UPRE_BYTES (64 * 1024)     // LDS for a workgroup's phase-B sign bytes (single launch)
 #define LB_UPRE_OPS 8                 // 1 KB global-to-LDS loads per wave filling it
 #define LB_UPRE_HROWS 512             // row scales of the copied tiles (an LDS table)
@@ -934,7 +935,14 @@ __global__ __launch_bounds__(LB_THREADS) void lb_decode_kernel(
   }
 
   int ut0 = 0, ut1 = 0;
-  if (!SINGLE) share(A.vq, A.vr, wg, vt0, vt1);
+  if (!SINGLE) {
+    if (MODE == 2) {
+      vt0 = A.vt_begin[wg];
+      vt1 = A.vt_begin[wg + 1];
+    } else {
+      share(A.vq, A.vr, wg, vt0, vt1);
+    }
+  }
   if (MODE == 1) vt1 = vt0;
   // this workgroup's call counter (single launch only): the tag is its value
   // + 1.  Loaded with the phase-B prefetch, after the first V-tile loads.
@@ -951,7 +959,12 @@ __global__ __launch_bounds__(LB_THREADS) void lb_decode_kernel(
   // wait counts exact; tiles beyond ut1 are never used
   auto prefetch = [&]() {
     if (MODE == 2) ctr = ld32c(sync + LB_SYNC_CTR + 8 * wg);
-    share(A.uq, A.ur, wg, ut0, ut1);
+    if (SINGLE) {
+      share(A.uq, A.ur, wg, ut0, ut1);
+    } else {
+      ut0 = A.ut_begin[wg];
+      ut1 = A.ut_begin[wg + 1];
+    }
     const int nut = A.nut;
     if (UPRE) {
       upre_issue<SINGLE>(A, M, ut0, ut1, span_max, upre_lds, plan, hval);
@@ -1071,6 +1084,63 @@ size_t lb_decode_lds_bytes(const LbDecodeArgs& a, int chunk_pairs) {
   return (pa > pb ? pa : pb) * sizeof(uint16_t);
 }
 
+// Splits costs c[0..n) into G contiguous ranges, begin[0..G], whose largest
+// total is the smallest possible: a binary search on that total, each trial
+// filling ranges greedily; ranges past the last tile are empty.
+static void balanced_split(const int64_t* c, int n, int G, int* begin) {
+  int64_t lo = 0, hi = 0;
+  for (int i = 0; i < n; ++i) {
+    lo = c[i] > lo ? c[i] : lo;
+    hi += c[i];
+  }
+  auto parts = [&](int64_t cap) {
+    int k = n > 0 ? 1 : 0;
+    int64_t sum = 0;
+    for (int i = 0; i < n; ++i) {
+      if (sum > 0 && sum + c[i] > cap) {
+        ++k;
+        sum = 0;
+      }
+      sum += c[i];
+    }
+    return k;
+  };
+  while (lo < hi) {
+    const int64_t mid = lo + (hi - lo) / 2;
+    if (parts(mid) <= G) hi = mid; else lo = mid + 1;
+  }
+  int w = 0;
+  int64_t sum = 0;
+  begin[0] = 0;
+  for (int i = 0; i < n; ++i) {
+    if (sum > 0 && sum + c[i] > lo) {
+      begin[++w] = i;
+      sum = 0;
+    }
+    sum += c[i];
+  }
+  while (w < G) begin[++w] = n;
+}
+
+// Cost-balanced tile ranges of a multi-layer single launch.  A V tile costs
+// its reduction length plus a fixed share (u staging, cross-wave sums, z
+// store, about a 4096-input pass); a U tile its two branches' ranks plus a
+// smaller fixed share.
+static void cost_split(LbDecodeArgs& a, int G) {
+  std::vector<int64_t> c;
+  c.reserve(a.nvt > a.nut ? a.nvt : a.nut);
+  for (int li = 0; li < a.nlayers; ++li)
+    for (int b = 0; b < a.L[li].nb; ++b)
+      for (int t = 0; t < (a.L[li].br[b].r + 15) / 16; ++t) c.push_back(a.L[li].n + 4096);
+  balanced_split(c.data(), (int)c.size(), G, a.vt_begin);
+  c.clear();
+  for (int li = 0; li < a.nlayers; ++li) {
+    const int64_t k = a.L[li].br[0].r + (a.L[li].nb == 2 ? a.L[li].br[1].r : 0) + 512;
+    for (int t = 0; t < (a.L[li].m + 15) / 16; ++t) c.push_back(k);
+  }
+  balanced_split(c.data(), (int)c.size(), G, a.ut_begin);
+}
+
 template <bool SINGLE>
 static hipError_t launch_decode_t(const LbDecodeArgs& args, int chunk_pairs, void* sync, int allow_fused,
                                   hipStream_t stream) {
@@ -1118,6 +1188,7 @@ static hipError_t launch_decode_t(const LbDecodeArgs& args, int chunk_pairs, voi
       LbDecodeArgs a = args;
       a.vq = a.nvt / G; a.vr = a.nvt % G;
       a.uq = a.nut / G; a.ur = a.nut % G;
+      if (!SINGLE) cost_split(a, G);
       // the variant that copies phase B's sign bytes to LDS during phase A,
       // when the dynamic LDS leaves room for the copy and a workgroup's U
       // tiles are more than the register prefetch holds (one group of

@@ -11,6 +11,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 #define LB_MAX_LAYERS 7
+#define LB_MAX_GRID 256  // workgroups of the single-launch decode kernel
 #define LB_DECODE_LDS_MAX (120 * 1024)  // dynamic LDS limit of a decode launch (bytes)
 
 // ---------------------------------------------------------------- LB16 layout
@@ -119,6 +120,12 @@ struct LbDecodeArgs {
   int uq, ur;                       // U tiles likewise
   int pad_[3];
   LbLayerArgs L[LB_MAX_LAYERS];
+  // single launch of several layers: workgroup w takes V tiles
+  // [vt_begin[w], vt_begin[w + 1]) and U tiles [ut_begin[w], ut_begin[w + 1]),
+  // contiguous ranges balanced by their cost (one layer splits evenly with
+  // vq/vr and uq/ur instead)
+  int vt_begin[LB_MAX_GRID + 1];
+  int ut_begin[LB_MAX_GRID + 1];
 };
 
 // Kernel arguments of the prefill (matrix-core GEMM) kernels for one layer
