@@ -299,12 +299,15 @@ __device__ __forceinline__ void v_issue(const VGeom& G, int cb, int chunk_pairs,
 // V pass over one 16-row tile of branch b of layer L (all its pairs, in
 // chunks of chunk_pairs whose u = g*x is staged in u_lds), then z = l*t of
 // the tile's rows stored as tagged words.  HOOK: hook() runs once the first
-// chunk's loads have landed, before its matrix steps.  EARLY: the first chunk's loads were
-// issued by the caller (`early`, from v_issue with the same geometry).
+// chunk's loads have landed, before its matrix steps.  EARLY: the first
+// chunk's loads were issued by the caller (`early`, from v_issue with the
+// same geometry).  reuse_u: u_lds already holds this tile's u (the previous
+// tile had the same layer and branch, and one chunk covers the reduction).
 template <bool HOOK, bool EARLY, class Hook>
 __device__ __forceinline__ void v_tile(const LayerView& L, int batch, int b, int tile, int chunk_pairs,
                                        const uint32_t& ctr, const LbSignConsts& sc, uint16_t* u_lds,
-                                       float (*red)[256], uint32_t* zstage, Hook&& hook, const VLoads& early) {
+                                       float (*red)[256], uint32_t* zstage, Hook&& hook, const VLoads& early,
+                                       bool reuse_u = false) {
   const VGeom G = v_geom(L, batch, b, tile);
   const int n = G.n, nu = G.nu, np = G.np;
   const int r = b ? L.r1 : L.r0;
@@ -326,22 +329,24 @@ __device__ __forceinline__ void v_tile(const LayerView& L, int batch, int b, int
     // arrive with the kernel arguments, so its load comes after the words
     if (cb == 0) lj_raw = (b ? L.l1 : L.l0)[min(j, r - 1)];
 
-    __syncthreads();  // previous users of u_lds are done
-    if (G.my_tok < batch) {
-      uint4 xv = R.xv0, gv = R.gv0;
-      for (int k8 = G.my_sub; k8 < (kc >> 3); k8 += G.tpt) {
-        const int k = k0 + 8 * k8;
-        if (k8 != G.my_sub) v_load_xg(G, k, xv, gv);
-        if (G.fast && k >= n) xv = gv = make_uint4(0u, 0u, 0u, 0u);
-        const uint16_t* xe = reinterpret_cast<const uint16_t*>(&xv);
-        const uint16_t* ge = reinterpret_cast<const uint16_t*>(&gv);
-        uint16_t vals[8];
+    if (!reuse_u) {
+      __syncthreads();  // previous users of u_lds are done
+      if (G.my_tok < batch) {
+        uint4 xv = R.xv0, gv = R.gv0;
+        for (int k8 = G.my_sub; k8 < (kc >> 3); k8 += G.tpt) {
+          const int k = k0 + 8 * k8;
+          if (k8 != G.my_sub) v_load_xg(G, k, xv, gv);
+          if (G.fast && k >= n) xv = gv = make_uint4(0u, 0u, 0u, 0u);
+          const uint16_t* xe = reinterpret_cast<const uint16_t*>(&xv);
+          const uint16_t* ge = reinterpret_cast<const uint16_t*>(&gv);
+          uint16_t vals[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) vals[e] = f2h(h2f(ge[e]) * h2f(xe[e]));
-        *reinterpret_cast<uint4*>(u_lds + G.my_tok * rowh + 8 * k8) = *reinterpret_cast<uint4*>(vals);
+          for (int e = 0; e < 8; ++e) vals[e] = f2h(h2f(ge[e]) * h2f(xe[e]));
+          *reinterpret_cast<uint4*>(u_lds + G.my_tok * rowh + 8 * k8) = *reinterpret_cast<uint4*>(vals);
+        }
       }
+      __syncthreads();
     }
-    __syncthreads();
 
     // the phase-B loads (hook) go out once this chunk's sign words are in, so
     // they do not compete with them, and arrive while the matrix steps run
@@ -945,8 +950,12 @@ __global__ __launch_bounds__(LB_THREADS) void lb_decode_kernel(
   }
   if (MODE == 1) vt1 = vt0;
   // this workgroup's call counter (single launch only): the tag is its value
-  // + 1.  Loaded with the phase-B prefetch, after the first V-tile loads.
+  // + 1.  Loaded (load_ctr) once the first V tile's sign words have landed,
+  // before that tile's z store, so waiting for the words never waits for it.
   uint32_t ctr = 0;
+  auto load_ctr = [&]() {
+    if (MODE == 2) ctr = ld32c(sync + LB_SYNC_CTR + 8 * wg);
+  };
   UTilePre pre[LB_MAXT];
   HPre hpre;
   UPrePlan plan;
@@ -958,7 +967,6 @@ __global__ __launch_bounds__(LB_THREADS) void lb_decode_kernel(
   // every load is issued (tiles clamped to a valid one), which keeps the
   // wait counts exact; tiles beyond ut1 are never used
   auto prefetch = [&]() {
-    if (MODE == 2) ctr = ld32c(sync + LB_SYNC_CTR + 8 * wg);
     if (SINGLE) {
       share(A.uq, A.ur, wg, ut0, ut1);
     } else {
@@ -983,26 +991,60 @@ __global__ __launch_bounds__(LB_THREADS) void lb_decode_kernel(
       load_h(SINGLE ? V0 : layer_view(A.L[li]), tile, hpre, j);
     }
   };
-  // phase-B loads are issued during phase A: after the first V tile's sign
-  // words and activations, or at once by a workgroup without V tiles
-  if (vt0 < vt1) {
+  // V tiles, then phase B.  Phase-B loads (prefetch) are issued during phase
+  // A, after the sign words they would otherwise delay (loads complete in
+  // issue order), or after a pause by a workgroup without V tiles (letting
+  // the V-tile workgroups' sign words go to memory first).
+  if (vt0 < vt1 && SINGLE) {
+    // one layer: the first tile's loads came from the early issue (single
+    // launch) or are issued in v_tile; phase-B loads follow its sign words
     int tile;
     const int k = v_slot<SINGLE>(M, pre_vsplit, vt0, tile);
-    v_tile<MODE == 2, EARLY>(SINGLE ? V0 : layer_view(A.L[k >> 1]), batch, k & 1, tile, chunk_pairs, ctr, sc, u_lds,
-                             red[0], zstage, prefetch, early);
+    auto first_hook = [&]() {
+      load_ctr();
+      prefetch();
+    };
+    v_tile<MODE == 2, EARLY>(V0, batch, k & 1, tile, chunk_pairs, ctr, sc, u_lds, red[0], zstage, first_hook, early);
     __syncthreads();
-  } else if (MODE == 2) {
-    // no V tile here: let the V-tile workgroups' sign words go to memory
-    // first (about 2 us), then fetch this workgroup's phase-B data
-    for (int i = 0; i < 3; ++i) __builtin_amdgcn_s_sleep(24);
-    prefetch();
-  }
-  for (int t = vt0 + 1; t < vt1; ++t) {
+    for (int t = vt0 + 1; t < vt1; ++t) {
+      const int kt = v_slot<SINGLE>(M, pre_vsplit, t, tile);
+      v_tile<false, false>(V0, batch, kt & 1, tile, chunk_pairs, ctr, sc, u_lds, red[0], zstage, prefetch, early);
+      __syncthreads();
+    }
+  } else if (vt0 < vt1) {
+    // several layers: a tile's first loads are issued during the previous
+    // tile, once that tile's own sign words have landed; the phase-B loads
+    // go out with the last tile's (or, for one tile, after its words).  A
+    // tile of the same layer and branch as the previous one reuses u from
+    // LDS when one chunk covers the reduction.
     int tile;
-    const int k = v_slot<SINGLE>(M, pre_vsplit, t, tile);
-    v_tile<false, false>(SINGLE ? V0 : layer_view(A.L[k >> 1]), batch, k & 1, tile, chunk_pairs, ctr, sc, u_lds,
-                         red[0], zstage, prefetch, early);
-    __syncthreads();
+    int k = v_slot<SINGLE>(M, pre_vsplit, vt0, tile);
+    VLoads cur;
+    v_issue(v_geom(layer_view(A.L[k >> 1]), batch, k & 1, tile), 0, chunk_pairs, cur);
+    const int t_pre = max(vt0, vt1 - 2);
+    int prev_k = -1;
+    for (int t = vt0; t < vt1; ++t) {
+      int ntile = 0;
+      const int nk = t + 1 < vt1 ? v_slot<SINGLE>(M, pre_vsplit, t + 1, ntile) : -1;
+      VLoads nxt;
+      auto hook = [&]() {
+        if (nk >= 0) v_issue(v_geom(layer_view(A.L[nk >> 1]), batch, nk & 1, ntile), 0, chunk_pairs, nxt);
+        if (t == vt0) load_ctr();
+        if (MODE == 2 && t == t_pre) prefetch();
+      };
+      const LayerView L = layer_view(A.L[k >> 1]);
+      const bool reuse_u = k == prev_k && ((lb16_units(L.n) + 1) >> 1) <= chunk_pairs;
+      v_tile<true, true>(L, batch, k & 1, tile, chunk_pairs, ctr, sc, u_lds, red[0], zstage, hook, cur, reuse_u);
+      __syncthreads();
+      prev_k = k;
+      k = nk;
+      tile = ntile;
+      cur = nxt;
+    }
+  } else if (MODE == 2) {
+    for (int i = 0; i < 3; ++i) __builtin_amdgcn_s_sleep(24);
+    load_ctr();
+    prefetch();
   }
   if (MODE == 1) share(A.uq, A.ur, wg, ut0, ut1);
   if (MODE != 0) {

@@ -172,6 +172,33 @@ def test_determinism_and_poisoned_buffers(lb):
     assert counters[:grid] == [6] * grid and not any(counters[grid:]), counters
 
 
+@pytest.mark.parametrize("setting", ["0.55", "0.1"])
+def test_block_repeated_calls_one_workspace(lb, setting):
+    """Consecutive block calls on one workspace: each equals the first bit for
+    bit, no z poll gave up, and every workgroup's call counter advanced once
+    per call (a tag taken before the counter is read would fail from the
+    second call on)."""
+    print(f"[case] 13b block {setting} repeated calls", flush=True)
+    shapes, layers, xs = synth.make_block13b(setting, batch=1, seed=3)
+    dev_layers = [_layer(lb, br) for br in layers]
+    xt = [torch.from_numpy(a).cuda() for a in xs]
+    ws = torch.zeros((lb.littlebit_block_workspace_bytes(dev_layers, 1),), dtype=torch.uint8, device="cuda")
+    first = [y.clone() for y in lb.littlebit_block_fwd(dev_layers, *xt, workspace=ws)]
+    for _ in range(3):
+        ys = lb.littlebit_block_fwd(dev_layers, *xt, workspace=ws)
+        for a, b in zip(first, ys):
+            assert torch.equal(a, b)
+    torch.cuda.synchronize()
+    hdr = ws[:4096].cpu()
+    assert int(hdr[2048:2052].view(torch.int32)) == 0, "z poll spin limit hit"
+    counters = hdr[:2048].view(torch.int64).tolist()
+    grid = min(torch.cuda.get_device_properties(0).multi_processor_count, 256)
+    assert counters[:grid] == [4] * grid and not any(counters[grid:]), counters
+    for i in (0, 6):
+        xi = synth.block_inputs_for(i, xs)
+        _assert_parity(first[i], oracle.factored_forward(xi, layers[i]), f"13B {setting} {shapes[i].name} repeated")
+
+
 def test_strided_rows(lb):
     print("[case] strided x/y", flush=True)
     br, x = synth.make_layer(synth.LayerShape("strided", 256, 320, (32, 32)), batch=4, seed=6)
