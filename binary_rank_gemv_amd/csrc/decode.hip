@@ -35,8 +35,8 @@
 #define LB_UPRE_OPS 8                 // 1 KB global-to-LDS loads per wave filling it
 #define LB_UPRE_HROWS 512             // row scales of the copied tiles (an LDS table)
 // dynamic LDS a launch of that variant may take: what the static arrays
-// (partial sums 24 KB, z tile 512 B, the copy, the row-scale table) leave of 160 KB
-#define LB_UPRE_DYN_MAX (160 * 1024 - LB_MAXT * LB_WAVES * 256 * 4 - 512 - LB_UPRE_BYTES - 2 * LB_UPRE_HROWS)
+// (partial sums 24 KB, two z tiles 1 KB, the copy, the row-scale table) leave of 160 KB
+#define LB_UPRE_DYN_MAX (160 * 1024 - LB_MAXT * LB_WAVES * 256 * 4 - 1024 - LB_UPRE_BYTES - 2 * LB_UPRE_HROWS)
 #define LB_SPIN_LIMIT (1 << 20)
 
 // workspace header (bytes): one 64-bit call counter per workgroup of the
@@ -133,42 +133,36 @@ __device__ __forceinline__ LayerView layer_view(const LbLayerArgs& L) {
   return v;
 }
 
-// Mapping of global tile indices to layers, kept in registers.
+// Mapping of global tile indices to layers: the cumulative tile counts are
+// read from the argument block where needed (scalar loads, wave-uniform
+// indices), not copied into a per-thread array the compiler could only
+// index through scratch memory.
 struct TileMap {
-  int nl;
-  int ue[LB_MAX_LAYERS];      // cumulative U-tile ends
-  int ve[2 * LB_MAX_LAYERS];  // cumulative V-tile ends per (layer, branch)
+  const LbDecodeArgs* A;
 };
 
-__device__ __forceinline__ void load_map(const LbDecodeArgs& A, TileMap& M) {
-  M.nl = A.nlayers;
-#pragma unroll
-  for (int i = 0; i < LB_MAX_LAYERS; ++i) M.ue[i] = A.ut_end[i];
-#pragma unroll
-  for (int i = 0; i < 2 * LB_MAX_LAYERS; ++i) M.ve[i] = A.vt_end[i];
-}
+__device__ __forceinline__ void load_map(const LbDecodeArgs& A, TileMap& M) { M.A = &A; }
 
 // Layer of global U tile t (tile index inside the layer in `tile`).
 template <bool SINGLE>
 __device__ __forceinline__ int u_layer(const TileMap& M, int t, int& tile) {
-  int li = 0, beg = 0;
-  if (!SINGLE) {
-#pragma unroll
-    for (int i = 0; i < LB_MAX_LAYERS - 1; ++i)
-      if (i < M.nl - 1 && t >= M.ue[i]) { li = i + 1; beg = M.ue[i]; }
+  if (SINGLE) {
+    tile = t;
+    return 0;
   }
-  tile = t - beg;
+  const LbDecodeArgs& A = *M.A;
+  int li = 0;
+#pragma unroll
+  for (int i = 0; i < LB_MAX_LAYERS - 1; ++i)
+    if (i < A.nlayers - 1 && t >= A.ut_end[i]) li = i + 1;
+  li = __builtin_amdgcn_readfirstlane(li);
+  tile = t - (li > 0 ? A.ut_end[li - 1] : 0);
   return li;
 }
 
-// End (exclusive) of layer li's global U tiles, without indexing the
-// register array by a run-time value.
+// End (exclusive) of layer li's global U tiles.
 __device__ __forceinline__ int layer_u_end(const TileMap& M, int li) {
-  int e = M.ue[0];
-#pragma unroll
-  for (int i = 1; i < LB_MAX_LAYERS; ++i)
-    if (li == i) e = M.ue[i];
-  return e;
+  return M.A->ut_end[__builtin_amdgcn_readfirstlane(li)];
 }
 
 // Slot 2*layer + branch of global V tile t (one layer: `vsplit` = tiles of
@@ -180,11 +174,13 @@ __device__ __forceinline__ int v_slot(const TileMap& M, int vsplit, int t, int& 
     tile = t - (k ? vsplit : 0);
     return k;
   }
-  int k = 0, beg = 0;
+  const LbDecodeArgs& A = *M.A;
+  int k = 0;
 #pragma unroll
   for (int q = 0; q < 2 * LB_MAX_LAYERS - 1; ++q)
-    if (q < 2 * M.nl - 1 && t >= M.ve[q]) { k = q + 1; beg = M.ve[q]; }
-  tile = t - beg;
+    if (q < 2 * A.nlayers - 1 && t >= A.vt_end[q]) k = q + 1;
+  k = __builtin_amdgcn_readfirstlane(k);
+  tile = t - (k > 0 ? A.vt_end[k - 1] : 0);
   return k;
 }
 
@@ -296,6 +292,32 @@ __device__ __forceinline__ void v_issue(const VGeom& G, int cb, int chunk_pairs,
   for (int i = 0; i < LB_MAXPV; ++i) R.words[i] = lb16_load_pair(G.tile_ptr, min(pb + i, plast), lane, G.nu);
 }
 
+// Stores one V tile's z (zstage: [token][16 rows] fp16, in LDS) as tagged
+// words [tag | z(2q) | z(2q+1)], 8 words per token for the 16 rows; the
+// branch's last tile also writes the zero words between 16*ceil(r/16) and
+// 64*ceil(r/64).
+__device__ __forceinline__ void v_store_z(const LayerView& L, int batch, int b, int tile, uint32_t tag,
+                                          const uint32_t* zstage) {
+  const int tid = threadIdx.x;
+  const int r = b ? L.r1 : L.r0;
+  uint64_t* __restrict__ zw = L.z;
+  const int zrow = L.zs >> 1, zoff = (b ? L.zoff1 : L.zoff0) >> 1;
+  if (tid < 8 * batch) {
+    const int q = tid & 7, tt = tid >> 3;
+    const uint32_t v = zstage[tt * 8 + q];
+    st64c(zw + (long)tt * zrow + zoff + 8 * tile + q, (uint64_t)tag | ((uint64_t)v << 32));
+  }
+  const int ntv = (r + 15) >> 4;
+  if (tile == ntv - 1) {
+    const int w0 = 8 * ntv, w1 = 32 * lb16_units(r);
+    const int nw = w1 - w0;
+    for (int i = tid; i < nw * batch; i += LB_THREADS) {
+      const int tt = i / nw, ww = w0 + i % nw;
+      st64c(zw + (long)tt * zrow + zoff + ww, (uint64_t)tag);
+    }
+  }
+}
+
 // V pass over one 16-row tile of branch b of layer L (all its pairs, in
 // chunks of chunk_pairs whose u = g*x is staged in u_lds), then z = l*t of
 // the tile's rows stored as tagged words.  HOOK: hook() runs once the first
@@ -303,7 +325,8 @@ __device__ __forceinline__ void v_issue(const VGeom& G, int cb, int chunk_pairs,
 // chunk's loads were issued by the caller (`early`, from v_issue with the
 // same geometry).  reuse_u: u_lds already holds this tile's u (the previous
 // tile had the same layer and branch, and one chunk covers the reduction).
-template <bool HOOK, bool EARLY, class Hook>
+// DEFER: z is left in zstage for the caller to store (v_store_z).
+template <bool HOOK, bool EARLY, bool DEFER = false, class Hook>
 __device__ __forceinline__ void v_tile(const LayerView& L, int batch, int b, int tile, int chunk_pairs,
                                        const uint32_t& ctr, const LbSignConsts& sc, uint16_t* u_lds,
                                        float (*red)[256], uint32_t* zstage, Hook&& hook, const VLoads& early,
@@ -317,7 +340,7 @@ __device__ __forceinline__ void v_tile(const LayerView& L, int batch, int b, int
   const int trow = min(tok, batch - 1);      // operand row read by this lane
   const int rho = tid & 15, tk = (tid >> 4) & 15;  // epilogue role (threads < 256)
   const int j = 16 * tile + rho;
-  uint32_t lj_raw = 0;  // fp16 bits of l[j], loaded after the first sign words
+  uint32_t lj_raw = 0;  // fp16 bits of l[j]
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   auto chunk = [&](int cb, const VLoads& R, auto with_hook) {
@@ -325,10 +348,6 @@ __device__ __forceinline__ void v_tile(const LayerView& L, int batch, int b, int
     const int pb = cb + ((cn * wave) >> 3), pe = cb + ((cn * (wave + 1)) >> 3);
     const int k0 = 128 * cb, kc = 128 * cn;
     const int rowh = kc + 8;
-    // l[j] (from an always-valid index; converted at use) needs fields that
-    // arrive with the kernel arguments, so its load comes after the words
-    if (cb == 0) lj_raw = (b ? L.l1 : L.l0)[min(j, r - 1)];
-
     if (!reuse_u) {
       __syncthreads();  // previous users of u_lds are done
       if (G.my_tok < batch) {
@@ -354,6 +373,9 @@ __device__ __forceinline__ void v_tile(const LayerView& L, int batch, int b, int
       __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
       hook();
     }
+    // l[j] (from an always-valid index; converted at use in the epilogue) is
+    // loaded after the hook's wait, which would otherwise wait for it too
+    if (cb == 0) lj_raw = (b ? L.l1 : L.l0)[min(j, r - 1)];
     // inputs beyond n are zero in LDS, so the odd last unit's two missing
     // steps contribute nothing and every pair runs all 4 steps; the next
     // pair's operands are read from LDS while the current pair computes
@@ -411,25 +433,7 @@ __device__ __forceinline__ void v_tile(const LayerView& L, int batch, int b, int
     reinterpret_cast<uint16_t*>(zstage)[tk * 16 + rho] = __builtin_bit_cast(uint16_t, zv);
   }
   __syncthreads();
-  // tagged words: [tag | z(2q) | z(2q+1)], 8 words per token for the 16 rows
-  uint64_t* __restrict__ zw = L.z;
-  const int zrow = L.zs >> 1, zoff = (b ? L.zoff1 : L.zoff0) >> 1;
-  const uint32_t tag = late(ctr) + 1u;
-  if (tid < 8 * batch) {
-    const int q = tid & 7, tt = tid >> 3;
-    const uint32_t v = zstage[tt * 8 + q];
-    st64c(zw + (long)tt * zrow + zoff + 8 * tile + q, (uint64_t)tag | ((uint64_t)v << 32));
-  }
-  // the last tile also writes the zero words between 16*ceil(r/16) and 64*ceil(r/64)
-  const int ntv = (r + 15) >> 4;
-  if (tile == ntv - 1) {
-    const int w0 = 8 * ntv, w1 = 32 * lb16_units(r);
-    const int nw = w1 - w0;
-    for (int i = tid; i < nw * batch; i += LB_THREADS) {
-      const int tt = i / nw, ww = w0 + i % nw;
-      st64c(zw + (long)tt * zrow + zoff + ww, (uint64_t)tag);
-    }
-  }
+  if constexpr (!DEFER) v_store_z(L, batch, b, tile, late(ctr) + 1u, zstage);
 }
 
 // ------------------------------------------------------------------ phase B
@@ -616,7 +620,7 @@ __device__ __forceinline__ void upre_issue(const LbDecodeArgs& A, const TileMap&
   int tile0;
   const int li0 = u_layer<SINGLE>(M, min(ut0, A.nut - 1), tile0);
   const int end0 = SINGLE ? ut1 : min(ut1, layer_u_end(M, li0));
-  const int li1 = SINGLE ? li0 : min(li0 + 1, M.nl - 1);
+  const int li1 = SINGLE ? li0 : min(li0 + 1, A.nlayers - 1);
   const int end1 = SINGLE ? ut1 : min(ut1, layer_u_end(M, li1));
   const LayerView L0 = layer_view(A.L[li0]);
   const LayerView L1 = layer_view(A.L[li1]);
@@ -892,7 +896,10 @@ __global__ __launch_bounds__(LB_THREADS) void lb_decode_kernel(
     LbDecodeArgs, int chunk_pairs_arg, uint8_t* sync) {
   extern __shared__ __align__(16) uint16_t u_lds[];
   __shared__ __align__(16) float red[LB_MAXT][LB_WAVES][256];  // cross-wave partial sums
-  __shared__ __align__(16) uint32_t zstage[128];  // one tile's z (16 tokens x 16 rows of fp16)
+  // z of a V tile (16 tokens x 16 rows of fp16); two, so a multi-layer
+  // launch stores a tile's z during the next tile
+  __shared__ __align__(16) uint32_t zst[2][128];
+  uint32_t* zstage = zst[0];
   __shared__ __align__(16) uint8_t upre_lds[UPRE ? LB_UPRE_BYTES : 16];  // phase-B sign bytes
   __shared__ uint16_t hl_lds[UPRE ? LB_UPRE_HROWS : 1];                  // and row scales
   static_assert(!UPRE || MODE == 2, "the sign-byte copy belongs to the single launch");
@@ -1013,16 +1020,17 @@ __global__ __launch_bounds__(LB_THREADS) void lb_decode_kernel(
     }
   } else if (vt0 < vt1) {
     // several layers: a tile's first loads are issued during the previous
-    // tile, once that tile's own sign words have landed; the phase-B loads
-    // go out with the last tile's (or, for one tile, after its words).  A
-    // tile of the same layer and branch as the previous one reuses u from
-    // LDS when one chunk covers the reduction.
+    // tile, once that tile's own sign words have landed, and the previous
+    // tile's z is stored then (so no wait for a tile's words also waits for
+    // the stores before them).  The phase-B loads go out with the last
+    // tile's hook, after every V word.  A tile of the same layer and branch
+    // as the previous one reuses u from LDS when one chunk covers the
+    // reduction.
     int tile;
     int k = v_slot<SINGLE>(M, pre_vsplit, vt0, tile);
     VLoads cur;
     v_issue(v_geom(layer_view(A.L[k >> 1]), batch, k & 1, tile), 0, chunk_pairs, cur);
-    const int t_pre = max(vt0, vt1 - 2);
-    int prev_k = -1;
+    int prev_k = -1, prev_tile = 0;
     for (int t = vt0; t < vt1; ++t) {
       int ntile = 0;
       const int nk = t + 1 < vt1 ? v_slot<SINGLE>(M, pre_vsplit, t + 1, ntile) : -1;
@@ -1030,17 +1038,22 @@ __global__ __launch_bounds__(LB_THREADS) void lb_decode_kernel(
       auto hook = [&]() {
         if (nk >= 0) v_issue(v_geom(layer_view(A.L[nk >> 1]), batch, nk & 1, ntile), 0, chunk_pairs, nxt);
         if (t == vt0) load_ctr();
-        if (MODE == 2 && t == t_pre) prefetch();
+        if (prev_k >= 0)
+          v_store_z(layer_view(A.L[prev_k >> 1]), batch, prev_k & 1, prev_tile, late(ctr) + 1u, zst[(t - vt0 + 1) & 1]);
+        if (MODE == 2 && t == vt1 - 1) prefetch();
       };
       const LayerView L = layer_view(A.L[k >> 1]);
       const bool reuse_u = k == prev_k && ((lb16_units(L.n) + 1) >> 1) <= chunk_pairs;
-      v_tile<true, true>(L, batch, k & 1, tile, chunk_pairs, ctr, sc, u_lds, red[0], zstage, hook, cur, reuse_u);
+      v_tile<true, true, true>(L, batch, k & 1, tile, chunk_pairs, ctr, sc, u_lds, red[0], zst[(t - vt0) & 1], hook,
+                               cur, reuse_u);
       __syncthreads();
       prev_k = k;
+      prev_tile = tile;
       k = nk;
       tile = ntile;
       cur = nxt;
     }
+    v_store_z(layer_view(A.L[prev_k >> 1]), batch, prev_k & 1, prev_tile, late(ctr) + 1u, zst[(vt1 - 1 - vt0) & 1]);
   } else if (MODE == 2) {
     for (int i = 0; i < 3; ++i) __builtin_amdgcn_s_sleep(24);
     load_ctr();
