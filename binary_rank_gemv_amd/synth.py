@@ -115,6 +115,22 @@ def make_block13b(setting: str, batch: int, seed: int = 0):
     return shapes, layers, (x_qkv, x_o, x_gu, x_down)
 
 
+def make_dense_weight(m: int, n: int, seed: int = 0, decay: float = 0.75, noise: float = 0.05) -> np.ndarray:
+    """A synthetic dense weight (m x n float32) with a decaying spectrum, the
+    input of the initialization: Gaussian factors A (m x k) and B (n x k),
+    k = min(m, n), with column i of A weighted by (i + 1)^-decay, times
+    1/sqrt(k), plus independent Gaussian noise of standard deviation
+    ``noise``.  Drawn from one ``default_rng(seed)`` stream: A, B, noise."""
+    rng = np.random.default_rng(seed)
+    k = min(m, n)
+    A = rng.standard_normal((m, k), dtype=np.float32)
+    B = rng.standard_normal((n, k), dtype=np.float32)
+    w = (np.arange(1, k + 1, dtype=np.float32) ** np.float32(-decay)) / np.float32(np.sqrt(k))
+    W = (A * w) @ B.T
+    W += np.float32(noise) * rng.standard_normal((m, n), dtype=np.float32)
+    return W
+
+
 def block_inputs_for(index: int, xs: Sequence[np.ndarray]) -> np.ndarray:
     """Which of the four block inputs feeds projection ``index`` (0..6)."""
     x_qkv, x_o, x_gu, x_down = xs

@@ -31,6 +31,13 @@ from .littlebit_oracle import (  # noqa: F401
     rank_for_bpw,
     model_footprint_bytes,
 )
+from .dual_svid import (  # noqa: F401
+    truncated_svd_factors,
+    svid,
+    dual_svid_branch,
+    dual_svid_init,
+    reconstruction_error,
+)
 from .packing import (  # noqa: F401
     pack_factor,
     unpack_factor,

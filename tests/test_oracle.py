@@ -306,3 +306,74 @@ def test_pins_catch_planted_oracle_mistakes(mistake, monkeypatch):
         monkeypatch.setattr(lo, "branch_weight", bad_bw)
     y = lo.linear_forward(x, br)
     assert not np.array_equal(y, want), mistake
+
+
+# ------------------------------------------------------ Dual-SVID initialization
+
+def _orthonormal(rng, rows, cols):
+    q, _ = np.linalg.qr(rng.standard_normal((rows, cols)))
+    return q
+
+
+def test_truncated_svd_factors_meet_the_eckart_young_closed_form():
+    """A weight built as P diag(s) Q^T with known orthonormal P, Q and
+    decreasing s: U'V'^T equals P_r diag(s_r) Q_r^T and the squared error
+    is the sum of the discarded s_i^2."""
+    rng = np.random.default_rng(11)
+    m, n, k, r = 40, 30, 30, 7
+    P, Q = _orthonormal(rng, m, k), _orthonormal(rng, n, k)
+    s = np.sort(rng.uniform(0.5, 4.0, k))[::-1] + np.arange(k)[::-1] * 0.1
+    W = (P * s) @ Q.T
+    U, V = oracle.truncated_svd_factors(W, r)
+    np.testing.assert_allclose(U @ V.T, (P[:, :r] * s[:r]) @ Q[:, :r].T, atol=1e-10)
+    assert abs(np.linalg.norm(W - U @ V.T) ** 2 - np.sum(s[r:] ** 2)) < 1e-9
+    # singular values split evenly: column norms of U' and V' are both sqrt(s)
+    np.testing.assert_allclose(np.linalg.norm(U, axis=0), np.sqrt(s[:r]), rtol=1e-10)
+    np.testing.assert_allclose(np.linalg.norm(V, axis=0), np.sqrt(s[:r]), rtol=1e-10)
+    for j in range(r):  # orientation rule
+        assert V[np.argmax(np.abs(V[:, j])), j] > 0
+
+
+def test_svid_recovers_a_sign_times_rank1_magnitude_matrix():
+    rng = np.random.default_rng(12)
+    p, q = rng.uniform(0.2, 3.0, 25), rng.uniform(0.2, 3.0, 9)
+    S = np.where(rng.random((25, 9)) < 0.5, -1.0, 1.0)
+    signs, a, b = oracle.svid(S * np.outer(p, q))
+    np.testing.assert_array_equal(signs, S)
+    assert (a > 0).all() and (b > 0).all()
+    np.testing.assert_allclose(np.outer(a, b), np.outer(p, q), rtol=1e-12)
+
+
+def test_dual_svid_rank1_sign_magnitude_weight_is_exact():
+    """W = (h * s)(g * t)^T with sign vectors s, t: one branch of rank 1
+    reproduces W exactly before the fp16 rounding of its scales."""
+    rng = np.random.default_rng(13)
+    h, g = rng.uniform(0.5, 2.0, 12), rng.uniform(0.5, 2.0, 8)
+    s_, t_ = np.where(rng.random(12) < 0.5, -1.0, 1.0), np.where(rng.random(8) < 0.5, -1.0, 1.0)
+    W = np.outer(h * s_, g * t_)
+    br = oracle.dual_svid_branch(W, 1)
+    what = (br["h64"][:, None] * oracle.sign_matrix(br["U"]) * br["l64"]) @ (oracle.sign_matrix(br["V"]) * br["g64"][:, None]).T
+    np.testing.assert_allclose(what, W, rtol=1e-10, atol=1e-12)
+    # the deployed (fp16-scaled) branch is within fp16 rounding of W
+    assert oracle.reconstruction_error(W, [br]) < 2e-3
+
+
+def test_dual_svid_is_positively_homogeneous():
+    rng = np.random.default_rng(14)
+    W = rng.standard_normal((20, 16))
+    b1, b2 = oracle.dual_svid_branch(W, 4), oracle.dual_svid_branch(3.0 * W, 4)
+    rec = lambda b: (b["h64"][:, None] * oracle.sign_matrix(b["U"]) * b["l64"]) @ (oracle.sign_matrix(b["V"]) * b["g64"][:, None]).T
+    np.testing.assert_allclose(rec(b2), 3.0 * rec(b1), rtol=1e-9, atol=1e-12)
+    np.testing.assert_array_equal(oracle.sign_matrix(b1["U"]), oracle.sign_matrix(b2["U"]))
+
+
+def test_dual_svid_residual_branch_lowers_the_error():
+    from binary_rank_gemv_amd import synth
+    W = synth.make_dense_weight(96, 64, seed=3).astype(np.float64)
+    brs = oracle.dual_svid_init(W, 16, nbranches=2)
+    e1, e2 = oracle.reconstruction_error(W, brs[:1]), oracle.reconstruction_error(W, brs)
+    assert e2 < e1 < 1.0
+    # branch 2 was fitted to W minus the deployed branch 1
+    R = W - oracle.branch_weight(brs[0])
+    ref = oracle.dual_svid_branch(R, 16)
+    np.testing.assert_array_equal(ref["h"], brs[1]["h"])
