@@ -270,6 +270,44 @@ def bpw_sweep(lb, torch, synth, args):
             "shape": {"m": m, "n": n, "branches": 2}, "data": "synthetic"}
 
 
+def init_bench(lb, torch, synth, args):
+    """Dual-SVID initialization (littlebit_dual_svid_init, the step before
+    the layer) of a synthetic dense weight of the 7B up-projection's shape
+    (11008 x 4096, decaying spectrum), two branches of rank 1472: seconds on
+    the GPU and the relative reconstruction error; the float64 oracle is
+    timed on a quarter-size sample (2752 x 1024, rank 368) as context."""
+    import time
+    sh = synth.UP7B
+    r = sh.ranks[0]
+    W = torch.from_numpy(synth.make_dense_weight(sh.m, sh.n, seed=7)).cuda()
+    lb.littlebit_dual_svid_init(torch.from_numpy(synth.make_dense_weight(256, 128, seed=1)).cuda(), 8)  # library warm-up
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    brs = lb.littlebit_dual_svid_init(W, r, nbranches=2)
+    torch.cuda.synchronize()
+    gpu_s = time.perf_counter() - t0
+    what = torch.zeros_like(W)
+    for b in brs:
+        su = torch.where(b["U"] < 0, -1.0, 1.0) * b["h"].float()[:, None] * b["l"].float()[None, :]
+        sv = torch.where(b["V"] < 0, -1.0, 1.0) * b["g"].float()[:, None]
+        what += su @ sv.T
+        err = float(torch.linalg.norm(W - what) / torch.linalg.norm(W))
+        b["error_after"] = err
+    out = {"init": {"method": "dual-svid", "shape": {"m": sh.m, "n": sh.n, "rank": r, "branches": 2},
+                    "gpu_seconds": round(gpu_s, 3),
+                    "rel_error_branch1": round(brs[0]["error_after"], 5),
+                    "rel_error_branches12": round(brs[1]["error_after"], 5), "data": "synthetic"}}
+    if args.cpu_seconds > 0:
+        import oracle
+        Wq = synth.make_dense_weight(sh.m // 4, sh.n // 4, seed=7).astype(np.float64)
+        t0 = time.perf_counter()
+        oracle.dual_svid_init(Wq, r // 4, nbranches=2)
+        out["init"]["cpu_baseline"] = {"kind": "oracle", "seconds": round(time.perf_counter() - t0, 3),
+                                       "cores": _blas_threads(),
+                                       "sample": f"quarter-size weight {sh.m // 4} x {sh.n // 4}, rank {r // 4}"}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -282,6 +320,8 @@ def main():
                     help="skip the 13B-block, 70B and prefill measurements")
     ap.add_argument("--bpw-sweep", action="store_true",
                     help="only the bits-per-weight sweep of the 70B up-projection against fp16 dense")
+    ap.add_argument("--init", action="store_true",
+                    help="only the Dual-SVID initialization of a 7B-shaped dense weight")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="no timing: one call per layer copy plus a 256 MiB device copy, for hardware counters")
     args = ap.parse_args()
@@ -297,6 +337,10 @@ def main():
     if args.bpw_sweep:
         torch.cuda.set_device(0)
         print(json.dumps(bpw_sweep(lb, torch, synth, args)))
+        return
+    if args.init:
+        torch.cuda.set_device(0)
+        print(json.dumps(init_bench(lb, torch, synth, args)))
         return
 
     shape, batch = synth.UP7B, 1

@@ -35,7 +35,7 @@ def build_library(verbose: bool = False, extra_flags=()) -> str:
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-I", os.path.join(ROOT, "include"), "-I", CSRC, *DEVICE_FLAGS, *extra_flags,
-           *sources(), "-o", tmp]
+           *sources(), "-L/opt/rocm/lib", "-lrocblas", "-lrocsolver", "-Wl,-rpath,/opt/rocm/lib", "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

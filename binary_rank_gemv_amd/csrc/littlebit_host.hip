@@ -15,6 +15,8 @@ hipError_t lb_launch_prefill(const LbPrefillArgs& args, hipStream_t stream);
 hipError_t lb_launch_transpose_packed(const void* src, int R, int K, void* dst, hipStream_t stream);
 hipError_t lb_launch_decode(const LbDecodeArgs& args, int chunk_pairs, void* sync, int allow_fused,
                             hipStream_t stream);
+int lb_run_dual_svid(const float* W, int64_t m, int64_t n, int64_t ldw, int r, int nbranches,
+                     const lb_init_branch* out, hipStream_t stream, std::string& err);
 
 namespace {
 
@@ -236,6 +238,26 @@ lb_status littlebit_transpose_packed(const void* src, int64_t R, int64_t K, void
   if (src == dst) return fail(LB_ERR_INVALID_ARG, "littlebit_transpose_packed: src and dst must not be the same buffer");
   hipError_t e = lb_launch_transpose_packed(src, (int)R, (int)K, dst, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "littlebit_transpose_packed launch");
+  return LB_OK;
+}
+
+lb_status littlebit_dual_svid_init(const float* W, int64_t m, int64_t n, int64_t ldw, int64_t r, int nbranches,
+                                   const lb_init_branch* out, void* stream) {
+  if (!W || !out) return fail(LB_ERR_INVALID_ARG, "littlebit_dual_svid_init: NULL pointer");
+  if (m < 1 || n < 1 || ldw < n)
+    return fail(LB_ERR_INVALID_ARG, "littlebit_dual_svid_init: m=%lld n=%lld ldw=%lld", (long long)m, (long long)n,
+                (long long)ldw);
+  if (nbranches < 1 || nbranches > 2)
+    return fail(LB_ERR_INVALID_ARG, "littlebit_dual_svid_init: nbranches=%d (1 or 2)", nbranches);
+  if (r < 1 || r > (m < n ? m : n) || r > kMaxRank)
+    return fail(LB_ERR_INVALID_ARG, "littlebit_dual_svid_init: r=%lld outside 1..min(m, n, %d)", (long long)r, kMaxRank);
+  if (m > kMaxN || n > kMaxN) return fail(LB_ERR_UNSUPPORTED, "littlebit_dual_svid_init: m, n <= %d", kMaxN);
+  for (int b = 0; b < nbranches; ++b)
+    if (!out[b].U || !out[b].V || !out[b].h || !out[b].l || !out[b].g)
+      return fail(LB_ERR_INVALID_ARG, "littlebit_dual_svid_init: NULL output of branch %d", b);
+  std::string err;
+  const int rc = lb_run_dual_svid(W, m, n, ldw, (int)r, nbranches, out, (hipStream_t)stream, err);
+  if (rc != 0) return fail((lb_status)rc, "littlebit_dual_svid_init: %s", err.c_str());
   return LB_OK;
 }
 

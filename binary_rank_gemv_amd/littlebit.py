@@ -37,6 +37,7 @@ EXPORTED = (
     "littlebit_packed_bytes", "littlebit_pack", "littlebit_linear_workspace_bytes",
     "littlebit_linear_fwd", "littlebit_block_workspace_bytes", "littlebit_block_fwd",
     "littlebit_status_string", "littlebit_last_error", "littlebit_transpose_packed",
+    "littlebit_dual_svid_init",
 )
 
 
@@ -50,6 +51,11 @@ class _Branch(ctypes.Structure):
     _fields_ = [("v_bits", ctypes.c_void_p), ("u_bits", ctypes.c_void_p),
                 ("h", ctypes.c_void_p), ("l", ctypes.c_void_p), ("g", ctypes.c_void_p),
                 ("r", ctypes.c_int32)]
+
+
+class _InitBranch(ctypes.Structure):
+    _fields_ = [("U", ctypes.c_void_p), ("V", ctypes.c_void_p), ("h", ctypes.c_void_p),
+                ("l", ctypes.c_void_p), ("g", ctypes.c_void_p)]
 
 
 class _Layer(ctypes.Structure):
@@ -76,6 +82,8 @@ def _load():
     lib.littlebit_block_workspace_bytes.restype = sz
     lib.littlebit_block_fwd.argtypes = [ctypes.POINTER(_Layer), vp, vp, vp, vp, ctypes.POINTER(vp), i64, vp, sz, vp]
     lib.littlebit_block_fwd.restype = i32
+    lib.littlebit_dual_svid_init.argtypes = [vp, i64, i64, i64, i64, i32, ctypes.POINTER(_InitBranch), vp]
+    lib.littlebit_dual_svid_init.restype = i32
     lib.littlebit_status_string.argtypes = [i32]
     lib.littlebit_status_string.restype = ctypes.c_char_p
     lib.littlebit_last_error.argtypes = []
@@ -136,6 +144,27 @@ def littlebit_transpose_packed(bits: torch.Tensor, R: int, K: int, stream=None) 
     out = torch.empty(littlebit_packed_bytes(K, R), dtype=torch.uint8, device=bits.device)
     _check(LIB.littlebit_transpose_packed(_ptr(bits), R, K, _ptr(out), _stream_ptr(stream)))
     return out
+
+
+def littlebit_dual_svid_init(W: torch.Tensor, r: int, nbranches: int = 2, stream=None) -> List[dict]:
+    """Branches (dicts with U, V fp32 latents and fp16 h, l, g, all on W's
+    device) of the Dual-SVID initialization of the dense weight W (m x n
+    fp32 CUDA tensor, unit column stride); ready for LittleBitLayer.from_latents."""
+    if W.dtype != torch.float32 or not W.is_cuda or W.dim() != 2 or W.stride(1) != 1:
+        raise ValueError("W must be a 2-D fp32 CUDA tensor with unit column stride")
+    m, n = W.shape
+    outs = []
+    arr = (_InitBranch * nbranches)()
+    for b in range(nbranches):
+        br = {"U": torch.empty((m, r), dtype=torch.float32, device=W.device),
+              "V": torch.empty((n, r), dtype=torch.float32, device=W.device),
+              "h": torch.empty(m, dtype=torch.float16, device=W.device),
+              "l": torch.empty(r, dtype=torch.float16, device=W.device),
+              "g": torch.empty(n, dtype=torch.float16, device=W.device)}
+        arr[b] = _InitBranch(_ptr(br["U"]), _ptr(br["V"]), _ptr(br["h"]), _ptr(br["l"]), _ptr(br["g"]))
+        outs.append(br)
+    _check(LIB.littlebit_dual_svid_init(_ptr(W), m, n, W.stride(0), r, nbranches, arr, _stream_ptr(stream)))
+    return outs
 
 
 @dataclass

@@ -178,6 +178,48 @@ lb_status littlebit_block_fwd(const lb_layer L[7], const uint16_t *x_qkv,
                               int64_t batch, void *ws, size_t ws_bytes,
                               void *stream);
 
+/*
+ * Dual-SVID initialization (explainx.ai explainer, "How it works" item 3:
+ * training starts from a truncated SVD of the real weights whose signs and
+ * magnitudes are mapped into the layer's parameters, and a residual branch
+ * models what the first branch missed).  The step before the layer: it turns
+ * a dense weight into branches for littlebit_pack / the layer.
+ *
+ * Per branch, from R (W for the first branch, then W minus the deployed
+ * earlier branches): the rank-r truncated SVD R ~ P S Q^T gives the latent
+ * factors U = P S^(1/2) (m x r) and V = Q S^(1/2) (n x r), each component
+ * oriented so the largest-magnitude entry of its V column (first index on
+ * ties) is positive; |U| and |V| are each approximated by the rank-1 product
+ * a b^T of their leading singular triplet (a = sqrt(sigma) p, b =
+ * sqrt(sigma) q, non-negative); h = a_U, g = a_V, l = b_U * b_V, rounded to
+ * fp16 (nearest even).  The deployed branch diag(h) sign(U) diag(l)
+ * sign(V)^T diag(g) (signs of the fp32 latents, -1 iff < 0) is subtracted
+ * before the next branch.  Float64 throughout on the device (rocBLAS GEMMs,
+ * rocSOLVER symmetric eigendecomposition of the smaller-side Gram matrix,
+ * power iteration for the rank-1 fits).
+ *
+ *   W         device fp32, m x n row-major, row stride ldw >= n (elements).
+ *   r         rank per branch, 1 <= r <= min(m, n), r <= 4096.
+ *   nbranches 1 or 2; out[b] receives branch b:
+ *             U device fp32 m x r row-major, V device fp32 n x r row-major
+ *             (the latent factors; their signs are the binary factors),
+ *             h (m), l (r), g (n) device fp16.
+ * Unlike the layer calls this one allocates device memory (about
+ * 8 (m n + k^2 + 4 max(m, n) r) bytes, k = min(m, n)) and returns after
+ * the work on `stream` has finished.  m, n <= 32768.
+ */
+typedef struct lb_init_branch {
+  float *U;
+  float *V;
+  uint16_t *h;
+  uint16_t *l;
+  uint16_t *g;
+} lb_init_branch;
+
+lb_status littlebit_dual_svid_init(const float *W, int64_t m, int64_t n,
+                                   int64_t ldw, int64_t r, int nbranches,
+                                   const lb_init_branch *out, void *stream);
+
 /* Static description of a status code. */
 const char *littlebit_status_string(lb_status s);
 

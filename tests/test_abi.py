@@ -133,3 +133,19 @@ def test_block_fwd_rejects_bad_arguments():
     assert B(arr, FAKE, FAKE, FAKE, FAKE, ys, 1, FAKE, 16, None) == lb.LB_ERR_WORKSPACE
     ys2 = (ctypes.c_void_p * 7)(*([FAKE] * 6 + [None]))
     assert B(arr, FAKE, FAKE, FAKE, FAKE, ys2, 1, FAKE, 1 << 30, None) == lb.LB_ERR_INVALID_ARG
+
+
+def test_dual_svid_init_rejects_bad_arguments():
+    arr = (lb._InitBranch * 2)()
+    for b in range(2):
+        arr[b] = lb._InitBranch(FAKE, FAKE, FAKE, FAKE, FAKE)
+    f = lb.LIB.littlebit_dual_svid_init
+    assert f(None, 64, 32, 32, 8, 2, arr, None) == lb.LB_ERR_INVALID_ARG
+    assert f(FAKE, 64, 32, 16, 8, 2, arr, None) == lb.LB_ERR_INVALID_ARG       # ldw < n
+    assert f(FAKE, 64, 32, 32, 33, 2, arr, None) == lb.LB_ERR_INVALID_ARG      # r > min(m, n)
+    assert f(FAKE, 64, 32, 32, 0, 2, arr, None) == lb.LB_ERR_INVALID_ARG
+    assert f(FAKE, 64, 32, 32, 8, 3, arr, None) == lb.LB_ERR_INVALID_ARG      # nbranches
+    assert f(FAKE, 40000, 32, 32, 8, 1, arr, None) == lb.LB_ERR_UNSUPPORTED
+    arr[1] = lb._InitBranch(FAKE, None, FAKE, FAKE, FAKE)
+    assert f(FAKE, 64, 32, 32, 8, 2, arr, None) == lb.LB_ERR_INVALID_ARG
+    assert "NULL output" in lb.littlebit_last_error()
