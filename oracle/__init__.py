@@ -37,6 +37,8 @@ from .dual_svid import (  # noqa: F401
     dual_svid_branch,
     dual_svid_init,
     reconstruction_error,
+    itq_rotation,
+    itq_objective,
 )
 from .packing import (  # noqa: F401
     pack_factor,

@@ -40,6 +40,11 @@ Parity status (tests/test_oracle.py):
   the orientation rule.
 * ``svid``: pinned by exact recovery of a matrix diag(p) S diag(q) with S a
   sign matrix and p, q > 0, and by the positivity of the magnitude vectors.
+* ``itq_rotation``: pinned by orthogonality of R, invariance of the product
+  U R (V R)^T = U V^T, the monotone objective (no iteration lowers
+  sum |[U; V] R|), and exact recovery in one iteration when the stacked
+  factors are a sign matrix H with orthogonal columns times a small rotation
+  Q^T (sign(H Q^T) = H, so the Procrustes step returns R = Q and Z R = H).
 * ``dual_svid_init``: pinned by exact reconstruction of a rank-1
   sign-magnitude weight (h * s)(g * t)^T with r = 1 (before fp16 rounding),
   by positive homogeneity (scaling W scales the unrounded reconstruction),
@@ -95,20 +100,53 @@ def svid(M: np.ndarray):
     return signs, np.abs(p) * root, np.abs(q) * root
 
 
-def dual_svid_branch(R: np.ndarray, r: int) -> dict:
-    """One branch from the matrix it approximates: truncated SVD, then the
-    sign-value split of both latent factors; scales rounded to fp16.
+def itq_rotation(U: np.ndarray, V: np.ndarray, iters: int) -> np.ndarray:
+    """Orthogonal R (r x r) of Joint-ITQ for the latent factors U (m x r) and
+    V (n x r): from R = I, each iteration takes B = sign([U; V] R) (-1 iff
+    < 0) and then the R that best maps [U; V] onto B, R = P Q^T from the SVD
+    P S Q^T of [U; V]^T B (orthogonal Procrustes).
 
-    explainx.ai explainer, "How it works" items 2 and 3.
+    explainx.ai explainer, the LittleBit-2 paragraph: Internal Latent Rotation
+    with Joint Iterative Quantization aligns the SVD-derived latent factors
+    with the binary hypercube before training.  Reading: one rotation shared
+    by both factors, so U R (V R)^T = U V^T and the product is unchanged;
+    "joint" = both factors stacked in one objective; start R = I, a fixed
+    iteration count.
+    """
+    Z = np.vstack([np.asarray(U, np.float64), np.asarray(V, np.float64)])
+    R = np.eye(Z.shape[1])
+    for _ in range(iters):
+        B = np.where(Z @ R < 0, -1.0, 1.0)
+        P, _, Qt = np.linalg.svd(Z.T @ B)
+        R = P @ Qt
+    return R
+
+
+def itq_objective(U: np.ndarray, V: np.ndarray, R: np.ndarray) -> float:
+    """sum |[U; V] R|, the alignment with the hypercube that each ITQ step
+    cannot lower (it equals max over sign matrices B of tr(B^T [U; V] R))."""
+    return float(np.abs(np.vstack([U, V]) @ R).sum())
+
+
+def dual_svid_branch(R: np.ndarray, r: int, itq_iters: int = 0) -> dict:
+    """One branch from the matrix it approximates: truncated SVD, an optional
+    Joint-ITQ rotation of the latent factors, then the sign-value split of
+    both latent factors; scales rounded to fp16.
+
+    explainx.ai explainer, "How it works" items 2 and 3, and the LittleBit-2
+    paragraph (the rotation).
     """
     U, V = truncated_svd_factors(R, r)
+    if itq_iters > 0:
+        Q = itq_rotation(U, V, itq_iters)
+        U, V = U @ Q, V @ Q
     _, hU, lU = svid(U)
     _, gV, lV = svid(V)
     return {"U": U, "V": V, "h": hU.astype(np.float16), "l": (lU * lV).astype(np.float16),
             "g": gV.astype(np.float16), "h64": hU, "l64": lU * lV, "g64": gV}
 
 
-def dual_svid_init(W: np.ndarray, r: int, nbranches: int = 2) -> list:
+def dual_svid_init(W: np.ndarray, r: int, nbranches: int = 2, itq_iters: int = 0) -> list:
     """Branches of the Dual-SVID initialization of W: branch 1 from W, each
     later branch from the residual W minus the deployed earlier branches.
 
@@ -119,7 +157,7 @@ def dual_svid_init(W: np.ndarray, r: int, nbranches: int = 2) -> list:
     out = []
     R = W.copy()
     for _ in range(nbranches):
-        br = dual_svid_branch(R, r)
+        br = dual_svid_branch(R, r, itq_iters)
         out.append(br)
         R = R - branch_weight(br)
     return out

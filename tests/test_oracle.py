@@ -377,3 +377,42 @@ def test_dual_svid_residual_branch_lowers_the_error():
     R = W - oracle.branch_weight(brs[0])
     ref = oracle.dual_svid_branch(R, 16)
     np.testing.assert_array_equal(ref["h"], brs[1]["h"])
+
+
+# ---------------------------------------------------- Joint-ITQ latent rotation
+
+def test_itq_rotation_is_orthogonal_keeps_the_product_and_never_lowers_the_objective():
+    rng = np.random.default_rng(21)
+    U, V = rng.standard_normal((40, 8)) * np.linspace(2, 0.5, 8), rng.standard_normal((30, 8))
+    prev = oracle.itq_objective(U, V, np.eye(8))
+    for it in (1, 2, 3, 5, 8, 13):
+        R = oracle.itq_rotation(U, V, it)
+        np.testing.assert_allclose(R.T @ R, np.eye(8), atol=1e-12)
+        np.testing.assert_allclose((U @ R) @ (V @ R).T, U @ V.T, atol=1e-10)
+        obj = oracle.itq_objective(U, V, R)
+        assert obj >= prev - 1e-9
+        prev = obj
+
+
+def test_itq_recovers_a_rotated_sign_matrix_in_one_iteration():
+    """Z = H Q^T, H a 32 x 8 sign matrix with orthogonal columns (columns
+    1..8 of a Sylvester-Hadamard matrix, rows split over U and V) and Q a
+    small rotation: sign(Z) = H, the Procrustes step gives R = Q and Z R = H."""
+    from scipy.linalg import expm, hadamard
+    rng = np.random.default_rng(22)
+    H = hadamard(32).astype(np.float64)[:, 1:9]
+    A = rng.standard_normal((8, 8)) * 0.02
+    Q = expm(A - A.T)
+    Z = H @ Q.T
+    assert np.array_equal(np.where(Z < 0, -1.0, 1.0), H)
+    R = oracle.itq_rotation(Z[:20], Z[20:], 1)
+    np.testing.assert_allclose(R, Q, atol=1e-12)
+    np.testing.assert_allclose(Z @ R, H, atol=1e-12)
+    assert abs(oracle.itq_objective(Z[:20], Z[20:], R) - np.abs(H).sum()) < 1e-9
+
+
+def test_dual_svid_with_itq_keeps_the_latent_product():
+    from binary_rank_gemv_amd import synth
+    W = synth.make_dense_weight(80, 60, seed=5).astype(np.float64)
+    plain, rot = oracle.dual_svid_branch(W, 12), oracle.dual_svid_branch(W, 12, itq_iters=10)
+    np.testing.assert_allclose(rot["U"] @ rot["V"].T, plain["U"] @ plain["V"].T, atol=1e-10)
