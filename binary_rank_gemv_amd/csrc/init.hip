@@ -11,6 +11,9 @@
 //      U' = P S^(1/2), V' = Q S^(1/2); each component oriented so that the
 //      largest-magnitude entry of its V' column (first index on ties) is
 //      positive;
+//   2b. optionally, a Joint-ITQ rotation of both latent factors (LittleBit-2
+//      paragraph of the explainer: the latent factors aligned with the binary
+//      hypercube before training), which leaves U' V'^T unchanged;
 //   3. sign-value split of U' and of V': the rank-1 approximation a b^T of
 //      |U'| (and of |V'|) by power iteration (non-negative leading singular
 //      vectors), a = sqrt(sigma) p, b = sqrt(sigma) q; h = a_U, g = a_V,
@@ -183,6 +186,18 @@ __global__ void deployed_factors_kernel(const float* __restrict__ Ul, const uint
   }
 }
 
+__global__ void identity_kernel(double* __restrict__ R, int r) {
+  const int64_t total = (int64_t)r * r;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x)
+    R[e] = (e / r == e % r) ? 1.0 : 0.0;
+}
+
+// A = sign(A) as +-1 (-1 iff < 0), in place
+__global__ void sign_kernel(double* __restrict__ A, int64_t total) {
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x)
+    A[e] = A[e] < 0.0 ? -1.0 : 1.0;
+}
+
 int grid_for(int64_t total) {
   const int64_t g = (total + kThreads - 1) / kThreads;
   return (int)(g < 4096 ? (g > 0 ? g : 1) : 4096);
@@ -238,21 +253,24 @@ static int power_rank1(rocblas_handle hb, hipStream_t stream, const double* M, i
   return 0;
 }
 
-int lb_run_dual_svid(const float* W, int64_t m, int64_t n, int64_t ldw, int r, int nbranches,
+int lb_run_dual_svid(const float* W, int64_t m, int64_t n, int64_t ldw, int r, int nbranches, int itq_iters,
                      const lb_init_branch* out, hipStream_t stream, std::string& err) {
   const int64_t k = m < n ? m : n;
   const bool gram_on_n = n <= m;  // eigenvectors on the input side (V) when n <= m
   auto alloc = [&](DevBuf& b, size_t bytes) {
     return hipMalloc(&b.p, bytes > 0 ? bytes : 8) == hipSuccess;
   };
-  DevBuf X, G, D, E, Y, sig, Ud, Vd, Mabs, p, q, qU, A, B, info;
+  DevBuf X, G, D, E, Y, sig, Ud, Vd, Mabs, p, q, qU, A, B, info, Rm, Mm, Su, Svt, Sv, Ee;
   const size_t dz = sizeof(double);
   const int64_t mr = (m > n ? m : n) * (int64_t)r;
   if (!alloc(X, (size_t)(m * n) * dz) || !alloc(G, (size_t)(k * k) * dz) || !alloc(D, (size_t)k * dz) ||
       !alloc(E, (size_t)k * dz) || !alloc(Y, (size_t)(k * r) * dz) || !alloc(sig, (size_t)r * dz) ||
       !alloc(Ud, (size_t)(m * r) * dz) || !alloc(Vd, (size_t)(n * r) * dz) || !alloc(Mabs, (size_t)mr * dz) ||
       !alloc(p, (size_t)(m > n ? m : n) * dz) || !alloc(q, (size_t)r * dz) || !alloc(qU, (size_t)r * dz) ||
-      !alloc(A, (size_t)(m * r) * dz) || !alloc(B, (size_t)(n * r) * dz) || !alloc(info, sizeof(rocblas_int))) {
+      !alloc(A, (size_t)(m * r) * dz) || !alloc(B, (size_t)(n * r) * dz) || !alloc(info, sizeof(rocblas_int)) ||
+      !alloc(Rm, itq_iters > 0 ? (size_t)r * r * dz : 8) || !alloc(Mm, itq_iters > 0 ? (size_t)r * r * dz : 8) ||
+      !alloc(Su, itq_iters > 0 ? (size_t)r * r * dz : 8) || !alloc(Svt, itq_iters > 0 ? (size_t)r * r * dz : 8) ||
+      !alloc(Sv, itq_iters > 0 ? (size_t)r * dz : 8) || !alloc(Ee, itq_iters > 0 ? (size_t)r * dz : 8)) {
     err = "device allocation for the initialization failed";
     return LB_ERR_HIP;
   }
@@ -332,6 +350,63 @@ int lb_run_dual_svid(const float* W, int64_t m, int64_t n, int64_t ldw, int r, i
       return LB_ERR_HIP;
     }
     hipLaunchKernelGGL(orient_kernel, dim3(r), dim3(kThreads), 0, stream, Ub, m, Vb, n);
+    // 2b. Joint-ITQ rotation shared by both factors (the product U' V'^T is
+    // unchanged): from R = I, B = sign([U'; V'] R), then R = P Q^T for the
+    // SVD P S Q^T of M = U'^T B_U + V'^T B_V (taken as the polar factor
+    // M (M^T M)^(-1/2)); finally U' <- U' R, V' <- V' R
+    if (itq_iters > 0) {
+      double* Ad = (double*)A.p;
+      double* Bd = (double*)B.p;
+      double* R = (double*)Rm.p;
+      double* M = (double*)Mm.p;
+      hipLaunchKernelGGL(identity_kernel, dim3(grid_for((int64_t)r * r)), dim3(kThreads), 0, stream, R, r);
+      for (int it = 0; it < itq_iters; ++it) {
+        rocblas_status s1 = rocblas_dgemm(hb, rocblas_operation_none, rocblas_operation_none, (rocblas_int)m, r, r, &one,
+                                          Ub, (rocblas_int)m, R, r, &zero, Ad, (rocblas_int)m);
+        rocblas_status s2 = rocblas_dgemm(hb, rocblas_operation_none, rocblas_operation_none, (rocblas_int)n, r, r, &one,
+                                          Vb, (rocblas_int)n, R, r, &zero, Bd, (rocblas_int)n);
+        hipLaunchKernelGGL(sign_kernel, dim3(grid_for(m * r)), dim3(kThreads), 0, stream, Ad, m * r);
+        hipLaunchKernelGGL(sign_kernel, dim3(grid_for(n * r)), dim3(kThreads), 0, stream, Bd, n * r);
+        rocblas_status s3 = rocblas_dgemm(hb, rocblas_operation_transpose, rocblas_operation_none, r, r, (rocblas_int)m,
+                                          &one, Ub, (rocblas_int)m, Ad, (rocblas_int)m, &zero, M, r);
+        rocblas_status s4 = rocblas_dgemm(hb, rocblas_operation_transpose, rocblas_operation_none, r, r, (rocblas_int)n,
+                                          &one, Vb, (rocblas_int)n, Bd, (rocblas_int)n, &one, M, r);
+        // R = polar factor of M = M (M^T M)^(-1/2) = P Q^T for M = P S Q^T:
+        // N = M^T M = E diag(lambda) E^T (dsyevd), F = E diag(lambda^(-1/4)),
+        // R = (M F) F^T
+        double* N = (double*)Su.p;
+        double* T1 = (double*)Svt.p;
+        rocblas_status s5 = rocblas_dgemm(hb, rocblas_operation_transpose, rocblas_operation_none, r, r, r, &one, M, r,
+                                          M, r, &zero, N, r);
+        rocblas_status s6 = rocsolver_dsyevd(hb, rocblas_evect_original, rocblas_fill_upper, r, N, r, (double*)Sv.p,
+                                             (double*)Ee.p, (rocblas_int*)info.p);
+        rocblas_int sinfo = 0;
+        if (s1 || s2 || s3 || s4 || s5 || s6 ||
+            hipMemcpyAsync(&sinfo, info.p, sizeof sinfo, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+            hipStreamSynchronize(stream) != hipSuccess || sinfo != 0) {
+          err = "Joint-ITQ step failed (rocBLAS/rocSOLVER dsyevd, info " + std::to_string((int)sinfo) + ")";
+          return LB_ERR_HIP;
+        }
+        hipLaunchKernelGGL(scale_cols_kernel, dim3(grid_for(r) < 64 ? grid_for(r) : 64, r), dim3(kThreads), 0, stream, N,
+                           (int64_t)r, r, (const double*)Sv.p, -0.25);
+        if (rocblas_dgemm(hb, rocblas_operation_none, rocblas_operation_none, r, r, r, &one, M, r, N, r, &zero, T1, r) !=
+                rocblas_status_success ||
+            rocblas_dgemm(hb, rocblas_operation_none, rocblas_operation_transpose, r, r, r, &one, T1, r, N, r, &zero, R,
+                          r) != rocblas_status_success) {
+          err = "rocBLAS dgemm (rotation) failed";
+          return LB_ERR_HIP;
+        }
+      }
+      if (rocblas_dgemm(hb, rocblas_operation_none, rocblas_operation_none, (rocblas_int)m, r, r, &one, Ub,
+                        (rocblas_int)m, R, r, &zero, Ad, (rocblas_int)m) != rocblas_status_success ||
+          rocblas_dgemm(hb, rocblas_operation_none, rocblas_operation_none, (rocblas_int)n, r, r, &one, Vb,
+                        (rocblas_int)n, R, r, &zero, Bd, (rocblas_int)n) != rocblas_status_success ||
+          hipMemcpyAsync(Ub, Ad, (size_t)(m * r) * dz, hipMemcpyDeviceToDevice, stream) != hipSuccess ||
+          hipMemcpyAsync(Vb, Bd, (size_t)(n * r) * dz, hipMemcpyDeviceToDevice, stream) != hipSuccess) {
+        err = "applying the Joint-ITQ rotation failed";
+        return LB_ERR_HIP;
+      }
+    }
     // 3. sign-value split of both factors
     double sU = 0.0, sV = 0.0;
     hipLaunchKernelGGL(abs_kernel, dim3(grid_for(m * r)), dim3(kThreads), 0, stream, (const double*)Ub, m * r,

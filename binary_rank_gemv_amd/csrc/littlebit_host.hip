@@ -15,7 +15,7 @@ hipError_t lb_launch_prefill(const LbPrefillArgs& args, hipStream_t stream);
 hipError_t lb_launch_transpose_packed(const void* src, int R, int K, void* dst, hipStream_t stream);
 hipError_t lb_launch_decode(const LbDecodeArgs& args, int chunk_pairs, void* sync, int allow_fused,
                             hipStream_t stream);
-int lb_run_dual_svid(const float* W, int64_t m, int64_t n, int64_t ldw, int r, int nbranches,
+int lb_run_dual_svid(const float* W, int64_t m, int64_t n, int64_t ldw, int r, int nbranches, int itq_iters,
                      const lb_init_branch* out, hipStream_t stream, std::string& err);
 
 namespace {
@@ -242,7 +242,7 @@ lb_status littlebit_transpose_packed(const void* src, int64_t R, int64_t K, void
 }
 
 lb_status littlebit_dual_svid_init(const float* W, int64_t m, int64_t n, int64_t ldw, int64_t r, int nbranches,
-                                   const lb_init_branch* out, void* stream) {
+                                   int itq_iters, const lb_init_branch* out, void* stream) {
   if (!W || !out) return fail(LB_ERR_INVALID_ARG, "littlebit_dual_svid_init: NULL pointer");
   if (m < 1 || n < 1 || ldw < n)
     return fail(LB_ERR_INVALID_ARG, "littlebit_dual_svid_init: m=%lld n=%lld ldw=%lld", (long long)m, (long long)n,
@@ -252,11 +252,13 @@ lb_status littlebit_dual_svid_init(const float* W, int64_t m, int64_t n, int64_t
   if (r < 1 || r > (m < n ? m : n) || r > kMaxRank)
     return fail(LB_ERR_INVALID_ARG, "littlebit_dual_svid_init: r=%lld outside 1..min(m, n, %d)", (long long)r, kMaxRank);
   if (m > kMaxN || n > kMaxN) return fail(LB_ERR_UNSUPPORTED, "littlebit_dual_svid_init: m, n <= %d", kMaxN);
+  if (itq_iters < 0 || itq_iters > 1000)
+    return fail(LB_ERR_INVALID_ARG, "littlebit_dual_svid_init: itq_iters=%d outside 0..1000", itq_iters);
   for (int b = 0; b < nbranches; ++b)
     if (!out[b].U || !out[b].V || !out[b].h || !out[b].l || !out[b].g)
       return fail(LB_ERR_INVALID_ARG, "littlebit_dual_svid_init: NULL output of branch %d", b);
   std::string err;
-  const int rc = lb_run_dual_svid(W, m, n, ldw, (int)r, nbranches, out, (hipStream_t)stream, err);
+  const int rc = lb_run_dual_svid(W, m, n, ldw, (int)r, nbranches, itq_iters, out, (hipStream_t)stream, err);
   if (rc != 0) return fail((lb_status)rc, "littlebit_dual_svid_init: %s", err.c_str());
   return LB_OK;
 }

@@ -82,7 +82,7 @@ def _load():
     lib.littlebit_block_workspace_bytes.restype = sz
     lib.littlebit_block_fwd.argtypes = [ctypes.POINTER(_Layer), vp, vp, vp, vp, ctypes.POINTER(vp), i64, vp, sz, vp]
     lib.littlebit_block_fwd.restype = i32
-    lib.littlebit_dual_svid_init.argtypes = [vp, i64, i64, i64, i64, i32, ctypes.POINTER(_InitBranch), vp]
+    lib.littlebit_dual_svid_init.argtypes = [vp, i64, i64, i64, i64, i32, i32, ctypes.POINTER(_InitBranch), vp]
     lib.littlebit_dual_svid_init.restype = i32
     lib.littlebit_status_string.argtypes = [i32]
     lib.littlebit_status_string.restype = ctypes.c_char_p
@@ -146,10 +146,12 @@ def littlebit_transpose_packed(bits: torch.Tensor, R: int, K: int, stream=None) 
     return out
 
 
-def littlebit_dual_svid_init(W: torch.Tensor, r: int, nbranches: int = 2, stream=None) -> List[dict]:
+def littlebit_dual_svid_init(W: torch.Tensor, r: int, nbranches: int = 2, itq_iters: int = 0,
+                             stream=None) -> List[dict]:
     """Branches (dicts with U, V fp32 latents and fp16 h, l, g, all on W's
     device) of the Dual-SVID initialization of the dense weight W (m x n
-    fp32 CUDA tensor, unit column stride); ready for LittleBitLayer.from_latents."""
+    fp32 CUDA tensor, unit column stride), optionally with a Joint-ITQ
+    rotation of the latent factors; ready for LittleBitLayer.from_latents."""
     if W.dtype != torch.float32 or not W.is_cuda or W.dim() != 2 or W.stride(1) != 1:
         raise ValueError("W must be a 2-D fp32 CUDA tensor with unit column stride")
     m, n = W.shape
@@ -163,7 +165,8 @@ def littlebit_dual_svid_init(W: torch.Tensor, r: int, nbranches: int = 2, stream
               "g": torch.empty(n, dtype=torch.float16, device=W.device)}
         arr[b] = _InitBranch(_ptr(br["U"]), _ptr(br["V"]), _ptr(br["h"]), _ptr(br["l"]), _ptr(br["g"]))
         outs.append(br)
-    _check(LIB.littlebit_dual_svid_init(_ptr(W), m, n, W.stride(0), r, nbranches, arr, _stream_ptr(stream)))
+    _check(LIB.littlebit_dual_svid_init(_ptr(W), m, n, W.stride(0), r, nbranches, itq_iters, arr,
+                                        _stream_ptr(stream)))
     return outs
 
 

@@ -204,6 +204,15 @@ lb_status littlebit_block_fwd(const lb_layer L[7], const uint16_t *x_qkv,
  *             U device fp32 m x r row-major, V device fp32 n x r row-major
  *             (the latent factors; their signs are the binary factors),
  *             h (m), l (r), g (n) device fp16.
+ *   itq_iters 0: no rotation.  > 0 (at most 1000): before the sign-value
+ *             split, the latent factors of each branch are rotated by one
+ *             orthogonal R (r x r), which leaves U V^T unchanged, chosen by
+ *             that many Joint-ITQ iterations from R = I (explainx.ai
+ *             explainer, LittleBit-2 paragraph: Internal Latent Rotation with
+ *             Joint Iterative Quantization aligns the latent factors with the
+ *             binary hypercube): B = sign([U; V] R), then R = P Q^T for the
+ *             SVD P S Q^T of M = [U; V]^T B, computed as the polar factor
+ *             M (M^T M)^(-1/2) (rocSOLVER dsyevd of M^T M).
  * Unlike the layer calls this one allocates device memory (about
  * 8 (m n + k^2 + 4 max(m, n) r) bytes, k = min(m, n)) and returns after
  * the work on `stream` has finished.  m, n <= 32768.
@@ -218,7 +227,8 @@ typedef struct lb_init_branch {
 
 lb_status littlebit_dual_svid_init(const float *W, int64_t m, int64_t n,
                                    int64_t ldw, int64_t r, int nbranches,
-                                   const lb_init_branch *out, void *stream);
+                                   int itq_iters, const lb_init_branch *out,
+                                   void *stream);
 
 /* Static description of a status code. */
 const char *littlebit_status_string(lb_status s);

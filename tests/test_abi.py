@@ -140,12 +140,13 @@ def test_dual_svid_init_rejects_bad_arguments():
     for b in range(2):
         arr[b] = lb._InitBranch(FAKE, FAKE, FAKE, FAKE, FAKE)
     f = lb.LIB.littlebit_dual_svid_init
-    assert f(None, 64, 32, 32, 8, 2, arr, None) == lb.LB_ERR_INVALID_ARG
-    assert f(FAKE, 64, 32, 16, 8, 2, arr, None) == lb.LB_ERR_INVALID_ARG       # ldw < n
-    assert f(FAKE, 64, 32, 32, 33, 2, arr, None) == lb.LB_ERR_INVALID_ARG      # r > min(m, n)
-    assert f(FAKE, 64, 32, 32, 0, 2, arr, None) == lb.LB_ERR_INVALID_ARG
-    assert f(FAKE, 64, 32, 32, 8, 3, arr, None) == lb.LB_ERR_INVALID_ARG      # nbranches
-    assert f(FAKE, 40000, 32, 32, 8, 1, arr, None) == lb.LB_ERR_UNSUPPORTED
+    assert f(None, 64, 32, 32, 8, 2, 0, arr, None) == lb.LB_ERR_INVALID_ARG
+    assert f(FAKE, 64, 32, 16, 8, 2, 0, arr, None) == lb.LB_ERR_INVALID_ARG       # ldw < n
+    assert f(FAKE, 64, 32, 32, 33, 2, 0, arr, None) == lb.LB_ERR_INVALID_ARG      # r > min(m, n)
+    assert f(FAKE, 64, 32, 32, 0, 2, 0, arr, None) == lb.LB_ERR_INVALID_ARG
+    assert f(FAKE, 64, 32, 32, 8, 3, 0, arr, None) == lb.LB_ERR_INVALID_ARG      # nbranches
+    assert f(FAKE, 40000, 32, 32, 8, 1, 0, arr, None) == lb.LB_ERR_UNSUPPORTED
+    assert f(FAKE, 64, 32, 32, 8, 2, -1, arr, None) == lb.LB_ERR_INVALID_ARG   # itq_iters
     arr[1] = lb._InitBranch(FAKE, None, FAKE, FAKE, FAKE)
-    assert f(FAKE, 64, 32, 32, 8, 2, arr, None) == lb.LB_ERR_INVALID_ARG
+    assert f(FAKE, 64, 32, 32, 8, 2, 0, arr, None) == lb.LB_ERR_INVALID_ARG
     assert "NULL output" in lb.littlebit_last_error()

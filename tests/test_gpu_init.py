@@ -1,5 +1,6 @@
 """GPU parity of the Dual-SVID initialization (littlebit_dual_svid_init,
-through the C ABI) against the float64 oracle (oracle.dual_svid_init).
+through the C ABI), with and without the Joint-ITQ rotation, against the
+float64 oracle (oracle.dual_svid_init).
 
 Bar (a reading: the method reaches the oracle's result up to floating-point
 rounding, and the singular vectors are oriented by the same rule on both
@@ -37,13 +38,14 @@ def _ulp_close(a16, b16):
     return np.max(np.abs(a - b)) <= 1
 
 
-@pytest.mark.parametrize("m,n,r,seed", [(300, 200, 16, 0), (150, 260, 24, 1), (1024, 768, 96, 2),
-                                        (2048, 1536, 192, 3)])
-def test_dual_svid_matches_the_oracle(lb, m, n, r, seed):
-    print(f"[case] dual-svid m={m} n={n} r={r}", flush=True)
+@pytest.mark.parametrize("m,n,r,seed,itq", [(300, 200, 16, 0, 0), (150, 260, 24, 1, 0), (1024, 768, 96, 2, 0),
+                                            (2048, 1536, 192, 3, 0), (300, 200, 16, 0, 10), (150, 260, 24, 1, 5),
+                                            (1024, 768, 96, 2, 8)])
+def test_dual_svid_matches_the_oracle(lb, m, n, r, seed, itq):
+    print(f"[case] dual-svid m={m} n={n} r={r} itq={itq}", flush=True)
     W = synth.make_dense_weight(m, n, seed=seed)
-    ref = oracle.dual_svid_init(W.astype(np.float64), r, nbranches=2)
-    got = lb.littlebit_dual_svid_init(torch.from_numpy(W).cuda(), r, nbranches=2)
+    ref = oracle.dual_svid_init(W.astype(np.float64), r, nbranches=2, itq_iters=itq)
+    got = lb.littlebit_dual_svid_init(torch.from_numpy(W).cuda(), r, nbranches=2, itq_iters=itq)
     torch.cuda.synchronize()
     gb = [{k: v.cpu().numpy() for k, v in b.items()} for b in got]
     for b, (g, o) in enumerate(zip(gb, ref)):
@@ -59,7 +61,7 @@ def test_dual_svid_matches_the_oracle(lb, m, n, r, seed):
     e_ref = oracle.reconstruction_error(W, ref)
     got_np = [{"U": b["U"], "V": b["V"], "h": b["h"], "l": b["l"], "g": b["g"]} for b in gb]
     e_got = oracle.reconstruction_error(W, got_np)
-    print(f"[parity] dual-svid {m}x{n} r={r}: error gpu {e_got:.6f} oracle {e_ref:.6f}", flush=True)
+    print(f"[parity] dual-svid {m}x{n} r={r} itq={itq}: error gpu {e_got:.6f} oracle {e_ref:.6f}", flush=True)
     assert abs(e_got - e_ref) <= 1e-5
     assert e_got < oracle.reconstruction_error(W, got_np[:1])
 
