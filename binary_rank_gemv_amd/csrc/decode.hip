@@ -585,7 +585,9 @@ __device__ __forceinline__ void u_enter_layer(const LayerView& L, int li, int ba
   const int s0 = 4 * S.p0;
   const int s1 = min(4 * S.p1, 2 * S.nu);  // steps of this wave's range that hold data
   if (s1 <= s0) return;
-  if (batch * 8 * (s1 - s0) <= 64 * LB_POLL_LOADS_SMALL)
+  // without polling (z written by an earlier launch) a pass never repeats, so
+  // the small variant (batches of loads one after another) is enough
+  if (!check || batch * 8 * (s1 - s0) <= 64 * LB_POLL_LOADS_SMALL)
     u_copy_z<LB_POLL_LOADS_SMALL>(L, batch, tag, check, sync, S, zl, s0, s1);
   else
     u_copy_z<LB_POLL_LOADS>(L, batch, tag, check, sync, S, zl, s0, s1);
