@@ -38,6 +38,7 @@
 // (partial sums 24 KB, two z tiles 1 KB, the copy, the row-scale table) leave of 160 KB
 #define LB_UPRE_DYN_MAX (160 * 1024 - LB_MAXT * LB_WAVES * 256 * 4 - 1024 - LB_UPRE_BYTES - 2 * LB_UPRE_HROWS)
 #define LB_SPIN_LIMIT (1 << 20)
+#define LB_MAX_BATCH 16               // tokens of a decode call (phase-A kernels for 1 and for up to 16)
 
 // workspace header (bytes): one 64-bit call counter per workgroup of the
 // single launch, then an error word set when a poll gives up.
@@ -208,9 +209,12 @@ __device__ inline void u_role(const LayerView& L, int wave, int& b, int& p0, int
 // ------------------------------------------------------------------ phase A
 // One 16-row tile of sign(V)^T of branch b of layer L: t, then
 // z = fp16(l*t), stored as tagged words.
-// The reduction over n runs in LDS chunks of `chunk_pairs` pairs (128 inputs
-// each, at most LB_WAVES * LB_MAXPV); each wave takes a contiguous eighth of
-// a chunk and holds all its sign words in registers.
+// The sign words are loaded in batches of LB_WAVES * LB_MAXPV pairs (128
+// inputs each; one batch covers n <= 8192): wave w holds pairs
+// w, w + 8, w + 16, ... of the batch in registers.  The reduction runs over
+// LDS chunks of `chunk_pairs` pairs (a multiple of 8 unless one chunk covers
+// the tile), so each wave has the same number of pairs in every chunk and a
+// batch's words are waited for once, whatever the number of chunks.
 // With HOOK, `hook` runs after the first chunk's matrix steps are issued, i.e.
 // once this tile's sign words have arrived, so its loads do not compete with
 // them for memory.  The first chunk is its
@@ -223,73 +227,62 @@ struct BoolTag {
 // Geometry of this thread's part of the V pass over one 16-row tile of
 // branch b of layer L.
 struct VGeom {
-  const uint16_t* xr;       // x row of this thread's token (building u)
+  const uint16_t* x;        // token t's activations at x + t * ldx
   const uint16_t* g;
   const uint8_t* tile_ptr;  // the tile's packed sign words
+  long ldx;
   int n, nu, np;
-  int tpt, my_tok, my_sub;  // threads per token building u, and this thread's token and share
   bool fast;                // 16-byte loads of x and g
 };
 
 // Reads only the fields a caller may know before the rest of the arguments:
 // the factor's sign words (vb0, vb1), x, ldx, g0, g1 and n.
-__device__ __forceinline__ VGeom v_geom(const LayerView& L, int batch, int b, int tile) {
+__device__ __forceinline__ VGeom v_geom(const LayerView& L, int b, int tile) {
   VGeom G;
-  const int tid = threadIdx.x;
   G.n = L.n;
   G.g = b ? L.g1 : L.g0;
   G.nu = lb16_units(G.n);
   G.np = (G.nu + 1) >> 1;
   G.tile_ptr = (b ? L.vb1 : L.vb0) + (long)tile * lb16_tile_bytes(G.n);
-  int lb = 0;
-  while ((1 << lb) < batch) ++lb;
-  static_assert(LB_THREADS == 512, "token split assumes 512 threads");
-  G.tpt = LB_THREADS >> lb;
-  G.my_tok = tid >> (9 - lb);
-  G.my_sub = tid & (G.tpt - 1);
   // 16-byte loads of x and g when aligned and n % 8 == 0 (then a group of 8
   // inputs is either wholly below n or wholly at/after it)
   G.fast = ((((uintptr_t)L.x) & 15) == 0) && ((L.ldx & 7) == 0) && ((G.n & 7) == 0);
-  G.xr = L.x + (long)min(G.my_tok, batch - 1) * L.ldx;
+  G.x = L.x;
+  G.ldx = L.ldx;
   return G;
 }
 
-// x and g of inputs k..k+7 (zero at and beyond n)
-__device__ __forceinline__ void v_load_xg(const VGeom& G, int k, uint4& xv, uint4& gv) {
-  if (G.fast) {
-    const int kk = min(k, G.n - 8);  // always-valid address; zeroed by the caller when k >= n
-    xv = *reinterpret_cast<const uint4*>(G.xr + kk);
-    gv = *reinterpret_cast<const uint4*>(G.g + kk);
-  } else {
-    uint16_t xe[8], ge[8];
-    for (int e = 0; e < 8; ++e) {
-      xe[e] = (k + e < G.n) ? G.xr[k + e] : (uint16_t)0;
-      ge[e] = (k + e < G.n) ? G.g[k + e] : (uint16_t)0;
-    }
-    xv = *reinterpret_cast<uint4*>(xe);
-    gv = *reinterpret_cast<uint4*>(ge);
-  }
+// Inputs k..k+7 of a row of x or of g: with 16-byte loads (fast) from an
+// always-valid address, zeroed by the caller when k >= n; else one by one,
+// zero at and beyond n.
+__device__ __forceinline__ uint4 v_load8(const VGeom& G, const uint16_t* row, int k) {
+  if (G.fast) return *reinterpret_cast<const uint4*>(row + min(k, G.n - 8));
+  uint16_t e8[8];
+  for (int e = 0; e < 8; ++e) e8[e] = (k + e < G.n) ? row[k + e] : (uint16_t)0;
+  return *reinterpret_cast<uint4*>(e8);
 }
 
-// The loads that open a chunk of V pairs [cb, cb + chunk_pairs) of a tile:
-// this thread's first group of activations, then the wave's sign words (the
-// activations come first, so waiting for them leaves the words in flight).
+// The loads that open the batch of V pairs starting at pair wb of a tile:
+// this thread's first group of inputs of the batch's first chunk (token 0's
+// x and g), then
+// the wave's sign words, pair wb + wave + 8 i in slot i (the activations come
+// first, so waiting for them leaves the words in flight).
 struct VLoads {
   uint4 xv0, gv0;
   uint32_t words[LB_MAXPV];
 };
 
-__device__ __forceinline__ void v_issue(const VGeom& G, int cb, int chunk_pairs, VLoads& R) {
+__device__ __forceinline__ void v_issue(const VGeom& G, int wb, int chunk_pairs, VLoads& R) {
   const int lane = threadIdx.x & 63, wave = wave_id();
-  const int cn = min(G.np - cb, chunk_pairs);
-  const int pb = cb + ((cn * wave) >> 3), pe = cb + ((cn * (wave + 1)) >> 3);
-  const int kc = 128 * cn;
-  v_load_xg(G, 128 * cb + 8 * min(G.my_sub, (kc >> 3) - 1), R.xv0, R.gv0);
-  // unconditional loads (clamped to a valid pair) keep the wait counts
-  // exact; pairs beyond pe are never used
-  const int plast = max(pe - 1, 0);
+  const int cn = min(G.np - wb, chunk_pairs);
+  const int k = 128 * wb + 8 * min((int)threadIdx.x, 16 * cn - 1);
+  R.xv0 = v_load8(G, G.x, k);  // token 0
+  R.gv0 = v_load8(G, G.g, k);
+  // unconditional loads (clamped to the tile's last pair) keep the wait
+  // counts exact; slots beyond the tile are never used
 #pragma unroll
-  for (int i = 0; i < LB_MAXPV; ++i) R.words[i] = lb16_load_pair(G.tile_ptr, min(pb + i, plast), lane, G.nu);
+  for (int i = 0; i < LB_MAXPV; ++i)
+    R.words[i] = lb16_load_pair(G.tile_ptr, min(wb + wave + 8 * i, G.np - 1), lane, G.nu);
 }
 
 // Stores one V tile's z (zstage: [token][16 rows] fp16, in LDS) as tagged
@@ -325,13 +318,14 @@ __device__ __forceinline__ void v_store_z(const LayerView& L, int batch, int b, 
 // chunk's loads were issued by the caller (`early`, from v_issue with the
 // same geometry).  reuse_u: u_lds already holds this tile's u (the previous
 // tile had the same layer and branch, and one chunk covers the reduction).
-// DEFER: z is left in zstage for the caller to store (v_store_z).
-template <bool HOOK, bool EARLY, bool DEFER = false, class Hook>
+// DEFER: z is left in zstage for the caller to store (v_store_z).  MAXB:
+// the most tokens a call may have (1, or LB_MAX_BATCH).
+template <int MAXB, bool HOOK, bool EARLY, bool DEFER = false, class Hook>
 __device__ __forceinline__ void v_tile(const LayerView& L, int batch, int b, int tile, int chunk_pairs,
                                        const uint32_t& ctr, const LbSignConsts& sc, uint16_t* u_lds,
                                        float (*red)[256], uint32_t* zstage, Hook&& hook, const VLoads& early,
                                        bool reuse_u = false) {
-  const VGeom G = v_geom(L, batch, b, tile);
+  const VGeom G = v_geom(L, b, tile);
   const int n = G.n, nu = G.nu, np = G.np;
   const int r = b ? L.r1 : L.r0;
 
@@ -343,25 +337,47 @@ __device__ __forceinline__ void v_tile(const LayerView& L, int batch, int b, int
   uint32_t lj_raw = 0;  // fp16 bits of l[j]
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  auto chunk = [&](int cb, const VLoads& R, auto with_hook) {
-    const int cn = min(np - cb, chunk_pairs);
-    const int pb = cb + ((cn * wave) >> 3), pe = cb + ((cn * (wave + 1)) >> 3);
-    const int k0 = 128 * cb, kc = 128 * cn;
+  // u = fp16(g*x) of inputs k0 + 8 k8 .. + 7 of this thread's token, to LDS
+  // (an fp16 product rounds the exact product once, as fp32 then fp16 would)
+  auto u_put = [&](int t, int k0, int rowh, int k8, uint4 xv, uint4 gv) {
+    if (G.fast && k0 + 8 * k8 >= n) xv = gv = make_uint4(0u, 0u, 0u, 0u);
+    const f16x8 u = __builtin_bit_cast(f16x8, xv) * __builtin_bit_cast(f16x8, gv);
+    *reinterpret_cast<f16x8*>(u_lds + t * rowh + 8 * k8) = u;
+  };
+  // chunk of pairs [cb, cb + cn) of the batch that starts at wb (cb - wb is a
+  // multiple of 8); first: R.xv0/gv0 hold this thread's first group of
+  // token 0.  Thread i builds groups i, i + 512, ... of every token (one load
+  // of g serves all tokens; all of a group's loads are issued before use).
+  constexpr int WB = LB_WAVES * LB_MAXPV;
+  auto chunk = [&](int wb, int cb, const VLoads& R, bool first, auto with_hook) {
+    const int cn = min(min(np, wb + WB) - cb, chunk_pairs);
+    const int k0 = 128 * cb, kc = 128 * cn, ng = kc >> 3;
     const int rowh = kc + 8;
     if (!reuse_u) {
       __syncthreads();  // previous users of u_lds are done
-      if (G.my_tok < batch) {
-        uint4 xv = R.xv0, gv = R.gv0;
-        for (int k8 = G.my_sub; k8 < (kc >> 3); k8 += G.tpt) {
+      int k8 = tid;
+      if (first && batch == 1 && k8 < ng) {
+        u_put(0, k0, rowh, k8, R.xv0, R.gv0);
+        k8 += LB_THREADS;
+      }
+      if (G.fast) {
+        for (; k8 < ng; k8 += LB_THREADS) {
           const int k = k0 + 8 * k8;
-          if (k8 != G.my_sub) v_load_xg(G, k, xv, gv);
-          if (G.fast && k >= n) xv = gv = make_uint4(0u, 0u, 0u, 0u);
-          const uint16_t* xe = reinterpret_cast<const uint16_t*>(&xv);
-          const uint16_t* ge = reinterpret_cast<const uint16_t*>(&gv);
-          uint16_t vals[8];
+          const uint4 gv = v_load8(G, G.g, k);
+          uint4 xs[MAXB];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) vals[e] = f2h(h2f(ge[e]) * h2f(xe[e]));
-          *reinterpret_cast<uint4*>(u_lds + G.my_tok * rowh + 8 * k8) = *reinterpret_cast<uint4*>(vals);
+          for (int t = 0; t < MAXB; ++t)
+            xs[t] = t < batch ? v_load8(G, G.x + t * G.ldx, k) : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+          for (int t = 0; t < MAXB; ++t)
+            if (t < batch) u_put(t, k0, rowh, k8, xs[t], gv);
+        }
+      } else {
+        for (; k8 < ng; k8 += LB_THREADS) {
+          const int k = k0 + 8 * k8;
+          const uint4 gv = v_load8(G, G.g, k);
+#pragma unroll 1
+          for (int t = 0; t < batch; ++t) u_put(t, k0, rowh, k8, v_load8(G, G.x + t * G.ldx, k), gv);
         }
       }
       __syncthreads();
@@ -379,16 +395,19 @@ __device__ __forceinline__ void v_tile(const LayerView& L, int batch, int b, int
     // inputs beyond n are zero in LDS, so the odd last unit's two missing
     // steps contribute nothing and every pair runs all 4 steps; the next
     // pair's operands are read from LDS while the current pair computes
+    // this wave's pairs in the chunk: slots i0, i0 + 1, ... while below pe
+    const int i0 = (cb - wb) >> 3, pe = cb + cn;
     const uint16_t* ub = u_lds + trow * rowh + 8 * grp - k0;
     f16x8 bv[4];
+    const int pf = min(wb + wave + 8 * i0, pe - 1);
 #pragma unroll
-    for (int st = 0; st < 4; ++st) bv[st] = *reinterpret_cast<const f16x8*>(ub + 32 * (4 * pb + st));
+    for (int st = 0; st < 4; ++st) bv[st] = *reinterpret_cast<const f16x8*>(ub + 32 * (4 * pf + st));
 #pragma unroll
     for (int i = 0; i < LB_MAXPV; ++i) {
-      const int p = pb + i;
-      if (p < pe) {
+      const int p = wb + wave + 8 * i;
+      if (i >= i0 && p < pe) {
         f16x8 bn[4];
-        const int pn = (p + 1 < pe) ? p + 1 : p;
+        const int pn = (p + 8 < pe) ? p + 8 : p;
 #pragma unroll
         for (int st = 0; st < 4; ++st) bn[st] = *reinterpret_cast<const f16x8*>(ub + 32 * (4 * pn + st));
         // late(): the expansion is not hoisted above this point (it would hold
@@ -403,20 +422,23 @@ __device__ __forceinline__ void v_tile(const LayerView& L, int batch, int b, int
       }
     }
   };
-  int cb0 = 0;
-  if constexpr (EARLY) {
-    chunk(0, early, BoolTag<HOOK>());
-    cb0 = chunk_pairs;
-  } else if constexpr (HOOK) {
-    VLoads R;
-    v_issue(G, 0, chunk_pairs, R);
-    chunk(0, R, BoolTag<true>());
-    cb0 = chunk_pairs;
+  // with a hook or early loads the first chunk is its own copy of the code;
+  // the rest run in one loop, which issues a batch's loads at its first chunk
+  VLoads R;
+  int wb = 0, cb = 0;
+  auto advance = [&]() {
+    cb += chunk_pairs;
+    if (cb >= min(np, wb + WB)) cb = wb = wb + WB;
+  };
+  if constexpr (EARLY || HOOK) {
+    if constexpr (EARLY) R = early;
+    else v_issue(G, 0, chunk_pairs, R);
+    chunk(0, 0, R, true, BoolTag<HOOK>());
+    advance();
   }
-  for (int cb = cb0; cb < np; cb += chunk_pairs) {
-    VLoads R;
-    v_issue(G, cb, chunk_pairs, R);
-    chunk(cb, R, BoolTag<false>());
+  for (; cb < np; advance()) {
+    if (cb == wb) v_issue(G, wb, chunk_pairs, R);
+    chunk(wb, cb, R, false, BoolTag<false>());
   }
   acc += acc1;
 
@@ -883,7 +905,8 @@ __device__ __forceinline__ void u_span_lds(const LayerView& L, int li, int batch
 
 // MODE 0: phase A only; 1: phase B only; 2: both in one launch (z tagged and
 // polled).  SINGLE: one layer.  Workgroup w takes a contiguous range of the V
-// tiles and of the U tiles.
+// tiles and of the U tiles.  MAXB: the most tokens (1, or LB_MAX_BATCH: a
+// separate build, so the single-token kernel keeps its registers).
 //
 // The leading arguments are preloaded into scalar registers by the dispatch
 // (kernel-argument preloading), so a single-layer kernel issues its first
@@ -891,7 +914,7 @@ __device__ __forceinline__ void u_span_lds(const LayerView& L, int li, int batch
 // They repeat fields of A.L[0]; the multi-layer kernel ignores them.
 //   misc = vq | vr << 8 | batch << 16 | chunk_pairs << 21  (V tiles of
 //          workgroup w: vq + (w < vr), contiguous)
-template <int MODE, bool SINGLE, bool UPRE>
+template <int MODE, bool SINGLE, bool UPRE, int MAXB = 1>
 __global__ __launch_bounds__(LB_THREADS) void lb_decode_kernel(
     const uint8_t* pre_vb0, const uint8_t* pre_vb1, const uint16_t* pre_x, const uint16_t* pre_g0,
     const uint16_t* pre_g1, int pre_n, int pre_ldx, int pre_vsplit, uint32_t pre_misc,
@@ -924,7 +947,7 @@ __global__ __launch_bounds__(LB_THREADS) void lb_decode_kernel(
       P.n = pre_n;
       P.ldx = pre_ldx;
       const int b = vt0 >= pre_vsplit ? 1 : 0;
-      v_issue(v_geom(P, (int)((pre_misc >> 16) & 31u), b, vt0 - (b ? pre_vsplit : 0)), 0, (int)(pre_misc >> 21),
+      v_issue(v_geom(P, b, vt0 - (b ? pre_vsplit : 0)), 0, (int)(pre_misc >> 21),
               early);
     }
   }
@@ -1013,11 +1036,11 @@ __global__ __launch_bounds__(LB_THREADS) void lb_decode_kernel(
       load_ctr();
       prefetch();
     };
-    v_tile<MODE == 2, EARLY>(V0, batch, k & 1, tile, chunk_pairs, ctr, sc, u_lds, red[0], zstage, first_hook, early);
+    v_tile<MAXB, MODE == 2, EARLY>(V0, batch, k & 1, tile, chunk_pairs, ctr, sc, u_lds, red[0], zstage, first_hook, early);
     __syncthreads();
     for (int t = vt0 + 1; t < vt1; ++t) {
       const int kt = v_slot<SINGLE>(M, pre_vsplit, t, tile);
-      v_tile<false, false>(V0, batch, kt & 1, tile, chunk_pairs, ctr, sc, u_lds, red[0], zstage, prefetch, early);
+      v_tile<MAXB, false, false>(V0, batch, kt & 1, tile, chunk_pairs, ctr, sc, u_lds, red[0], zstage, prefetch, early);
       __syncthreads();
     }
   } else if (vt0 < vt1) {
@@ -1031,14 +1054,14 @@ __global__ __launch_bounds__(LB_THREADS) void lb_decode_kernel(
     int tile;
     int k = v_slot<SINGLE>(M, pre_vsplit, vt0, tile);
     VLoads cur;
-    v_issue(v_geom(layer_view(A.L[k >> 1]), batch, k & 1, tile), 0, chunk_pairs, cur);
+    v_issue(v_geom(layer_view(A.L[k >> 1]), k & 1, tile), 0, chunk_pairs, cur);
     int prev_k = -1, prev_tile = 0;
     for (int t = vt0; t < vt1; ++t) {
       int ntile = 0;
       const int nk = t + 1 < vt1 ? v_slot<SINGLE>(M, pre_vsplit, t + 1, ntile) : -1;
       VLoads nxt;
       auto hook = [&]() {
-        if (nk >= 0) v_issue(v_geom(layer_view(A.L[nk >> 1]), batch, nk & 1, ntile), 0, chunk_pairs, nxt);
+        if (nk >= 0) v_issue(v_geom(layer_view(A.L[nk >> 1]), nk & 1, ntile), 0, chunk_pairs, nxt);
         if (t == vt0) load_ctr();
         if (prev_k >= 0)
           v_store_z(layer_view(A.L[prev_k >> 1]), batch, prev_k & 1, prev_tile, late(ctr) + 1u, zst[(t - vt0 + 1) & 1]);
@@ -1046,7 +1069,7 @@ __global__ __launch_bounds__(LB_THREADS) void lb_decode_kernel(
       };
       const LayerView L = layer_view(A.L[k >> 1]);
       const bool reuse_u = k == prev_k && ((lb16_units(L.n) + 1) >> 1) <= chunk_pairs;
-      v_tile<true, true, true>(L, batch, k & 1, tile, chunk_pairs, ctr, sc, u_lds, red[0], zst[(t - vt0) & 1], hook,
+      v_tile<MAXB, true, true, true>(L, batch, k & 1, tile, chunk_pairs, ctr, sc, u_lds, red[0], zst[(t - vt0) & 1], hook,
                                cur, reuse_u);
       __syncthreads();
       prev_k = k;
@@ -1198,7 +1221,27 @@ static void cost_split(LbDecodeArgs& a, int G) {
   balanced_split(c.data(), (int)c.size(), G, a.ut_begin);
 }
 
-template <bool SINGLE>
+// Smallest per-CU occupancy of the single-launch kernels of one token limit.
+template <int MAXB>
+static hipError_t fused_occupancy(int& occ) {
+  int o[4] = {0, 0, 0, 0};
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o[0], lb_decode_kernel<2, true, false, MAXB>,
+                                                              LB_THREADS, LB_DECODE_LDS_MAX);
+  if (e == hipSuccess)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o[1], lb_decode_kernel<2, false, false, MAXB>, LB_THREADS,
+                                                     LB_DECODE_LDS_MAX);
+  if (e == hipSuccess)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o[2], lb_decode_kernel<2, true, true, MAXB>, LB_THREADS,
+                                                     LB_UPRE_DYN_MAX);
+  if (e == hipSuccess)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o[3], lb_decode_kernel<2, false, true, MAXB>, LB_THREADS,
+                                                     LB_UPRE_DYN_MAX);
+  occ = o[0];
+  for (int i = 1; i < 4; ++i) occ = o[i] < occ ? o[i] : occ;
+  return e;
+}
+
+template <bool SINGLE, int MAXB>
 static hipError_t launch_decode_t(const LbDecodeArgs& args, int chunk_pairs, void* sync, int allow_fused,
                                   hipStream_t stream) {
   const size_t lds = lb_decode_lds_bytes(args, chunk_pairs);
@@ -1219,26 +1262,16 @@ static hipError_t launch_decode_t(const LbDecodeArgs& args, int chunk_pairs, voi
   };
   if (allow_fused && dev >= 0 && dev < 64) {
     if (g_fused_grid[dev] == 0) {
-      int ncu = 0, occ1 = 0, occ7 = 0;
+      int ncu = 0, occa = 0, occb = 0;
       e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
       if (e != hipSuccess) return e;
       // every workgroup of the single launch must be resident at once: size
       // the grid for the largest dynamic LDS a launch may request
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ1, lb_decode_kernel<2, true, false>, LB_THREADS,
-                                                       LB_DECODE_LDS_MAX);
+      e = fused_occupancy<1>(occa);
       if (e != hipSuccess) return e;
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ7, lb_decode_kernel<2, false, false>, LB_THREADS,
-                                                       LB_DECODE_LDS_MAX);
+      e = fused_occupancy<LB_MAX_BATCH>(occb);
       if (e != hipSuccess) return e;
-      int occ1p = 0, occ7p = 0;
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ1p, lb_decode_kernel<2, true, true>, LB_THREADS,
-                                                       LB_UPRE_DYN_MAX);
-      if (e != hipSuccess) return e;
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ7p, lb_decode_kernel<2, false, true>, LB_THREADS,
-                                                       LB_UPRE_DYN_MAX);
-      if (e != hipSuccess) return e;
-      g_fused_grid[dev] = (occ1 >= 1 && occ7 >= 1 && occ1p >= 1 && occ7p >= 1) ? (ncu < LB_MAX_GRID ? ncu : LB_MAX_GRID)
-                                                                                : -1;
+      g_fused_grid[dev] = (occa >= 1 && occb >= 1) ? (ncu < LB_MAX_GRID ? ncu : LB_MAX_GRID) : -1;
     }
     const int G = g_fused_grid[dev];
     if (G > 0) {
@@ -1256,17 +1289,17 @@ static hipError_t launch_decode_t(const LbDecodeArgs& args, int chunk_pairs, voi
         regs_hold = (np + (args.L[0].nb == 2 ? 3 : 7)) / (args.L[0].nb == 2 ? 4 : 8) <= LB_MAXPW;
       }
       if (lds <= LB_UPRE_DYN_MAX && !regs_hold)
-        hipLaunchKernelGGL((lb_decode_kernel<2, SINGLE, true>), dim3(G), dim3(LB_THREADS), lds, stream, vb0, vb1, px,
+        hipLaunchKernelGGL((lb_decode_kernel<2, SINGLE, true, MAXB>), dim3(G), dim3(LB_THREADS), lds, stream, vb0, vb1, px,
                            g0, g1, pn, pldx, vsplit, misc(a), a, chunk_pairs, (uint8_t*)sync);
       else
-        hipLaunchKernelGGL((lb_decode_kernel<2, SINGLE, false>), dim3(G), dim3(LB_THREADS), lds, stream, vb0, vb1, px,
+        hipLaunchKernelGGL((lb_decode_kernel<2, SINGLE, false, MAXB>), dim3(G), dim3(LB_THREADS), lds, stream, vb0, vb1, px,
                            g0, g1, pn, pldx, vsplit, misc(a), a, chunk_pairs, (uint8_t*)sync);
       return hipGetLastError();
     }
   }
   LbDecodeArgs a = args;
   a.vq = 1; a.vr = 0;
-  hipLaunchKernelGGL((lb_decode_kernel<0, SINGLE, false>), dim3(a.nvt), dim3(LB_THREADS), lds, stream, vb0, vb1, px, g0,
+  hipLaunchKernelGGL((lb_decode_kernel<0, SINGLE, false, MAXB>), dim3(a.nvt), dim3(LB_THREADS), lds, stream, vb0, vb1, px, g0,
                      g1, pn, pldx, vsplit, misc(a), a, chunk_pairs, (uint8_t*)sync);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1279,6 +1312,9 @@ static hipError_t launch_decode_t(const LbDecodeArgs& args, int chunk_pairs, voi
 
 hipError_t lb_launch_decode(const LbDecodeArgs& args, int chunk_pairs, void* sync, int allow_fused,
                             hipStream_t stream) {
-  return args.nlayers == 1 ? launch_decode_t<true>(args, chunk_pairs, sync, allow_fused, stream)
-                           : launch_decode_t<false>(args, chunk_pairs, sync, allow_fused, stream);
+  if (args.batch == 1)
+    return args.nlayers == 1 ? launch_decode_t<true, 1>(args, chunk_pairs, sync, allow_fused, stream)
+                             : launch_decode_t<false, 1>(args, chunk_pairs, sync, allow_fused, stream);
+  return args.nlayers == 1 ? launch_decode_t<true, LB_MAX_BATCH>(args, chunk_pairs, sync, allow_fused, stream)
+                           : launch_decode_t<false, LB_MAX_BATCH>(args, chunk_pairs, sync, allow_fused, stream);
 }

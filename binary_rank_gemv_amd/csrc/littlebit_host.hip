@@ -120,13 +120,19 @@ lb_status check_layer(const lb_layer* L, uint32_t mask, int* sel, int* nsel, con
   return LB_OK;
 }
 
-// Pairs (128 inputs each) of the decode V pass staged in LDS at once.
-int decode_chunk_pairs(int64_t batch, int n) {
+// Pairs (128 inputs each) of the decode V pass staged in LDS at once: a
+// multiple of 8 (every wave gets the same number of pairs per chunk), or all
+// the tile's pairs.  The budget is the larger of a fixed share and what phase
+// B's z takes (zs + 8 halves per token) in the same space anyway.
+int decode_chunk_pairs(int64_t batch, int n, int zs) {
   const int np = (lb16_units(n) + 1) / 2;
-  int cp = (int)((kDecodeLdsBudget / sizeof(uint16_t) / batch - 8) / 128);
-  cp = cp / 4 * 4;
+  size_t budget = (size_t)batch * (zs + 8) * sizeof(uint16_t);
+  if (budget < kDecodeLdsBudget) budget = kDecodeLdsBudget;
+  if (budget > LB_DECODE_LDS_MAX) budget = LB_DECODE_LDS_MAX;
+  int cp = (int)((budget / sizeof(uint16_t) / batch - 8) / 128);
+  cp = cp / 8 * 8;
   if (cp > kDecodeMaxChunkPairs) cp = kDecodeMaxChunkPairs;
-  if (cp < 4) cp = 4;
+  if (cp < 8) cp = 8;
   return cp >= np ? np : cp;
 }
 
@@ -185,9 +191,10 @@ lb_status run_decode(LbLayerArgs* layers, int nl, int batch, void* sync, int all
   memset(&args, 0, sizeof args);
   args.nlayers = nl;
   args.batch = batch;
-  int vt = 0, ut = 0, maxn = 1;
+  int vt = 0, ut = 0, maxn = 1, maxzs = 0;
   for (int i = 0; i < nl; ++i) {
     args.L[i] = layers[i];
+    if (layers[i].zs > maxzs) maxzs = layers[i].zs;
     for (int b = 0; b < 2; ++b) {
       if (b < layers[i].nb) vt += (layers[i].br[b].r + 15) / 16;
       args.vt_end[2 * i + b] = vt;
@@ -198,7 +205,7 @@ lb_status run_decode(LbLayerArgs* layers, int nl, int batch, void* sync, int all
   }
   args.nvt = vt;
   args.nut = ut;
-  const int cp = decode_chunk_pairs(batch, maxn);
+  const int cp = decode_chunk_pairs(batch, maxn, maxzs);
   hipError_t e = lb_launch_decode(args, cp, sync, allow_fused, stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return LB_OK;
