@@ -402,7 +402,7 @@ def main():
     achieved = abytes / (ms_per_step * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                "kernel": "lb_decode_kernel<2, true> (one launch per call: V pass, tagged z exchange, U pass)",
+                "kernel": "lb_decode_kernel<2, true, false, 1> (one launch per call: V pass, tagged z exchange, U pass)",
                 "algorithmic_bytes_per_call": abytes,
                 "avg_call_us": round(ms_per_step * 1e3, 3),
                 "two_launch_variant_us": round(ms_two / args.steps * 1e3, 3)}
