@@ -42,6 +42,20 @@ def algorithmic_bytes(m, n, ranks, batch):
     return bits // 8 + scales + 2 * batch * n + 2 * batch * m
 
 
+def time_eager(torch, call, steps, warmup):
+    """Milliseconds per call of `call` launched back to back (no graph)."""
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        call()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / steps
+
+
 def time_graph(torch, calls, steps, warmup):
     """Capture a HIP graph over one cycle of `calls` (plus remainders) and
     return milliseconds per call over `steps` timed calls."""
@@ -145,8 +159,31 @@ def extra_measurements(lb, torch, synth, args):
     out["prefill_7b_up_2048"] = {"us_per_call": round(ms * 1e3, 2), "tokens_per_s": round(M * 1e3 / ms, 1),
                                  "flops": flops, "tflops": round(tflops, 1),
                                  "mfma_util": round(tflops / FP16_MFMA_PEAK_TFLOPS, 4),
-                                 "peak_tflops": FP16_MFMA_PEAK_TFLOPS}
+                                 "peak_tflops": FP16_MFMA_PEAK_TFLOPS,
+                                 "dense_fp16_library": dense_gemm_context(torch, M, sh.n, sum(sh.ranks), sh.m)}
     return out
+
+
+def dense_gemm_context(torch, M, n, rsum, m):
+    """Context for the prefill figure: the same two contractions as plain
+    dense fp16 GEMMs through torch.matmul (the vendor GEMM library), with no
+    sign expansion, in the faster of two operand layouts each.  Not part of
+    the layer."""
+    res = {}
+    for name, (a_rows, k, b_cols) in (("gemm1", (M, n, rsum)), ("gemm2", (M, rsum, m))):
+        a = torch.randn((a_rows, k), device="cuda").half()
+        b_kn = torch.randn((k, b_cols), device="cuda").half()
+        b_nk = torch.randn((b_cols, k), device="cuda").half()
+        c = torch.empty((a_rows, b_cols), device="cuda", dtype=torch.float16)
+        best = min(time_eager(torch, lambda: torch.matmul(a, b_kn, out=c), 30, 5),
+                   time_eager(torch, lambda: torch.matmul(a, b_nk.t(), out=c), 30, 5))
+        res[name + "_us"] = round(best * 1e3, 2)
+        del a, b_kn, b_nk, c
+    total = res["gemm1_us"] + res["gemm2_us"]
+    flops = 2 * M * rsum * (n + m)
+    res["total_us"] = round(total, 2)
+    res["mfma_util"] = round(flops / (total * 1e-6) / 1e12 / FP16_MFMA_PEAK_TFLOPS, 4)
+    return res
 
 
 def make_copy(lb, torch, shape, seed):

@@ -99,6 +99,12 @@ def test_tiny_config_full_oracle(lb, batch, two_launches):
     (20000, 512, (1600,), 2),      # one branch, 5 tiles per workgroup
     (40000, 128, (96, 96), 5),     # batch 5: 9 tiles copied per workgroup, the rest from memory
     (600, 300, (3000, 3000), 13),  # z of 13 tokens exceeds the LDS: launches of 9 and 4 tokens
+    # phase A's staging of g*x: n % 8 != 0 (element-wise loads), and n > 8192
+    # (a second batch of sign words, a chunk cut at the batch's end)
+    (90, 130, (24, 40), 3),
+    (64, 1001, (32,), 1),
+    (256, 9000, (48, 48), 4),
+    (200, 9001, (40, 24), 16),
 ])
 def test_ragged_shapes(lb, m, n, ranks, batch):
     print(f"[case] ragged m={m} n={n} r={ranks} batch={batch}", flush=True)
@@ -110,6 +116,23 @@ def test_ragged_shapes(lb, m, n, ranks, batch):
     _assert_parity(y, oracle.linear_forward(x, br), f"ragged {m}x{n} r={ranks} b={batch}")
     # the single launch and the two-launch path sum in the same order
     assert torch.equal(y, lb.littlebit_linear_fwd(layer, xt, path=lb.LB_DECODE_TWO_LAUNCHES))
+
+
+@pytest.mark.parametrize("batch", [1, 5, 16])
+def test_unaligned_activations(lb, batch):
+    """x as a view whose rows start 2 bytes past a 16-byte boundary and whose
+    row stride is odd: phase A stages g*x with element-wise loads."""
+    print(f"[case] unaligned x batch={batch}", flush=True)
+    shape = synth.LayerShape("unaligned", 300, 520, (40, 56))
+    br, x = synth.make_layer(shape, batch=batch, seed=11)
+    layer = _layer(lb, br)
+    big = torch.zeros((batch, 521), dtype=torch.float16, device="cuda")
+    big[:, 1:] = torch.from_numpy(x).cuda()
+    xv = big[:, 1:]
+    assert xv.data_ptr() % 16 == 2 and xv.stride(0) == 521
+    y = lb.littlebit_linear_fwd(layer, xv)
+    _assert_parity(y, oracle.linear_forward(x, br), f"unaligned x b={batch}")
+    assert torch.equal(y, lb.littlebit_linear_fwd(layer, torch.from_numpy(x).cuda()))
 
 
 def test_branch_masks_and_additivity(lb):
