@@ -30,7 +30,8 @@
 #define LB_THREADS (64 * LB_WAVES)
 #define LB_MAXPV 8                    // V-pass pairs per wave held in registers
 #define LB_MAXT 3                     // phase-B tiles whose sign words are prefetched
-#define LB_MAXPW 3                    // phase-B pairs per wave held in registers
+#define LB_MAXPW 3                    // phase-B pairs per wave held in registers (1-token kernels)
+#define LB_MAXPW_MULTI 4              // the same, kernels for up to LB_MAX_BATCH tokens
 #define LB_UPRE_BYTES (64 * 1024)     // LDS for a workgroup's phase-B sign bytes (single launch)
 #define LB_UPRE_OPS 8                 // 1 KB global-to-LDS loads per wave filling it
 #define LB_UPRE_HROWS 512             // row scales of the copied tiles (an LDS table)
@@ -460,8 +461,9 @@ __device__ __forceinline__ void v_tile(const LayerView& L, int batch, int b, int
 
 // ------------------------------------------------------------------ phase B
 // Prefetched per-tile data: this wave's sign words.
+template <int NPW>
 struct UTilePre {
-  uint32_t w[LB_MAXPW];
+  uint32_t w[NPW];
 };
 
 // Row scales (h of both branches, fp16 bits: converting here would wait for
@@ -479,7 +481,8 @@ __device__ __forceinline__ void load_h(const LayerView& L, int tile, HPre& H, in
   H.h1[j] = (L.nb == 2 ? L.h1 : L.h0)[i];
 }
 
-__device__ __forceinline__ void u_prefetch(const LayerView& L, int tile, UTilePre& P) {
+template <int NPW>
+__device__ __forceinline__ void u_prefetch(const LayerView& L, int tile, UTilePre<NPW>& P) {
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   int b, p0, p1;
   u_role(L, wave, b, p0, p1);
@@ -488,7 +491,7 @@ __device__ __forceinline__ void u_prefetch(const LayerView& L, int tile, UTilePr
   const uint8_t* tp = (b ? L.ub1 : L.ub0) + (long)tile * lb16_tile_bytes(r);
   const int plast = max(p1 - 1, 0);
 #pragma unroll
-  for (int i = 0; i < LB_MAXPW; ++i) P.w[i] = lb16_load_pair(tp, min(p0 + i, plast), lane, nu);
+  for (int i = 0; i < NPW; ++i) P.w[i] = lb16_load_pair(tp, min(p0 + i, plast), lane, nu);
 }
 
 // Phase-B role of a wave for the layer whose z is staged in LDS.
@@ -760,8 +763,10 @@ __device__ __forceinline__ YOut u_finish(const LayerView& L, int batch, int tile
 // Phase B for nt <= LB_MAXT consecutive U tiles (from tile0) of layer L, whose
 // sign words and row scales are in P[0..nt): the matrix steps of all tiles
 // run interleaved, then one epilogue (one pair of barriers) finishes them all.
+// NPW pairs per wave are in registers; any further pairs are loaded here.
+template <int NPW>
 __device__ __forceinline__ YOut u_group(const LayerView& L, int li, int batch, int tile0, int nt,
-                                        const UTilePre (&P)[LB_MAXT], const HPre& H, uint32_t ctr, bool check,
+                                        const UTilePre<NPW> (&P)[LB_MAXT], const HPre& H, uint32_t ctr, bool check,
                                         uint8_t* sync,
                                         const LbSignConsts& sc, UState& S, uint16_t* zl,
                                         float (*red)[LB_WAVES][256]) {
@@ -776,7 +781,7 @@ __device__ __forceinline__ YOut u_group(const LayerView& L, int li, int batch, i
 #pragma unroll
   for (int k = 0; k < LB_MAXT; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < LB_MAXPW; ++i) {
+  for (int i = 0; i < NPW; ++i) {
     const int p = S.p0 + i;
     if (p < S.p1) {
       const uint32_t sel = lb16_pair_sel(p, lane, S.nu);
@@ -796,10 +801,10 @@ __device__ __forceinline__ YOut u_group(const LayerView& L, int li, int batch, i
       }
     }
   }
-  // pairs beyond the register window (ranks above 64 * 4 * LB_MAXPW per wave)
-  if (S.p1 > S.p0 + LB_MAXPW) {
+  // pairs beyond the register window (ranks above 64 * 4 * NPW per wave)
+  if (S.p1 > S.p0 + NPW) {
     const int r = S.b ? L.r1 : L.r0;
-    for (int p = S.p0 + LB_MAXPW; p < S.p1; ++p) {
+    for (int p = S.p0 + NPW; p < S.p1; ++p) {
       const uint32_t sel = lb16_pair_sel(p, lane, S.nu);
       uint32_t w[LB_MAXT];
 #pragma unroll
@@ -988,7 +993,9 @@ __global__ __launch_bounds__(LB_THREADS) void lb_decode_kernel(
   auto load_ctr = [&]() {
     if (MODE == 2) ctr = ld32c(sync + LB_SYNC_CTR + 8 * wg);
   };
-  UTilePre pre[LB_MAXT];
+  // phase-B pairs per wave in registers
+  constexpr int NPW = MAXB > 1 ? LB_MAXPW_MULTI : LB_MAXPW;
+  UTilePre<NPW> pre[LB_MAXT];
   HPre hpre;
   UPrePlan plan;
   plan.split = plan.cover = 0;
@@ -1136,7 +1143,7 @@ __global__ __launch_bounds__(LB_THREADS) void lb_decode_kernel(
       const int lend = SINGLE ? ut1 : min(ut1, layer_u_end(M, li));
       const int nt = min(LB_MAXT, lend - t);
       const LayerView L = SINGLE ? V0 : layer_view(A.L[li]);
-      UTilePre p[LB_MAXT];
+      UTilePre<NPW> p[LB_MAXT];
 #pragma unroll
       for (int k = 0; k < LB_MAXT; ++k) u_prefetch(L, tile + min(k, nt - 1), p[k]);
       HPre h;
@@ -1282,7 +1289,8 @@ static hipError_t launch_decode_t(const LbDecodeArgs& args, int chunk_pairs, voi
       // the variant that copies phase B's sign bytes to LDS during phase A,
       // when the dynamic LDS leaves room for the copy and a workgroup's U
       // tiles are more than the register prefetch holds (one group of
-      // LB_MAXT tiles of one layer, LB_MAXPW pairs per wave)
+      // LB_MAXT tiles of one layer, LB_MAXPW pairs per wave: the 1-token
+      // window, which the multi-token kernels' window contains)
       bool regs_hold = SINGLE && (a.nut + G - 1) / G <= LB_MAXT;
       for (int b = 0; b < args.L[0].nb && regs_hold; ++b) {
         const int np = (lb16_units(args.L[0].br[b].r) + 1) >> 1;
