@@ -504,6 +504,7 @@ struct UState {
 // batches, 8 (fewer registers to set up) when the range is at most that
 #define LB_POLL_LOADS 24
 #define LB_POLL_LOADS_SMALL 8
+#define LB_POLL_LOADS_MULTI 32  // multi-token kernels
 
 // Copies the steps [s0, s1) of a wave's range of layer L's z into LDS (zl:
 // [token][zs + 8] fp16), polling (check) until every word carries this call's
@@ -560,7 +561,8 @@ __device__ __forceinline__ void u_copy_z(const LayerView& L, int batch, uint32_t
         }
       }
     }
-    uint32_t todo = (1u << nj) - 1u;  // loads of this batch still to read
+    static_assert(NL <= 32, "one bit per load");
+    uint32_t todo = nj >= 32 ? ~0u : (1u << nj) - 1u;  // loads of this batch still to read
     u32x4 q[NL];
     int spins = 0;
     for (;;) {
@@ -598,7 +600,10 @@ __device__ __forceinline__ void u_copy_z(const LayerView& L, int batch, uint32_t
 }
 
 // Copies this wave's range of layer L's z into LDS (u_copy_z), after taking
-// the wave's phase-B role for the layer.
+// the wave's phase-B role for the layer.  NLB: loads per lane per pass for a
+// large range (the multi-token kernels take more, so 16 tokens of a 4-pair
+// range need one pass batch, not two).
+template <int NLB = LB_POLL_LOADS>
 __device__ __forceinline__ void u_enter_layer(const LayerView& L, int li, int batch, uint32_t ctr, bool check,
                                               uint8_t* sync, UState& S, uint16_t* zl) {
   const int wave = wave_id();
@@ -615,7 +620,7 @@ __device__ __forceinline__ void u_enter_layer(const LayerView& L, int li, int ba
   if (!check || batch * 8 * (s1 - s0) <= 64 * LB_POLL_LOADS_SMALL)
     u_copy_z<LB_POLL_LOADS_SMALL>(L, batch, tag, check, sync, S, zl, s0, s1);
   else
-    u_copy_z<LB_POLL_LOADS>(L, batch, tag, check, sync, S, zl, s0, s1);
+    u_copy_z<NLB>(L, batch, tag, check, sync, S, zl, s0, s1);
 }
 
 // ---------------------------------------------- phase-B sign bytes in LDS
@@ -772,7 +777,7 @@ __device__ __forceinline__ YOut u_group(const LayerView& L, int li, int batch, i
                                         float (*red)[LB_WAVES][256]) {
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int tok = lane & 15, grp = lane >> 4;
-  if (li != S.li) u_enter_layer(L, li, batch, ctr, check, sync, S, zl);
+  if (li != S.li) u_enter_layer<(NPW == LB_MAXPW ? LB_POLL_LOADS : LB_POLL_LOADS_MULTI)>(L, li, batch, ctr, check, sync, S, zl);
   // operand rows: absent tokens read the last token's row (never stored)
   const uint16_t* zb = zl + min(tok, batch - 1) * (L.zs + 8) + (S.b ? L.zoff1 : L.zoff0) + 8 * grp;
   const int s1 = 2 * S.nu;  // steps of the branch that hold data
@@ -836,13 +841,15 @@ __device__ __forceinline__ YOut u_group(const LayerView& L, int li, int batch, i
 // time, and leaves its sums in `part` ([wave][tile][row][token], no barrier);
 // one barrier, then every output is y = h_0 * (sum over branch-0 waves) +
 // h_1 * (sum over branch-1 waves), the sums taken in wave order as in u_group.
+// NLB: as for u_enter_layer.
+template <int NLB>
 __device__ __forceinline__ void u_span_lds(const LayerView& L, int li, int batch, int tile0, int T, int span_max,
                                            const uint8_t* w0, const uint8_t* w1, int tb0, int tb1, const uint16_t* hl,
                                            uint32_t ctr, bool check, uint8_t* sync, const LbSignConsts& sc, UState& S,
                                            uint16_t* zl, float* part) {
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int tok = lane & 15, grp = lane >> 4;
-  if (li != S.li) u_enter_layer(L, li, batch, ctr, check, sync, S, zl);
+  if (li != S.li) u_enter_layer<NLB>(L, li, batch, ctr, check, sync, S, zl);
   const uint16_t* zb = zl + min(tok, batch - 1) * (L.zs + 8) + (S.b ? L.zoff1 : L.zoff0) + 8 * grp;
   const int s1 = 2 * S.nu;  // steps of the branch that hold data
   const uint8_t* wb = S.b ? w1 : w0;
@@ -1124,7 +1131,7 @@ __global__ __launch_bounds__(LB_THREADS) void lb_decode_kernel(
         const int tb0 = tile_bytes_b(L, 0), tb1 = tile_bytes_b(L, L.nb == 2 ? 1 : 0);
         const uint8_t* w0 = upre_lds + (slot ? plan.off[2] : plan.off[0]) + (t - first) * tb0;
         const uint8_t* w1 = upre_lds + (slot ? plan.off[3] : plan.off[1]) + (t - first) * tb1;
-        u_span_lds(L, li, batch, tile, T, span_max, w0, w1, tb0, tb1, hl_lds + 32 * (t - ut0), ctr, check, sync, sc, S,
+        u_span_lds<(MAXB > 1 ? LB_POLL_LOADS_MULTI : LB_POLL_LOADS)>(L, li, batch, tile, T, span_max, w0, w1, tb0, tb1, hl_lds + 32 * (t - ut0), ctr, check, sync, sc, S,
                    u_lds, &red[0][0][0]);
         t += T;
       }
