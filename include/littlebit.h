@@ -17,9 +17,11 @@
  *     (hipMalloc'd or torch CUDA tensors).  lb_layer / lb_branch structs and
  *     the y[] pointer array of littlebit_block_fwd live in HOST memory and are
  *     read only during the call.
- *   - The caller owns all memory.  The library never allocates, frees or
- *     synchronises; work is enqueued on `stream` (a hipStream_t, NULL = the
- *     default stream) and the call returns once it is enqueued.
+ *   - The caller owns all memory.  The layer and packing calls never
+ *     allocate, free or synchronise; work is enqueued on `stream` (a
+ *     hipStream_t, NULL = the default stream) and the call returns once it
+ *     is enqueued.  The one exception is the initialization,
+ *     littlebit_dual_svid_init (documented at its declaration).
  *   - fp16 data is IEEE binary16, passed as uint16_t.
  *   - Arguments are validated before anything is enqueued; on failure nothing
  *     is launched and a negative lb_status is returned.  littlebit_last_error
