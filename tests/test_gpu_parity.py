@@ -272,6 +272,24 @@ def test_70b_bpw_sweep_ranks(lb, bpw, batch):
     _full_size_check(lb, br, x, f"70B up {bpw} BPW b={batch}")
 
 
+@pytest.mark.parametrize("setting,batch", [("0.1", 16), ("0.55", 4)])
+def test_llama2_13b_block_several_tokens(lb, setting, batch):
+    """The multi-layer launch at several tokens (the multi-token kernels):
+    every projection against the oracle, and equal to the single-launch
+    per-layer call's sums order (two-launch path) bit for bit."""
+    print(f"[case] 13b block {setting} batch {batch}", flush=True)
+    shapes, layers, xs = synth.make_block13b(setting, batch=batch, seed=4)
+    dev_layers = [_layer(lb, br) for br in layers]
+    xt = [torch.from_numpy(a).cuda() for a in xs]
+    ys = lb.littlebit_block_fwd(dev_layers, *xt)
+    torch.cuda.synchronize()
+    for i, (shape, br) in enumerate(zip(shapes, layers)):
+        xi = synth.block_inputs_for(i, xs)
+        _assert_parity(ys[i], oracle.factored_forward(xi, br), f"13B {setting} b={batch} {shape.name}")
+        y2 = lb.littlebit_linear_fwd(dev_layers[i], torch.from_numpy(xi).cuda(), path=lb.LB_DECODE_TWO_LAUNCHES)
+        assert torch.equal(ys[i], y2), f"13B {setting} b={batch} {shape.name}: block and two-launch differ"
+
+
 @pytest.mark.parametrize("setting", ["0.55", "0.1"])
 def test_llama2_13b_block(lb, setting):
     print(f"[case] 13b block {setting}", flush=True)
