@@ -15,11 +15,13 @@
 // is stored as 64-bit words [32-bit call tag | two fp16 values] with
 // device-coherent stores, and phase B polls its z words until every tag
 // equals this call's tag, so there is no separate grid barrier.  The tag is
-// one more than a per-workgroup call counter in the workspace header, read at
-// kernel start and incremented by the workgroup as its last action (calls on
-// one stream run one after another, so every workgroup reads the same value).
+// one more than a per-workgroup call counter in the workspace header (never
+// 0), read at kernel start and incremented by the workgroup as its last action
+// (calls on one stream run one after another, so every workgroup reads the
+// same value).  The two-launch path stores z with tag 0, so a later single
+// launch never accepts its words.
 // Every word a call polls is written by that same call, so a stale word could
-// only pass if its address went unwritten for a multiple of 2^32 calls.  Each
+// only pass if its address went unwritten for a multiple of 2^32 - 1 calls.  Each
 // workgroup issues the loads of its phase-B sign words and row scales during
 // phase A, so their latency overlaps phase A.
 #include "lb_common.h"
@@ -69,6 +71,14 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) 
 // 16 bytes (two tagged z words) with a device-coherent (sc1) load.
 __device__ inline u32x4 ld_tagged2(__amdgpu_buffer_rsrc_t rs, int byte_off) {
   return __builtin_amdgcn_raw_buffer_load_b128(rs, byte_off, 0, 16 /* sc1 */);
+}
+
+// The z tag of a single-launch call from the workgroup's call counter: the
+// counter + 1, skipping 0 when the 32-bit value wraps.  Tag 0 marks z stored
+// by the two-launch path (phase A alone), so no poll ever accepts it.
+__device__ inline uint32_t call_tag(uint32_t ctr) {
+  const uint32_t t = ctr + 1u;
+  return t + (t == 0u ? 1u : 0u);
 }
 
 // Compiler-only barrier: memory may have changed here, so loads after it are
@@ -323,7 +333,7 @@ __device__ __forceinline__ void v_store_z(const LayerView& L, int batch, int b, 
 // the most tokens a call may have (1, or LB_MAX_BATCH).
 template <int MAXB, bool HOOK, bool EARLY, bool DEFER = false, class Hook>
 __device__ __forceinline__ void v_tile(const LayerView& L, int batch, int b, int tile, int chunk_pairs,
-                                       const uint32_t& ctr, const LbSignConsts& sc, uint16_t* u_lds,
+                                       const uint32_t& tag, const LbSignConsts& sc, uint16_t* u_lds,
                                        float (*red)[256], uint32_t* zstage, Hook&& hook, const VLoads& early,
                                        bool reuse_u = false) {
   const VGeom G = v_geom(L, b, tile);
@@ -456,7 +466,7 @@ __device__ __forceinline__ void v_tile(const LayerView& L, int batch, int b, int
     reinterpret_cast<uint16_t*>(zstage)[tk * 16 + rho] = __builtin_bit_cast(uint16_t, zv);
   }
   __syncthreads();
-  if constexpr (!DEFER) v_store_z(L, batch, b, tile, late(ctr) + 1u, zstage);
+  if constexpr (!DEFER) v_store_z(L, batch, b, tile, late(tag), zstage);
 }
 
 // ------------------------------------------------------------------ phase B
@@ -604,10 +614,10 @@ __device__ __forceinline__ void u_copy_z(const LayerView& L, int batch, uint32_t
 // large range (the multi-token kernels take more, so 16 tokens of a 4-pair
 // range need one pass batch, not two).
 template <int NLB = LB_POLL_LOADS>
-__device__ __forceinline__ void u_enter_layer(const LayerView& L, int li, int batch, uint32_t ctr, bool check,
+__device__ __forceinline__ void u_enter_layer(const LayerView& L, int li, int batch, uint32_t tag, bool check,
                                               uint8_t* sync, UState& S, uint16_t* zl) {
   const int wave = wave_id();
-  const uint32_t tag = late(ctr) + 1u;
+  tag = late(tag);
   __syncthreads();  // earlier readers of zl (previous layer, or phase A's u) are done
   S.li = li;
   u_role(L, wave, S.b, S.p0, S.p1);
@@ -771,13 +781,13 @@ __device__ __forceinline__ YOut u_finish(const LayerView& L, int batch, int tile
 // NPW pairs per wave are in registers; any further pairs are loaded here.
 template <int NPW>
 __device__ __forceinline__ YOut u_group(const LayerView& L, int li, int batch, int tile0, int nt,
-                                        const UTilePre<NPW> (&P)[LB_MAXT], const HPre& H, uint32_t ctr, bool check,
+                                        const UTilePre<NPW> (&P)[LB_MAXT], const HPre& H, uint32_t tag, bool check,
                                         uint8_t* sync,
                                         const LbSignConsts& sc, UState& S, uint16_t* zl,
                                         float (*red)[LB_WAVES][256]) {
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int tok = lane & 15, grp = lane >> 4;
-  if (li != S.li) u_enter_layer<(NPW == LB_MAXPW ? LB_POLL_LOADS : LB_POLL_LOADS_MULTI)>(L, li, batch, ctr, check, sync, S, zl);
+  if (li != S.li) u_enter_layer<(NPW == LB_MAXPW ? LB_POLL_LOADS : LB_POLL_LOADS_MULTI)>(L, li, batch, tag, check, sync, S, zl);
   // operand rows: absent tokens read the last token's row (never stored)
   const uint16_t* zb = zl + min(tok, batch - 1) * (L.zs + 8) + (S.b ? L.zoff1 : L.zoff0) + 8 * grp;
   const int s1 = 2 * S.nu;  // steps of the branch that hold data
@@ -845,11 +855,11 @@ __device__ __forceinline__ YOut u_group(const LayerView& L, int li, int batch, i
 template <int NLB>
 __device__ __forceinline__ void u_span_lds(const LayerView& L, int li, int batch, int tile0, int T, int span_max,
                                            const uint8_t* w0, const uint8_t* w1, int tb0, int tb1, const uint16_t* hl,
-                                           uint32_t ctr, bool check, uint8_t* sync, const LbSignConsts& sc, UState& S,
+                                           uint32_t tag, bool check, uint8_t* sync, const LbSignConsts& sc, UState& S,
                                            uint16_t* zl, float* part) {
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int tok = lane & 15, grp = lane >> 4;
-  if (li != S.li) u_enter_layer<NLB>(L, li, batch, ctr, check, sync, S, zl);
+  if (li != S.li) u_enter_layer<NLB>(L, li, batch, tag, check, sync, S, zl);
   const uint16_t* zb = zl + min(tok, batch - 1) * (L.zs + 8) + (S.b ? L.zoff1 : L.zoff0) + 8 * grp;
   const int s1 = 2 * S.nu;  // steps of the branch that hold data
   const uint8_t* wb = S.b ? w1 : w0;
@@ -993,12 +1003,13 @@ __global__ __launch_bounds__(LB_THREADS) void lb_decode_kernel(
     }
   }
   if (MODE == 1) vt1 = vt0;
-  // this workgroup's call counter (single launch only): the tag is its value
-  // + 1.  Loaded (load_ctr) once the first V tile's sign words have landed,
-  // before that tile's z store, so waiting for the words never waits for it.
-  uint32_t ctr = 0;
+  // this call's z tag (single launch only): call_tag of the workgroup's call
+  // counter, loaded (load_ctr) once the first V tile's sign words have
+  // landed, before that tile's z store, so waiting for the words never waits
+  // for it.  The two-launch path keeps tag 0, which no poll accepts.
+  uint32_t tag = 0;
   auto load_ctr = [&]() {
-    if (MODE == 2) ctr = ld32c(sync + LB_SYNC_CTR + 8 * wg);
+    if (MODE == 2) tag = call_tag(ld32c(sync + LB_SYNC_CTR + 8 * wg));
   };
   // phase-B pairs per wave in registers
   constexpr int NPW = MAXB > 1 ? LB_MAXPW_MULTI : LB_MAXPW;
@@ -1050,11 +1061,11 @@ __global__ __launch_bounds__(LB_THREADS) void lb_decode_kernel(
       load_ctr();
       prefetch();
     };
-    v_tile<MAXB, MODE == 2, EARLY>(V0, batch, k & 1, tile, chunk_pairs, ctr, sc, u_lds, red[0], zstage, first_hook, early);
+    v_tile<MAXB, MODE == 2, EARLY>(V0, batch, k & 1, tile, chunk_pairs, tag, sc, u_lds, red[0], zstage, first_hook, early);
     __syncthreads();
     for (int t = vt0 + 1; t < vt1; ++t) {
       const int kt = v_slot<SINGLE>(M, pre_vsplit, t, tile);
-      v_tile<MAXB, false, false>(V0, batch, kt & 1, tile, chunk_pairs, ctr, sc, u_lds, red[0], zstage, prefetch, early);
+      v_tile<MAXB, false, false>(V0, batch, kt & 1, tile, chunk_pairs, tag, sc, u_lds, red[0], zstage, prefetch, early);
       __syncthreads();
     }
   } else if (vt0 < vt1) {
@@ -1078,12 +1089,12 @@ __global__ __launch_bounds__(LB_THREADS) void lb_decode_kernel(
         if (nk >= 0) v_issue(v_geom(layer_view(A.L[nk >> 1]), nk & 1, ntile), 0, chunk_pairs, nxt);
         if (t == vt0) load_ctr();
         if (prev_k >= 0)
-          v_store_z(layer_view(A.L[prev_k >> 1]), batch, prev_k & 1, prev_tile, late(ctr) + 1u, zst[(t - vt0 + 1) & 1]);
+          v_store_z(layer_view(A.L[prev_k >> 1]), batch, prev_k & 1, prev_tile, late(tag), zst[(t - vt0 + 1) & 1]);
         if (MODE == 2 && t == vt1 - 1) prefetch();
       };
       const LayerView L = layer_view(A.L[k >> 1]);
       const bool reuse_u = k == prev_k && ((lb16_units(L.n) + 1) >> 1) <= chunk_pairs;
-      v_tile<MAXB, true, true, true>(L, batch, k & 1, tile, chunk_pairs, ctr, sc, u_lds, red[0], zst[(t - vt0) & 1], hook,
+      v_tile<MAXB, true, true, true>(L, batch, k & 1, tile, chunk_pairs, tag, sc, u_lds, red[0], zst[(t - vt0) & 1], hook,
                                cur, reuse_u);
       __syncthreads();
       prev_k = k;
@@ -1092,7 +1103,7 @@ __global__ __launch_bounds__(LB_THREADS) void lb_decode_kernel(
       tile = ntile;
       cur = nxt;
     }
-    v_store_z(layer_view(A.L[prev_k >> 1]), batch, prev_k & 1, prev_tile, late(ctr) + 1u, zst[(vt1 - 1 - vt0) & 1]);
+    v_store_z(layer_view(A.L[prev_k >> 1]), batch, prev_k & 1, prev_tile, late(tag), zst[(vt1 - 1 - vt0) & 1]);
   } else if (MODE == 2) {
     for (int i = 0; i < 3; ++i) __builtin_amdgcn_s_sleep(24);
     load_ctr();
@@ -1131,7 +1142,7 @@ __global__ __launch_bounds__(LB_THREADS) void lb_decode_kernel(
         const int tb0 = tile_bytes_b(L, 0), tb1 = tile_bytes_b(L, L.nb == 2 ? 1 : 0);
         const uint8_t* w0 = upre_lds + (slot ? plan.off[2] : plan.off[0]) + (t - first) * tb0;
         const uint8_t* w1 = upre_lds + (slot ? plan.off[3] : plan.off[1]) + (t - first) * tb1;
-        u_span_lds<(MAXB > 1 ? LB_POLL_LOADS_MULTI : LB_POLL_LOADS)>(L, li, batch, tile, T, span_max, w0, w1, tb0, tb1, hl_lds + 32 * (t - ut0), ctr, check, sync, sc, S,
+        u_span_lds<(MAXB > 1 ? LB_POLL_LOADS_MULTI : LB_POLL_LOADS)>(L, li, batch, tile, T, span_max, w0, w1, tb0, tb1, hl_lds + 32 * (t - ut0), tag, check, sync, sc, S,
                    u_lds, &red[0][0][0]);
         t += T;
       }
@@ -1140,7 +1151,7 @@ __global__ __launch_bounds__(LB_THREADS) void lb_decode_kernel(
       const int li = u_layer<SINGLE>(M, t, tile);
       const int lend = SINGLE ? ut1 : min(ut1, layer_u_end(M, li));
       const int nt = min(LB_MAXT, lend - t);
-      yo = u_group(SINGLE ? V0 : layer_view(A.L[li]), li, batch, tile, nt, pre, hpre, ctr, check, sync, sc, S, u_lds,
+      yo = u_group(SINGLE ? V0 : layer_view(A.L[li]), li, batch, tile, nt, pre, hpre, tag, check, sync, sc, S, u_lds,
                    red);
       t += nt;
     }
@@ -1157,13 +1168,28 @@ __global__ __launch_bounds__(LB_THREADS) void lb_decode_kernel(
 #pragma unroll
       for (int j = 0; j < 2; ++j) load_h(L, tile + min((wave_id() >> 2) + 2 * j, nt - 1), h, j);
       store_y(yo);
-      yo = u_group(L, li, batch, tile, nt, p, h, ctr, check, sync, sc, S, u_lds, red);
+      yo = u_group(L, li, batch, tile, nt, p, h, tag, check, sync, sc, S, u_lds, red);
       t += nt;
     }
     store_y(yo);
   }
   // this workgroup's call is done: the next call's tag is one higher
   if (MODE == 2 && threadIdx.x == 0) add64c_noret(sync + LB_SYNC_CTR + 8 * wg, 1ull);
+}
+
+// Copies the workspace's poll error word to *out and clears it (one thread;
+// a kernel rather than a copy call, so it can sit in a captured graph).
+__global__ void lb_take_error_kernel(uint8_t* sync, uint32_t* out) {
+  if (threadIdx.x == 0) {
+    uint32_t* e = reinterpret_cast<uint32_t*>(sync + LB_SYNC_ERR);
+    *out = ld32c(e);
+    st32c(e, 0u);
+  }
+}
+
+hipError_t lb_launch_take_error(void* sync, uint32_t* out, hipStream_t stream) {
+  hipLaunchKernelGGL(lb_take_error_kernel, dim3(1), dim3(64), 0, stream, (uint8_t*)sync, out);
+  return hipGetLastError();
 }
 
 static int g_fused_grid[64];  // per device: workgroups of the single-launch kernel (0: unknown, -1: none)

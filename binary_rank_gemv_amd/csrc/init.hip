@@ -1,7 +1,7 @@
 // Dual-SVID initialization of a layer's branches from a dense weight, on the
-// GPU (the step before the layer; explainx.ai explainer, "How it works"
+// GPU (liblittlebit_init.so, an offline library of its own) (the step before the layer; explainx.ai explainer, "How it works"
 // item 3: a truncated SVD of the weights, its signs and magnitudes mapped
-// into the parameters, and a residual branch fitting what the first missed).
+// into the parameters, and a residual branch fitted to what the first leaves).
 //
 // Per branch, with R the matrix to approximate (W, then the residual):
 //   1. Gram matrix of R on its smaller side (rocBLAS dgemm) and its
@@ -32,7 +32,10 @@
 #include <string>
 #include <vector>
 
-#include "littlebit.h"
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "littlebit_init.h"
 
 namespace {
 
@@ -253,7 +256,7 @@ static int power_rank1(rocblas_handle hb, hipStream_t stream, const double* M, i
   return 0;
 }
 
-int lb_run_dual_svid(const float* W, int64_t m, int64_t n, int64_t ldw, int r, int nbranches, int itq_iters,
+static int lb_run_dual_svid(const float* W, int64_t m, int64_t n, int64_t ldw, int r, int nbranches, int itq_iters,
                      const lb_init_branch* out, hipStream_t stream, std::string& err) {
   const int64_t k = m < n ? m : n;
   const bool gram_on_n = n <= m;  // eigenvectors on the input side (V) when n <= m
@@ -445,3 +448,53 @@ int lb_run_dual_svid(const float* W, int64_t m, int64_t n, int64_t ldw, int r, i
   }
   return 0;
 }
+
+// ------------------------------------------------------------------ C ABI
+namespace {
+
+thread_local std::string g_init_error;
+
+lb_status init_fail(lb_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_init_error = buf;
+  return s;
+}
+
+constexpr int kInitMaxRank = 4096;
+constexpr int kInitMaxDim = 32768;
+
+}  // namespace
+
+extern "C" {
+
+lb_status littlebit_dual_svid_init(const float* W, int64_t m, int64_t n, int64_t ldw, int64_t r, int nbranches,
+                                   int itq_iters, const lb_init_branch* out, void* stream) {
+  if (!W || !out) return init_fail(LB_ERR_INVALID_ARG, "littlebit_dual_svid_init: NULL pointer");
+  if (m < 1 || n < 1 || ldw < n)
+    return init_fail(LB_ERR_INVALID_ARG, "littlebit_dual_svid_init: m=%lld n=%lld ldw=%lld", (long long)m,
+                     (long long)n, (long long)ldw);
+  if (nbranches < 1 || nbranches > 2)
+    return init_fail(LB_ERR_INVALID_ARG, "littlebit_dual_svid_init: nbranches=%d (1 or 2)", nbranches);
+  if (r < 1 || r > (m < n ? m : n) || r > kInitMaxRank)
+    return init_fail(LB_ERR_INVALID_ARG, "littlebit_dual_svid_init: r=%lld outside 1..min(m, n, %d)", (long long)r,
+                     kInitMaxRank);
+  if (m > kInitMaxDim || n > kInitMaxDim)
+    return init_fail(LB_ERR_UNSUPPORTED, "littlebit_dual_svid_init: m, n <= %d", kInitMaxDim);
+  if (itq_iters < 0 || itq_iters > 1000)
+    return init_fail(LB_ERR_INVALID_ARG, "littlebit_dual_svid_init: itq_iters=%d outside 0..1000", itq_iters);
+  for (int b = 0; b < nbranches; ++b)
+    if (!out[b].U || !out[b].V || !out[b].h || !out[b].l || !out[b].g)
+      return init_fail(LB_ERR_INVALID_ARG, "littlebit_dual_svid_init: NULL output of branch %d", b);
+  std::string err;
+  const int rc = lb_run_dual_svid(W, m, n, ldw, (int)r, nbranches, itq_iters, out, (hipStream_t)stream, err);
+  if (rc != 0) return init_fail((lb_status)rc, "littlebit_dual_svid_init: %s", err.c_str());
+  return LB_OK;
+}
+
+const char* littlebit_init_last_error(void) { return g_init_error.c_str(); }
+
+}  // extern "C"

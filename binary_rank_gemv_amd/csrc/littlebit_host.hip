@@ -15,8 +15,7 @@ hipError_t lb_launch_prefill(const LbPrefillArgs& args, hipStream_t stream);
 hipError_t lb_launch_transpose_packed(const void* src, int R, int K, void* dst, hipStream_t stream);
 hipError_t lb_launch_decode(const LbDecodeArgs& args, int chunk_pairs, void* sync, int allow_fused,
                             hipStream_t stream);
-int lb_run_dual_svid(const float* W, int64_t m, int64_t n, int64_t ldw, int r, int nbranches, int itq_iters,
-                     const lb_init_branch* out, hipStream_t stream, std::string& err);
+hipError_t lb_launch_take_error(void* sync, uint32_t* out, hipStream_t stream);
 
 namespace {
 
@@ -220,12 +219,12 @@ size_t littlebit_packed_bytes(int64_t R, int64_t K) {
   return (size_t)(16 * ((R + 15) / 16)) * (size_t)(64 * ((K + 63) / 64)) / 8;
 }
 
-lb_status littlebit_pack(const void* latent, lb_dtype dtype, int64_t rows, int64_t cols, int64_t ld,
+lb_status littlebit_pack(const void* latent, int dtype, int64_t rows, int64_t cols, int64_t ld,
                          int transpose, void* dst, void* stream) {
   if (!latent || !dst) return fail(LB_ERR_INVALID_ARG, "littlebit_pack: NULL pointer");
   if (rows < 1 || cols < 1) return fail(LB_ERR_INVALID_ARG, "littlebit_pack: rows=%lld cols=%lld", (long long)rows, (long long)cols);
   if (ld < cols) return fail(LB_ERR_INVALID_ARG, "littlebit_pack: ld=%lld < cols=%lld", (long long)ld, (long long)cols);
-  if (dtype != LB_F32 && dtype != LB_F16) return fail(LB_ERR_INVALID_ARG, "littlebit_pack: bad dtype %d", (int)dtype);
+  if (dtype != LB_F32 && dtype != LB_F16) return fail(LB_ERR_INVALID_ARG, "littlebit_pack: bad dtype %d", dtype);
   if (transpose != 0 && transpose != 1) return fail(LB_ERR_INVALID_ARG, "littlebit_pack: transpose must be 0 or 1");
   if (!aligned(dst, 4)) return fail(LB_ERR_INVALID_ARG, "littlebit_pack: dst must be 4-byte aligned");
   const int64_t R = transpose ? cols : rows, K = transpose ? rows : cols;
@@ -245,28 +244,6 @@ lb_status littlebit_transpose_packed(const void* src, int64_t R, int64_t K, void
   if (src == dst) return fail(LB_ERR_INVALID_ARG, "littlebit_transpose_packed: src and dst must not be the same buffer");
   hipError_t e = lb_launch_transpose_packed(src, (int)R, (int)K, dst, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "littlebit_transpose_packed launch");
-  return LB_OK;
-}
-
-lb_status littlebit_dual_svid_init(const float* W, int64_t m, int64_t n, int64_t ldw, int64_t r, int nbranches,
-                                   int itq_iters, const lb_init_branch* out, void* stream) {
-  if (!W || !out) return fail(LB_ERR_INVALID_ARG, "littlebit_dual_svid_init: NULL pointer");
-  if (m < 1 || n < 1 || ldw < n)
-    return fail(LB_ERR_INVALID_ARG, "littlebit_dual_svid_init: m=%lld n=%lld ldw=%lld", (long long)m, (long long)n,
-                (long long)ldw);
-  if (nbranches < 1 || nbranches > 2)
-    return fail(LB_ERR_INVALID_ARG, "littlebit_dual_svid_init: nbranches=%d (1 or 2)", nbranches);
-  if (r < 1 || r > (m < n ? m : n) || r > kMaxRank)
-    return fail(LB_ERR_INVALID_ARG, "littlebit_dual_svid_init: r=%lld outside 1..min(m, n, %d)", (long long)r, kMaxRank);
-  if (m > kMaxN || n > kMaxN) return fail(LB_ERR_UNSUPPORTED, "littlebit_dual_svid_init: m, n <= %d", kMaxN);
-  if (itq_iters < 0 || itq_iters > 1000)
-    return fail(LB_ERR_INVALID_ARG, "littlebit_dual_svid_init: itq_iters=%d outside 0..1000", itq_iters);
-  for (int b = 0; b < nbranches; ++b)
-    if (!out[b].U || !out[b].V || !out[b].h || !out[b].l || !out[b].g)
-      return fail(LB_ERR_INVALID_ARG, "littlebit_dual_svid_init: NULL output of branch %d", b);
-  std::string err;
-  const int rc = lb_run_dual_svid(W, m, n, ldw, (int)r, nbranches, itq_iters, out, (hipStream_t)stream, err);
-  if (rc != 0) return fail((lb_status)rc, "littlebit_dual_svid_init: %s", err.c_str());
   return LB_OK;
 }
 
@@ -409,6 +386,17 @@ lb_status littlebit_block_fwd(const lb_layer L[7], const uint16_t* x_qkv, const 
     lb_status st = run_decode(la, 7, nb, ws, 1, (hipStream_t)stream);
     if (st != LB_OK) return st;
   }
+  return LB_OK;
+}
+
+lb_status littlebit_workspace_error(void* ws, size_t ws_bytes, uint32_t* error, void* stream) {
+  if (!ws || !error) return fail(LB_ERR_INVALID_ARG, "littlebit_workspace_error: NULL pointer");
+  if (!aligned(ws, 256)) return fail(LB_ERR_WORKSPACE, "littlebit_workspace_error: workspace must be 256-byte aligned");
+  if (!aligned(error, 4)) return fail(LB_ERR_INVALID_ARG, "littlebit_workspace_error: error must be 4-byte aligned");
+  if (ws_bytes < kWsHeader)
+    return fail(LB_ERR_WORKSPACE, "littlebit_workspace_error: workspace has %zu bytes, needs %zu", ws_bytes, kWsHeader);
+  hipError_t e = lb_launch_take_error(ws, error, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "littlebit_workspace_error launch");
   return LB_OK;
 }
 

@@ -12,9 +12,14 @@ The functions keep the C names:
   (``LittleBitLayer.transposed()`` builds the layer of W^T from it)
 * ``littlebit_linear_fwd(layer, x, branch_mask=3, path=LB_PATH_AUTO)`` -> y
 * ``littlebit_block_fwd(layers, x_qkv, x_o, x_gu, x_down)`` -> list of 7 y
+* ``littlebit_workspace_error(ws)`` -> device int32 tensor, non-zero if a
+  decode call on ``ws`` gave up waiting since the previous report
 * ``littlebit_packed_bytes``, ``littlebit_linear_workspace_bytes``,
   ``littlebit_block_workspace_bytes``, ``littlebit_status_string``,
   ``littlebit_last_error``
+* ``littlebit_dual_svid_init(W, r, ...)`` -> branches; from the separate
+  offline library ``_lib/liblittlebit_init.so`` (include/littlebit_init.h),
+  loaded on first use
 """
 
 from __future__ import annotations
@@ -26,7 +31,11 @@ from typing import List, Optional, Sequence
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "liblittlebit.so")
+# LITTLEBIT_LIBRARY names another build of the same library (the host-side
+# sanitizer build of the CPU tests); by default the in-tree build is loaded.
+LIB_PATH = os.environ.get("LITTLEBIT_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib",
+                                                               "liblittlebit.so")
+INIT_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "liblittlebit_init.so")
 
 LB_OK, LB_ERR_INVALID_ARG, LB_ERR_UNSUPPORTED, LB_ERR_WORKSPACE, LB_ERR_HIP = 0, -1, -2, -3, -4
 LB_F32, LB_F16 = 0, 1
@@ -37,8 +46,9 @@ EXPORTED = (
     "littlebit_packed_bytes", "littlebit_pack", "littlebit_linear_workspace_bytes",
     "littlebit_linear_fwd", "littlebit_block_workspace_bytes", "littlebit_block_fwd",
     "littlebit_status_string", "littlebit_last_error", "littlebit_transpose_packed",
-    "littlebit_dual_svid_init",
+    "littlebit_workspace_error",
 )
+INIT_EXPORTED = ("littlebit_dual_svid_init", "littlebit_init_last_error")
 
 
 class LittleBitError(RuntimeError):
@@ -82,8 +92,8 @@ def _load():
     lib.littlebit_block_workspace_bytes.restype = sz
     lib.littlebit_block_fwd.argtypes = [ctypes.POINTER(_Layer), vp, vp, vp, vp, ctypes.POINTER(vp), i64, vp, sz, vp]
     lib.littlebit_block_fwd.restype = i32
-    lib.littlebit_dual_svid_init.argtypes = [vp, i64, i64, i64, i64, i32, i32, ctypes.POINTER(_InitBranch), vp]
-    lib.littlebit_dual_svid_init.restype = i32
+    lib.littlebit_workspace_error.argtypes = [vp, sz, vp, vp]
+    lib.littlebit_workspace_error.restype = i32
     lib.littlebit_status_string.argtypes = [i32]
     lib.littlebit_status_string.restype = ctypes.c_char_p
     lib.littlebit_last_error.argtypes = []
@@ -92,6 +102,23 @@ def _load():
 
 
 LIB = _load()
+_INIT_LIB = None
+
+
+def _init_lib():
+    """The offline initialization library, loaded on first use."""
+    global _INIT_LIB
+    if _INIT_LIB is None:
+        if not os.path.exists(INIT_LIB_PATH):
+            raise ImportError(f"{INIT_LIB_PATH} is missing: build it with `python -m binary_rank_gemv_amd.build`")
+        lib = ctypes.CDLL(INIT_LIB_PATH)
+        vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        lib.littlebit_dual_svid_init.argtypes = [vp, i64, i64, i64, i64, i32, i32, ctypes.POINTER(_InitBranch), vp]
+        lib.littlebit_dual_svid_init.restype = i32
+        lib.littlebit_init_last_error.argtypes = []
+        lib.littlebit_init_last_error.restype = ctypes.c_char_p
+        _INIT_LIB = lib
+    return _INIT_LIB
 
 
 def _check(status: int):
@@ -165,8 +192,11 @@ def littlebit_dual_svid_init(W: torch.Tensor, r: int, nbranches: int = 2, itq_it
               "g": torch.empty(n, dtype=torch.float16, device=W.device)}
         arr[b] = _InitBranch(_ptr(br["U"]), _ptr(br["V"]), _ptr(br["h"]), _ptr(br["l"]), _ptr(br["g"]))
         outs.append(br)
-    _check(LIB.littlebit_dual_svid_init(_ptr(W), m, n, W.stride(0), r, nbranches, itq_iters, arr,
-                                        _stream_ptr(stream)))
+    lib = _init_lib()
+    status = lib.littlebit_dual_svid_init(_ptr(W), m, n, W.stride(0), r, nbranches, itq_iters, arr,
+                                          _stream_ptr(stream))
+    if status != LB_OK:
+        raise LittleBitError(status, lib.littlebit_init_last_error().decode())
     return outs
 
 
@@ -239,6 +269,18 @@ class Workspace:
 
 
 _WS = Workspace()
+
+
+def littlebit_workspace_error(workspace: torch.Tensor, stream=None) -> torch.Tensor:
+    """A one-element int32 device tensor receiving the workspace's poll error
+    word (non-zero: a decode call on it since the previous report gave up
+    waiting, and its outputs are wrong); the word is cleared.  Asynchronous
+    on the stream: read the tensor after the stream has reached this point."""
+    if workspace.dtype != torch.uint8 or not workspace.is_cuda:
+        raise ValueError("workspace must be a uint8 CUDA tensor")
+    out = torch.empty(1, dtype=torch.int32, device=workspace.device)
+    _check(LIB.littlebit_workspace_error(_ptr(workspace), workspace.numel(), _ptr(out), _stream_ptr(stream)))
+    return out
 
 
 def littlebit_linear_workspace_bytes(layer: LittleBitLayer, batch: int) -> int:

@@ -17,11 +17,11 @@
  *     (hipMalloc'd or torch CUDA tensors).  lb_layer / lb_branch structs and
  *     the y[] pointer array of littlebit_block_fwd live in HOST memory and are
  *     read only during the call.
- *   - The caller owns all memory.  The layer and packing calls never
- *     allocate, free or synchronise; work is enqueued on `stream` (a
- *     hipStream_t, NULL = the default stream) and the call returns once it
- *     is enqueued.  The one exception is the initialization,
- *     littlebit_dual_svid_init (documented at its declaration).
+ *   - The caller owns all memory.  No entry point allocates, frees or
+ *     synchronises; work is enqueued on `stream` (a hipStream_t, NULL = the
+ *     default stream) and the call returns once it is enqueued.  (The
+ *     offline initialization, which does allocate and synchronise, is a
+ *     separate library: littlebit_init.h.)
  *   - fp16 data is IEEE binary16, passed as uint16_t.
  *   - Arguments are validated before anything is enqueued; on failure nothing
  *     is launched and a negative lb_status is returned.  littlebit_last_error
@@ -89,8 +89,10 @@ size_t littlebit_packed_bytes(int64_t R, int64_t K);
 /*
  * Pack the signs of a latent matrix into LB16 (explainx.ai explainer, "How
  * it works" item 1: only the signs of the thin factors are kept).
- *   latent    device, dtype LB_F32 or LB_F16, row-major `rows` x `cols` with
- *             leading dimension ld >= cols (elements).
+ *   latent    device, row-major `rows` x `cols` with leading dimension
+ *             ld >= cols (elements).
+ *   dtype     an lb_dtype value, LB_F32 or LB_F16 (passed as int so that any
+ *             other value is rejected rather than being undefined).
  *   transpose 0: the factor is latent itself (R = rows, K = cols) -- use for
  *             U (m x r).  1: the factor is latent^T (R = cols, K = rows) -- use
  *             for V (n x r), giving sign(V)^T.
@@ -98,7 +100,7 @@ size_t littlebit_packed_bytes(int64_t R, int64_t K);
  *             every byte (padding included) is written.
  * Bit = 1 iff the latent value is < 0 (+0, -0 and NaN give +1).
  */
-lb_status littlebit_pack(const void *latent, lb_dtype dtype, int64_t rows,
+lb_status littlebit_pack(const void *latent, int dtype, int64_t rows,
                          int64_t cols, int64_t ld, int transpose, void *dst,
                          void *stream);
 
@@ -137,9 +139,14 @@ typedef struct lb_layer {
 /*
  * Workspace bytes littlebit_linear_fwd needs for this layer and batch
  * (0 on invalid arguments).  The workspace must be zero-filled once before
- * its first use; the library leaves it reusable after every call.  It holds
- * per-workspace call counters, so calls that run concurrently must not share
- * a workspace, and a workspace stays with the device it was first used on.
+ * its first use; the library leaves it reusable after every call.  Its first
+ * 4096 bytes are a header: one call counter per workgroup of the decode
+ * kernel's single launch and a poll error word.  A header that was not
+ * zero-filled (counters that differ between workgroups) is a precondition
+ * violation: the call's z polls then wait in vain until their spin limit,
+ * and the call reports it through littlebit_workspace_error.  Calls that run
+ * concurrently must not share a workspace, and a workspace stays with the
+ * device it was first used on.
  */
 size_t littlebit_linear_workspace_bytes(const lb_layer *L, int64_t batch);
 
@@ -158,6 +165,16 @@ size_t littlebit_linear_workspace_bytes(const lb_layer *L, int64_t batch);
  *   flags        LB_PATH_* optionally OR-ed with LB_DECODE_TWO_LAUNCHES.
  * Intermediates: g*x and l*t are rounded to fp16 before the sign
  * contractions; accumulation is fp32; y is rounded to fp16 once.
+ *
+ * Decode (up to 16 tokens) runs, unless LB_DECODE_TWO_LAUNCHES is given, as
+ * one launch of one workgroup per compute unit whose workgroups hand the
+ * rank-space intermediate to each other through the workspace: every
+ * workgroup of that launch must be resident at the same time.  The library
+ * sizes the grid from the device's occupancy for this kernel, so the
+ * precondition holds when no other kernel keeps compute units busy for
+ * long while the call runs; if one does, a workgroup that waits more than
+ * about 2^20 polls gives up, its outputs are wrong, and the workspace's
+ * error word is set (littlebit_workspace_error reports it).
  */
 lb_status littlebit_linear_fwd(const lb_layer *L, uint32_t branch_mask,
                                const uint16_t *x, int64_t batch, int64_t ldx,
@@ -166,11 +183,19 @@ lb_status littlebit_linear_fwd(const lb_layer *L, uint32_t branch_mask,
 
 /*
  * The seven projections of one decoder block in one call (q, k, v, o, gate,
- * up, down; all branches of each).  q, k, v read x_qkv; o reads x_o; gate
- * and up read x_gu; down reads x_down.  Every x row stride equals that
- * projection's n and every y row stride its m (dense batch x n / batch x m
- * arrays).  Attention, norms and activations are not part of the layer and
- * are left to the caller.  For batch <= 16 all seven run in one launch.
+ * up, down; all branches of each).  The pages compress the linear layers of
+ * the Transformer blocks and keep the architecture (explainx.ai explainer,
+ * "What LittleBit is"; trueseeker.com case, "The trace / claim to source":
+ * only the Transformer blocks are quantized, embedding and head stay FP16),
+ * so a block's seven projections are seven independent layers of the form
+ * above.  q, k, v read x_qkv; o reads x_o; gate and up read x_gu; down reads
+ * x_down.  Every x row stride equals that projection's n and every y row
+ * stride its m (dense batch x n / batch x m arrays).  Attention, norms and
+ * activations are not part of the layer and are left to the caller.  For
+ * batch <= 16 all seven run in one launch (with the residency precondition
+ * of littlebit_linear_fwd's decode); y[i] is written as by
+ * littlebit_linear_fwd on layer i.  Workspace as for
+ * littlebit_linear_workspace_bytes, with its own size.
  */
 size_t littlebit_block_workspace_bytes(const lb_layer L[7], int64_t batch);
 
@@ -181,56 +206,15 @@ lb_status littlebit_block_fwd(const lb_layer L[7], const uint16_t *x_qkv,
                               void *stream);
 
 /*
- * Dual-SVID initialization (explainx.ai explainer, "How it works" item 3:
- * training starts from a truncated SVD of the real weights whose signs and
- * magnitudes are mapped into the layer's parameters, and a residual branch
- * models what the first branch missed).  The step before the layer: it turns
- * a dense weight into branches for littlebit_pack / the layer.
- *
- * Per branch, from R (W for the first branch, then W minus the deployed
- * earlier branches): the rank-r truncated SVD R ~ P S Q^T gives the latent
- * factors U = P S^(1/2) (m x r) and V = Q S^(1/2) (n x r), each component
- * oriented so the largest-magnitude entry of its V column (first index on
- * ties) is positive; |U| and |V| are each approximated by the rank-1 product
- * a b^T of their leading singular triplet (a = sqrt(sigma) p, b =
- * sqrt(sigma) q, non-negative); h = a_U, g = a_V, l = b_U * b_V, rounded to
- * fp16 (nearest even).  The deployed branch diag(h) sign(U) diag(l)
- * sign(V)^T diag(g) (signs of the fp32 latents, -1 iff < 0) is subtracted
- * before the next branch.  Float64 throughout on the device (rocBLAS GEMMs,
- * rocSOLVER symmetric eigendecomposition of the smaller-side Gram matrix,
- * power iteration for the rank-1 fits).
- *
- *   W         device fp32, m x n row-major, row stride ldw >= n (elements).
- *   r         rank per branch, 1 <= r <= min(m, n), r <= 4096.
- *   nbranches 1 or 2; out[b] receives branch b:
- *             U device fp32 m x r row-major, V device fp32 n x r row-major
- *             (the latent factors; their signs are the binary factors),
- *             h (m), l (r), g (n) device fp16.
- *   itq_iters 0: no rotation.  > 0 (at most 1000): before the sign-value
- *             split, the latent factors of each branch are rotated by one
- *             orthogonal R (r x r), which leaves U V^T unchanged, chosen by
- *             that many Joint-ITQ iterations from R = I (explainx.ai
- *             explainer, LittleBit-2 paragraph: Internal Latent Rotation with
- *             Joint Iterative Quantization aligns the latent factors with the
- *             binary hypercube): B = sign([U; V] R), then R = P Q^T for the
- *             SVD P S Q^T of M = [U; V]^T B, computed as the polar factor
- *             M (M^T M)^(-1/2) (rocSOLVER dsyevd of M^T M).
- * Unlike the layer calls this one allocates device memory (about
- * 8 (m n + k^2 + 4 max(m, n) r) bytes, k = min(m, n)) and returns after
- * the work on `stream` has finished.  m, n <= 32768.
+ * Failure report of the decode kernels' waits.  Enqueues, on `stream`, a
+ * copy of the workspace's poll error word into *error (device, one uint32,
+ * 4-byte aligned) and clears the word.  *error != 0 means that, in some
+ * decode call on this workspace since the previous report, a workgroup gave
+ * up waiting for the rank-space intermediate (see littlebit_linear_fwd):
+ * that call's outputs are wrong.  ws_bytes >= 4096.
  */
-typedef struct lb_init_branch {
-  float *U;
-  float *V;
-  uint16_t *h;
-  uint16_t *l;
-  uint16_t *g;
-} lb_init_branch;
-
-lb_status littlebit_dual_svid_init(const float *W, int64_t m, int64_t n,
-                                   int64_t ldw, int64_t r, int nbranches,
-                                   int itq_iters, const lb_init_branch *out,
-                                   void *stream);
+lb_status littlebit_workspace_error(void *ws, size_t ws_bytes, uint32_t *error,
+                                    void *stream);
 
 /* Static description of a status code. */
 const char *littlebit_status_string(lb_status s);

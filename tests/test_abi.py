@@ -12,24 +12,50 @@ import oracle
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "littlebit.h")
+INIT_HEADER = os.path.join(ROOT, "include", "littlebit_init.h")
 
 lb = pytest.importorskip("binary_rank_gemv_amd.littlebit",
                          reason="liblittlebit.so not built (run python -m binary_rank_gemv_amd.build)")
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(littlebit_\w+)\s*\(", text)))
 
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) >= 8
+    assert len(names) >= 9
     lib = ctypes.CDLL(lb.LIB_PATH)
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(lb.EXPORTED)
+
+
+def test_init_library_is_separate():
+    """The offline initialization lives in its own library; the layer library
+    neither exports it nor links rocBLAS / rocSOLVER."""
+    import subprocess
+    names = declared_functions(INIT_HEADER)
+    assert set(names) == set(lb.INIT_EXPORTED)
+    init = ctypes.CDLL(lb.INIT_LIB_PATH)
+    for name in names:
+        assert hasattr(init, name), name
+    layer = ctypes.CDLL(lb.LIB_PATH)
+    assert not hasattr(layer, "littlebit_dual_svid_init")
+    deps = subprocess.run(["readelf", "-d", lb.LIB_PATH], capture_output=True, text=True).stdout
+    needed = re.findall(r"\(NEEDED\).*\[(.*)\]", deps)
+    assert needed and not any("rocblas" in d or "rocsolver" in d for d in needed), needed
+
+
+def test_workspace_error_rejects_bad_arguments():
+    f = lb.LIB.littlebit_workspace_error
+    assert f(None, 4096, FAKE, None) == lb.LB_ERR_INVALID_ARG
+    assert f(FAKE, 4096, None, None) == lb.LB_ERR_INVALID_ARG
+    assert f(FAKE + 16, 4096, FAKE, None) == lb.LB_ERR_WORKSPACE
+    assert f(FAKE, 4095, FAKE, None) == lb.LB_ERR_WORKSPACE
+    assert f(FAKE, 4096, FAKE + 2, None) == lb.LB_ERR_INVALID_ARG
 
 
 @pytest.mark.parametrize("R,K", [(16, 64), (20, 600), (1472, 4096), (11008, 1472), (168, 13824), (1, 1)])
@@ -139,7 +165,8 @@ def test_dual_svid_init_rejects_bad_arguments():
     arr = (lb._InitBranch * 2)()
     for b in range(2):
         arr[b] = lb._InitBranch(FAKE, FAKE, FAKE, FAKE, FAKE)
-    f = lb.LIB.littlebit_dual_svid_init
+    init = lb._init_lib()
+    f = init.littlebit_dual_svid_init
     assert f(None, 64, 32, 32, 8, 2, 0, arr, None) == lb.LB_ERR_INVALID_ARG
     assert f(FAKE, 64, 32, 16, 8, 2, 0, arr, None) == lb.LB_ERR_INVALID_ARG       # ldw < n
     assert f(FAKE, 64, 32, 32, 33, 2, 0, arr, None) == lb.LB_ERR_INVALID_ARG      # r > min(m, n)
@@ -149,4 +176,4 @@ def test_dual_svid_init_rejects_bad_arguments():
     assert f(FAKE, 64, 32, 32, 8, 2, -1, arr, None) == lb.LB_ERR_INVALID_ARG   # itq_iters
     arr[1] = lb._InitBranch(FAKE, None, FAKE, FAKE, FAKE)
     assert f(FAKE, 64, 32, 32, 8, 2, 0, arr, None) == lb.LB_ERR_INVALID_ARG
-    assert "NULL output" in lb.littlebit_last_error()
+    assert "NULL output" in init.littlebit_init_last_error().decode()
