@@ -10,7 +10,8 @@ in three steps, which this module takes in order:
 2. the signs and magnitudes of the resulting latent factors are mapped into
    the learnable parameters (signs -> sign(U), sign(V); magnitudes -> the
    scales h, l, g);
-3. a second, residual branch models what the first branch missed.
+3. a second branch is fitted to the residual, the part of W that the first
+   branch does not capture.
 
 The page names the decomposition "Sign-Value-Independent": a matrix is split
 into its sign pattern and a magnitude part that does not depend on the signs.
@@ -48,9 +49,11 @@ Parity status (tests/test_oracle.py):
 * ``dual_svid_init``: pinned by exact reconstruction of a rank-1
   sign-magnitude weight (h * s)(g * t)^T with r = 1 (before fp16 rounding),
   by positive homogeneity (scaling W scales the unrounded reconstruction),
-  and by the residual branch lowering the error on synthetic weights with a
-  decaying spectrum.  The residual step beyond "fit what is left" is a
-  reading; parity unpinned for exact values of branch 2 beyond those checks.
+  by the residual branch lowering the error on synthetic weights with a
+  decaying spectrum, and by a block-diagonal weight of two rank-1
+  sign-magnitude blocks, which rank-1 branches split exactly (up to the fp16
+  rounding of the scales): branch 1 reproduces the larger block and branch 2
+  the smaller one, each zero outside its block.
 """
 
 from __future__ import annotations
@@ -150,8 +153,8 @@ def dual_svid_init(W: np.ndarray, r: int, nbranches: int = 2, itq_iters: int = 0
     """Branches of the Dual-SVID initialization of W: branch 1 from W, each
     later branch from the residual W minus the deployed earlier branches.
 
-    explainx.ai explainer, "How it works" item 3 (a second, residual branch
-    models what the first missed).
+    explainx.ai explainer, "How it works" item 3 (the second branch takes
+    over the part of the weight that the first leaves).
     """
     W = np.asarray(W, dtype=np.float64)
     out = []

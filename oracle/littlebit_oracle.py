@@ -9,8 +9,8 @@ The explainx.ai explainer, "How it works" item 1, approximates a weight matrix
 W by the product of two thin matrices U and V and keeps, for inference, only
 the signs (+1 or -1) of their entries.  Item 2 ("Multi-scale compensation")
 adds learned FP16 scale vectors on three axes: rows, columns and the latent
-dimension.  Item 3 adds a second, residual branch that models what the first
-one missed.  With W of shape out x in = m x n, U of shape m x r and V of shape
+dimension.  Item 3 adds a second, residual branch for the part of the weight
+the first one leaves.  With W of shape out x in = m x n, U of shape m x r and V of shape
 n x r, the only placement of one scale per named axis is
 
     W_b = diag(h_b) . sign(U_b) . diag(l_b) . sign(V_b)^T . diag(g_b)
@@ -89,8 +89,8 @@ def branch_weight(br) -> np.ndarray:
 
 def dense_weight(branches: Sequence) -> np.ndarray:
     """Sum of the branch weights (explainx.ai explainer, "How it works" item 3:
-    the residual branch models what the primary branch missed, so the two
-    approximations add)."""
+    the residual branch covers what the primary branch leaves over, so the
+    two approximations add)."""
     w = None
     for br in branches:
         wb = branch_weight(br)

@@ -379,6 +379,33 @@ def test_dual_svid_residual_branch_lowers_the_error():
     np.testing.assert_array_equal(ref["h"], brs[1]["h"])
 
 
+def test_dual_svid_block_diagonal_weight_splits_into_the_two_branches():
+    """W = blockdiag(B1, B2), each block a rank-1 sign-magnitude matrix, with
+    ||B1|| > ||B2||, rank 1 per branch: the first branch is the best rank-1
+    approximation of W, i.e. B1 (zero outside its block), and the second is
+    fitted to what is left, i.e. B2.  Each is exact up to the fp16 rounding of
+    its scales.  A second branch fitted to W rather than to the residual
+    would reproduce B1 again; one fitted with the wrong sign, -B2."""
+    rng = np.random.default_rng(3)
+    m1, n1, m2, n2 = 24, 20, 16, 12
+
+    def block(m, n, scale):
+        s, t = rng.choice([-1.0, 1.0], m), rng.choice([-1.0, 1.0], n)
+        return scale * np.outer(rng.uniform(0.5, 1.5, m) * s, rng.uniform(0.5, 1.5, n) * t)
+
+    B1, B2 = block(m1, n1, 3.0), block(m2, n2, 1.0)
+    W = np.zeros((m1 + m2, n1 + n2))
+    W[:m1, :n1], W[m1:, n1:] = B1, B2
+    brs = oracle.dual_svid_init(W, 1, nbranches=2)
+    W1, W2 = oracle.branch_weight(brs[0]), oracle.branch_weight(brs[1])
+    E1, E2 = np.zeros_like(W), np.zeros_like(W)
+    E1[:m1, :n1], E2[m1:, n1:] = B1, B2
+    assert np.linalg.norm(W1 - E1) / np.linalg.norm(B1) < 2e-3
+    assert np.linalg.norm(W2 - E2) / np.linalg.norm(B2) < 2e-3
+    assert np.abs(W1[m1:, :]).max() == 0 and np.abs(W1[:, n1:]).max() == 0
+    assert np.abs(W2[:m1, :]).max() == 0 and np.abs(W2[:, :n1]).max() == 0
+
+
 # ---------------------------------------------------- Joint-ITQ latent rotation
 
 def test_itq_rotation_is_orthogonal_keeps_the_product_and_never_lowers_the_objective():
