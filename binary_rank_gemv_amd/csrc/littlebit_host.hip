@@ -4,6 +4,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "littlebit.h"
@@ -255,54 +256,150 @@ size_t littlebit_linear_workspace_bytes(const lb_layer* L, int64_t batch) {
   return kWsHeader + w.z_bytes + prefill_z_bytes(w.zs_p, batch);
 }
 
-lb_status littlebit_linear_fwd(const lb_layer* L, uint32_t branch_mask, const uint16_t* x, int64_t batch,
-                               int64_t ldx, uint16_t* y, int64_t ldy, void* ws, size_t ws_bytes,
-                               uint32_t flags, void* stream) {
-  int sel[2], nsel = 0;
-  lb_status st = check_layer(L, branch_mask, sel, &nsel, "littlebit_linear_fwd");
+}  // extern "C"
+
+namespace {
+
+// Argument checks shared by littlebit_linear_fwd and its no-alloc variant
+// (everything but the workspace).
+lb_status check_linear_args(const char* name, const lb_layer* L, uint32_t branch_mask, const uint16_t* x,
+                            int64_t batch, int64_t ldx, uint16_t* y, int64_t ldy, uint32_t flags, int* sel,
+                            int* nsel) {
+  lb_status st = check_layer(L, branch_mask, sel, nsel, name);
   if (st != LB_OK) return st;
-  if (!x || !y) return fail(LB_ERR_INVALID_ARG, "littlebit_linear_fwd: x or y is NULL");
-  if (batch < 1) return fail(LB_ERR_INVALID_ARG, "littlebit_linear_fwd: batch=%lld must be >= 1", (long long)batch);
-  if (ldx < L->n || ldy < L->m) return fail(LB_ERR_INVALID_ARG, "littlebit_linear_fwd: ldx/ldy smaller than n/m");
+  if (!x || !y) return fail(LB_ERR_INVALID_ARG, "%s: x or y is NULL", name);
+  if (batch < 1) return fail(LB_ERR_INVALID_ARG, "%s: batch=%lld must be >= 1", name, (long long)batch);
+  if (ldx < L->n || ldy < L->m) return fail(LB_ERR_INVALID_ARG, "%s: ldx/ldy smaller than n/m", name);
   if (ldx > INT32_MAX || ldy > INT32_MAX)
-    return fail(LB_ERR_UNSUPPORTED, "littlebit_linear_fwd: row strides above 2^31-1 elements");
-  if (!aligned(x, 2) || !aligned(y, 2)) return fail(LB_ERR_INVALID_ARG, "littlebit_linear_fwd: x and y must be 2-byte aligned");
+    return fail(LB_ERR_UNSUPPORTED, "%s: row strides above 2^31-1 elements", name);
+  if (!aligned(x, 2) || !aligned(y, 2)) return fail(LB_ERR_INVALID_ARG, "%s: x and y must be 2-byte aligned", name);
   if ((flags & 3u) == 3u || (flags & ~(3u | LB_DECODE_TWO_LAUNCHES)))
-    return fail(LB_ERR_INVALID_ARG, "littlebit_linear_fwd: unknown flags %u", flags);
+    return fail(LB_ERR_INVALID_ARG, "%s: unknown flags %u", name, flags);
   if ((flags & 3u) == LB_PATH_DECODE && batch > kDecodeMaxBatch)
-    return fail(LB_ERR_INVALID_ARG, "littlebit_linear_fwd: decode path takes at most %d tokens", kDecodeMaxBatch);
-  if (!ws) return fail(LB_ERR_WORKSPACE, "littlebit_linear_fwd: workspace is NULL");
-  if (!aligned(ws, 256)) return fail(LB_ERR_WORKSPACE, "littlebit_linear_fwd: workspace must be 256-byte aligned");
+    return fail(LB_ERR_INVALID_ARG, "%s: decode path takes at most %d tokens", name, kDecodeMaxBatch);
+  return LB_OK;
+}
+
+// The layer on a workspace whose size has been checked by the caller; prefill
+// runs in chunks of at most max_prefill_tokens tokens.
+lb_status linear_fwd_impl(const char* name, const lb_layer* L, const int* sel, int nsel, const uint16_t* x,
+                          int64_t batch, int64_t ldx, uint16_t* y, int64_t ldy, void* ws, uint32_t flags,
+                          int64_t max_prefill_tokens, hipStream_t stream) {
   const LayerWs w = layer_ws(*L, sel, nsel, kDecodeMaxBatch);
   const uint32_t path = flags & 3u;
   const int chunk = decode_chunk_tokens(w.zs);
-  if (path == LB_PATH_DECODE && chunk == 0)
-    return fail(LB_ERR_UNSUPPORTED, "littlebit_linear_fwd: rank %d exceeds the decode kernels' LDS", w.zs);
   const bool prefill = path == LB_PATH_PREFILL || (path == LB_PATH_AUTO && (batch > kDecodeMaxBatch || chunk == 0));
-  const size_t need = kWsHeader + w.z_bytes + (prefill ? prefill_z_bytes(w.zs_p, batch) : 0);
-  if (ws_bytes < need)
-    return fail(LB_ERR_WORKSPACE, "littlebit_linear_fwd: workspace has %zu bytes, needs %zu", ws_bytes, need);
-
   uint8_t* base = static_cast<uint8_t*>(ws) + kWsHeader;
   if (prefill) {
-    for (int64_t t0 = 0; t0 < batch; t0 += LB_PREFILL_MAX_TOKENS) {
-      const int nt = (int)((batch - t0) < LB_PREFILL_MAX_TOKENS ? (batch - t0) : LB_PREFILL_MAX_TOKENS);
+    for (int64_t t0 = 0; t0 < batch; t0 += max_prefill_tokens) {
+      const int nt = (int)((batch - t0) < max_prefill_tokens ? (batch - t0) : max_prefill_tokens);
       LbPrefillArgs pa;
       fill_prefill_args(pa, *L, sel, nsel, w, base + w.z_bytes, x + t0 * ldx, (long)ldx, y + t0 * ldy,
                         (long)ldy, nt);
-      hipError_t e = lb_launch_prefill(pa, (hipStream_t)stream);
+      hipError_t e = lb_launch_prefill(pa, stream);
       if (e != hipSuccess) return hip_fail(e, "prefill launch");
     }
     return LB_OK;
   }
+  (void)name;
   for (int64_t t0 = 0; t0 < batch; t0 += chunk) {
     const int nb = (int)((batch - t0) < chunk ? (batch - t0) : chunk);
     LbLayerArgs la;
     fill_layer_args(la, *L, sel, nsel, w, base, x + t0 * ldx, (long)ldx, y + t0 * ldy, (long)ldy);
-    st = run_decode(&la, 1, nb, ws, !(flags & LB_DECODE_TWO_LAUNCHES), (hipStream_t)stream);
+    lb_status st = run_decode(&la, 1, nb, ws, !(flags & LB_DECODE_TWO_LAUNCHES), stream);
     if (st != LB_OK) return st;
   }
   return LB_OK;
+}
+
+// ------------------------------------------------------- no-alloc variant
+// The workspace of littlebit_linear_fwd_noalloc: one array per device,
+// zero-filled when the code object is loaded onto the device (static storage
+// without an initializer) and kept for the life of the process.  Host code
+// never passes the array's name to a kernel: it is only a host-side stand-in
+// for the symbol; its device address comes from hipGetSymbolAddress.
+constexpr size_t kScratchBytes = 8u << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];
+
+// This device's scratch address, looked up once per device (with that device
+// current, as it is for the calling thread here).
+lb_status scratch_for_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(LB_ERR_UNSUPPORTED, "device index %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p || !aligned(p, 256)) return fail(LB_ERR_HIP, "scratch symbol address %p is not 256-byte aligned", p);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return LB_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+lb_status littlebit_linear_fwd(const lb_layer* L, uint32_t branch_mask, const uint16_t* x, int64_t batch,
+                               int64_t ldx, uint16_t* y, int64_t ldy, void* ws, size_t ws_bytes,
+                               uint32_t flags, void* stream) {
+  const char* name = "littlebit_linear_fwd";
+  int sel[2], nsel = 0;
+  lb_status st = check_linear_args(name, L, branch_mask, x, batch, ldx, y, ldy, flags, sel, &nsel);
+  if (st != LB_OK) return st;
+  if (!ws) return fail(LB_ERR_WORKSPACE, "%s: workspace is NULL", name);
+  if (!aligned(ws, 256)) return fail(LB_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", name);
+  const LayerWs w = layer_ws(*L, sel, nsel, kDecodeMaxBatch);
+  const uint32_t path = flags & 3u;
+  const int chunk = decode_chunk_tokens(w.zs);
+  if (path == LB_PATH_DECODE && chunk == 0)
+    return fail(LB_ERR_UNSUPPORTED, "%s: rank %d exceeds the decode kernels' LDS", name, w.zs);
+  const bool prefill = path == LB_PATH_PREFILL || (path == LB_PATH_AUTO && (batch > kDecodeMaxBatch || chunk == 0));
+  const size_t need = kWsHeader + w.z_bytes + (prefill ? prefill_z_bytes(w.zs_p, batch) : 0);
+  if (ws_bytes < need)
+    return fail(LB_ERR_WORKSPACE, "%s: workspace has %zu bytes, needs %zu", name, ws_bytes, need);
+  return linear_fwd_impl(name, L, sel, nsel, x, batch, ldx, y, ldy, ws, flags, LB_PREFILL_MAX_TOKENS,
+                         (hipStream_t)stream);
+}
+
+lb_status littlebit_linear_fwd_noalloc(const lb_layer* L, uint32_t branch_mask, const uint16_t* x, int64_t batch,
+                                       int64_t ldx, uint16_t* y, int64_t ldy, uint32_t flags, void* stream) {
+  const char* name = "littlebit_linear_fwd_noalloc";
+  int sel[2], nsel = 0;
+  lb_status st = check_linear_args(name, L, branch_mask, x, batch, ldx, y, ldy, flags, sel, &nsel);
+  if (st != LB_OK) return st;
+  const LayerWs w = layer_ws(*L, sel, nsel, kDecodeMaxBatch);
+  const uint32_t path = flags & 3u;
+  const int chunk = decode_chunk_tokens(w.zs);
+  if (path == LB_PATH_DECODE && chunk == 0)
+    return fail(LB_ERR_UNSUPPORTED, "%s: rank %d exceeds the decode kernels' LDS", name, w.zs);
+  const bool prefill = path == LB_PATH_PREFILL || (path == LB_PATH_AUTO && (batch > kDecodeMaxBatch || chunk == 0));
+  const size_t fixed = kWsHeader + w.z_bytes;
+  int64_t max_tokens = LB_PREFILL_MAX_TOKENS;
+  if (prefill) {
+    // prefill in chunks whose rank-space intermediate fits the scratch
+    const size_t per_token = (size_t)w.zs_p * sizeof(uint16_t);
+    const int64_t fit = fixed < kScratchBytes ? (int64_t)((kScratchBytes - fixed) / per_token) / 128 * 128 : 0;
+    if (fit < 1)
+      return fail(LB_ERR_UNSUPPORTED, "%s: %zu scratch bytes hold no 128-token prefill chunk of this layer", name,
+                  kScratchBytes);
+    max_tokens = fit < max_tokens ? fit : max_tokens;
+  } else if (fixed > kScratchBytes) {
+    return fail(LB_ERR_UNSUPPORTED, "%s: the layer needs %zu bytes of scratch, the limit is %zu", name, fixed,
+                kScratchBytes);
+  }
+  void* ws = nullptr;
+  st = scratch_for_device(&ws);
+  if (st != LB_OK) return st;
+  return linear_fwd_impl(name, L, sel, nsel, x, batch, ldx, y, ldy, ws, flags, max_tokens, (hipStream_t)stream);
 }
 
 size_t littlebit_block_workspace_bytes(const lb_layer L[7], int64_t batch) {

@@ -11,6 +11,8 @@ The functions keep the C names:
 * ``littlebit_transpose_packed(bits, R, K)`` -> packing of the K x R transpose
   (``LittleBitLayer.transposed()`` builds the layer of W^T from it)
 * ``littlebit_linear_fwd(layer, x, branch_mask=3, path=LB_PATH_AUTO)`` -> y
+* ``littlebit_linear_fwd_noalloc(layer, x, ...)`` -> y, on the library's
+  per-device scratch instead of a workspace
 * ``littlebit_block_fwd(layers, x_qkv, x_o, x_gu, x_down)`` -> list of 7 y
 * ``littlebit_workspace_error(ws)`` -> device int32 tensor, non-zero if a
   decode call on ``ws`` gave up waiting since the previous report
@@ -46,7 +48,7 @@ EXPORTED = (
     "littlebit_packed_bytes", "littlebit_pack", "littlebit_linear_workspace_bytes",
     "littlebit_linear_fwd", "littlebit_block_workspace_bytes", "littlebit_block_fwd",
     "littlebit_status_string", "littlebit_last_error", "littlebit_transpose_packed",
-    "littlebit_workspace_error",
+    "littlebit_workspace_error", "littlebit_linear_fwd_noalloc",
 )
 INIT_EXPORTED = ("littlebit_dual_svid_init", "littlebit_init_last_error")
 
@@ -92,6 +94,8 @@ def _load():
     lib.littlebit_block_workspace_bytes.restype = sz
     lib.littlebit_block_fwd.argtypes = [ctypes.POINTER(_Layer), vp, vp, vp, vp, ctypes.POINTER(vp), i64, vp, sz, vp]
     lib.littlebit_block_fwd.restype = i32
+    lib.littlebit_linear_fwd_noalloc.argtypes = [ctypes.POINTER(_Layer), u32, vp, i64, i64, vp, i64, u32, vp]
+    lib.littlebit_linear_fwd_noalloc.restype = i32
     lib.littlebit_workspace_error.argtypes = [vp, sz, vp, vp]
     lib.littlebit_workspace_error.restype = i32
     lib.littlebit_status_string.argtypes = [i32]
@@ -308,6 +312,24 @@ def littlebit_linear_fwd(layer: LittleBitLayer, x: torch.Tensor, branch_mask: in
     ws = workspace if workspace is not None else _WS.get(need, x.device, sp)
     _check(LIB.littlebit_linear_fwd(ctypes.byref(s), branch_mask, _ptr(x), batch, x.stride(0),
                                     _ptr(y), y.stride(0), _ptr(ws), ws.numel(), path, sp))
+    return y
+
+
+def littlebit_linear_fwd_noalloc(layer: LittleBitLayer, x: torch.Tensor, branch_mask: int = 3,
+                                 path: int = LB_PATH_AUTO, out: Optional[torch.Tensor] = None,
+                                 stream=None) -> torch.Tensor:
+    """littlebit_linear_fwd on the library's own per-device scratch (no
+    workspace argument; the library allocates nothing).  `out` must be given
+    where the caller cannot allocate either."""
+    if x.dim() != 2 or x.dtype != torch.float16 or not x.is_cuda or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D CUDA float16 tensor with unit column stride")
+    batch = x.shape[0]
+    if branch_mask == 3 and len(layer.branches) == 1:
+        branch_mask = 1
+    y = out if out is not None else torch.empty((batch, layer.m), dtype=torch.float16, device=x.device)
+    s = layer.c_struct()
+    _check(LIB.littlebit_linear_fwd_noalloc(ctypes.byref(s), branch_mask, _ptr(x), batch, x.stride(0),
+                                            _ptr(y), y.stride(0), path, _stream_ptr(stream)))
     return y
 
 

@@ -182,6 +182,26 @@ lb_status littlebit_linear_fwd(const lb_layer *L, uint32_t branch_mask,
                                size_t ws_bytes, uint32_t flags, void *stream);
 
 /*
+ * littlebit_linear_fwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the intermediates live in a scratch
+ * array that the library holds in device memory, 8 MiB per device, from the
+ * first use of the library on the device until the process ends.  Same
+ * arguments, results and residency precondition as littlebit_linear_fwd;
+ * prefill runs in chunks of tokens whose intermediate fits the scratch.
+ * Nothing is allocated or freed and nothing is synchronised.  Every call on
+ * one device shares that device's scratch and leaves its contents for the
+ * next: calls that may overlap on one device (different streams, or threads
+ * without ordering) race and must not be issued.  LB_ERR_UNSUPPORTED if the
+ * layer's decode intermediate exceeds the scratch (it cannot within the
+ * rank and size limits above) or no 128-token prefill chunk fits.
+ */
+lb_status littlebit_linear_fwd_noalloc(const lb_layer *L, uint32_t branch_mask,
+                                       const uint16_t *x, int64_t batch,
+                                       int64_t ldx, uint16_t *y, int64_t ldy,
+                                       uint32_t flags, void *stream);
+
+/*
  * The seven projections of one decoder block in one call (q, k, v, o, gate,
  * up, down; all branches of each).  The pages compress the linear layers of
  * the Transformer blocks and keep the architecture (explainx.ai explainer,

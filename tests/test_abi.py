@@ -177,3 +177,24 @@ def test_dual_svid_init_rejects_bad_arguments():
     arr[1] = lb._InitBranch(FAKE, None, FAKE, FAKE, FAKE)
     assert f(FAKE, 64, 32, 32, 8, 2, 0, arr, None) == lb.LB_ERR_INVALID_ARG
     assert "NULL output" in init.littlebit_init_last_error().decode()
+
+
+def _noalloc(layer, mask=3, x=FAKE, batch=1, ldx=64, y=FAKE, ldy=64, flags=0):
+    return lb.LIB.littlebit_linear_fwd_noalloc(ctypes.byref(layer), mask, x, batch, ldx, y, ldy, flags, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(x=None), lb.LB_ERR_INVALID_ARG),
+    (dict(y=None), lb.LB_ERR_INVALID_ARG),
+    (dict(batch=0), lb.LB_ERR_INVALID_ARG),
+    (dict(mask=4), lb.LB_ERR_INVALID_ARG),
+    (dict(ldx=32), lb.LB_ERR_INVALID_ARG),
+    (dict(x=FAKE + 1), lb.LB_ERR_INVALID_ARG),
+    (dict(flags=3), lb.LB_ERR_INVALID_ARG),
+    (dict(flags=1, batch=17), lb.LB_ERR_INVALID_ARG),
+])
+def test_noalloc_rejects_bad_arguments(kwargs, status):
+    """The no-alloc variant validates like littlebit_linear_fwd, before it
+    looks up its scratch or launches anything."""
+    assert _noalloc(_layer(), **kwargs) == status
+    assert "littlebit_linear_fwd_noalloc" in lb.littlebit_last_error()
