@@ -34,7 +34,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                 "-mllvm", "-amdgpu-kernarg-preload-count=14"]
 
-LAYER_SOURCES = ("decode.hip", "littlebit_host.hip", "pack.hip", "prefill.hip")
+LAYER_SOURCES = ("decode.hip", "decode1.hip", "littlebit_host.hip", "pack.hip", "prefill.hip")
 INIT_SOURCES = ("init.hip",)
 
 

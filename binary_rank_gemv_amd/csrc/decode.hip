@@ -25,6 +25,7 @@
 // workgroup issues the loads of its phase-B sign words and row scales during
 // phase A, so their latency overlaps phase A.
 #include "lb_common.h"
+#include "lb_sync.h"
 
 #include <vector>
 
@@ -40,60 +41,10 @@
 // dynamic LDS a launch of that variant may take: what the static arrays
 // (partial sums 24 KB, two z tiles 1 KB, the copy, the row-scale table) leave of 160 KB
 #define LB_UPRE_DYN_MAX (160 * 1024 - LB_MAXT * LB_WAVES * 256 * 4 - 1024 - LB_UPRE_BYTES - 2 * LB_UPRE_HROWS)
-#define LB_SPIN_LIMIT (1 << 20)
 #define LB_MAX_BATCH 16               // tokens of a decode call (phase-A kernels for 1 and for up to 16)
-
-// workspace header (bytes): one 64-bit call counter per workgroup of the
-// single launch, then an error word set when a poll gives up.
-#define LB_SYNC_CTR 0  // + 8 * workgroup
-#define LB_SYNC_ERR 2048
 
 namespace {
 
-__device__ inline uint32_t ld32c(const void* p) {
-  return __hip_atomic_load(reinterpret_cast<uint32_t*>(const_cast<void*>(p)), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline void st32c(void* p, uint32_t v) {
-  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline void st64c(void* p, uint64_t v) {
-  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline void add64c_noret(void* p, uint64_t v) {
-  (void)__hip_atomic_fetch_add(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Raw buffer resource over `bytes` bytes (loads beyond return 0).
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
-}
-// 16 bytes (two tagged z words) with a device-coherent (sc1) load.
-__device__ inline u32x4 ld_tagged2(__amdgpu_buffer_rsrc_t rs, int byte_off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(rs, byte_off, 0, 16 /* sc1 */);
-}
-
-// The z tag of a single-launch call from the workgroup's call counter: the
-// counter + 1, skipping 0 when the 32-bit value wraps.  Tag 0 marks z stored
-// by the two-launch path (phase A alone), so no poll ever accepts it.
-__device__ inline uint32_t call_tag(uint32_t ctr) {
-  const uint32_t t = ctr + 1u;
-  return t + (t == 0u ? 1u : 0u);
-}
-
-// Compiler-only barrier: memory may have changed here, so loads after it are
-// neither hoisted above it nor merged with loads before it.
-__device__ inline void compiler_memory_barrier() { __asm__ volatile("" ::: "memory"); }
-
-// Index of the calling wave in its workgroup, as a wave-uniform (scalar) value.
-__device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
-
-// Hands `v` to the compiler as if modified here, so work that depends on it
-// (and the wait for the load that produced it) is not hoisted above this point.
-__device__ inline uint32_t late(uint32_t v) {
-  __asm__ volatile("" : "+v"(v));
-  return v;
-}
 // The decode kernel's explicit arguments in order, as laid out in the kernel
 // argument segment (each at its natural alignment, as in a struct).
 struct LbDecodeKernargs {
@@ -1281,14 +1232,45 @@ static hipError_t fused_occupancy(int& occ) {
   return e;
 }
 
+hipError_t lb_decode1_occupancy(bool single, size_t lds, int& occ);
+size_t lb_decode1_lds_bytes(const LbDecodeArgs& a);
+hipError_t lb_launch_decode1(const LbDecodeArgs& args, int G, void* sync, hipStream_t stream);
+
+// Workgroups of a single launch on this device (0: none fits).  Every single
+// launch, of any decode kernel, uses this one grid, so that every workgroup's
+// call counter in a workspace advances by one per call.
+static hipError_t fused_grid(int& G) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  G = 0;
+  if (dev < 0 || dev >= 64) return hipSuccess;
+  if (g_fused_grid[dev] == 0) {
+    int ncu = 0, occa = 0, occb = 0, occ1 = 0, occ2 = 0;
+    e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    // every workgroup of the single launch must be resident at once: size
+    // the grid for the largest dynamic LDS a launch may request
+    e = fused_occupancy<1>(occa);
+    if (e != hipSuccess) return e;
+    e = fused_occupancy<LB_MAX_BATCH>(occb);
+    if (e != hipSuccess) return e;
+    e = lb_decode1_occupancy(true, LB_DECODE1_LDS_MAX, occ1);
+    if (e != hipSuccess) return e;
+    e = lb_decode1_occupancy(false, LB_DECODE1_LDS_MAX, occ2);
+    if (e != hipSuccess) return e;
+    g_fused_grid[dev] = (occa >= 1 && occb >= 1 && occ1 >= 1 && occ2 >= 1) ? (ncu < LB_MAX_GRID ? ncu : LB_MAX_GRID) : -1;
+  }
+  G = g_fused_grid[dev] > 0 ? g_fused_grid[dev] : 0;
+  return hipSuccess;
+}
+
 template <bool SINGLE, int MAXB>
 static hipError_t launch_decode_t(const LbDecodeArgs& args, int chunk_pairs, void* sync, int allow_fused,
                                   hipStream_t stream) {
   const size_t lds = lb_decode_lds_bytes(args, chunk_pairs);
   if (lds > LB_DECODE_LDS_MAX) return hipErrorInvalidValue;  // the host routes such calls elsewhere
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
   // preloaded copies of layer 0's phase-A fields (single-layer kernels)
   const LbLayerArgs& L0 = args.L[0];
   const uint8_t* vb0 = SINGLE ? L0.br[0].vbits : nullptr;
@@ -1300,20 +1282,10 @@ static hipError_t launch_decode_t(const LbDecodeArgs& args, int chunk_pairs, voi
   auto misc = [&](const LbDecodeArgs& a) {
     return (uint32_t)a.vq | ((uint32_t)a.vr << 8) | ((uint32_t)a.batch << 16) | ((uint32_t)chunk_pairs << 21);
   };
-  if (allow_fused && dev >= 0 && dev < 64) {
-    if (g_fused_grid[dev] == 0) {
-      int ncu = 0, occa = 0, occb = 0;
-      e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
-      if (e != hipSuccess) return e;
-      // every workgroup of the single launch must be resident at once: size
-      // the grid for the largest dynamic LDS a launch may request
-      e = fused_occupancy<1>(occa);
-      if (e != hipSuccess) return e;
-      e = fused_occupancy<LB_MAX_BATCH>(occb);
-      if (e != hipSuccess) return e;
-      g_fused_grid[dev] = (occa >= 1 && occb >= 1) ? (ncu < LB_MAX_GRID ? ncu : LB_MAX_GRID) : -1;
-    }
-    const int G = g_fused_grid[dev];
+  if (allow_fused) {
+    int G = 0;
+    e = fused_grid(G);
+    if (e != hipSuccess) return e;
     if (G > 0) {
       LbDecodeArgs a = args;
       a.vq = a.nvt / G; a.vr = a.nvt % G;
@@ -1353,9 +1325,18 @@ static hipError_t launch_decode_t(const LbDecodeArgs& args, int chunk_pairs, voi
 
 hipError_t lb_launch_decode(const LbDecodeArgs& args, int chunk_pairs, void* sync, int allow_fused,
                             hipStream_t stream) {
-  if (args.batch == 1)
-    return args.nlayers == 1 ? launch_decode_t<true, 1>(args, chunk_pairs, sync, allow_fused, stream)
-                             : launch_decode_t<false, 1>(args, chunk_pairs, sync, allow_fused, stream);
+  if (args.batch == 1) {
+    // one token: the sparse-instruction kernels of decode1.hip
+    if (lb_decode1_lds_bytes(args) > LB_DECODE1_LDS_MAX) return hipErrorInvalidValue;
+    int G = 0;
+    if (allow_fused) {
+      hipError_t e = fused_grid(G);
+      if (e != hipSuccess) return e;
+    }
+    LbDecodeArgs a = args;
+    if (G > 0 && a.nlayers > 1) cost_split(a, G);
+    return lb_launch_decode1(a, G, sync, stream);
+  }
   return args.nlayers == 1 ? launch_decode_t<true, LB_MAX_BATCH>(args, chunk_pairs, sync, allow_fused, stream)
                            : launch_decode_t<false, LB_MAX_BATCH>(args, chunk_pairs, sync, allow_fused, stream);
 }

@@ -1,0 +1,804 @@
+// One-token decode of the LittleBit layer on gfx950's sparse matrix
+// instruction (v_smfmac_f32_16x16x64_f16).
+//
+// Per branch (explainx.ai explainer, "How it works" items 1-3):
+//   u = g*x (fp16), t = sign(V)^T u, z = l*t (fp16), s = sign(U) z, y = sum_b h_b*s_b.
+//
+// The signs never become operand values.  The sparse instruction's A operand
+// is 16 rows x 64 positions in which every group of 4 positions holds 2
+// values, placed by a 2-bit index each.  Here every row of A holds the
+// activations of its lane group (a lane's 8 values), B holds +1 at even and -1
+// at odd positions in every column, and each activation may sit at an even
+// (+1) or the next odd (-1) position: its weight's sign bit is the low bit of
+// its index.  Row i of the product is then the sum of +-a with row i's signs,
+// exactly (every column alike; column 0 is used).  The raw LB16 word of a
+// lane gives the indices of four instructions with three VALU operations:
+// (w & 0x55555555) | 0x88888888 and the same of w >> 1; the activations are
+// stored in the matching order ("sparse order", below), so no bit is moved.
+//
+// Structure (as in the multi-token kernels of decode.hip): phase A runs the V
+// pass over 16-row tiles of sign(V)^T and stores z as tagged 64-bit words
+// [call tag | two fp16]; phase B polls the z range of each wave, then runs the
+// U pass over groups of 16-row output tiles with the h epilogue.  One launch
+// of one 512-thread workgroup per compute unit (MODE 2), or two launches
+// (MODE 0: phase A with tag 0, MODE 1: phase B without polling).  A tile's
+// sums do not depend on the workgroup or launch that runs it, so every path
+// returns the same bits.
+#include <stddef.h>
+
+#include "lb_common.h"
+#include "lb_sync.h"
+
+#define DK_WAVES 8
+#define DK_THREADS (64 * DK_WAVES)
+#define DK_VPW 16  // V-pass pairs per wave per batch of sign words
+#define DK_UTG 8   // U tiles per group (one epilogue)
+#define DK_UPW 4   // U-pass pairs per wave per block of sign words
+
+namespace {
+
+typedef f16 f16x16 __attribute__((ext_vector_type(16)));
+
+// ------------------------------------------------------------ sparse order
+// Reduction index k of a packed factor (k < 64 NU) is stored at
+// sparse_pos(k): unit u = k / 64 holds steps 2u (q = 0) and 2u + 1 (q = 1);
+// lane group G owns k = 64u + 32q + 8G + e, e = 0..7.  For unit u and group G
+// the 16 halves at 64u + 16G are the A operands of two instructions, "even"
+// (the signs at the even bits of the lane's 16-bit unit) then "odd".  Bit b
+// of the unit is element (q, e) with 8(e%2) + 7 - (4q + e/2) = b (LB16);
+// (unit & 0x5555) puts the bits 4d and 4d+2 in index nibble d, whose two
+// values are the operand's slots 2d and 2d+1, and likewise for unit >> 1.
+// Worked out: element (q, e) is slot 2 dword + half of operand `which` with
+//   which = 1 - (e/2 % 2), dword = 2 (e % 2) + 1 - q, half = 1 - e/4.
+__host__ __device__ inline int sparse_pos(int k) {
+  const int u = k >> 6, q = (k >> 5) & 1, G = (k >> 3) & 3, e = k & 7;
+  const int which = 1 - ((e >> 1) & 1), dword = 2 * (e & 1) + 1 - q, half = 1 - (e >> 2);
+  return 64 * u + 16 * G + 8 * which + 2 * dword + half;
+}
+
+// Workgroup barrier that orders LDS only.  Global loads stay in flight across
+// it (__syncthreads' fence would also wait for every outstanding global load,
+// which would serialise the prefetches with each barrier).  The kernels share
+// data between waves only through LDS.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// B operand: +1 at even, -1 at odd positions of every column.
+__device__ inline f16x16 alt_ones() {
+  uint32_t d = 0xBC003C00u;
+  __asm__ volatile("" : "+v"(d));
+  typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+  u32x8 v = {d, d, d, d, d, d, d, d};
+  return __builtin_bit_cast(f16x16, v);
+}
+
+__device__ __forceinline__ f32x4 smfmac(f16x8 a, f16x16 b, f32x4 c, int idx, int abid) {
+  if (abid == 0) return __builtin_amdgcn_smfmac_f32_16x16x64_f16(a, b, c, idx, 0, 0);
+  return __builtin_amdgcn_smfmac_f32_16x16x64_f16(a, b, c, idx, 0, 1);
+}
+
+// A lane's activation operands of one pair (sparse order): even and odd
+// operands of the pair's two units (the second unit's only when it exists).
+struct PairAct {
+  f16x8 e0, o0, e1, o1;
+};
+
+__device__ __forceinline__ PairAct load_pair_act(const uint16_t* act, bool two_units) {
+  const int G = (threadIdx.x & 63) >> 4;
+  const uint16_t* a0 = act + 16 * G;
+  PairAct a;
+  a.e0 = *reinterpret_cast<const f16x8*>(a0);
+  a.o0 = *reinterpret_cast<const f16x8*>(a0 + 8);
+  a.e1 = two_units ? *reinterpret_cast<const f16x8*>(a0 + 64) : a.e0;
+  a.o1 = two_units ? *reinterpret_cast<const f16x8*>(a0 + 72) : a.o0;
+  return a;
+}
+
+// The products of one pair: raw LB16 word w (for an odd last unit, the
+// lane's unit in bits 0..15 and two_units false).  Three VALU operations
+// make the indices of up to four instructions.
+__device__ __forceinline__ void pair_products(const PairAct& a, uint32_t w, bool two_units, const f16x16& B,
+                                              f32x4& acc0, f32x4& acc1) {
+  const int ie = (int)((w & 0x55555555u) | 0x88888888u);
+  const int io = (int)(((w >> 1) & 0x55555555u) | 0x88888888u);
+  acc0 = smfmac(a.e0, B, acc0, ie, 0);
+  acc1 = smfmac(a.o0, B, acc1, io, 0);
+  if (two_units) {
+    acc0 = smfmac(a.e1, B, acc0, ie, 1);
+    acc1 = smfmac(a.o1, B, acc1, io, 1);
+  }
+}
+
+// Lane's raw word of pair p of a tile (units 2p, 2p + 1), or, for an odd last
+// unit, the lane's own 16-bit unit in the low half.
+// The address is selected first, so every call is one load that is not waited
+// for here (two conditional loads would each be waited for in turn).
+__device__ __forceinline__ uint32_t pair_word(const uint8_t* tile, int p, int nu) {
+  const int lane = threadIdx.x & 63;
+  const bool full = 2 * p + 1 < nu;
+  return *reinterpret_cast<const uint32_t*>(tile + 256 * p + (full ? 4 * lane : 4 * (lane >> 1)));
+}
+
+// The word as pair_products takes it: an odd last unit's word holds this
+// lane's unit and its neighbour's; the lane's own goes to bits 0..15.
+__device__ __forceinline__ uint32_t pair_bits(uint32_t w, bool full) {
+  const int lane = threadIdx.x & 63;
+  return full ? w : ((lane & 1) ? (w >> 16) : (w & 0xFFFFu));
+}
+
+// ------------------------------------------------------------- arguments
+// The kernels read the header and layer records of the argument block from
+// an LDS copy: one round of 16-byte loads at kernel start, overlapping the
+// first sign-word loads, instead of scalar loads on the critical path.
+// Fields that steer control flow or form addresses are read into scalar
+// registers (readfirstlane: every lane of a wave holds the same value).
+#define DK_ARGS_BYTES ((int)offsetof(LbDecodeArgs, vt_begin))  // header + layer records
+static_assert(DK_ARGS_BYTES % 16 == 0, "16-byte copy of the argument block");
+
+__device__ __forceinline__ int rfl(int v) { return __builtin_amdgcn_readfirstlane(v); }
+// A pointer into device memory read from the LDS copy: made wave-uniform and
+// marked as global, so that its loads are global (vector memory counter only)
+// rather than flat ones, which the LDS waits would also have to drain.
+template <class T>
+__device__ __forceinline__ T* rflp(T* p) {
+  typedef __attribute__((address_space(1))) T GT;
+  const uint64_t u = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = (uint32_t)rfl((int)(uint32_t)u), hi = (uint32_t)rfl((int)(uint32_t)(u >> 32));
+  return (T*)(GT*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// One layer's fields, wave-uniform; branch fields are selected with
+// `b ? x1 : x0`, so no array is indexed at run time.
+struct SL {
+  const uint8_t *vb0, *vb1, *ub0, *ub1;
+  const uint16_t *h0, *h1, *l0, *l1, *g0, *g1;
+  const uint16_t* x;
+  uint16_t* y;
+  uint64_t* z;
+  int r0, r1, zoff0, zoff1, nb, m, n;
+  __device__ int r(int b) const { return b ? r1 : r0; }
+  __device__ int zoff(int b) const { return b ? zoff1 : zoff0; }
+  __device__ const uint8_t* vb(int b) const { return b ? vb1 : vb0; }
+  __device__ const uint8_t* ub(int b) const { return b ? ub1 : ub0; }
+  __device__ const uint16_t* l(int b) const { return b ? l1 : l0; }
+  __device__ const uint16_t* g(int b) const { return b ? g1 : g0; }
+};
+
+__device__ __forceinline__ SL scalar_layer(const LbLayerArgs& L) {
+  SL s;
+  s.vb0 = rflp(L.br[0].vbits);
+  s.vb1 = rflp(L.br[1].vbits);
+  s.ub0 = rflp(L.br[0].ubits);
+  s.ub1 = rflp(L.br[1].ubits);
+  s.h0 = rflp(L.br[0].h);
+  s.h1 = rflp(L.br[1].h);
+  s.l0 = rflp(L.br[0].l);
+  s.l1 = rflp(L.br[1].l);
+  s.g0 = rflp(L.br[0].g);
+  s.g1 = rflp(L.br[1].g);
+  s.x = rflp(L.x);
+  s.y = rflp(L.y);
+  s.z = rflp(L.z);
+  s.r0 = rfl(L.br[0].r);
+  s.r1 = rfl(L.br[1].r);
+  s.zoff0 = rfl(L.br[0].zoff);
+  s.zoff1 = rfl(L.br[1].zoff);
+  s.nb = rfl(L.nb);
+  s.m = rfl(L.m);
+  s.n = rfl(L.n);
+  return s;
+}
+
+// ------------------------------------------------------------- tile map
+__host__ __device__ inline int nunits(int k) { return (k + 63) >> 6; }
+
+// Layer and branch slot (2 layer + branch) of global V tile t, and the tile
+// inside its branch.
+template <bool SINGLE>
+__device__ __forceinline__ int v_slot1(const LbDecodeArgs& A, int t, int& tile) {
+  int k = 0;
+  if (SINGLE) {
+    k = t >= A.vt_end[0] ? 1 : 0;
+  } else {
+    const int nl = rfl(A.nlayers);
+#pragma unroll
+    for (int q = 0; q < 2 * LB_MAX_LAYERS - 1; ++q)
+      if (q < 2 * nl - 1 && t >= A.vt_end[q]) k = q + 1;
+  }
+  k = rfl(k);
+  tile = rfl(t - (k > 0 ? A.vt_end[k - 1] : 0));
+  return k;
+}
+
+// Layer of global U tile t and the tile inside it.
+template <bool SINGLE>
+__device__ __forceinline__ int u_layer1(const LbDecodeArgs& A, int t, int& tile) {
+  int li = 0;
+  if (!SINGLE) {
+    const int nl = rfl(A.nlayers);
+#pragma unroll
+    for (int i = 0; i < LB_MAX_LAYERS - 1; ++i)
+      if (i < nl - 1 && t >= A.ut_end[i]) li = i + 1;
+  }
+  li = rfl(li);
+  tile = rfl(t - (li > 0 ? A.ut_end[li - 1] : 0));
+  return li;
+}
+
+__device__ __forceinline__ void share1(int q, int r, int i, int& beg, int& end) {
+  beg = i * q + min(i, r);
+  end = beg + q + (i < r ? 1 : 0);
+}
+
+// ------------------------------------------------------------- phase A
+// u = fp16(g*x) of one branch of one layer, in sparse order, into LDS (all
+// 64 nu values; zero beyond n).  Thread i builds natural groups of 8 inputs
+// i, i + 512, ...; the 8 values of a group share unit, step and lane group
+// and land as four 32-bit pairs.
+__device__ __forceinline__ void stage_u(const uint16_t* x, const uint16_t* g, int n, uint16_t* up) {
+  const int nu = nunits(n);
+  const bool aligned16 = (((uintptr_t)x) & 15) == 0;  // g is 16-byte aligned by contract
+  for (int grp = threadIdx.x; grp < 8 * nu; grp += DK_THREADS) {
+    const int k = 8 * grp;
+    // products as packed pairs: dword d holds elements 2d (low) and 2d + 1
+    // (one fp16 rounding of the exact product, as fp32 then fp16 would give)
+    u32x4 uw;
+    if (aligned16 && k + 8 <= n) {
+      const uint4 xr = *reinterpret_cast<const uint4*>(x + k);
+      const uint4 gr = *reinterpret_cast<const uint4*>(g + k);
+      uw = __builtin_bit_cast(u32x4, __builtin_bit_cast(f16x8, xr) * __builtin_bit_cast(f16x8, gr));
+    } else {
+      // element by element from always-valid indices (no branch, so the 16
+      // loads are in flight together), zero at and beyond n
+      uint32_t h[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int kk = min(k + e, n - 1);
+        const f16 uv = __builtin_bit_cast(f16, x[kk]) * __builtin_bit_cast(f16, g[kk]);
+        h[e] = (k + e < n) ? (uint32_t)__builtin_bit_cast(uint16_t, uv) : 0u;
+      }
+#pragma unroll
+      for (int d = 0; d < 4; ++d) uw[d] = h[2 * d] | (h[2 * d + 1] << 16);
+    }
+    // elements (e + 4, e) share a 32-bit pair (low, high) for e = 0..3
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t lo = (uw[(e + 4) >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+      const uint32_t hi = (uw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+      *reinterpret_cast<uint32_t*>(up + sparse_pos(k + e + 4)) = lo | (hi << 16);  // even position: low half
+    }
+  }
+}
+
+// Word (of a branch's z region) holding z value pair j (0..7) of V tile T in
+// sparse order: tile T covers rows 64u + 16 tl + i (u = T / 4, tl = T % 4),
+// i.e. step q = tl / 2, lane groups 2 (tl % 2) and 2 (tl % 2) + 1; pair j
+// is group 2 (tl % 2) + j / 4, elements (e + 4, e) with e = j % 4, which
+// share one word (low, high halves) and belong to rows i + 4 and i,
+// i = 8 (j / 4) + e.
+__device__ __forceinline__ int z_word(int T, int j) {
+  const int u = T >> 2, tl = T & 3, q = tl >> 1;
+  const int G = 2 * (tl & 1) + (j >> 2), e = j & 3;
+  const int which = 1 - ((e >> 1) & 1), dword = 2 * (e & 1) + 1 - q;
+  return 32 * u + 8 * G + 4 * which + dword;
+}
+
+// Stores the 16 z values of V tile T of branch b (zv in LDS) as 8 tagged
+// words in sparse order; the branch's last tile also writes the tagged zero
+// words of the padding tiles up to 64 nu rows.
+__device__ __forceinline__ void store_z_tile(const SL& L, int b, int T, uint32_t tag, const uint16_t* zv) {
+  const int tid = threadIdx.x;
+  const int r = L.r(b), nu = nunits(r);
+  uint64_t* zb = L.z + (L.zoff(b) >> 1);
+  if (tid < 8) {
+    const int i = 8 * (tid >> 2) + (tid & 3);
+    const uint32_t v = (uint32_t)zv[i + 4] | ((uint32_t)zv[i] << 16);
+    st64c(zb + z_word(T, tid), (uint64_t)tag | ((uint64_t)v << 32));
+  }
+  const int ntv = (r + 15) >> 4;
+  if (T == ntv - 1) {
+    for (int w = tid; w < 8 * (4 * nu - ntv); w += DK_THREADS) st64c(zb + z_word(ntv + (w >> 3), w & 7), (uint64_t)tag);
+  }
+}
+
+// The V pass over one tile: wave w sums its even share [pa, pb) of the
+// tile's pairs, the sign words in batches of DK_VPW pairs per wave.
+struct VTile {
+  const uint8_t* tile;
+  int nu, pa, pb;
+};
+
+__device__ __forceinline__ VTile v_tile_geom(const uint8_t* vbits, int n, int T) {
+  VTile v;
+  v.nu = nunits(n);
+  const int np = (v.nu + 1) >> 1, wave = wave_id();
+  v.tile = vbits + (long)T * lb16_tile_bytes(n);
+  v.pa = (np * wave) >> 3;
+  v.pb = (np * (wave + 1)) >> 3;
+  return v;
+}
+
+// Sign words of batch [pc, pc + DK_VPW) (clamped to the share: unconditional
+// loads keep the wait counts static; words beyond pb are never used).
+__device__ __forceinline__ void v_load_words(const VTile& v, int pc, uint32_t (&w)[DK_VPW]) {
+  const int plast = max(v.pb - 1, 0);
+#pragma unroll
+  for (int i = 0; i < DK_VPW; ++i) w[i] = pair_word(v.tile, min(pc + i, plast), v.nu);
+}
+
+// Returns this lane's partial sums (rows 4 (lane / 16) + q of column
+// lane % 16); `w` holds the first batch's words on entry.
+__device__ __forceinline__ f32x4 v_tile_sums(const VTile& v, const uint16_t* up, const f16x16& B,
+                                             uint32_t (&w)[DK_VPW]) {
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  for (int pc = v.pa; pc < v.pb; pc += DK_VPW) {
+    if (pc != v.pa) v_load_words(v, pc, w);
+#pragma unroll
+    for (int i = 0; i < DK_VPW; ++i) {
+      const int p = pc + i;
+      if (p < v.pb) {
+        const bool two = 2 * p + 1 < v.nu;
+        pair_products(load_pair_act(up + 128 * p, two), pair_bits(late(w[i]), two), two, B, acc0, acc1);
+      }
+    }
+  }
+  return acc0 + acc1;
+}
+
+// ------------------------------------------------------------- phase B
+// Copies units [u0, u1) of branch b's z (tagged words) into zl (sparse order,
+// values only), polling until every word carries `tag` (unless !check).
+// Chunk c (16 bytes: two words) of the range is load c / 64 of lane c % 64.
+template <int NL>
+__device__ __forceinline__ void copy_z(const SL& L, int b, int u0, int u1, uint32_t tag, bool check, uint8_t* sync,
+                                       uint16_t* zl) {
+  const int lane = threadIdx.x & 63;
+  const int nchunks = 16 * (u1 - u0);
+  if (nchunks <= 0) return;
+  const uint8_t* base = reinterpret_cast<const uint8_t*>(L.z + (L.zoff(b) >> 1) + 32 * u0);
+  const int bytes = 16 * nchunks;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, bytes);
+  uint16_t* dst = zl + L.zoff(b) + 64 * u0;
+  for (int c0 = 0; c0 < nchunks; c0 += 64 * NL) {
+    uint32_t todo = 0;
+    u32x4 q[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i)
+      if (c0 + 64 * i < nchunks) todo |= 1u << i;
+    int spins = 0;
+    for (;;) {
+      compiler_memory_barrier();
+#pragma unroll
+      for (int i = 0; i < NL; ++i)
+        if (todo & (1u << i)) q[i] = ld_tagged2(rs, 16 * (c0 + 64 * i + lane));  // beyond the range: zeros
+      if (!check) break;
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        if (todo & (1u << i)) {
+          const bool in = c0 + 64 * i + lane < nchunks;
+          const bool ok = !in || ((q[i][0] == tag) & (q[i][2] == tag));
+          if (__all(ok)) todo &= ~(1u << i);
+        }
+      }
+      if (todo == 0) break;
+      if (++spins > LB_SPIN_LIMIT) {
+        st32c(sync + LB_SYNC_ERR, 1u);
+        break;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int c = c0 + 64 * i + lane;
+      if (c < nchunks) {
+        uint2 d;
+        d.x = q[i][1];
+        d.y = q[i][3];
+        *reinterpret_cast<uint2*>(dst + 4 * c) = d;
+      }
+    }
+  }
+}
+
+// Wave's phase-B role for a layer: branch and pair range of that branch.
+__device__ __forceinline__ void u_role1(const SL& L, int wave, int& b, int& p0, int& p1) {
+  if (L.nb == 2) {
+    b = wave >> 2;
+    const int np = (nunits(L.r(b)) + 1) >> 1, w = wave & 3;
+    p0 = (np * w) >> 2;
+    p1 = (np * (w + 1)) >> 2;
+  } else {
+    b = 0;
+    const int np = (nunits(L.r0) + 1) >> 1;
+    p0 = (np * wave) >> 3;
+    p1 = (np * (wave + 1)) >> 3;
+  }
+}
+
+// A block of U sign words: tiles [t0, t0 + nt) of one layer, this wave's pairs
+// [pc, pc + DK_UPW) of its range (clamped loads keep the wait counts static).
+struct UBlock {
+  uint32_t w[DK_UTG][DK_UPW];
+};
+
+// Row scales (fp16 bits) of this thread's epilogue entry of a group of tiles
+// [t0, t0 + nt): tile (tid / 16) % DK_UTG, row tid % 16, clamped to a valid
+// row (threads beyond the group's entries never store).  Unconditional loads,
+// so no wait is placed at a branch join.
+struct HPair {
+  uint32_t h0, h1;
+};
+
+__device__ __forceinline__ HPair load_group_h(const SL& L, int t0, int nt) {
+  const int tid = threadIdx.x;
+  const int row = min(16 * (t0 + min((tid >> 4) % DK_UTG, nt - 1)) + (tid & 15), L.m - 1);
+  const uint16_t* h1p = L.nb == 2 ? L.h1 : L.h0;
+  HPair h;
+  h.h0 = L.h0[row];
+  h.h1 = h1p[row];
+  return h;
+}
+
+__device__ __forceinline__ void load_ublock(const SL& L, int b, int t0, int nt, int pc, int p1, UBlock& U) {
+  const int r = L.r(b), nu = nunits(r);
+  const long tb = lb16_tile_bytes(r);
+  const uint8_t* base = L.ub(b);
+  const int plast = max(p1 - 1, 0);
+#pragma unroll
+  for (int k = 0; k < DK_UTG; ++k)
+#pragma unroll
+    for (int i = 0; i < DK_UPW; ++i)
+      U.w[k][i] = pair_word(base + (long)(t0 + min(k, nt - 1)) * tb, min(pc + i, plast), nu);
+}
+
+// The h epilogue of a group: cross-wave sums in wave order, y = h0 s0 + h1 s1.
+__device__ __forceinline__ void u_epilogue(const SL& L, int t0, int nt, const f32x4 (&acc)[DK_UTG],
+                                           float (*red)[DK_WAVES][16], uint32_t h0raw, uint32_t h1raw) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  if ((lane & 15) == 0) {
+#pragma unroll
+    for (int k = 0; k < DK_UTG; ++k)
+      if (k < nt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) red[k][wave][4 * (lane >> 4) + q] = acc[k][q];
+  }
+  lds_barrier();
+  if (tid < 16 * nt) {
+    const int k = tid >> 4, i = tid & 15;
+    const int row = 16 * (t0 + k) + i;
+    if (row < L.m) {
+      float y;
+      if (L.nb == 2) {
+        float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+        for (int w = 0; w < DK_WAVES / 2; ++w) {
+          s0 += red[k][w][i];
+          s1 += red[k][w + DK_WAVES / 2][i];
+        }
+        y = fmaf(h2f((uint16_t)h0raw), s0, h2f((uint16_t)h1raw) * s1);
+      } else {
+        float s0 = 0.f;
+#pragma unroll
+        for (int w = 0; w < DK_WAVES; ++w) s0 += red[k][w][i];
+        y = h2f((uint16_t)h0raw) * s0;
+      }
+      L.y[row] = f2h(y);
+    }
+  }
+}
+
+}  // namespace
+
+// The kernels' explicit arguments in order, as laid out in the kernel
+// argument segment (each at its natural alignment, as in a struct).  The
+// leading 14 dwords are preloaded into scalar registers by the dispatch: a
+// single-layer launch issues its first sign-word, activation and counter
+// loads from them without waiting for an argument fetch.
+struct Dk1Kernargs {
+  const uint8_t *pre_vb0, *pre_vb1;
+  const uint16_t *pre_x, *pre_g0, *pre_g1;
+  uint8_t* sync;
+  int pre_n;
+  uint32_t pre_misc;  // vq | vr << 8 | vsplit << 16 (V tiles of workgroup w: vq + (w < vr); vsplit: of branch 0)
+  LbDecodeArgs A;
+};
+
+// The argument block in the kernel argument segment (for the 16-byte copy
+// and the per-workgroup tile-range tables).
+__device__ __forceinline__ const LbDecodeArgs* dk1_kernarg_args() {
+  return (const LbDecodeArgs*)((const char*)__builtin_amdgcn_kernarg_segment_ptr() + offsetof(Dk1Kernargs, A));
+}
+
+// MODE 0: phase A only (z tagged 0); 1: phase B only (no polling); 2: both in
+// one launch of one workgroup per compute unit.  SINGLE: one layer (tile
+// ranges split evenly: V by pre_misc, U by uq/ur); else the cost-balanced
+// ranges vt_begin / ut_begin of the argument block (two launches: vq/vr,
+// uq/ur).
+template <int MODE, bool SINGLE>
+__global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* pre_vb0, const uint8_t* pre_vb1,
+                                                                const uint16_t* pre_x, const uint16_t* pre_g0,
+                                                                const uint16_t* pre_g1, uint8_t* sync, int pre_n,
+                                                                uint32_t pre_misc, LbDecodeArgs) {
+  extern __shared__ __align__(16) uint16_t dyn[];  // u in sparse order (phase A), z (phase B)
+  __shared__ __align__(16) uint8_t sA_bytes[DK_ARGS_BYTES];
+  __shared__ float vred[DK_WAVES][16];
+  __shared__ uint16_t zv[16];
+  __shared__ float ured[2][DK_UTG][DK_WAVES][16];
+  const LbDecodeArgs& A = *reinterpret_cast<const LbDecodeArgs*>(sA_bytes);
+
+  const int wg = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const f16x16 B = alt_ones();
+  const LbDecodeArgs* KA = dk1_kernarg_args();
+
+  // ---------------- start
+  // Load order (loads complete in issue order): the first V tile's sign
+  // words (single layer: from the preloaded arguments), the argument block's
+  // copy, this workgroup's call counter, the staging loads of x and g.
+  int vt0 = 0, vt1 = 0;
+  int k = 0, T = 0;
+  VTile v;
+  uint32_t w[DK_VPW];
+  const int vsplit = (int)(pre_misc >> 16);
+  if (SINGLE && MODE != 1) {
+    share1((int)(pre_misc & 255u), (int)((pre_misc >> 8) & 255u), wg, vt0, vt1);
+    if (vt0 < vt1) {
+      k = vt0 >= vsplit ? 1 : 0;
+      T = vt0 - (k ? vsplit : 0);
+      v = v_tile_geom(k ? pre_vb1 : pre_vb0, pre_n, T);
+      v_load_words(v, v.pa, w);
+    }
+  }
+  u32x4 acopy = {0u, 0u, 0u, 0u};
+  if (tid < DK_ARGS_BYTES / 16) acopy = reinterpret_cast<const u32x4*>(KA)[tid];
+  uint32_t ctr = 0;  // call counter; the tag (0 in the two-launch path, which no poll accepts) is taken at first use
+  if (MODE == 2) ctr = ld32c(sync + LB_SYNC_CTR + 8 * wg);
+  int ut0 = 0, ut1 = 0;
+  if (!SINGLE && MODE == 2) {
+    vt0 = KA->vt_begin[wg];
+    vt1 = KA->vt_begin[wg + 1];
+    ut0 = KA->ut_begin[wg];
+    ut1 = KA->ut_begin[wg + 1];
+  }
+  if (SINGLE && MODE != 1 && vt0 < vt1) stage_u(pre_x, k ? pre_g1 : pre_g0, pre_n, dyn);  // the first tile's u
+  if (tid < DK_ARGS_BYTES / 16) reinterpret_cast<u32x4*>(sA_bytes)[tid] = acopy;
+  lds_barrier();  // the argument copy (and a single layer's first u) is complete
+
+  if (SINGLE || MODE != 2) {
+    if (!SINGLE) share1(rfl(A.vq), rfl(A.vr), wg, vt0, vt1);
+    share1(rfl(A.uq), rfl(A.ur), wg, ut0, ut1);
+  }
+  if (MODE == 1) vt1 = vt0;
+  if (MODE == 0) ut1 = ut0;
+  if (!SINGLE && vt0 < vt1) {
+    k = v_slot1<SINGLE>(A, vt0, T);
+    const SL L = scalar_layer(A.L[k >> 1]);
+    v = v_tile_geom(L.vb(k & 1), L.n, T);
+    v_load_words(v, v.pa, w);
+  }
+
+  // ---------------- phase A
+  struct GroupInfo {
+    int li, tile, nt, b, p0, p1, nch;
+  };
+  auto group_at = [&](int t, const SL& L) {
+    GroupInfo g;
+    g.li = u_layer1<SINGLE>(A, t, g.tile);
+    const int lend = SINGLE ? ut1 : min(ut1, rfl(A.ut_end[g.li]));
+    g.nt = min(DK_UTG, lend - t);
+    u_role1(L, wave, g.b, g.p0, g.p1);
+    g.nch = max(1, (g.p1 - g.p0 + DK_UPW - 1) / DK_UPW);
+    return g;
+  };
+  auto layer_of_u = [&](int t) {
+    int tile;
+    return u_layer1<SINGLE>(A, t, tile);
+  };
+  UBlock cur;
+  uint32_t tag = 0;
+  bool tag_ready = MODE != 2;
+  auto get_tag = [&]() {
+    if (!tag_ready) {
+      tag = call_tag(late(ctr));
+      tag_ready = true;
+    }
+    return tag;
+  };
+
+  // one V tile (the first is its own copy of the code, so that no loop
+  // boundary makes the compiler wait for the loads issued ahead)
+  int staged = (SINGLE && vt0 < vt1) ? k : -1;  // the single-layer launch staged its first tile's u above
+  auto v_step = [&](int t) {
+    const SL L = scalar_layer(A.L[k >> 1]);
+    const int b = k & 1;
+    const int r = L.r(b);
+    const uint32_t lraw = L.l(b)[min(16 * T + (tid & 15), r - 1)];
+    if (k != staged) {
+      lds_barrier();  // earlier readers of the staged u are done
+      stage_u(L.x, L.g(b), L.n, dyn);
+      staged = k;
+      lds_barrier();  // the staged u is complete
+    }
+    // the next tile's sign words
+    int kn = k, Tn = T;
+    VTile vn = v;
+    uint32_t wn[DK_VPW];
+    if (t + 1 < vt1) {
+      kn = v_slot1<SINGLE>(A, t + 1, Tn);
+      const SL Ln = scalar_layer(A.L[kn >> 1]);
+      vn = v_tile_geom(Ln.vb(kn & 1), Ln.n, Tn);
+      v_load_words(vn, vn.pa, wn);
+    }
+    const f32x4 acc = v_tile_sums(v, dyn, B, w);
+    if ((lane & 15) == 0)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) vred[wave][4 * (lane >> 4) + q] = acc[q];
+    lds_barrier();
+    if (tid < 16) {
+      const int j = 16 * T + tid;
+      float s = 0.f;
+#pragma unroll
+      for (int w8 = 0; w8 < DK_WAVES; ++w8) s += vred[w8][tid];
+      const f16 z = (j < r) ? (f16)(h2f((uint16_t)late(lraw)) * s) : (f16)0.f;
+      zv[tid] = __builtin_bit_cast(uint16_t, z);
+    }
+    lds_barrier();
+    store_z_tile(L, b, T, get_tag(), zv);
+    if (t + 1 < vt1) {
+      k = kn;
+      T = Tn;
+      v = vn;
+#pragma unroll
+      for (int i = 0; i < DK_VPW; ++i) w[i] = wn[i];
+    }
+  };
+  if (vt0 < vt1) v_step(vt0);
+  for (int t = vt0 + 1; t < vt1; ++t) v_step(t);
+
+  // ---------------- phase B
+  // Groups of up to DK_UTG tiles of one layer; each wave runs its pair range
+  // [p0, p1) of its branch in blocks of DK_UPW pairs, whose sign words are
+  // loaded one block ahead (the first block's right after phase A, its
+  // latency overlapping the z exchange), with the group's row scales.
+  get_tag();
+  HPair hcur = {0u, 0u};
+  if (ut0 < ut1) {
+    const SL L = scalar_layer(A.L[layer_of_u(ut0)]);
+    const GroupInfo g = group_at(ut0, L);
+    load_ublock(L, g.b, g.tile, g.nt, g.p0, g.p1, cur);
+    hcur = load_group_h(L, g.tile, g.nt);
+  }
+  int zl_layer = -1, grp = 0;
+  for (int t = ut0; t < ut1;) {
+    const SL L = scalar_layer(A.L[layer_of_u(t)]);
+    const GroupInfo g = group_at(t, L);
+    const int nu = nunits(L.r(g.b));
+    if (g.li != zl_layer) {
+      lds_barrier();  // earlier readers of the LDS (phase A's u, the previous layer's z) are done
+      const int u0 = min(2 * g.p0, nu), u1 = min(2 * g.p1, nu);
+      if (16 * (u1 - u0) <= 64 * 4)
+        copy_z<4>(L, g.b, u0, u1, tag, MODE == 2, sync, dyn);
+      else
+        copy_z<16>(L, g.b, u0, u1, tag, MODE == 2, sync, dyn);
+      zl_layer = g.li;
+    }
+    const uint16_t* zb = dyn + L.zoff(g.b);
+    const HPair hg = hcur;  // this group's row scales (loaded with its first block)
+    f32x4 acc[DK_UTG], acc1[DK_UTG];
+#pragma unroll
+    for (int kk = 0; kk < DK_UTG; ++kk) acc[kk] = acc1[kk] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < g.nch; ++c) {
+      // the next block's words: this group's next chunk, or the next group's first
+      UBlock nxt;
+      bool more = false;
+      if (c + 1 < g.nch) {
+        load_ublock(L, g.b, g.tile, g.nt, g.p0 + (c + 1) * DK_UPW, g.p1, nxt);
+        more = true;
+      } else if (t + g.nt < ut1) {
+        const SL Ln = scalar_layer(A.L[layer_of_u(t + g.nt)]);
+        const GroupInfo h = group_at(t + g.nt, Ln);
+        load_ublock(Ln, h.b, h.tile, h.nt, h.p0, h.p1, nxt);
+        hcur = load_group_h(Ln, h.tile, h.nt);  // the next group's
+        more = true;
+      }
+      const int pc = g.p0 + c * DK_UPW;
+#pragma unroll
+      for (int i = 0; i < DK_UPW; ++i) {
+        const int p = pc + i;
+        if (p < g.p1) {
+          const bool two = 2 * p + 1 < nu;
+          const PairAct za = load_pair_act(zb + 128 * p, two);
+#pragma unroll
+          for (int kk = 0; kk < DK_UTG; ++kk)
+            if (kk < g.nt) pair_products(za, pair_bits(late(cur.w[kk][i]), two), two, B, acc[kk], acc1[kk]);
+        }
+      }
+      if (more) cur = nxt;
+    }
+#pragma unroll
+    for (int kk = 0; kk < DK_UTG; ++kk) acc[kk] += acc1[kk];
+    u_epilogue(L, g.tile, g.nt, acc, ured[grp & 1], late(hg.h0), late(hg.h1));
+    ++grp;
+    t += g.nt;
+  }
+  // this workgroup's call is done: the next call's tag is one higher
+  if (MODE == 2 && tid == 0) add64c_noret(sync + LB_SYNC_CTR + 8 * wg, 1ull);
+}
+
+// Dynamic LDS of a one-token launch: u of the largest input size in sparse
+// order, or the z row of the largest layer.
+size_t lb_decode1_lds_bytes(const LbDecodeArgs& a) {
+  size_t m = 0;
+  for (int i = 0; i < a.nlayers; ++i) {
+    const size_t u = (size_t)64 * nunits(a.L[i].n) * 2, z = (size_t)a.L[i].zs * 2;
+    m = u > m ? u : m;
+    m = z > m ? z : m;
+  }
+  return m;
+}
+
+// Workgroups of a single launch that fit at once, for the given dynamic LDS.
+hipError_t lb_decode1_occupancy(bool single, size_t lds, int& occ) {
+  return single ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, lb_decode1_kernel<2, true>, DK_THREADS, lds)
+                : hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, lb_decode1_kernel<2, false>, DK_THREADS, lds);
+}
+
+// Launches for one token.  G > 0: one launch of G workgroups (the caller has
+// checked that G are resident at once, and a.vt_begin / a.ut_begin hold the
+// ranges of a multi-layer call); G == 0: the two launches.
+hipError_t lb_launch_decode1(const LbDecodeArgs& args, int G, void* sync, hipStream_t stream) {
+  const size_t lds = lb_decode1_lds_bytes(args);
+  const bool single = args.nlayers == 1;
+  LbDecodeArgs a = args;
+  // preloaded copies of the single layer's phase-A fields
+  const LbLayerArgs& L0 = args.L[0];
+  const uint8_t* vb0 = single ? L0.br[0].vbits : nullptr;
+  const uint8_t* vb1 = single ? L0.br[1].vbits : nullptr;
+  const uint16_t* px = single ? L0.x : nullptr;
+  const uint16_t* g0 = single ? L0.br[0].g : nullptr;
+  const uint16_t* g1 = single ? L0.br[1].g : nullptr;
+  const int pn = single ? L0.n : 0;
+  uint8_t* sy = static_cast<uint8_t*>(sync);
+  auto misc = [&](int vq, int vr) {
+    return (uint32_t)vq | ((uint32_t)vr << 8) | ((uint32_t)(single ? args.vt_end[0] : 0) << 16);
+  };
+  if (G > 0) {
+    a.vq = a.nvt / G;
+    a.vr = a.nvt % G;
+    a.uq = a.nut / G;
+    a.ur = a.nut % G;
+    if (a.vq > 255 || a.vr > 255) return hipErrorInvalidValue;
+    if (single)
+      hipLaunchKernelGGL((lb_decode1_kernel<2, true>), dim3(G), dim3(DK_THREADS), lds, stream, vb0, vb1, px, g0, g1,
+                         sy, pn, misc(a.vq, a.vr), a);
+    else
+      hipLaunchKernelGGL((lb_decode1_kernel<2, false>), dim3(G), dim3(DK_THREADS), lds, stream, vb0, vb1, px, g0, g1,
+                         sy, pn, 0u, a);
+    return hipGetLastError();
+  }
+  a.vq = 1;
+  a.vr = 0;
+  a.uq = 0;
+  a.ur = 0;
+  if (single)
+    hipLaunchKernelGGL((lb_decode1_kernel<0, true>), dim3(a.nvt), dim3(DK_THREADS), lds, stream, vb0, vb1, px, g0, g1,
+                       sy, pn, misc(1, 0), a);
+  else
+    hipLaunchKernelGGL((lb_decode1_kernel<0, false>), dim3(a.nvt), dim3(DK_THREADS), lds, stream, vb0, vb1, px, g0,
+                       g1, sy, pn, 0u, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int gb = a.nut < 1024 ? a.nut : 1024;
+  a.vq = 0;
+  a.vr = 0;
+  a.uq = a.nut / gb;
+  a.ur = a.nut % gb;
+  if (single)
+    hipLaunchKernelGGL((lb_decode1_kernel<1, true>), dim3(gb), dim3(DK_THREADS), lds, stream, vb0, vb1, px, g0, g1,
+                       sy, pn, misc(0, 0), a);
+  else
+    hipLaunchKernelGGL((lb_decode1_kernel<1, false>), dim3(gb), dim3(DK_THREADS), lds, stream, vb0, vb1, px, g0, g1,
+                       sy, pn, 0u, a);
+  return hipGetLastError();
+}

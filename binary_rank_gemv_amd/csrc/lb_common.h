@@ -13,6 +13,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #define LB_MAX_LAYERS 7
 #define LB_MAX_GRID 256  // workgroups of the single-launch decode kernel
 #define LB_DECODE_LDS_MAX (120 * 1024)  // dynamic LDS limit of a decode launch (bytes)
+#define LB_DECODE1_LDS_MAX (64 * 1024)  // the same, one-token kernels (u of n <= 32768 in sparse order)
 
 // ---------------------------------------------------------------- LB16 layout
 // A packed factor with R rows and reduction length K is a sequence of tiles of
