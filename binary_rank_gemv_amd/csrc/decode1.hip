@@ -6,24 +6,28 @@
 //
 // The signs never become operand values.  The sparse instruction's A operand
 // is 16 rows x 64 positions in which every group of 4 positions holds 2
-// values, placed by a 2-bit index each.  Here every row of A holds the
-// activations of its lane group (a lane's 8 values), B holds +1 at even and -1
-// at odd positions in every column, and each activation may sit at an even
-// (+1) or the next odd (-1) position: its weight's sign bit is the low bit of
-// its index.  Row i of the product is then the sum of +-a with row i's signs,
-// exactly (every column alike; column 0 is used).  The raw LB16 word of a
-// lane gives the indices of four instructions with three VALU operations:
-// (w & 0x55555555) | 0x88888888 and the same of w >> 1; the activations are
-// stored in the matching order ("sparse order", below), so no bit is moved.
+// values, each placed by a 2-bit index.  Here every row of A holds the
+// activations of its lane group (a lane's 8 values) and the index carries
+// the signs: B's column 0 holds -1 where bit 0 of the in-group position is
+// set and column 1 where bit 1 is, +1 elsewhere (sign_columns).  With bit 0
+// of each index the sign bit of one tile's row and bit 1 that of a second
+// tile's, column 0 of the product is the first row's sum of +-a and column 1
+// the second's, exactly: one instruction serves two 16-row tiles.  The raw
+// LB16 words give the indices with two or three VALU operations per word;
+// the activations are stored in the matching order ("sparse order", below),
+// so no bit is moved.
 //
 // Structure (as in the multi-token kernels of decode.hip): phase A runs the V
-// pass over 16-row tiles of sign(V)^T and stores z as tagged 64-bit words
-// [call tag | two fp16]; phase B polls the z range of each wave, then runs the
-// U pass over groups of 16-row output tiles with the h epilogue.  One launch
-// of one 512-thread workgroup per compute unit (MODE 2), or two launches
-// (MODE 0: phase A with tag 0, MODE 1: phase B without polling).  A tile's
-// sums do not depend on the workgroup or launch that runs it, so every path
-// returns the same bits.
+// pass over 16-row tiles of sign(V)^T (the 8 waves of a workgroup split the
+// reduction; the activation operands reach each 16-lane row by a DPP row
+// broadcast) and stores z as tagged 64-bit words [call tag | two fp16];
+// phase B polls the z range of each wave, then runs the U pass over groups
+// of 16-row output tiles, two tiles per instruction, with the h epilogue.
+// The first U block of each wave is copied straight into LDS during phase A.
+// One launch of one 512-thread workgroup per compute unit (MODE 2), or two
+// launches (MODE 0: phase A with tag 0, MODE 1: phase B without polling).  A
+// tile's sums do not depend on the workgroup or launch that runs it, so every
+// path returns the same bits.
 #include <stddef.h>
 
 #include "lb_common.h"
@@ -31,7 +35,7 @@
 
 #define DK_WAVES 8
 #define DK_THREADS (64 * DK_WAVES)
-#define DK_VPW 16  // V-pass pairs per wave per batch of sign words
+#define DK_VPW 8   // V-pass pairs per wave per batch of sign words
 #define DK_UTG 8   // U tiles per group (one epilogue)
 #define DK_UPW 4   // U-pass pairs per wave per block of sign words
 
@@ -66,12 +70,31 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// B operand: +1 at even, -1 at odd positions of every column.
-__device__ inline f16x16 alt_ones() {
-  uint32_t d = 0xBC003C00u;
-  __asm__ volatile("" : "+v"(d));
+// Workgroup barrier for LDS data written by ds instructions, without a
+// memory fence: loads that write LDS straight from memory and are still in
+// flight (the first U block's, read only in phase B) are not waited for.
+// The asm statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_barrier_nf() {
+  compiler_memory_barrier();
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS accesses are done
+  __builtin_amdgcn_s_barrier();
+  compiler_memory_barrier();
+}
+
+// B operand.  The in-group index t (0..3) of an A value selects the B row
+// 4 g + t of its group g; here column 0 holds -1 where bit 0 of t is set and
+// column 1 where bit 1 is set, +1 elsewhere, and columns 2..15 are zero.  So
+// column 0 of the product sums the values signed by their index's bit 0 and
+// column 1 by its bit 1: one instruction serves two rows of signs (lane
+// element e of B sits at a position p with p % 4 = e % 4).  The instruction
+// gathers B rows for any pair of indices of a group, equal ones included.
+__device__ inline f16x16 sign_columns() {
+  const int col = threadIdx.x & 15;
+  uint32_t d0 = col == 0 ? 0xBC003C00u : (col == 1 ? 0x3C003C00u : 0u);  // t = 0, 1
+  uint32_t d1 = col == 0 ? 0xBC003C00u : (col == 1 ? 0xBC00BC00u : 0u);  // t = 2, 3
+  __asm__ volatile("" : "+v"(d0), "+v"(d1));
   typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
-  u32x8 v = {d, d, d, d, d, d, d, d};
+  u32x8 v = {d0, d1, d0, d1, d0, d1, d0, d1};
   return __builtin_bit_cast(f16x16, v);
 }
 
@@ -97,13 +120,30 @@ __device__ __forceinline__ PairAct load_pair_act(const uint16_t* act, bool two_u
   return a;
 }
 
-// The products of one pair: raw LB16 word w (for an odd last unit, the
-// lane's unit in bits 0..15 and two_units false).  Three VALU operations
-// make the indices of up to four instructions.
+// The products of one pair for one tile (column 0): raw LB16 word w (for an
+// odd last unit, the lane's unit in bits 0..15 and two_units false).  Bit 1
+// of every index is clear and bit 3 set, so each slot pair keeps its own two
+// positions; three VALU operations make the indices of up to four
+// instructions.
 __device__ __forceinline__ void pair_products(const PairAct& a, uint32_t w, bool two_units, const f16x16& B,
                                               f32x4& acc0, f32x4& acc1) {
   const int ie = (int)((w & 0x55555555u) | 0x88888888u);
   const int io = (int)(((w >> 1) & 0x55555555u) | 0x88888888u);
+  acc0 = smfmac(a.e0, B, acc0, ie, 0);
+  acc1 = smfmac(a.o0, B, acc1, io, 0);
+  if (two_units) {
+    acc0 = smfmac(a.e1, B, acc0, ie, 1);
+    acc1 = smfmac(a.o1, B, acc1, io, 1);
+  }
+}
+
+// The same for two tiles at once: the sign bit of tile a's row becomes bit 0
+// and tile b's bit 1 of each index, so column 0 sums tile a's row and column
+// 1 tile b's (wa, wb as for pair_products; four VALU operations).
+__device__ __forceinline__ void pair_products2(const PairAct& a, uint32_t wa, uint32_t wb, bool two_units,
+                                               const f16x16& B, f32x4& acc0, f32x4& acc1) {
+  const int ie = (int)((wa & 0x55555555u) | ((wb << 1) & 0xAAAAAAAAu));
+  const int io = (int)(((wa >> 1) & 0x55555555u) | (wb & 0xAAAAAAAAu));
   acc0 = smfmac(a.e0, B, acc0, ie, 0);
   acc1 = smfmac(a.o0, B, acc1, io, 0);
   if (two_units) {
@@ -137,6 +177,9 @@ __device__ __forceinline__ uint32_t pair_bits(uint32_t w, bool full) {
 // registers (readfirstlane: every lane of a wave holds the same value).
 #define DK_ARGS_BYTES ((int)offsetof(LbDecodeArgs, vt_begin))  // header + layer records
 static_assert(DK_ARGS_BYTES % 16 == 0, "16-byte copy of the argument block");
+
+// Waits for every outstanding vector memory load of the wave.
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
 __device__ __forceinline__ int rfl(int v) { return __builtin_amdgcn_readfirstlane(v); }
 // A pointer into device memory read from the LDS copy: made wave-uniform and
@@ -321,29 +364,84 @@ __device__ __forceinline__ VTile v_tile_geom(const uint8_t* vbits, int n, int T)
   return v;
 }
 
-// Sign words of batch [pc, pc + DK_VPW) (clamped to the share: unconditional
-// loads keep the wait counts static; words beyond pb are never used).
+// Sign words of batch [pc, pc + DK_VPW), in groups of four pairs; groups
+// that start beyond the share are not loaded (their words are never used),
+// and the last group's slots beyond pb repeat its last word.
 __device__ __forceinline__ void v_load_words(const VTile& v, int pc, uint32_t (&w)[DK_VPW]) {
   const int plast = max(v.pb - 1, 0);
 #pragma unroll
-  for (int i = 0; i < DK_VPW; ++i) w[i] = pair_word(v.tile, min(pc + i, plast), v.nu);
+  for (int j = 0; j < DK_VPW / 4; ++j)
+    if (j == 0 || pc + 4 * j < v.pb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[4 * j + i] = pair_word(v.tile, min(pc + 4 * j + i, plast), v.nu);
+}
+
+// V activations through a row broadcast.  Every lane of a 16-lane row (one
+// lane group) needs the same 8 activations for an instruction; rather than
+// each lane reading them (16 bytes per lane per instruction), lane r of each
+// row reads operand r of a group of four pairs (pair r / 4, unit (r / 2) % 2
+// of the pair, even or odd operand r % 2) and each instruction's operand is
+// broadcast from its lane across the row (DPP row broadcast, one move per
+// dword): a sixteenth of the LDS traffic, for four moves per instruction.
+template <int N>
+__device__ __forceinline__ f16x8 bcast_operand(const u32x4& q) {
+  u32x4 d;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) d[i] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)q[i], 0x150 + N, 0xF, 0xF, false);
+  return __builtin_bit_cast(f16x8, d);
+}
+
+// This lane's operand of the group of pairs [pc, pc + 4), clamped to the
+// share and to the staged units.
+__device__ __forceinline__ u32x4 load_act_group(const uint16_t* up, int pc, int plast, int nu) {
+  const int lane = threadIdx.x & 63, r = lane & 15, G = lane >> 4;
+  const int p = min(pc + (r >> 2), plast);
+  const int unit = min(2 * p + ((r >> 1) & 1), nu - 1);
+  return *reinterpret_cast<const u32x4*>(up + 64 * unit + 16 * G + 8 * (r & 1));
+}
+
+// Pair I (0..3) of a group: its four operands from the group's reads.
+template <int I>
+__device__ __forceinline__ PairAct bcast_pair(const u32x4& q) {
+  PairAct a;
+  a.e0 = bcast_operand<4 * I + 0>(q);
+  a.o0 = bcast_operand<4 * I + 1>(q);
+  a.e1 = bcast_operand<4 * I + 2>(q);
+  a.o1 = bcast_operand<4 * I + 3>(q);
+  return a;
+}
+
+template <int J, int I>
+__device__ __forceinline__ void v_pair(const VTile& v, int pc, const u32x4& q, const uint32_t (&w)[DK_VPW],
+                                       const f16x16& B, f32x4& acc0, f32x4& acc1) {
+  const int p = pc + 4 * J + I;
+  if (p < v.pb) {
+    const bool two = 2 * p + 1 < v.nu;
+    pair_products(bcast_pair<I>(q), pair_bits(late(w[4 * J + I]), two), two, B, acc0, acc1);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // one pair's operands live at a time
+}
+
+template <int J>
+__device__ __forceinline__ void v_group(const VTile& v, int pc, const u32x4& q, const uint32_t (&w)[DK_VPW],
+                                        const f16x16& B, f32x4& acc0, f32x4& acc1) {
+  v_pair<J, 0>(v, pc, q, w, B, acc0, acc1);
+  v_pair<J, 1>(v, pc, q, w, B, acc0, acc1);
+  v_pair<J, 2>(v, pc, q, w, B, acc0, acc1);
+  v_pair<J, 3>(v, pc, q, w, B, acc0, acc1);
 }
 
 // Returns this lane's partial sums (rows 4 (lane / 16) + q of column
 // lane % 16); `w` holds the first batch's words on entry.
 __device__ __forceinline__ f32x4 v_tile_sums(const VTile& v, const uint16_t* up, const f16x16& B,
                                              uint32_t (&w)[DK_VPW]) {
+  static_assert(DK_VPW == 8, "two activation groups per batch");
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  const int plast = max(v.pb - 1, 0);
   for (int pc = v.pa; pc < v.pb; pc += DK_VPW) {
     if (pc != v.pa) v_load_words(v, pc, w);
-#pragma unroll
-    for (int i = 0; i < DK_VPW; ++i) {
-      const int p = pc + i;
-      if (p < v.pb) {
-        const bool two = 2 * p + 1 < v.nu;
-        pair_products(load_pair_act(up + 128 * p, two), pair_bits(late(w[i]), two), two, B, acc0, acc1);
-      }
-    }
+    v_group<0>(v, pc, load_act_group(up, pc, plast, v.nu), w, B, acc0, acc1);
+    v_group<1>(v, pc, load_act_group(up, pc + 4, plast, v.nu), w, B, acc0, acc1);
   }
   return acc0 + acc1;
 }
@@ -351,62 +449,100 @@ __device__ __forceinline__ f32x4 v_tile_sums(const VTile& v, const uint16_t* up,
 // ------------------------------------------------------------- phase B
 // Copies units [u0, u1) of branch b's z (tagged words) into zl (sparse order,
 // values only), polling until every word carries `tag` (unless !check).
-// Chunk c (16 bytes: two words) of the range is load c / 64 of lane c % 64.
+// Chunk c (16 bytes: two words) of the range is load c / 64 of lane c % 64,
+// in rounds of 64 NL chunks.  zc_begin issues the first round's loads and
+// zc_finish completes the copy, so that other loads can be issued between
+// the two while the first round is in flight.
 template <int NL>
-__device__ __forceinline__ void copy_z(const SL& L, int b, int u0, int u1, uint32_t tag, bool check, uint8_t* sync,
-                                       uint16_t* zl) {
+struct ZCopy {
+  __amdgpu_buffer_rsrc_t rs;
+  uint16_t* dst;
+  int nchunks;
+  uint32_t todo;  // loads of the current round still to land with the tag
+  u32x4 q[NL];
+};
+
+template <int NL>
+__device__ __forceinline__ uint32_t zc_round_bits(int nchunks, int c0) {
+  uint32_t todo = 0;
+#pragma unroll
+  for (int i = 0; i < NL; ++i)
+    if (c0 + 64 * i < nchunks) todo |= 1u << i;
+  return todo;
+}
+
+template <int NL>
+__device__ __forceinline__ void zc_issue(ZCopy<NL>& c, int c0) {
   const int lane = threadIdx.x & 63;
-  const int nchunks = 16 * (u1 - u0);
-  if (nchunks <= 0) return;
+  compiler_memory_barrier();
+#pragma unroll
+  for (int i = 0; i < NL; ++i)
+    if (c.todo & (1u << i)) c.q[i] = ld_tagged2(c.rs, 16 * (c0 + 64 * i + lane));  // beyond the range: zeros
+}
+
+template <int NL>
+__device__ __forceinline__ void zc_begin(ZCopy<NL>& c, const SL& L, int b, int u0, int u1, uint16_t* zl) {
+  c.nchunks = max(16 * (u1 - u0), 0);
   const uint8_t* base = reinterpret_cast<const uint8_t*>(L.z + (L.zoff(b) >> 1) + 32 * u0);
-  const int bytes = 16 * nchunks;
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, bytes);
-  uint16_t* dst = zl + L.zoff(b) + 64 * u0;
-  for (int c0 = 0; c0 < nchunks; c0 += 64 * NL) {
-    uint32_t todo = 0;
-    u32x4 q[NL];
-#pragma unroll
-    for (int i = 0; i < NL; ++i)
-      if (c0 + 64 * i < nchunks) todo |= 1u << i;
+  c.rs = make_rsrc(base, 16 * c.nchunks);
+  c.dst = zl + L.zoff(b) + 64 * u0;
+  c.todo = zc_round_bits<NL>(c.nchunks, 0);
+  zc_issue(c, 0);
+}
+
+template <int NL>
+__device__ __forceinline__ void zc_finish(ZCopy<NL>& c, uint32_t tag, bool check, uint8_t* sync) {
+  const int lane = threadIdx.x & 63;
+  for (int c0 = 0; c0 < c.nchunks; c0 += 64 * NL) {
+    if (c0 != 0) {
+      c.todo = zc_round_bits<NL>(c.nchunks, c0);
+      zc_issue(c, c0);
+    }
     int spins = 0;
-    for (;;) {
-      compiler_memory_barrier();
-#pragma unroll
-      for (int i = 0; i < NL; ++i)
-        if (todo & (1u << i)) q[i] = ld_tagged2(rs, 16 * (c0 + 64 * i + lane));  // beyond the range: zeros
-      if (!check) break;
+    while (check) {
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
-        if (todo & (1u << i)) {
-          const bool in = c0 + 64 * i + lane < nchunks;
-          const bool ok = !in || ((q[i][0] == tag) & (q[i][2] == tag));
-          if (__all(ok)) todo &= ~(1u << i);
+        if (c.todo & (1u << i)) {
+          const bool in = c0 + 64 * i + lane < c.nchunks;
+          const bool ok = !in || ((c.q[i][0] == tag) & (c.q[i][2] == tag));
+          if (__all(ok)) c.todo &= ~(1u << i);
         }
       }
-      if (todo == 0) break;
+      if (c.todo == 0) break;
       if (++spins > LB_SPIN_LIMIT) {
         st32c(sync + LB_SYNC_ERR, 1u);
         break;
       }
+      zc_issue(c, c0);  // the words not yet tagged, again
     }
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      const int c = c0 + 64 * i + lane;
-      if (c < nchunks) {
+      const int ch = c0 + 64 * i + lane;
+      if (ch < c.nchunks) {
         uint2 d;
-        d.x = q[i][1];
-        d.y = q[i][3];
-        *reinterpret_cast<uint2*>(dst + 4 * c) = d;
+        d.x = c.q[i][1];
+        d.y = c.q[i][3];
+        *reinterpret_cast<uint2*>(c.dst + 4 * ch) = d;
       }
     }
   }
 }
 
+template <int NL>
+__device__ __forceinline__ void copy_z(const SL& L, int b, int u0, int u1, uint32_t tag, bool check, uint8_t* sync,
+                                       uint16_t* zl) {
+  ZCopy<NL> c;
+  zc_begin(c, L, b, u0, u1, zl);
+  zc_finish(c, tag, check, sync);
+}
+
 // Wave's phase-B role for a layer: branch and pair range of that branch.
+// With two branches, waves w and w + 4 (which share a SIMD) take quarters w
+// and 3 - w, so that uneven quarters even out per SIMD.
 __device__ __forceinline__ void u_role1(const SL& L, int wave, int& b, int& p0, int& p1) {
   if (L.nb == 2) {
     b = wave >> 2;
-    const int np = (nunits(L.r(b)) + 1) >> 1, w = wave & 3;
+    const int np = (nunits(L.r(b)) + 1) >> 1, w = b ? 3 - (wave & 3) : (wave & 3);
     p0 = (np * w) >> 2;
     p1 = (np * (w + 1)) >> 2;
   } else {
@@ -441,28 +577,62 @@ __device__ __forceinline__ HPair load_group_h(const SL& L, int t0, int nt) {
   return h;
 }
 
-__device__ __forceinline__ void load_ublock(const SL& L, int b, int t0, int nt, int pc, int p1, UBlock& U) {
+// Words of tile k of a U block (pairs [pc, pc + DK_UPW) of the wave's range
+// ending at p1, tiles clamped to the group).
+__device__ __forceinline__ void load_utile(const SL& L, int b, int t0, int nt, int pc, int p1, int k,
+                                           uint32_t (&w)[DK_UPW]) {
   const int r = L.r(b), nu = nunits(r);
-  const long tb = lb16_tile_bytes(r);
-  const uint8_t* base = L.ub(b);
+  const uint8_t* tile = L.ub(b) + (long)(t0 + min(k, nt - 1)) * lb16_tile_bytes(r);
   const int plast = max(p1 - 1, 0);
 #pragma unroll
-  for (int k = 0; k < DK_UTG; ++k)
+  for (int i = 0; i < DK_UPW; ++i) w[i] = pair_word(tile, min(pc + i, plast), nu);
+}
+
+__device__ __forceinline__ void load_ublock(const SL& L, int b, int t0, int nt, int pc, int p1, UBlock& U) {
 #pragma unroll
-    for (int i = 0; i < DK_UPW; ++i)
-      U.w[k][i] = pair_word(base + (long)(t0 + min(k, nt - 1)) * tb, min(pc + i, plast), nu);
+  for (int k = 0; k < DK_UTG; ++k) load_utile(L, b, t0, nt, pc, p1, k, U.w[k]);
+}
+
+// The same block straight into LDS (no registers held while it is in
+// flight): tile k's pairs [pc, pc + DK_UPW), 1 KB contiguous in the LB16
+// layout, to dst + 64 DK_UPW k with one 16-byte load per lane, bounded by
+// the tile (lanes beyond it read zeros).  Word (k, i) of a lane is then
+// dst[64 (DK_UPW k + i) + lane] (lane / 2 for an odd last unit), as
+// pair_word reads it from memory.
+__device__ __forceinline__ void dma_ublock(const SL& L, int b, int t0, int nt, int pc, uint32_t* dst) {
+  static_assert(DK_UPW == 4, "one 16-byte load per lane and tile");
+  const int r = L.r(b), lane = threadIdx.x & 63;
+  const long tb = lb16_tile_bytes(r);
+#pragma unroll
+  for (int k = 0; k < DK_UTG; ++k) {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(L.ub(b) + (long)(t0 + min(k, nt - 1)) * tb, (int)tb);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + 64 * DK_UPW * k),
+                                             16, 256 * pc + 16 * lane, 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void lds_ublock(const uint32_t* src, int pc, int nu, UBlock& U) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < DK_UPW; ++i) {
+    const int li = 2 * (pc + i) + 1 < nu ? lane : lane >> 1;
+#pragma unroll
+    for (int k = 0; k < DK_UTG; ++k) U.w[k][i] = src[64 * (DK_UPW * k + i) + li];
+  }
 }
 
 // The h epilogue of a group: cross-wave sums in wave order, y = h0 s0 + h1 s1.
-__device__ __forceinline__ void u_epilogue(const SL& L, int t0, int nt, const f32x4 (&acc)[DK_UTG],
+// acc[j] holds tiles 2j (column 0) and 2j + 1 (column 1).
+__device__ __forceinline__ void u_epilogue(const SL& L, int t0, int nt, const f32x4 (&acc)[DK_UTG / 2],
                                            float (*red)[DK_WAVES][16], uint32_t h0raw, uint32_t h1raw) {
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
-  if ((lane & 15) == 0) {
+  const int col = lane & 15;
+  if (col < 2) {
 #pragma unroll
-    for (int k = 0; k < DK_UTG; ++k)
-      if (k < nt)
+    for (int j = 0; j < DK_UTG / 2; ++j)
+      if (2 * j + col < nt)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) red[k][wave][4 * (lane >> 4) + q] = acc[k][q];
+        for (int q = 0; q < 4; ++q) red[2 * j + col][wave][4 * (lane >> 4) + q] = acc[j][q];
   }
   lds_barrier();
   if (tid < 16 * nt) {
@@ -526,10 +696,11 @@ __global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* p
   __shared__ float vred[DK_WAVES][16];
   __shared__ uint16_t zv[16];
   __shared__ float ured[2][DK_UTG][DK_WAVES][16];
+  __shared__ __align__(16) uint32_t ublk[DK_WAVES][DK_UTG * DK_UPW * 64];  // each wave's first U block
   const LbDecodeArgs& A = *reinterpret_cast<const LbDecodeArgs*>(sA_bytes);
 
   const int wg = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = wave_id();
-  const f16x16 B = alt_ones();
+  const f16x16 B = sign_columns();
   const LbDecodeArgs* KA = dk1_kernarg_args();
 
   // ---------------- start
@@ -561,9 +732,11 @@ __global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* p
     ut0 = KA->ut_begin[wg];
     ut1 = KA->ut_begin[wg + 1];
   }
+  HPair hcur = {0u, 0u};  // row scales of the first U group
   if (SINGLE && MODE != 1 && vt0 < vt1) stage_u(pre_x, k ? pre_g1 : pre_g0, pre_n, dyn);  // the first tile's u
   if (tid < DK_ARGS_BYTES / 16) reinterpret_cast<u32x4*>(sA_bytes)[tid] = acopy;
-  lds_barrier();  // the argument copy (and a single layer's first u) is complete
+  lds_barrier_nf();  // the argument copy (and a single layer's first u) is complete
+  if (SINGLE) wait_vmem_all();  // (the staging waited already: this tells the compiler so)
 
   if (SINGLE || MODE != 2) {
     if (!SINGLE) share1(rfl(A.vq), rfl(A.vr), wg, vt0, vt1);
@@ -571,11 +744,17 @@ __global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* p
   }
   if (MODE == 1) vt1 = vt0;
   if (MODE == 0) ut1 = ut0;
-  if (!SINGLE && vt0 < vt1) {
-    k = v_slot1<SINGLE>(A, vt0, T);
+  // the first V tile's latent scales (and, for several layers, its sign
+  // words): loaded ahead, like those of each next tile
+  uint32_t lcur = 0;
+  if (vt0 < vt1) {
+    if (!SINGLE) k = v_slot1<SINGLE>(A, vt0, T);
     const SL L = scalar_layer(A.L[k >> 1]);
-    v = v_tile_geom(L.vb(k & 1), L.n, T);
-    v_load_words(v, v.pa, w);
+    if (!SINGLE) {
+      v = v_tile_geom(L.vb(k & 1), L.n, T);
+      v_load_words(v, v.pa, w);
+    }
+    lcur = L.l(k & 1)[min(16 * T + (tid & 15), L.r(k & 1) - 1)];
   }
 
   // ---------------- phase A
@@ -595,7 +774,36 @@ __global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* p
     int tile;
     return u_layer1<SINGLE>(A, t, tile);
   };
+  // The first U group.  Its first block of sign words is copied straight
+  // into LDS, and its row scales loaded, once the first V tile's loads are
+  // issued (those complete first): the copy streams in during phase A while
+  // holding no registers, and phase A's barriers do not wait for it.  A
+  // workgroup without U tiles copies a stand-in (the start of the workspace
+  // header, as one 16-row tile of one unit) instead: the loads stay
+  // unconditional, which keeps the compiler's waits for earlier loads exact.
   UBlock cur;
+  const bool have_u = ut0 < ut1;
+  SL uL = {};
+  GroupInfo ug = {};
+  if (have_u) {
+    uL = scalar_layer(A.L[layer_of_u(ut0)]);
+    ug = group_at(ut0, uL);
+  } else {
+    uL.ub0 = uL.ub1 = sync;
+    uL.h0 = uL.h1 = reinterpret_cast<const uint16_t*>(sync);
+    uL.r0 = uL.r1 = 16;
+    uL.m = uL.nb = 1;
+    ug.nt = ug.p1 = 1;
+  }
+  auto issue_first_u = [&]() {
+    if (MODE != 0) {
+      compiler_memory_barrier();
+      dma_ublock(uL, ug.b, ug.tile, ug.nt, ug.p0, ublk[wave]);
+      hcur = load_group_h(uL, ug.tile, ug.nt);
+      compiler_memory_barrier();
+    }
+  };
+  if (SINGLE || vt0 == vt1) issue_first_u();  // (a single layer staged its first u above)
   uint32_t tag = 0;
   bool tag_ready = MODE != 2;
   auto get_tag = [&]() {
@@ -613,42 +821,45 @@ __global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* p
     const SL L = scalar_layer(A.L[k >> 1]);
     const int b = k & 1;
     const int r = L.r(b);
-    const uint32_t lraw = L.l(b)[min(16 * T + (tid & 15), r - 1)];
     if (k != staged) {
-      lds_barrier();  // earlier readers of the staged u are done
+      lds_barrier_nf();  // earlier readers of the staged u are done
       stage_u(L.x, L.g(b), L.n, dyn);
       staged = k;
-      lds_barrier();  // the staged u is complete
+      lds_barrier_nf();  // the staged u is complete
+      if (t == vt0) wait_vmem_all();  // (staging waited already: this tells the compiler so)
     }
-    // the next tile's sign words
+    if (!SINGLE && t == vt0) issue_first_u();
+    // the next tile's sign words and latent scales
     int kn = k, Tn = T;
     VTile vn = v;
-    uint32_t wn[DK_VPW];
+    uint32_t wn[DK_VPW], lnext = 0;
     if (t + 1 < vt1) {
       kn = v_slot1<SINGLE>(A, t + 1, Tn);
       const SL Ln = scalar_layer(A.L[kn >> 1]);
       vn = v_tile_geom(Ln.vb(kn & 1), Ln.n, Tn);
       v_load_words(vn, vn.pa, wn);
+      lnext = Ln.l(kn & 1)[min(16 * Tn + (tid & 15), Ln.r(kn & 1) - 1)];
     }
     const f32x4 acc = v_tile_sums(v, dyn, B, w);
     if ((lane & 15) == 0)
 #pragma unroll
       for (int q = 0; q < 4; ++q) vred[wave][4 * (lane >> 4) + q] = acc[q];
-    lds_barrier();
+    lds_barrier_nf();
     if (tid < 16) {
       const int j = 16 * T + tid;
       float s = 0.f;
 #pragma unroll
       for (int w8 = 0; w8 < DK_WAVES; ++w8) s += vred[w8][tid];
-      const f16 z = (j < r) ? (f16)(h2f((uint16_t)late(lraw)) * s) : (f16)0.f;
+      const f16 z = (j < r) ? (f16)(h2f((uint16_t)late(lcur)) * s) : (f16)0.f;
       zv[tid] = __builtin_bit_cast(uint16_t, z);
     }
-    lds_barrier();
+    lds_barrier_nf();
     store_z_tile(L, b, T, get_tag(), zv);
     if (t + 1 < vt1) {
       k = kn;
       T = Tn;
       v = vn;
+      lcur = lnext;
 #pragma unroll
       for (int i = 0; i < DK_VPW; ++i) w[i] = wn[i];
     }
@@ -659,17 +870,24 @@ __global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* p
   // ---------------- phase B
   // Groups of up to DK_UTG tiles of one layer; each wave runs its pair range
   // [p0, p1) of its branch in blocks of DK_UPW pairs, whose sign words are
-  // loaded one block ahead (the first block's right after phase A, its
-  // latency overlapping the z exchange), with the group's row scales.
-  get_tag();
-  HPair hcur = {0u, 0u};
-  if (ut0 < ut1) {
-    const SL L = scalar_layer(A.L[layer_of_u(ut0)]);
-    const GroupInfo g = group_at(ut0, L);
-    load_ublock(L, g.b, g.tile, g.nt, g.p0, g.p1, cur);
-    hcur = load_group_h(L, g.tile, g.nt);
-  }
+  // loaded one block ahead, with the group's row scales.
+  //
+  // The first group's z: its first round of polling loads, then (once the
+  // LDS is free of phase A's u) the rest of the copy, and the first block's
+  // words from the LDS copy.
   int zl_layer = -1, grp = 0;
+  if (MODE != 0 && have_u) {
+    ZCopy<8> zc0;
+    const int nu0 = nunits(uL.r(ug.b));
+    compiler_memory_barrier();
+    zc_begin(zc0, uL, ug.b, min(2 * ug.p0, nu0), min(2 * ug.p1, nu0), dyn);
+    get_tag();
+    lds_barrier();  // phase A's readers of the LDS are done; the block copy has landed
+    zc_finish(zc0, tag, MODE == 2, sync);
+    zl_layer = ug.li;
+    lds_ublock(ublk[wave], ug.p0, nu0, cur);
+  }
+  get_tag();
   for (int t = ut0; t < ut1;) {
     const SL L = scalar_layer(A.L[layer_of_u(t)]);
     const GroupInfo g = group_at(t, L);
@@ -685,9 +903,9 @@ __global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* p
     }
     const uint16_t* zb = dyn + L.zoff(g.b);
     const HPair hg = hcur;  // this group's row scales (loaded with its first block)
-    f32x4 acc[DK_UTG], acc1[DK_UTG];
+    f32x4 acc[DK_UTG / 2], acc1[DK_UTG / 2];  // tile pairs (2j, 2j + 1)
 #pragma unroll
-    for (int kk = 0; kk < DK_UTG; ++kk) acc[kk] = acc1[kk] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < DK_UTG / 2; ++j) acc[j] = acc1[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int c = 0; c < g.nch; ++c) {
       // the next block's words: this group's next chunk, or the next group's first
       UBlock nxt;
@@ -710,14 +928,16 @@ __global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* p
           const bool two = 2 * p + 1 < nu;
           const PairAct za = load_pair_act(zb + 128 * p, two);
 #pragma unroll
-          for (int kk = 0; kk < DK_UTG; ++kk)
-            if (kk < g.nt) pair_products(za, pair_bits(late(cur.w[kk][i]), two), two, B, acc[kk], acc1[kk]);
+          for (int j = 0; j < DK_UTG / 2; ++j)
+            if (2 * j < g.nt)  // (for an odd count the last tile pairs with itself: load_ublock clamps)
+              pair_products2(za, pair_bits(late(cur.w[2 * j][i]), two), pair_bits(late(cur.w[2 * j + 1][i]), two), two,
+                             B, acc[j], acc1[j]);
         }
       }
       if (more) cur = nxt;
     }
 #pragma unroll
-    for (int kk = 0; kk < DK_UTG; ++kk) acc[kk] += acc1[kk];
+    for (int j = 0; j < DK_UTG / 2; ++j) acc[j] += acc1[j];
     u_epilogue(L, g.tile, g.nt, acc, ured[grp & 1], late(hg.h0), late(hg.h1));
     ++grp;
     t += g.nt;
