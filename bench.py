@@ -505,7 +505,8 @@ def main():
                     help="host time for the oracle baseline (0: skip)")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the other configurations (7B, 70B at 16 tokens, 13B block, prefill)")
-    ap.add_argument("--only", choices=sorted(DECODE_CONFIGS), help="time one decode configuration only")
+    ap.add_argument("--only", choices=sorted(DECODE_CONFIGS) + ["prefill_7b_up_2048"],
+                    help="time one configuration only")
     ap.add_argument("--bpw-sweep", action="store_true",
                     help="only the bits-per-weight sweep of the 70B up-projection against fp16 dense")
     ap.add_argument("--init", action="store_true",
@@ -532,6 +533,9 @@ def main():
         return
     if args.pmc_pass:
         print(json.dumps(pmc_pass(lb, torch, synth, args.pmc_pass, args.copies_gb)))
+        return
+    if args.only == "prefill_7b_up_2048":
+        print(json.dumps({args.only: measure_prefill(lb, torch, synth)}))
         return
     if args.only:
         w = DecodeWorkload(lb, torch, synth, args.only, args.copies_gb)

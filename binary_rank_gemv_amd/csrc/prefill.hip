@@ -292,6 +292,36 @@ __global__ __launch_bounds__(PF_THREADS, 2) void lb_prefill_kernel(LbPrefillArgs
 #define P2_G_OFF (P2_CHUNK + 4 * 4 * 256)
 #define P2_STAGE_BYTES (P2_G_OFF + 1024)
 
+// Tile of a workgroup of the one-dimensional grid: 256-row block bx, token
+// block by, branch bz (GEMM 1).  Workgroups go to the 8 XCDs (each with its
+// own L2) round-robin by index; XCD x takes a contiguous run of tiles in
+// token-block-major order, so that the activations of a token block (g*x,
+// or z) are fetched into one L2 and its workgroups share them there.
+struct P2Tile {
+  int bx, by, bz;
+};
+
+__device__ __forceinline__ P2Tile p2_tile(int rb, int tb, int nbz) {
+  const int n = rb * tb * nbz, L = (int)blockIdx.x;
+  const int xcd = L & 7, idx = L >> 3, per = n >> 3, rem = n & 7;
+  const int P = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+  P2Tile t;
+  t.by = P / (rb * nbz);
+  const int q = P - t.by * rb * nbz;
+  t.bz = q / rb;
+  t.bx = q - t.bz * rb;
+  return t;
+}
+
+__host__ __device__ inline int p2_row_blocks(const LbPrefillArgs& a, int mode) {
+  int t = 0;
+  if (mode == 1)
+    for (int b = 0; b < a.nb; ++b) t = max(t, (a.br[b].r + 15) >> 4);
+  else
+    t = (a.m + 15) >> 4;
+  return (t + 15) / 16;
+}
+
 template <int MODE>
 __global__ __launch_bounds__(64 * P2_WAVES, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 lb_prefill2_kernel(LbPrefillArgs A) {
@@ -304,17 +334,18 @@ lb_prefill2_kernel(LbPrefillArgs A) {
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int rg = wave & 3, kh = wave >> 2;  // row group, half of each chunk
   const int grp = lane >> 4, col = lane & 15;
-  const int tok0 = blockIdx.y * PF_BN;
-  const int tile0 = 16 * blockIdx.x + 4 * rg;  // first row tile of this wave
   const int M = A.M;
+  const P2Tile bt = p2_tile(p2_row_blocks(A, MODE), (M + PF_BN - 1) / PF_BN, MODE == 1 ? A.nb : 1);
+  const int tok0 = bt.by * PF_BN;
+  const int tile0 = 16 * bt.bx + 4 * rg;  // first row tile of this wave
   const LbSignConsts sc = lb16_sign_consts();
 
   // the reduction as a sequence of 128-input chunks over one or two segments
-  const int b1 = MODE == 1 ? (int)blockIdx.z : 0;
+  const int b1 = MODE == 1 ? bt.bz : 0;
   const LbBranchArgs& B0 = A.br[b1];
   const LbBranchArgs& B1 = A.br[MODE == 2 && A.nb == 2 ? 1 : b1];
   const int ntiles = MODE == 1 ? (B0.r + 15) >> 4 : (A.m + 15) >> 4;
-  if (16 * (int)blockIdx.x >= ntiles) return;  // rows beyond this branch (uniform)
+  if (16 * bt.bx >= ntiles) return;  // rows beyond this branch (uniform)
   const int K0 = MODE == 1 ? A.n : B0.r, K1 = MODE == 1 ? A.n : B1.r;
   const int nu0 = lb16_units(K0), nu1 = lb16_units(K1);
   const int np0 = MODE == 1 ? A.n / 128 : (nu0 + 1) >> 1;
@@ -422,7 +453,7 @@ lb_prefill2_kernel(LbPrefillArgs A) {
     for (int rt = 0; rt < 4; ++rt)
       reg[rt] = lb16_reg_word(words[64 * rt], sel) ^ (MODE == 2 && (hbits(rt) & 0x8000u) ? 0xFFFFFFFFu : 0u);
     auto mstep = [&](int st, const f16x8* bb, bool with_loads) {
-      if (with_loads) issue(min(c + 2, C - 1), ahead);
+      if (with_loads) issue(min(c + P2_STAGES - 1, C - 1), ahead);
       u32x4 gq = u32x4{0u, 0u, 0u, 0u};
       if (MODE == 1) gq = *reinterpret_cast<const u32x4*>(S + P2_G_OFF + 2 * (32 * st + 8 * grp));
 #pragma unroll
@@ -468,7 +499,9 @@ lb_prefill2_kernel(LbPrefillArgs A) {
   auto run = [&](auto loads) __attribute__((always_inline)) {
     constexpr bool LOADS = decltype(loads)::value;
     auto step = [&](int c, const uint8_t* cur, uint8_t* ahead) __attribute__((always_inline)) {
-      if (LOADS) __builtin_amdgcn_s_waitcnt(kOps | (7 << 4) | (15 << 8));
+      // vmcnt(kOps * (P2_STAGES - 2)): the loads of the next stages may still be in flight
+      constexpr int kWait = kOps * (P2_STAGES - 2);
+      if (LOADS) __builtin_amdgcn_s_waitcnt((kWait & 15) | ((kWait >> 4) << 14) | (7 << 4) | (15 << 8));
       __builtin_amdgcn_s_barrier();
       __asm__ volatile("" ::: "memory");
       compute(c, cur, ahead, loads);
@@ -553,7 +586,7 @@ lb_prefill2_kernel(LbPrefillArgs A) {
     }
     // the block holding the last row tile also zeroes this token block's
     // z entries between 16*ceil(r/16) and 128*ceil(r/128)
-    if ((int)blockIdx.x == (ntiles - 1) >> 4) {
+    if (bt.bx == (ntiles - 1) >> 4) {
       const int j0 = 16 * ntiles, nz = 128 * ((B.r + 127) / 128) - j0;
       const int per_tok = nz >> 2;
       for (int e = threadIdx.x; e < per_tok * PF_BN; e += 64 * P2_WAVES) {
@@ -598,8 +631,8 @@ hipError_t lb_launch_prefill(const LbPrefillArgs& a, hipStream_t stream) {
   auto fits32 = [&](long ld, long width) { return ((long)(a.M + 16) * ld + width) * 2 < (1l << 32); };
   hipError_t e;
   if (aligned_x && a.n % 128 == 0 && fits32(a.ldx, a.n)) {
-    // v2: GEMM 1 over both branches (blockIdx.z), then GEMM 2
-    hipLaunchKernelGGL((lb_prefill2_kernel<1>), dim3((unsigned)((maxt + 15) / 16), tb, (unsigned)a.nb),
+    // v2: GEMM 1 over both branches, then GEMM 2 (one-dimensional grids, see p2_tile)
+    hipLaunchKernelGGL((lb_prefill2_kernel<1>), dim3((unsigned)(p2_row_blocks(a, 1) * tb * a.nb)),
                        dim3(64 * P2_WAVES), 0, stream, a);
   } else {
     const dim3 g1((unsigned)((maxt + 7) / 8), tb, (unsigned)a.nb);
@@ -613,7 +646,7 @@ hipError_t lb_launch_prefill(const LbPrefillArgs& a, hipStream_t stream) {
   // GEMM 2 reads z (always 16-byte aligned, zero-padded to whole chunks)
   const int mt = (a.m + 15) >> 4;
   if (fits32(a.zs, a.zs))
-    hipLaunchKernelGGL((lb_prefill2_kernel<2>), dim3((unsigned)((mt + 15) / 16), tb, 1), dim3(64 * P2_WAVES), 0,
+    hipLaunchKernelGGL((lb_prefill2_kernel<2>), dim3((unsigned)(p2_row_blocks(a, 2) * tb)), dim3(64 * P2_WAVES), 0,
                        stream, a);
   else
     hipLaunchKernelGGL((lb_prefill_kernel<2, true>), dim3((unsigned)((mt + 7) / 8), tb, 1), dim3(PF_THREADS), 0,
