@@ -191,7 +191,7 @@ def make_copy(lb, torch, shape, seed):
 def decode_sources():
     """The sources whose code runs in (or launches) the decode kernels."""
     files = sorted(glob.glob(os.path.join(CSRC, "decode*.hip"))) + [
-        os.path.join(CSRC, "lb_common.h"), os.path.join(CSRC, "littlebit_host.hip")]
+        os.path.join(CSRC, "lb_common.h"), os.path.join(CSRC, "lb_sync.h"), os.path.join(CSRC, "littlebit_host.hip")]
     return files
 
 
@@ -205,8 +205,8 @@ def sources_hash(files):
 
 
 def pmc_summary_path(config):
-    kernel = "lb_prefill" if config.startswith("prefill") else "lb_decode"
-    return os.path.join(PROFILES, f"{kernel}_{config}_pmc.md")
+    name = f"lb_{config}" if config.startswith("prefill") else f"lb_decode_{config}"
+    return os.path.join(PROFILES, f"{name}_pmc.md")
 
 
 def measured_traffic(config):
@@ -551,9 +551,11 @@ def main():
     torch.cuda.synchronize()
     yg = head.ys[0].float().cpu().numpy().astype(np.float64)
     res = head.measure(torch, args.steps, args.warmup)
+    print(f"[bench] {HEADLINE}: {res['us_per_call']} us per call", file=sys.stderr, flush=True)
     ms_per_step = res["us_per_call"] * 1e-3
     roofline = dict(res["roofline"])
-    roofline["kernel"] = "lb_decode_kernel (one launch per call: V pass, z exchange, U pass)"
+    roofline["kernel"] = ("lb_decode1_kernel<2, true> (one launch per call: V pass, z exchange, U pass, "
+                          "on the sparse matrix instruction)")
     roofline["avg_call_us"] = res["us_per_call"]
     two = time_graph(torch, [lambda c=c: lb.littlebit_linear_fwd(c[0], head.xs[0], out=head.ys[0],
                                                                   workspace=head.ws,
@@ -577,7 +579,10 @@ def main():
             extra[cfg] = w.measure(torch, max(4 * nc, 400), nc)
             del w
             torch.cuda.empty_cache()
+            print(f"[bench] {cfg}: {extra[cfg]['us_per_call']} us per call", file=sys.stderr, flush=True)
         extra["prefill_7b_up_2048"] = measure_prefill(lb, torch, synth)
+        print(f"[bench] prefill: {extra['prefill_7b_up_2048']['us_per_call']} us per call", file=sys.stderr,
+              flush=True)
 
     cpu = None
     if args.cpu_seconds > 0:

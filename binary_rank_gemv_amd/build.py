@@ -6,7 +6,9 @@
   (include/littlebit_init.h).  Links rocBLAS and rocSOLVER; the layer
   library does not depend on it.
 
-Usage: ``python -m binary_rank_gemv_amd.build`` (or ``build_library()``).
+Usage: ``python -m binary_rank_gemv_amd.build`` (or ``build_library()``);
+``--phase-stamps`` also builds ``_lib/stamped/liblittlebit.so``, the layer
+library with phase timestamps in the one-token decode kernels.
 Every call compiles from source (one hipcc process per source file, in
 parallel, then one link per library); nothing is cached.
 """
@@ -106,6 +108,28 @@ def build_sanitized_host(verbose: bool = False) -> str:
     return SANITIZED_LIB
 
 
+STAMPED_LIB = os.path.join(LIBDIR, "stamped", "liblittlebit.so")
+
+
+def build_phase_stamped(verbose: bool = False) -> str:
+    """The layer library with phase timestamps in the one-token decode
+    kernels (decode1.hip built with -DLB_PHASE_STAMPS; it also exports
+    littlebit_phase_stamps_set), linked with the regular objects of the other
+    sources (build_library must have run).  For phase_timeline.py only."""
+    objdir = os.path.join(LIBDIR, "stamped")
+    os.makedirs(objdir, exist_ok=True)
+    obj = os.path.join(objdir, "decode1.hip.o")
+    _run([HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-c", "-DLB_PHASE_STAMPS",
+          "-I", os.path.join(ROOT, "include"), "-I", CSRC, *DEVICE_FLAGS, os.path.join(CSRC, "decode1.hip"),
+          "-o", obj], verbose)
+    others = [os.path.join(OBJDIR, f + ".o") for f in LAYER_SOURCES if f != "decode1.hip"]
+    missing = [o for o in others if not os.path.exists(o)]
+    if missing:
+        raise RuntimeError(f"build the library first; missing {missing}")
+    _link([obj, *others], STAMPED_LIB, [], verbose)
+    return STAMPED_LIB
+
+
 def build_library(verbose: bool = False, extra_flags=()) -> str:
     """Compile both libraries; returns the layer library's path."""
     os.makedirs(OBJDIR, exist_ok=True)
@@ -120,3 +144,5 @@ def build_library(verbose: bool = False, extra_flags=()) -> str:
 
 if __name__ == "__main__":
     print(build_library(verbose="-v" in sys.argv))
+    if "--phase-stamps" in sys.argv:
+        print(build_phase_stamped(verbose="-v" in sys.argv))

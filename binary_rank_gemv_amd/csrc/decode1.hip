@@ -33,6 +33,33 @@
 #include "lb_common.h"
 #include "lb_sync.h"
 
+// Phase timestamps, in an instrumented build only (-DLB_PHASE_STAMPS; the
+// regular library has none of this).  Every workgroup keeps the 100 MHz
+// real-time counter at fixed points of a call in registers and writes them
+// after its last phase to the device buffer given to
+// littlebit_phase_stamps_set: slot 16 w + i for workgroup w and point i
+// (0 start, 1 arguments and first u staged, 8 first V products start,
+// 2 first V products done, 3 first z round issued, 4 first z copied,
+// 5 first U group's products done, 6 end; 7 a multi-layer tile staged).
+#ifdef LB_PHASE_STAMPS
+__device__ uint64_t* g_phase_stamps;
+#define LB_STAMP_DECL uint64_t ts_[9] = {0, 0, 0, 0, 0, 0, 0, 0, 0};
+#define LB_STAMP(i) (ts_[i] = __builtin_amdgcn_s_memrealtime())
+#define LB_STAMP_WRITE()                                                              \
+  do {                                                                               \
+    uint64_t* sp_ = g_phase_stamps;                                                  \
+    if (threadIdx.x == 0 && sp_)                                                     \
+      for (int i_ = 0; i_ < 9; ++i_) sp_[16 * blockIdx.x + i_] = ts_[i_];            \
+  } while (0)
+extern "C" int littlebit_phase_stamps_set(void* p) {
+  return (int)hipMemcpyToSymbol(HIP_SYMBOL(g_phase_stamps), &p, sizeof(p));
+}
+#else
+#define LB_STAMP_DECL
+#define LB_STAMP(i) ((void)0)
+#define LB_STAMP_WRITE() ((void)0)
+#endif
+
 #define DK_WAVES 8
 #define DK_THREADS (64 * DK_WAVES)
 #define DK_VPW 8   // V-pass pairs per wave per batch of sign words
@@ -700,6 +727,8 @@ __global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* p
   const LbDecodeArgs& A = *reinterpret_cast<const LbDecodeArgs*>(sA_bytes);
 
   const int wg = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  LB_STAMP_DECL
+  LB_STAMP(0);
   const f16x16 B = sign_columns();
   const LbDecodeArgs* KA = dk1_kernarg_args();
 
@@ -736,6 +765,7 @@ __global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* p
   if (SINGLE && MODE != 1 && vt0 < vt1) stage_u(pre_x, k ? pre_g1 : pre_g0, pre_n, dyn);  // the first tile's u
   if (tid < DK_ARGS_BYTES / 16) reinterpret_cast<u32x4*>(sA_bytes)[tid] = acopy;
   lds_barrier_nf();  // the argument copy (and a single layer's first u) is complete
+  LB_STAMP(1);
   if (SINGLE) wait_vmem_all();  // (the staging waited already: this tells the compiler so)
 
   if (SINGLE || MODE != 2) {
@@ -826,6 +856,7 @@ __global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* p
       stage_u(L.x, L.g(b), L.n, dyn);
       staged = k;
       lds_barrier_nf();  // the staged u is complete
+      LB_STAMP(7);
       if (t == vt0) wait_vmem_all();  // (staging waited already: this tells the compiler so)
     }
     if (!SINGLE && t == vt0) issue_first_u();
@@ -840,7 +871,9 @@ __global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* p
       v_load_words(vn, vn.pa, wn);
       lnext = Ln.l(kn & 1)[min(16 * Tn + (tid & 15), Ln.r(kn & 1) - 1)];
     }
+    if (t == vt0) LB_STAMP(8);
     const f32x4 acc = v_tile_sums(v, dyn, B, w);
+    if (t == vt0) LB_STAMP(2);
     if ((lane & 15) == 0)
 #pragma unroll
       for (int q = 0; q < 4; ++q) vred[wave][4 * (lane >> 4) + q] = acc[q];
@@ -879,12 +912,14 @@ __global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* p
   if (MODE != 0 && have_u) {
     ZCopy<8> zc0;
     const int nu0 = nunits(uL.r(ug.b));
+    LB_STAMP(3);
     compiler_memory_barrier();
     zc_begin(zc0, uL, ug.b, min(2 * ug.p0, nu0), min(2 * ug.p1, nu0), dyn);
     get_tag();
     lds_barrier();  // phase A's readers of the LDS are done; the block copy has landed
     zc_finish(zc0, tag, MODE == 2, sync);
     zl_layer = ug.li;
+    LB_STAMP(4);
     lds_ublock(ublk[wave], ug.p0, nu0, cur);
   }
   get_tag();
@@ -938,10 +973,13 @@ __global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* p
     }
 #pragma unroll
     for (int j = 0; j < DK_UTG / 2; ++j) acc[j] += acc1[j];
+    if (t == ut0) LB_STAMP(5);
     u_epilogue(L, g.tile, g.nt, acc, ured[grp & 1], late(hg.h0), late(hg.h1));
     ++grp;
     t += g.nt;
   }
+  LB_STAMP(6);
+  LB_STAMP_WRITE();
   // this workgroup's call is done: the next call's tag is one higher
   if (MODE == 2 && tid == 0) add64c_noret(sync + LB_SYNC_CTR + 8 * wg, 1ull);
 }
