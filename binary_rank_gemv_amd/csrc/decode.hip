@@ -878,8 +878,9 @@ __device__ __forceinline__ void u_span_lds(const LayerView& L, int li, int batch
 
 // MODE 0: phase A only; 1: phase B only; 2: both in one launch (z tagged and
 // polled).  SINGLE: one layer.  Workgroup w takes a contiguous range of the V
-// tiles and of the U tiles.  MAXB: the most tokens (1, or LB_MAX_BATCH: a
-// separate build, so the single-token kernel keeps its registers).
+// tiles and of the U tiles.  MAXB: the most tokens a phase A handles
+// (LB_MAX_BATCH; calls of one token run decode1.hip's kernels); the
+// phase-B-only kernel (MODE 1) takes any batch with the default.
 //
 // The leading arguments are preloaded into scalar registers by the dispatch
 // (kernel-argument preloading), so a single-layer kernel issues its first
@@ -1246,20 +1247,19 @@ static hipError_t fused_grid(int& G) {
   G = 0;
   if (dev < 0 || dev >= 64) return hipSuccess;
   if (g_fused_grid[dev] == 0) {
-    int ncu = 0, occa = 0, occb = 0, occ1 = 0, occ2 = 0;
+    int ncu = 0, occb = 0, occ1 = 0, occ2 = 0;
     e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
     // every workgroup of the single launch must be resident at once: size
-    // the grid for the largest dynamic LDS a launch may request
-    e = fused_occupancy<1>(occa);
-    if (e != hipSuccess) return e;
+    // the grid for the largest dynamic LDS a launch may request (one token
+    // runs decode1.hip's kernels, two to LB_MAX_BATCH these)
     e = fused_occupancy<LB_MAX_BATCH>(occb);
     if (e != hipSuccess) return e;
     e = lb_decode1_occupancy(true, LB_DECODE1_LDS_MAX, occ1);
     if (e != hipSuccess) return e;
     e = lb_decode1_occupancy(false, LB_DECODE1_LDS_MAX, occ2);
     if (e != hipSuccess) return e;
-    g_fused_grid[dev] = (occa >= 1 && occb >= 1 && occ1 >= 1 && occ2 >= 1) ? (ncu < LB_MAX_GRID ? ncu : LB_MAX_GRID) : -1;
+    g_fused_grid[dev] = (occb >= 1 && occ1 >= 1 && occ2 >= 1) ? (ncu < LB_MAX_GRID ? ncu : LB_MAX_GRID) : -1;
   }
   G = g_fused_grid[dev] > 0 ? g_fused_grid[dev] : 0;
   return hipSuccess;
