@@ -31,7 +31,7 @@ Readings where the page is silent (each also listed in the design notes):
   model of both factors applied to the sign pattern.
 * Scales are stored as fp16 (round to nearest even), as the deployed layer
   uses them; the residual for branch 2 is W minus the deployed (fp16-scaled)
-  branch 1, since branch 2 models what the deployed first branch misses.
+  branch 1: branch 2 is fitted to the error the deployed first branch leaves.
 * Both branches use the same rank r.
 
 Parity status (tests/test_oracle.py):
