@@ -554,7 +554,7 @@ def main():
     print(f"[bench] {HEADLINE}: {res['us_per_call']} us per call", file=sys.stderr, flush=True)
     ms_per_step = res["us_per_call"] * 1e-3
     roofline = dict(res["roofline"])
-    roofline["kernel"] = ("lb_decode1_kernel<2, true> (one launch per call: V pass, z exchange, U pass, "
+    roofline["kernel"] = ("lb_decode1_kernel<2, true, 1> (one launch per call: V pass, z exchange, U pass, "
                           "on the sparse matrix instruction)")
     roofline["avg_call_us"] = res["us_per_call"]
     two = time_graph(torch, [lambda c=c: lb.littlebit_linear_fwd(c[0], head.xs[0], out=head.ys[0],

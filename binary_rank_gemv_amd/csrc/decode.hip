@@ -1198,12 +1198,12 @@ static void balanced_split(const int64_t* c, int n, int G, int* begin) {
 // its reduction length plus a fixed share (u staging, cross-wave sums, z
 // store, about a 4096-input pass); a U tile its two branches' ranks plus a
 // smaller fixed share.
-static void cost_split(LbDecodeArgs& a, int G) {
+static void cost_split(LbDecodeArgs& a, int G, int vrows = 16) {
   std::vector<int64_t> c;
   c.reserve(a.nvt > a.nut ? a.nvt : a.nut);
   for (int li = 0; li < a.nlayers; ++li)
     for (int b = 0; b < a.L[li].nb; ++b)
-      for (int t = 0; t < (a.L[li].br[b].r + 15) / 16; ++t) c.push_back(a.L[li].n + 4096);
+      for (int t = 0; t < (a.L[li].br[b].r + vrows - 1) / vrows; ++t) c.push_back(a.L[li].n + 4096);
   balanced_split(c.data(), (int)c.size(), G, a.vt_begin);
   c.clear();
   for (int li = 0; li < a.nlayers; ++li) {
@@ -1333,8 +1333,23 @@ hipError_t lb_launch_decode(const LbDecodeArgs& args, int chunk_pairs, void* syn
       hipError_t e = fused_grid(G);
       if (e != hipSuccess) return e;
     }
+    // its V work comes in units of one or two 16-rank tiles of a branch:
+    // two (one instruction serves both) when there are more tiles than
+    // workgroups, one otherwise (every workgroup then has at most one tile,
+    // and a second would only lengthen the busy ones)
     LbDecodeArgs a = args;
-    if (G > 0 && a.nlayers > 1) cost_split(a, G);
+    int tiles = 0;
+    for (int i = 0; i < a.nlayers; ++i)
+      for (int b = 0; b < a.L[i].nb; ++b) tiles += (a.L[i].br[b].r + 15) / 16;
+    a.vtpu = tiles > LB_MAX_GRID ? 2 : 1;
+    int vu = 0;
+    for (int i = 0; i < a.nlayers; ++i)
+      for (int b = 0; b < 2; ++b) {
+        if (b < a.L[i].nb) vu += ((a.L[i].br[b].r + 15) / 16 + a.vtpu - 1) / a.vtpu;
+        a.vt_end[2 * i + b] = vu;
+      }
+    a.nvt = vu;
+    if (G > 0 && a.nlayers > 1) cost_split(a, G, 16 * a.vtpu);
     return lb_launch_decode1(a, G, sync, stream);
   }
   return args.nlayers == 1 ? launch_decode_t<true, LB_MAX_BATCH>(args, chunk_pairs, sync, allow_fused, stream)

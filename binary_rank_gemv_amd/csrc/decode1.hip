@@ -18,7 +18,7 @@
 // so no bit is moved.
 //
 // Structure (as in the multi-token kernels of decode.hip): phase A runs the V
-// pass over 16-row tiles of sign(V)^T (the 8 waves of a workgroup split the
+// pass over pairs of 16-row tiles of sign(V)^T (the 8 waves of a workgroup split the
 // reduction; the activation operands reach each 16-lane row by a DPP row
 // broadcast) and stores z as tagged 64-bit words [call tag | two fp16];
 // phase B polls the z range of each wave, then runs the U pass over groups
@@ -147,26 +147,11 @@ __device__ __forceinline__ PairAct load_pair_act(const uint16_t* act, bool two_u
   return a;
 }
 
-// The products of one pair for one tile (column 0): raw LB16 word w (for an
-// odd last unit, the lane's unit in bits 0..15 and two_units false).  Bit 1
-// of every index is clear and bit 3 set, so each slot pair keeps its own two
-// positions; three VALU operations make the indices of up to four
-// instructions.
-__device__ __forceinline__ void pair_products(const PairAct& a, uint32_t w, bool two_units, const f16x16& B,
-                                              f32x4& acc0, f32x4& acc1) {
-  const int ie = (int)((w & 0x55555555u) | 0x88888888u);
-  const int io = (int)(((w >> 1) & 0x55555555u) | 0x88888888u);
-  acc0 = smfmac(a.e0, B, acc0, ie, 0);
-  acc1 = smfmac(a.o0, B, acc1, io, 0);
-  if (two_units) {
-    acc0 = smfmac(a.e1, B, acc0, ie, 1);
-    acc1 = smfmac(a.o1, B, acc1, io, 1);
-  }
-}
-
-// The same for two tiles at once: the sign bit of tile a's row becomes bit 0
-// and tile b's bit 1 of each index, so column 0 sums tile a's row and column
-// 1 tile b's (wa, wb as for pair_products; four VALU operations).
+// The products of one pair of units for two tiles at once: raw LB16 words
+// wa, wb of the tiles (for an odd last unit, the lane's unit in bits 0..15
+// and two_units false).  The sign bit of tile a's row becomes bit 0 and tile
+// b's bit 1 of each index, so column 0 sums tile a's row and column 1 tile
+// b's; four VALU operations make the indices of up to four instructions.
 __device__ __forceinline__ void pair_products2(const PairAct& a, uint32_t wa, uint32_t wb, bool two_units,
                                                const f16x16& B, f32x4& acc0, f32x4& acc1) {
   const int ie = (int)((wa & 0x55555555u) | ((wb << 1) & 0xAAAAAAAAu));
@@ -374,33 +359,52 @@ __device__ __forceinline__ void store_z_tile(const SL& L, int b, int T, uint32_t
   }
 }
 
-// The V pass over one tile: wave w sums its even share [pa, pb) of the
-// tile's pairs, the sign words in batches of DK_VPW pairs per wave.
+// The V pass over a pair of tiles of one branch (T0, T1; T1 == T0 for an
+// odd last tile): wave w sums its even share [pa, pb) of the tiles' unit
+// pairs, the sign words of both tiles in batches of DK_VPW pairs per wave.
 struct VTile {
-  const uint8_t* tile;
+  const uint8_t *tile0, *tile1;
   int nu, pa, pb;
 };
 
-__device__ __forceinline__ VTile v_tile_geom(const uint8_t* vbits, int n, int T) {
+__device__ __forceinline__ VTile v_tile_geom(const uint8_t* vbits, int n, int T0, int T1) {
   VTile v;
   v.nu = nunits(n);
   const int np = (v.nu + 1) >> 1, wave = wave_id();
-  v.tile = vbits + (long)T * lb16_tile_bytes(n);
+  v.tile0 = vbits + (long)T0 * lb16_tile_bytes(n);
+  v.tile1 = vbits + (long)T1 * lb16_tile_bytes(n);
   v.pa = (np * wave) >> 3;
   v.pb = (np * (wave + 1)) >> 3;
   return v;
 }
 
+// Unit u of V work (tpu = 1 or 2 16-rank tiles) of a branch with ntv tiles:
+// tiles T0 and T1 (T1 == T0 for one tile).
+__device__ __forceinline__ void v_pair_tiles(int u, int ntv, int tpu, int& T0, int& T1) {
+  T0 = tpu * u;
+  T1 = min(T0 + tpu - 1, ntv - 1);
+}
+
+struct VWords {
+  uint32_t w0[DK_VPW], w1[DK_VPW];
+};
+
 // Sign words of batch [pc, pc + DK_VPW), in groups of four pairs; groups
 // that start beyond the share are not loaded (their words are never used),
-// and the last group's slots beyond pb repeat its last word.
-__device__ __forceinline__ void v_load_words(const VTile& v, int pc, uint32_t (&w)[DK_VPW]) {
+// and the last group's slots beyond pb repeat its last word.  TPU = 1: the
+// unit is one tile (T1 == T0) and only its words are loaded.
+template <int TPU>
+__device__ __forceinline__ void v_load_words(const VTile& v, int pc, VWords& w) {
   const int plast = max(v.pb - 1, 0);
 #pragma unroll
   for (int j = 0; j < DK_VPW / 4; ++j)
-    if (j == 0 || pc + 4 * j < v.pb)
+    if (j == 0 || pc + 4 * j < v.pb) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) w[4 * j + i] = pair_word(v.tile, min(pc + 4 * j + i, plast), v.nu);
+      for (int i = 0; i < 4; ++i) w.w0[4 * j + i] = pair_word(v.tile0, min(pc + 4 * j + i, plast), v.nu);
+      if (TPU == 2)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w.w1[4 * j + i] = pair_word(v.tile1, min(pc + 4 * j + i, plast), v.nu);
+    }
 }
 
 // V activations through a row broadcast.  Every lane of a 16-lane row (one
@@ -438,37 +442,39 @@ __device__ __forceinline__ PairAct bcast_pair(const u32x4& q) {
   return a;
 }
 
-template <int J, int I>
-__device__ __forceinline__ void v_pair(const VTile& v, int pc, const u32x4& q, const uint32_t (&w)[DK_VPW],
-                                       const f16x16& B, f32x4& acc0, f32x4& acc1) {
+template <int TPU, int J, int I>
+__device__ __forceinline__ void v_pair(const VTile& v, int pc, const u32x4& q, const VWords& w, const f16x16& B,
+                                       f32x4& acc0, f32x4& acc1) {
   const int p = pc + 4 * J + I;
   if (p < v.pb) {
     const bool two = 2 * p + 1 < v.nu;
-    pair_products(bcast_pair<I>(q), pair_bits(late(w[4 * J + I]), two), two, B, acc0, acc1);
+    const uint32_t b0 = pair_bits(late(w.w0[4 * J + I]), two);
+    pair_products2(bcast_pair<I>(q), b0, TPU == 2 ? pair_bits(late(w.w1[4 * J + I]), two) : b0, two, B, acc0, acc1);
   }
   __builtin_amdgcn_sched_barrier(0);  // one pair's operands live at a time
 }
 
-template <int J>
-__device__ __forceinline__ void v_group(const VTile& v, int pc, const u32x4& q, const uint32_t (&w)[DK_VPW],
-                                        const f16x16& B, f32x4& acc0, f32x4& acc1) {
-  v_pair<J, 0>(v, pc, q, w, B, acc0, acc1);
-  v_pair<J, 1>(v, pc, q, w, B, acc0, acc1);
-  v_pair<J, 2>(v, pc, q, w, B, acc0, acc1);
-  v_pair<J, 3>(v, pc, q, w, B, acc0, acc1);
+template <int TPU, int J>
+__device__ __forceinline__ void v_group(const VTile& v, int pc, const u32x4& q, const VWords& w, const f16x16& B,
+                                        f32x4& acc0, f32x4& acc1) {
+  v_pair<TPU, J, 0>(v, pc, q, w, B, acc0, acc1);
+  v_pair<TPU, J, 1>(v, pc, q, w, B, acc0, acc1);
+  v_pair<TPU, J, 2>(v, pc, q, w, B, acc0, acc1);
+  v_pair<TPU, J, 3>(v, pc, q, w, B, acc0, acc1);
 }
 
 // Returns this lane's partial sums (rows 4 (lane / 16) + q of column
-// lane % 16); `w` holds the first batch's words on entry.
-__device__ __forceinline__ f32x4 v_tile_sums(const VTile& v, const uint16_t* up, const f16x16& B,
-                                             uint32_t (&w)[DK_VPW]) {
+// lane % 16: tile T0 in column 0, T1 in column 1); `w` holds the first
+// batch's words on entry.
+template <int TPU>
+__device__ __forceinline__ f32x4 v_tile_sums(const VTile& v, const uint16_t* up, const f16x16& B, VWords& w) {
   static_assert(DK_VPW == 8, "two activation groups per batch");
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   const int plast = max(v.pb - 1, 0);
   for (int pc = v.pa; pc < v.pb; pc += DK_VPW) {
-    if (pc != v.pa) v_load_words(v, pc, w);
-    v_group<0>(v, pc, load_act_group(up, pc, plast, v.nu), w, B, acc0, acc1);
-    v_group<1>(v, pc, load_act_group(up, pc + 4, plast, v.nu), w, B, acc0, acc1);
+    if (pc != v.pa) v_load_words<TPU>(v, pc, w);
+    v_group<TPU, 0>(v, pc, load_act_group(up, pc, plast, v.nu), w, B, acc0, acc1);
+    v_group<TPU, 1>(v, pc, load_act_group(up, pc + 4, plast, v.nu), w, B, acc0, acc1);
   }
   return acc0 + acc1;
 }
@@ -697,8 +703,8 @@ struct Dk1Kernargs {
   const uint8_t *pre_vb0, *pre_vb1;
   const uint16_t *pre_x, *pre_g0, *pre_g1;
   uint8_t* sync;
-  int pre_n;
-  uint32_t pre_misc;  // vq | vr << 8 | vsplit << 16 (V tiles of workgroup w: vq + (w < vr); vsplit: of branch 0)
+  int pre_n;          // n | (V tiles of branch 0) << 16
+  uint32_t pre_misc;  // vq | vr << 8 | (V tiles of branch 1) << 17 (V units of workgroup w: vq + (w < vr))
   LbDecodeArgs A;
 };
 
@@ -712,16 +718,17 @@ __device__ __forceinline__ const LbDecodeArgs* dk1_kernarg_args() {
 // one launch of one workgroup per compute unit.  SINGLE: one layer (tile
 // ranges split evenly: V by pre_misc, U by uq/ur); else the cost-balanced
 // ranges vt_begin / ut_begin of the argument block (two launches: vq/vr,
-// uq/ur).
-template <int MODE, bool SINGLE>
+// uq/ur).  TPU: 16-rank tiles per unit of V work (1, or 2 on one
+// instruction: the host takes 2 when there are more tiles than workgroups).
+template <int MODE, bool SINGLE, int TPU>
 __global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* pre_vb0, const uint8_t* pre_vb1,
                                                                 const uint16_t* pre_x, const uint16_t* pre_g0,
                                                                 const uint16_t* pre_g1, uint8_t* sync, int pre_n,
                                                                 uint32_t pre_misc, LbDecodeArgs) {
   extern __shared__ __align__(16) uint16_t dyn[];  // u in sparse order (phase A), z (phase B)
   __shared__ __align__(16) uint8_t sA_bytes[DK_ARGS_BYTES];
-  __shared__ float vred[DK_WAVES][16];
-  __shared__ uint16_t zv[16];
+  __shared__ float vred[DK_WAVES][32];
+  __shared__ uint16_t zv[32];
   __shared__ float ured[2][DK_UTG][DK_WAVES][16];
   __shared__ __align__(16) uint32_t ublk[DK_WAVES][DK_UTG * DK_UPW * 64];  // each wave's first U block
   const LbDecodeArgs& A = *reinterpret_cast<const LbDecodeArgs*>(sA_bytes);
@@ -733,21 +740,24 @@ __global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* p
   const LbDecodeArgs* KA = dk1_kernarg_args();
 
   // ---------------- start
-  // Load order (loads complete in issue order): the first V tile's sign
+  // Load order (loads complete in issue order): the first V unit's sign
   // words (single layer: from the preloaded arguments), the argument block's
   // copy, this workgroup's call counter, the staging loads of x and g.
+  // V work comes in units of two 16-rank tiles of one branch (T0, T1).
   int vt0 = 0, vt1 = 0;
-  int k = 0, T = 0;
+  int k = 0, T0 = 0, T1 = 0;
   VTile v;
-  uint32_t w[DK_VPW];
-  const int vsplit = (int)(pre_misc >> 16);
+  VWords w;
+  const int n1 = pre_n & 0xFFFF;  // the single layer's n, and its branches' V tile counts
+  const int ntv0 = (int)((uint32_t)pre_n >> 16), ntv1 = (int)(pre_misc >> 17);
+  const int vsplit = (ntv0 + TPU - 1) / TPU;  // V units of branch 0
   if (SINGLE && MODE != 1) {
     share1((int)(pre_misc & 255u), (int)((pre_misc >> 8) & 255u), wg, vt0, vt1);
     if (vt0 < vt1) {
       k = vt0 >= vsplit ? 1 : 0;
-      T = vt0 - (k ? vsplit : 0);
-      v = v_tile_geom(k ? pre_vb1 : pre_vb0, pre_n, T);
-      v_load_words(v, v.pa, w);
+      v_pair_tiles(vt0 - (k ? vsplit : 0), k ? ntv1 : ntv0, TPU, T0, T1);
+      v = v_tile_geom(k ? pre_vb1 : pre_vb0, n1, T0, T1);
+      v_load_words<TPU>(v, v.pa, w);
     }
   }
   u32x4 acopy = {0u, 0u, 0u, 0u};
@@ -762,7 +772,7 @@ __global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* p
     ut1 = KA->ut_begin[wg + 1];
   }
   HPair hcur = {0u, 0u};  // row scales of the first U group
-  if (SINGLE && MODE != 1 && vt0 < vt1) stage_u(pre_x, k ? pre_g1 : pre_g0, pre_n, dyn);  // the first tile's u
+  if (SINGLE && MODE != 1 && vt0 < vt1) stage_u(pre_x, k ? pre_g1 : pre_g0, n1, dyn);  // the first unit's u
   if (tid < DK_ARGS_BYTES / 16) reinterpret_cast<u32x4*>(sA_bytes)[tid] = acopy;
   lds_barrier_nf();  // the argument copy (and a single layer's first u) is complete
   LB_STAMP(1);
@@ -774,17 +784,23 @@ __global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* p
   }
   if (MODE == 1) vt1 = vt0;
   if (MODE == 0) ut1 = ut0;
-  // the first V tile's latent scales (and, for several layers, its sign
-  // words): loaded ahead, like those of each next tile
+  // the first V unit's latent scales (and, for several layers, its sign
+  // words): loaded ahead, like those of each next unit.  Thread i < 32
+  // holds l of row i % 16 of tile T0 (i < 16) or T1.
+  auto l_of = [&](const SL& L, int b, int t0, int t1) {
+    return (uint32_t)L.l(b)[min(16 * (tid & 16 ? t1 : t0) + (tid & 15), L.r(b) - 1)];
+  };
   uint32_t lcur = 0;
   if (vt0 < vt1) {
-    if (!SINGLE) k = v_slot1<SINGLE>(A, vt0, T);
+    int u = 0;
+    if (!SINGLE) k = v_slot1<SINGLE>(A, vt0, u);
     const SL L = scalar_layer(A.L[k >> 1]);
     if (!SINGLE) {
-      v = v_tile_geom(L.vb(k & 1), L.n, T);
-      v_load_words(v, v.pa, w);
+      v_pair_tiles(u, (L.r(k & 1) + 15) >> 4, TPU, T0, T1);
+      v = v_tile_geom(L.vb(k & 1), L.n, T0, T1);
+      v_load_words<TPU>(v, v.pa, w);
     }
-    lcur = L.l(k & 1)[min(16 * T + (tid & 15), L.r(k & 1) - 1)];
+    lcur = l_of(L, k & 1, T0, T1);
   }
 
   // ---------------- phase A
@@ -860,26 +876,29 @@ __global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* p
       if (t == vt0) wait_vmem_all();  // (staging waited already: this tells the compiler so)
     }
     if (!SINGLE && t == vt0) issue_first_u();
-    // the next tile's sign words and latent scales
-    int kn = k, Tn = T;
+    // the next unit's sign words and latent scales
+    int kn = k, Tn0 = T0, Tn1 = T1;
     VTile vn = v;
-    uint32_t wn[DK_VPW], lnext = 0;
+    VWords wn;
+    uint32_t lnext = 0;
     if (t + 1 < vt1) {
-      kn = v_slot1<SINGLE>(A, t + 1, Tn);
+      int un = 0;
+      kn = v_slot1<SINGLE>(A, t + 1, un);
       const SL Ln = scalar_layer(A.L[kn >> 1]);
-      vn = v_tile_geom(Ln.vb(kn & 1), Ln.n, Tn);
-      v_load_words(vn, vn.pa, wn);
-      lnext = Ln.l(kn & 1)[min(16 * Tn + (tid & 15), Ln.r(kn & 1) - 1)];
+      v_pair_tiles(un, (Ln.r(kn & 1) + 15) >> 4, TPU, Tn0, Tn1);
+      vn = v_tile_geom(Ln.vb(kn & 1), Ln.n, Tn0, Tn1);
+      v_load_words<TPU>(vn, vn.pa, wn);
+      lnext = l_of(Ln, kn & 1, Tn0, Tn1);
     }
     if (t == vt0) LB_STAMP(8);
-    const f32x4 acc = v_tile_sums(v, dyn, B, w);
+    const f32x4 acc = v_tile_sums<TPU>(v, dyn, B, w);
     if (t == vt0) LB_STAMP(2);
-    if ((lane & 15) == 0)
+    if ((lane & 15) < 2)  // column 0: tile T0, column 1: tile T1
 #pragma unroll
-      for (int q = 0; q < 4; ++q) vred[wave][4 * (lane >> 4) + q] = acc[q];
+      for (int q = 0; q < 4; ++q) vred[wave][16 * (lane & 15) + 4 * (lane >> 4) + q] = acc[q];
     lds_barrier_nf();
-    if (tid < 16) {
-      const int j = 16 * T + tid;
+    if (tid < 32) {
+      const int j = 16 * (tid & 16 ? T1 : T0) + (tid & 15);
       float s = 0.f;
 #pragma unroll
       for (int w8 = 0; w8 < DK_WAVES; ++w8) s += vred[w8][tid];
@@ -887,14 +906,16 @@ __global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* p
       zv[tid] = __builtin_bit_cast(uint16_t, z);
     }
     lds_barrier_nf();
-    store_z_tile(L, b, T, get_tag(), zv);
+    const uint32_t tg = get_tag();
+    store_z_tile(L, b, T0, tg, zv);
+    if (T1 != T0) store_z_tile(L, b, T1, tg, zv + 16);
     if (t + 1 < vt1) {
       k = kn;
-      T = Tn;
+      T0 = Tn0;
+      T1 = Tn1;
       v = vn;
       lcur = lnext;
-#pragma unroll
-      for (int i = 0; i < DK_VPW; ++i) w[i] = wn[i];
+      w = wn;
     }
   };
   if (vt0 < vt1) v_step(vt0);
@@ -996,13 +1017,30 @@ size_t lb_decode1_lds_bytes(const LbDecodeArgs& a) {
   return m;
 }
 
-// Workgroups of a single launch that fit at once, for the given dynamic LDS.
-hipError_t lb_decode1_occupancy(bool single, size_t lds, int& occ) {
-  return single ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, lb_decode1_kernel<2, true>, DK_THREADS, lds)
-                : hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, lb_decode1_kernel<2, false>, DK_THREADS, lds);
+typedef void (*Decode1Kernel)(const uint8_t*, const uint8_t*, const uint16_t*, const uint16_t*, const uint16_t*,
+                             uint8_t*, int, uint32_t, LbDecodeArgs);
+
+// The instantiation for a launch: one or several layers, one or two V tiles
+// per unit.
+template <int MODE>
+Decode1Kernel decode1_variant(bool single, bool one) {
+  if (single) return one ? lb_decode1_kernel<MODE, true, 1> : lb_decode1_kernel<MODE, true, 2>;
+  return one ? lb_decode1_kernel<MODE, false, 1> : lb_decode1_kernel<MODE, false, 2>;
 }
 
-// Launches for one token.  G > 0: one launch of G workgroups (the caller has
+// Workgroups of a single launch that fit at once, for the given dynamic LDS
+// (the lower count of the two V unit sizes).
+hipError_t lb_decode1_occupancy(bool single, size_t lds, int& occ) {
+  int o1 = 0, o2 = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o1, decode1_variant<2>(single, true), DK_THREADS, lds);
+  if (e == hipSuccess)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o2, decode1_variant<2>(single, false), DK_THREADS, lds);
+  occ = o1 < o2 ? o1 : o2;
+  return e;
+}
+
+// Launches for one token.  a.vt_end / a.nvt count V units (a.vtpu 16-rank
+// tiles of a branch each).  G > 0: one launch of G workgroups (the caller has
 // checked that G are resident at once, and a.vt_begin / a.ut_begin hold the
 // ranges of a multi-layer call); G == 0: the two launches.
 hipError_t lb_launch_decode1(const LbDecodeArgs& args, int G, void* sync, hipStream_t stream) {
@@ -1016,35 +1054,32 @@ hipError_t lb_launch_decode1(const LbDecodeArgs& args, int G, void* sync, hipStr
   const uint16_t* px = single ? L0.x : nullptr;
   const uint16_t* g0 = single ? L0.br[0].g : nullptr;
   const uint16_t* g1 = single ? L0.br[1].g : nullptr;
-  const int pn = single ? L0.n : 0;
+  // n, the branches' V tile counts and the tiles per V unit ride in the
+  // high bits of pre_n and pre_misc
+  const int ntv0 = single ? (L0.br[0].r + 15) / 16 : 0;
+  const int ntv1 = single && L0.nb == 2 ? (L0.br[1].r + 15) / 16 : 0;
+  if (single && (L0.n > 0xFFFF || ntv0 > 0xFFFF || ntv1 > 0x7FFF)) return hipErrorInvalidValue;
+  if (args.vtpu != 1 && args.vtpu != 2) return hipErrorInvalidValue;
+  const int pn = single ? (int)((uint32_t)L0.n | ((uint32_t)ntv0 << 16)) : 0;
   uint8_t* sy = static_cast<uint8_t*>(sync);
-  auto misc = [&](int vq, int vr) {
-    return (uint32_t)vq | ((uint32_t)vr << 8) | ((uint32_t)(single ? args.vt_end[0] : 0) << 16);
-  };
+  auto misc = [&](int vq, int vr) { return (uint32_t)vq | ((uint32_t)vr << 8) | ((uint32_t)ntv1 << 17); };
+  const bool one = args.vtpu == 1;
   if (G > 0) {
     a.vq = a.nvt / G;
     a.vr = a.nvt % G;
     a.uq = a.nut / G;
     a.ur = a.nut % G;
     if (a.vq > 255 || a.vr > 255) return hipErrorInvalidValue;
-    if (single)
-      hipLaunchKernelGGL((lb_decode1_kernel<2, true>), dim3(G), dim3(DK_THREADS), lds, stream, vb0, vb1, px, g0, g1,
-                         sy, pn, misc(a.vq, a.vr), a);
-    else
-      hipLaunchKernelGGL((lb_decode1_kernel<2, false>), dim3(G), dim3(DK_THREADS), lds, stream, vb0, vb1, px, g0, g1,
-                         sy, pn, 0u, a);
+    hipLaunchKernelGGL(decode1_variant<2>(single, one), dim3(G), dim3(DK_THREADS), lds, stream, vb0, vb1, px, g0, g1,
+                       sy, pn, single ? misc(a.vq, a.vr) : 0u, a);
     return hipGetLastError();
   }
   a.vq = 1;
   a.vr = 0;
   a.uq = 0;
   a.ur = 0;
-  if (single)
-    hipLaunchKernelGGL((lb_decode1_kernel<0, true>), dim3(a.nvt), dim3(DK_THREADS), lds, stream, vb0, vb1, px, g0, g1,
-                       sy, pn, misc(1, 0), a);
-  else
-    hipLaunchKernelGGL((lb_decode1_kernel<0, false>), dim3(a.nvt), dim3(DK_THREADS), lds, stream, vb0, vb1, px, g0,
-                       g1, sy, pn, 0u, a);
+  hipLaunchKernelGGL(decode1_variant<0>(single, one), dim3(a.nvt), dim3(DK_THREADS), lds, stream, vb0, vb1, px, g0,
+                     g1, sy, pn, single ? misc(1, 0) : 0u, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int gb = a.nut < 1024 ? a.nut : 1024;
@@ -1052,11 +1087,8 @@ hipError_t lb_launch_decode1(const LbDecodeArgs& args, int G, void* sync, hipStr
   a.vr = 0;
   a.uq = a.nut / gb;
   a.ur = a.nut % gb;
-  if (single)
-    hipLaunchKernelGGL((lb_decode1_kernel<1, true>), dim3(gb), dim3(DK_THREADS), lds, stream, vb0, vb1, px, g0, g1,
-                       sy, pn, misc(0, 0), a);
-  else
-    hipLaunchKernelGGL((lb_decode1_kernel<1, false>), dim3(gb), dim3(DK_THREADS), lds, stream, vb0, vb1, px, g0, g1,
-                       sy, pn, 0u, a);
+  // (the U launch does no V work: one instantiation per layer count)
+  hipLaunchKernelGGL(decode1_variant<1>(single, false), dim3(gb), dim3(DK_THREADS), lds, stream, vb0, vb1, px, g0, g1,
+                     sy, pn, single ? misc(0, 0) : 0u, a);
   return hipGetLastError();
 }

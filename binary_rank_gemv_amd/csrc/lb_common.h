@@ -119,7 +119,8 @@ struct LbDecodeArgs {
   int vt_end[2 * LB_MAX_LAYERS];    // cumulative V-tile count after (layer i, branch b) = 2i+b
   int vq, vr;                       // V tiles of workgroup w: vq + (w < vr), contiguous
   int uq, ur;                       // U tiles likewise
-  int pad_[3];
+  int vtpu;                         // one-token kernels: V tiles per unit of V work (1 or 2)
+  int pad_[2];
   LbLayerArgs L[LB_MAX_LAYERS];
   // single launch of several layers: workgroup w takes V tiles
   // [vt_begin[w], vt_begin[w + 1]) and U tiles [ut_begin[w], ut_begin[w + 1]),

@@ -99,6 +99,10 @@ def test_tiny_config_full_oracle(lb, batch, two_launches):
     (20000, 512, (1600,), 2),      # one branch, 5 tiles per workgroup
     (40000, 128, (96, 96), 5),     # batch 5: 9 tiles copied per workgroup, the rest from memory
     (600, 300, (3000, 3000), 13),  # z of 13 tokens exceeds the LDS: launches of 9 and 4 tokens
+    # one token, more V tiles than workgroups (two tiles per unit): odd tile
+    # counts (the last unit's second tile is its first) and partial tiles
+    (700, 520, (2600, 2072), 1),   # 163 + 130 tiles
+    (300, 200, (4088, 1000), 1),   # 256 + 63 tiles, rank near its limit
     # phase A's staging of g*x: n % 8 != 0 (element-wise loads), and n > 8192
     # (a second batch of sign words, a chunk cut at the batch's end)
     (90, 130, (24, 40), 3),
