@@ -40,16 +40,30 @@
 // littlebit_phase_stamps_set: slot 16 w + i for workgroup w and point i
 // (0 start, 1 arguments and first u staged, 8 first V products start,
 // 2 first V products done, 3 first z round issued, 4 first z copied,
-// 5 first U group's products done, 6 end; 7 a multi-layer tile staged).
+// 5 first U group's products done, 6 end; 7 a multi-layer tile staged;
+// 9 last V unit's z stored, 10 last z copy done, 13 first unit's words
+// landed, 14 next unit's words issued, 15 first unit's partial sums met)
+// and two counts (11 u stagings, 12 z copies).
 #ifdef LB_PHASE_STAMPS
 __device__ uint64_t* g_phase_stamps;
-#define LB_STAMP_DECL uint64_t ts_[9] = {0, 0, 0, 0, 0, 0, 0, 0, 0};
+#define LB_STAMP_N 16
+#define LB_STAMP_DECL uint64_t ts_[LB_STAMP_N] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
 #define LB_STAMP(i) (ts_[i] = __builtin_amdgcn_s_memrealtime())
+#define LB_COUNT(i) (++ts_[i])
 #define LB_STAMP_WRITE()                                                              \
   do {                                                                               \
     uint64_t* sp_ = g_phase_stamps;                                                  \
     if (threadIdx.x == 0 && sp_)                                                     \
-      for (int i_ = 0; i_ < 9; ++i_) sp_[16 * blockIdx.x + i_] = ts_[i_];            \
+      for (int i_ = 0; i_ < LB_STAMP_N; ++i_) sp_[16 * blockIdx.x + i_] = ts_[i_];   \
+  } while (0)
+// Per-wave points, lane 0 of every wave, in the buffer's spare rows:
+// 16 (256 R + w) + wave for region R (0 first V products done, 1 first U
+// group's products done) of workgroup w < 256.
+#define LB_WSTAMP(R)                                                                 \
+  do {                                                                               \
+    uint64_t* sp_ = g_phase_stamps;                                                  \
+    if ((threadIdx.x & 63) == 0 && sp_ && blockIdx.x < 256)                          \
+      sp_[16 * (256 * (R + 1) + blockIdx.x) + (threadIdx.x >> 6)] = __builtin_amdgcn_s_memrealtime(); \
   } while (0)
 extern "C" int littlebit_phase_stamps_set(void* p) {
   return (int)hipMemcpyToSymbol(HIP_SYMBOL(g_phase_stamps), &p, sizeof(p));
@@ -57,6 +71,8 @@ extern "C" int littlebit_phase_stamps_set(void* p) {
 #else
 #define LB_STAMP_DECL
 #define LB_STAMP(i) ((void)0)
+#define LB_COUNT(i) ((void)0)
+#define LB_WSTAMP(R) ((void)0)
 #define LB_STAMP_WRITE() ((void)0)
 #endif
 
@@ -222,7 +238,19 @@ struct SL {
   __device__ const uint16_t* g(int b) const { return b ? g1 : g0; }
 };
 
-__device__ __forceinline__ SL scalar_layer(const LbLayerArgs& L) {
+// The record (in the LDS copy) is read in one batch of 16-byte reads and
+// waited for once; field by field, each read would be waited for before its
+// readfirstlane, a round trip per field.
+__device__ __forceinline__ SL scalar_layer(const LbLayerArgs& rec) {
+  static_assert(sizeof(LbLayerArgs) % 16 == 0 && (int)offsetof(LbDecodeArgs, L) % 16 == 0,
+                "layer records are whole 16-byte chunks");
+  constexpr int NQ = (int)(sizeof(LbLayerArgs) / 16);
+  u32x4 q[NQ];
+  const u32x4* src = reinterpret_cast<const u32x4*>(&rec);
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) q[i] = src[i];
+  LbLayerArgs L;
+  __builtin_memcpy(&L, q, sizeof(L));
   SL s;
   s.vb0 = rflp(L.br[0].vbits);
   s.vb1 = rflp(L.br[1].vbits);
@@ -414,11 +442,14 @@ __device__ __forceinline__ void v_load_words(const VTile& v, int pc, VWords& w) 
 // of the pair, even or odd operand r % 2) and each instruction's operand is
 // broadcast from its lane across the row (DPP row broadcast, one move per
 // dword): a sixteenth of the LDS traffic, for four moves per instruction.
+// Every lane of every row is written (all rows and banks enabled, the source
+// lane always valid), so the moves take no prior value of the destination
+// and need no instruction to set one.
 template <int N>
 __device__ __forceinline__ f16x8 bcast_operand(const u32x4& q) {
   u32x4 d;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) d[i] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)q[i], 0x150 + N, 0xF, 0xF, false);
+  for (int i = 0; i < 4; ++i) d[i] = (uint32_t)__builtin_amdgcn_mov_dpp((int)q[i], 0x150 + N, 0xF, 0xF, false);
   return __builtin_bit_cast(f16x8, d);
 }
 
@@ -471,8 +502,16 @@ __device__ __forceinline__ f32x4 v_tile_sums(const VTile& v, const uint16_t* up,
   static_assert(DK_VPW == 8, "two activation groups per batch");
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   const int plast = max(v.pb - 1, 0);
-  for (int pc = v.pa; pc < v.pb; pc += DK_VPW) {
-    if (pc != v.pa) v_load_words<TPU>(v, pc, w);
+  // The first batch stands outside the loop.  Inside it, a batch's words are
+  // loaded at the top and used at once, and the compiler's wait for them is
+  // counted from there; had the first batch been an iteration, its words
+  // (loaded much earlier) would get that same wait, i.e. for all but the last
+  // few loads issued since: the first U block's copy among them.  (Pairs
+  // beyond an empty share are skipped by v_pair.)
+  v_group<TPU, 0>(v, v.pa, load_act_group(up, v.pa, plast, v.nu), w, B, acc0, acc1);
+  v_group<TPU, 1>(v, v.pa, load_act_group(up, v.pa + 4, plast, v.nu), w, B, acc0, acc1);
+  for (int pc = v.pa + DK_VPW; pc < v.pb; pc += DK_VPW) {
+    v_load_words<TPU>(v, pc, w);
     v_group<TPU, 0>(v, pc, load_act_group(up, pc, plast, v.nu), w, B, acc0, acc1);
     v_group<TPU, 1>(v, pc, load_act_group(up, pc + 4, plast, v.nu), w, B, acc0, acc1);
   }
@@ -772,7 +811,10 @@ __global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* p
     ut1 = KA->ut_begin[wg + 1];
   }
   HPair hcur = {0u, 0u};  // row scales of the first U group
-  if (SINGLE && MODE != 1 && vt0 < vt1) stage_u(pre_x, k ? pre_g1 : pre_g0, n1, dyn);  // the first unit's u
+  if (SINGLE && MODE != 1 && vt0 < vt1) {
+    stage_u(pre_x, k ? pre_g1 : pre_g0, n1, dyn);  // the first unit's u
+    LB_COUNT(11);
+  }
   if (tid < DK_ARGS_BYTES / 16) reinterpret_cast<u32x4*>(sA_bytes)[tid] = acopy;
   lds_barrier_nf();  // the argument copy (and a single layer's first u) is complete
   LB_STAMP(1);
@@ -784,6 +826,10 @@ __global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* p
   }
   if (MODE == 1) vt1 = vt0;
   if (MODE == 0) ut1 = ut0;
+  // Layer records: a single layer's is read once here and kept (in scalar
+  // registers); several layers' are read where they are needed.
+  const SL L1 = SINGLE ? scalar_layer(A.L[0]) : SL{};
+  auto layer_rec = [&](int li) { return SINGLE ? L1 : scalar_layer(A.L[li]); };
   // the first V unit's latent scales (and, for several layers, its sign
   // words): loaded ahead, like those of each next unit.  Thread i < 32
   // holds l of row i % 16 of tile T0 (i < 16) or T1.
@@ -794,7 +840,7 @@ __global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* p
   if (vt0 < vt1) {
     int u = 0;
     if (!SINGLE) k = v_slot1<SINGLE>(A, vt0, u);
-    const SL L = scalar_layer(A.L[k >> 1]);
+    const SL L = layer_rec(k >> 1);
     if (!SINGLE) {
       v_pair_tiles(u, (L.r(k & 1) + 15) >> 4, TPU, T0, T1);
       v = v_tile_geom(L.vb(k & 1), L.n, T0, T1);
@@ -832,7 +878,7 @@ __global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* p
   SL uL = {};
   GroupInfo ug = {};
   if (have_u) {
-    uL = scalar_layer(A.L[layer_of_u(ut0)]);
+    uL = layer_rec(layer_of_u(ut0));
     ug = group_at(ut0, uL);
   } else {
     uL.ub0 = uL.ub1 = sync;
@@ -864,18 +910,19 @@ __global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* p
   // boundary makes the compiler wait for the loads issued ahead)
   int staged = (SINGLE && vt0 < vt1) ? k : -1;  // the single-layer launch staged its first tile's u above
   auto v_step = [&](int t) {
-    const SL L = scalar_layer(A.L[k >> 1]);
+    const SL L = layer_rec(k >> 1);
     const int b = k & 1;
     const int r = L.r(b);
     if (k != staged) {
       lds_barrier_nf();  // earlier readers of the staged u are done
       stage_u(L.x, L.g(b), L.n, dyn);
+      LB_COUNT(11);
       staged = k;
       lds_barrier_nf();  // the staged u is complete
       LB_STAMP(7);
       if (t == vt0) wait_vmem_all();  // (staging waited already: this tells the compiler so)
+      if (t == vt0) LB_STAMP(13);
     }
-    if (!SINGLE && t == vt0) issue_first_u();
     // the next unit's sign words and latent scales
     int kn = k, Tn0 = T0, Tn1 = T1;
     VTile vn = v;
@@ -884,19 +931,25 @@ __global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* p
     if (t + 1 < vt1) {
       int un = 0;
       kn = v_slot1<SINGLE>(A, t + 1, un);
-      const SL Ln = scalar_layer(A.L[kn >> 1]);
+      const SL Ln = layer_rec(kn >> 1);
       v_pair_tiles(un, (Ln.r(kn & 1) + 15) >> 4, TPU, Tn0, Tn1);
       vn = v_tile_geom(Ln.vb(kn & 1), Ln.n, Tn0, Tn1);
       v_load_words<TPU>(vn, vn.pa, wn);
       lnext = l_of(Ln, kn & 1, Tn0, Tn1);
     }
+    if (t == vt0) LB_STAMP(14);
+    // the first U block after the next unit's words: loads complete in issue
+    // order, so words issued after the 64 KB block would wait for all of it
+    if (!SINGLE && t == vt0) issue_first_u();
     if (t == vt0) LB_STAMP(8);
     const f32x4 acc = v_tile_sums<TPU>(v, dyn, B, w);
     if (t == vt0) LB_STAMP(2);
+    if (t == vt0) LB_WSTAMP(0);
     if ((lane & 15) < 2)  // column 0: tile T0, column 1: tile T1
 #pragma unroll
       for (int q = 0; q < 4; ++q) vred[wave][16 * (lane & 15) + 4 * (lane >> 4) + q] = acc[q];
     lds_barrier_nf();
+    if (t == vt0) LB_STAMP(15);
     if (tid < 32) {
       const int j = 16 * (tid & 16 ? T1 : T0) + (tid & 15);
       float s = 0.f;
@@ -909,6 +962,7 @@ __global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* p
     const uint32_t tg = get_tag();
     store_z_tile(L, b, T0, tg, zv);
     if (T1 != T0) store_z_tile(L, b, T1, tg, zv + 16);
+    LB_STAMP(9);
     if (t + 1 < vt1) {
       k = kn;
       T0 = Tn0;
@@ -941,11 +995,13 @@ __global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* p
     zc_finish(zc0, tag, MODE == 2, sync);
     zl_layer = ug.li;
     LB_STAMP(4);
+    LB_STAMP(10);
+    LB_COUNT(12);
     lds_ublock(ublk[wave], ug.p0, nu0, cur);
   }
   get_tag();
   for (int t = ut0; t < ut1;) {
-    const SL L = scalar_layer(A.L[layer_of_u(t)]);
+    const SL L = layer_rec(layer_of_u(t));
     const GroupInfo g = group_at(t, L);
     const int nu = nunits(L.r(g.b));
     if (g.li != zl_layer) {
@@ -956,6 +1012,8 @@ __global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* p
       else
         copy_z<16>(L, g.b, u0, u1, tag, MODE == 2, sync, dyn);
       zl_layer = g.li;
+      LB_STAMP(10);
+      LB_COUNT(12);
     }
     const uint16_t* zb = dyn + L.zoff(g.b);
     const HPair hg = hcur;  // this group's row scales (loaded with its first block)
@@ -970,7 +1028,7 @@ __global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* p
         load_ublock(L, g.b, g.tile, g.nt, g.p0 + (c + 1) * DK_UPW, g.p1, nxt);
         more = true;
       } else if (t + g.nt < ut1) {
-        const SL Ln = scalar_layer(A.L[layer_of_u(t + g.nt)]);
+        const SL Ln = layer_rec(layer_of_u(t + g.nt));
         const GroupInfo h = group_at(t + g.nt, Ln);
         load_ublock(Ln, h.b, h.tile, h.nt, h.p0, h.p1, nxt);
         hcur = load_group_h(Ln, h.tile, h.nt);  // the next group's
@@ -995,6 +1053,7 @@ __global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* p
 #pragma unroll
     for (int j = 0; j < DK_UTG / 2; ++j) acc[j] += acc1[j];
     if (t == ut0) LB_STAMP(5);
+    if (t == ut0) LB_WSTAMP(1);
     u_epilogue(L, g.tile, g.nt, acc, ured[grp & 1], late(hg.h0), late(hg.h1));
     ++grp;
     t += g.nt;

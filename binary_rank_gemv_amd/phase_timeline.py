@@ -17,8 +17,11 @@ import sys
 import numpy as np
 
 POINTS = [(0, "start"), (1, "arguments + first u staged"), (7, "multi-layer tile staged"),
-          (8, "first V products start"), (2, "first V products done"), (3, "first z round issued"),
-          (4, "first z copied"), (5, "first U group products done"), (6, "end")]
+          (13, "first unit's words landed"), (14, "next unit's words issued"),
+          (8, "first V products start"), (2, "first V products done"), (15, "first unit's sums met"), (3, "first z round issued"),
+          (9, "last V unit's z stored"), (4, "first z copied"), (10, "last z copy done"),
+          (5, "first U group products done"), (6, "end")]
+COUNTS = (11, 12)  # u stagings, z copies of a workgroup
 
 
 def main(configs):
@@ -41,16 +44,22 @@ def main(configs):
         for c in w.calls:
             c()
         torch.cuda.synchronize()
-        rows = []
+        rows, wrows = [], []
         for i in range(24):
             stamps.zero_()
             w.calls[(7 * i) % len(w.calls)]()
             torch.cuda.synchronize()
-            s = stamps.view(nwg, 16)[:, :9].cpu().numpy().astype(np.float64)
+            s = stamps.view(nwg, 16)[:256, :16].cpu().numpy().astype(np.float64)  # one row per workgroup
             used = s[:, 0] > 0
             s = s[used]
             t0 = s[:, 0].min()
-            rows.append(np.where(s > 0, (s - t0) * 0.01, np.nan))  # 100 MHz ticks -> us
+            t = np.where(s > 0, (s - t0) * 0.01, np.nan)  # 100 MHz ticks -> us
+            t[:, COUNTS] = s[:, COUNTS]
+            rows.append(t)
+            # per-wave points (spare rows of the buffer): spread over waves
+            wv = stamps.view(nwg, 16)[256:768, :8].cpu().numpy().astype(np.float64).reshape(2, 256, 8)
+            wv = np.where(wv > 0, (wv - t0) * 0.01, np.nan)
+            wrows.append(wv[:, used])
         a = np.stack(rows)
         print(f"== {cfg}: {a.shape[1]} workgroups; us from the first workgroup's start "
               f"(median over 24 calls of the per-call percentile over workgroups)")
@@ -62,6 +71,25 @@ def main(configs):
                 continue
             v = [np.nanmedian(np.nanpercentile(col, q, axis=1)) for q in (0, 10, 50, 90, 100)]
             print(f"  {name:30s} {n:4d} " + " ".join(f"{x:7.2f}" for x in v))
+        wa = np.stack(wrows)  # call, region, workgroup, wave
+        for R, name in ((0, "first V products done"), (1, "first U group products done")):
+            x = wa[:, R]
+            if np.all(np.isnan(x)):
+                continue
+            spread = np.nanmax(x, axis=2) - np.nanmin(x, axis=2)
+            print(f"  per wave, {name}: median over calls of the median workgroup's earliest / latest wave "
+                  f"{np.nanmedian(np.nanmedian(np.nanmin(x, axis=2), axis=1)):.2f} / "
+                  f"{np.nanmedian(np.nanmedian(np.nanmax(x, axis=2), axis=1)):.2f} us; "
+                  f"median spread {np.nanmedian(spread):.2f} us; by wave: "
+                  + " ".join(f"{np.nanmedian(x[:, :, k]):.2f}" for k in range(8)))
+        # workgroups grouped by their counts of u stagings and z copies:
+        # how many, and the median over calls of their median end
+        keys = sorted({(int(a[0, i, 11]), int(a[0, i, 12])) for i in range(a.shape[1])})
+        print("  by (u stagings, z copies): workgroups, median last z stored / last z copy done / end")
+        for key in keys:
+            sel = (a[0, :, 11] == key[0]) & (a[0, :, 12] == key[1])
+            med = [np.nanmedian(np.nanmedian(a[:, sel, j], axis=1)) for j in (9, 10, 6)]
+            print(f"    {str(key):10s} {int(sel.sum()):4d}   " + " ".join(f"{x:7.2f}" for x in med))
         del w
         torch.cuda.empty_cache()
 
