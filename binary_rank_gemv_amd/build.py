@@ -112,21 +112,26 @@ STAMPED_LIB = os.path.join(LIBDIR, "stamped", "liblittlebit.so")
 
 
 def build_phase_stamped(verbose: bool = False) -> str:
-    """The layer library with phase timestamps in the one-token decode
-    kernels (decode1.hip built with -DLB_PHASE_STAMPS; it also exports
-    littlebit_phase_stamps_set), linked with the regular objects of the other
-    sources (build_library must have run).  For phase_timeline.py only."""
+    """The layer library with phase timestamps in the decode kernels
+    (decode1.hip and decode.hip built with -DLB_PHASE_STAMPS; they also
+    export littlebit_phase_stamps_set and littlebit_phase_stamps_multi_set),
+    linked with the regular objects of the other sources (build_library must
+    have run).  For phase_timeline.py only."""
     objdir = os.path.join(LIBDIR, "stamped")
     os.makedirs(objdir, exist_ok=True)
-    obj = os.path.join(objdir, "decode1.hip.o")
-    _run([HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-c", "-DLB_PHASE_STAMPS",
-          "-I", os.path.join(ROOT, "include"), "-I", CSRC, *DEVICE_FLAGS, os.path.join(CSRC, "decode1.hip"),
-          "-o", obj], verbose)
-    others = [os.path.join(OBJDIR, f + ".o") for f in LAYER_SOURCES if f != "decode1.hip"]
+    stamped = ("decode1.hip", "decode.hip")
+    objs = []
+    for f in stamped:
+        obj = os.path.join(objdir, f + ".o")
+        _run([HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-c", "-DLB_PHASE_STAMPS",
+              "-I", os.path.join(ROOT, "include"), "-I", CSRC, *DEVICE_FLAGS, os.path.join(CSRC, f), "-o", obj],
+             verbose)
+        objs.append(obj)
+    others = [os.path.join(OBJDIR, f + ".o") for f in LAYER_SOURCES if f not in stamped]
     missing = [o for o in others if not os.path.exists(o)]
     if missing:
         raise RuntimeError(f"build the library first; missing {missing}")
-    _link([obj, *others], STAMPED_LIB, [], verbose)
+    _link([*objs, *others], STAMPED_LIB, [], verbose)
     return STAMPED_LIB
 
 

@@ -29,6 +29,37 @@
 
 #include <vector>
 
+// Phase timestamps, in an instrumented build only (-DLB_PHASE_STAMPS; the
+// regular library has none of this): thread 0 of each workgroup stores the
+// 100 MHz real-time counter at fixed points of a call to the device buffer
+// given to littlebit_phase_stamps_multi_set, slot 16 w + i for workgroup w
+// and point i (0 start, 10 + c / 13 + c chunk c < 3 of a V tile begun /
+// staged, 1 phase-B loads issued, 3 V products done, 2 first V tile done,
+// 9 last V tile done, 4 z copy done (the last layer entered), 5 first U
+// group done, 8 / 7 a U group begun / its products issued, 6 end; each
+// stamp holds its last time); lane 0 of every wave
+// stores its z copy's end at slot 16 (256 + w) + wave.
+#ifdef LB_PHASE_STAMPS
+__device__ uint64_t* g_phase_stamps_multi;
+#define LB_MSTAMP(i)                                                                 \
+  do {                                                                               \
+    uint64_t* sp_ = g_phase_stamps_multi;                                            \
+    if (threadIdx.x == 0 && sp_) sp_[16 * blockIdx.x + (i)] = __builtin_amdgcn_s_memrealtime(); \
+  } while (0)
+#define LB_MWSTAMP()                                                                 \
+  do {                                                                               \
+    uint64_t* sp_ = g_phase_stamps_multi;                                            \
+    if ((threadIdx.x & 63) == 0 && sp_ && blockIdx.x < 256)                          \
+      sp_[16 * (256 + blockIdx.x) + (threadIdx.x >> 6)] = __builtin_amdgcn_s_memrealtime(); \
+  } while (0)
+extern "C" int littlebit_phase_stamps_multi_set(void* p) {
+  return (int)hipMemcpyToSymbol(HIP_SYMBOL(g_phase_stamps_multi), &p, sizeof(p));
+}
+#else
+#define LB_MSTAMP(i) ((void)0)
+#define LB_MWSTAMP() ((void)0)
+#endif
+
 #define LB_WAVES 8                    // waves per workgroup (2 per SIMD)
 #define LB_THREADS (64 * LB_WAVES)
 #define LB_MAXPV 8                    // V-pass pairs per wave held in registers
@@ -311,10 +342,12 @@ __device__ __forceinline__ void v_tile(const LayerView& L, int batch, int b, int
   // token 0.  Thread i builds groups i, i + 512, ... of every token (one load
   // of g serves all tokens; all of a group's loads are issued before use).
   constexpr int WB = LB_WAVES * LB_MAXPV;
+  int nchunk = 0;  // (phase stamps only)
   auto chunk = [&](int wb, int cb, const VLoads& R, bool first, auto with_hook) {
     const int cn = min(min(np, wb + WB) - cb, chunk_pairs);
     const int k0 = 128 * cb, kc = 128 * cn, ng = kc >> 3;
     const int rowh = kc + 8;
+    if (nchunk < 3) LB_MSTAMP(10 + nchunk);
     if (!reuse_u) {
       __syncthreads();  // previous users of u_lds are done
       int k8 = tid;
@@ -344,12 +377,15 @@ __device__ __forceinline__ void v_tile(const LayerView& L, int batch, int b, int
       }
       __syncthreads();
     }
+    if (nchunk < 3) LB_MSTAMP(13 + nchunk);
+    ++nchunk;
 
     // the phase-B loads (hook) go out once this chunk's sign words are in, so
     // they do not compete with them, and arrive while the matrix steps run
     if constexpr (decltype(with_hook)::value) {
       __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
       hook();
+      LB_MSTAMP(1);
     }
     // l[j] (from an always-valid index; converted at use in the epilogue) is
     // loaded after the hook's wait, which would otherwise wait for it too
@@ -392,17 +428,29 @@ __device__ __forceinline__ void v_tile(const LayerView& L, int batch, int b, int
     cb += chunk_pairs;
     if (cb >= min(np, wb + WB)) cb = wb = wb + WB;
   };
+  // With several chunks the hook runs after the last one instead: its loads
+  // (sign words of phase B, from memory) would otherwise sit in front of the
+  // next chunks' activation loads, which complete after them.
+  const bool one_chunk = np <= chunk_pairs;
   if constexpr (EARLY || HOOK) {
     if constexpr (EARLY) R = early;
     else v_issue(G, 0, chunk_pairs, R);
-    chunk(0, 0, R, true, BoolTag<HOOK>());
+    if (one_chunk) chunk(0, 0, R, true, BoolTag<HOOK>());
+    else chunk(0, 0, R, true, BoolTag<false>());
     advance();
   }
   for (; cb < np; advance()) {
     if (cb == wb) v_issue(G, wb, chunk_pairs, R);
     chunk(wb, cb, R, false, BoolTag<false>());
   }
+  if constexpr (HOOK) {
+    if (!one_chunk) {
+      hook();
+      LB_MSTAMP(1);
+    }
+  }
   acc += acc1;
+  LB_MSTAMP(3);
 
 #pragma unroll
   for (int i = 0; i < 4; ++i) red[wave][(4 * grp + i) * 16 + tok] = acc[i];
@@ -582,6 +630,8 @@ __device__ __forceinline__ void u_enter_layer(const LayerView& L, int li, int ba
     u_copy_z<LB_POLL_LOADS_SMALL>(L, batch, tag, check, sync, S, zl, s0, s1);
   else
     u_copy_z<NLB>(L, batch, tag, check, sync, S, zl, s0, s1);
+  LB_MSTAMP(4);
+  LB_MWSTAMP();
 }
 
 // ---------------------------------------------- phase-B sign bytes in LDS
@@ -739,6 +789,7 @@ __device__ __forceinline__ YOut u_group(const LayerView& L, int li, int batch, i
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int tok = lane & 15, grp = lane >> 4;
   if (li != S.li) u_enter_layer<(NPW == LB_MAXPW ? LB_POLL_LOADS : LB_POLL_LOADS_MULTI)>(L, li, batch, tag, check, sync, S, zl);
+  LB_MSTAMP(8);
   // operand rows: absent tokens read the last token's row (never stored)
   const uint16_t* zb = zl + min(tok, batch - 1) * (L.zs + 8) + (S.b ? L.zoff1 : L.zoff0) + 8 * grp;
   const int s1 = 2 * S.nu;  // steps of the branch that hold data
@@ -792,6 +843,7 @@ __device__ __forceinline__ YOut u_group(const LayerView& L, int li, int batch, i
       }
     }
   }
+  LB_MSTAMP(7);
   return u_finish(L, batch, tile0, nt, acc, H, red);
 }
 
@@ -904,6 +956,7 @@ __global__ __launch_bounds__(LB_THREADS) void lb_decode_kernel(
   static_assert(!UPRE || MODE == 2, "the sign-byte copy belongs to the single launch");
 
   const int wg = blockIdx.x;
+  LB_MSTAMP(0);
   // single launch of one layer: the first V tile's first loads need only the
   // preloaded arguments, so they are issued before anything else
   constexpr bool EARLY = SINGLE && MODE == 2;
@@ -1015,11 +1068,13 @@ __global__ __launch_bounds__(LB_THREADS) void lb_decode_kernel(
     };
     v_tile<MAXB, MODE == 2, EARLY>(V0, batch, k & 1, tile, chunk_pairs, tag, sc, u_lds, red[0], zstage, first_hook, early);
     __syncthreads();
+    LB_MSTAMP(2);
     for (int t = vt0 + 1; t < vt1; ++t) {
       const int kt = v_slot<SINGLE>(M, pre_vsplit, t, tile);
       v_tile<MAXB, false, false>(V0, batch, kt & 1, tile, chunk_pairs, tag, sc, u_lds, red[0], zstage, prefetch, early);
       __syncthreads();
     }
+    LB_MSTAMP(9);
   } else if (vt0 < vt1) {
     // several layers: a tile's first loads are issued during the previous
     // tile, once that tile's own sign words have landed, and the previous
@@ -1049,6 +1104,7 @@ __global__ __launch_bounds__(LB_THREADS) void lb_decode_kernel(
       v_tile<MAXB, true, true, true>(L, batch, k & 1, tile, chunk_pairs, tag, sc, u_lds, red[0], zst[(t - vt0) & 1], hook,
                                cur, reuse_u);
       __syncthreads();
+      if (t == vt0) LB_MSTAMP(2);
       prev_k = k;
       prev_tile = tile;
       k = nk;
@@ -1056,6 +1112,7 @@ __global__ __launch_bounds__(LB_THREADS) void lb_decode_kernel(
       cur = nxt;
     }
     v_store_z(layer_view(A.L[prev_k >> 1]), batch, prev_k & 1, prev_tile, late(tag), zst[(vt1 - 1 - vt0) & 1]);
+    LB_MSTAMP(9);
   } else if (MODE == 2) {
     for (int i = 0; i < 3; ++i) __builtin_amdgcn_s_sleep(24);
     load_ctr();
@@ -1096,35 +1153,60 @@ __global__ __launch_bounds__(LB_THREADS) void lb_decode_kernel(
         const uint8_t* w1 = upre_lds + (slot ? plan.off[3] : plan.off[1]) + (t - first) * tb1;
         u_span_lds<(MAXB > 1 ? LB_POLL_LOADS_MULTI : LB_POLL_LOADS)>(L, li, batch, tile, T, span_max, w0, w1, tb0, tb1, hl_lds + 32 * (t - ut0), tag, check, sync, sc, S,
                    u_lds, &red[0][0][0]);
+        if (t == ut0) LB_MSTAMP(5);
         t += T;
       }
-    } else if (MODE == 2 && t < ut1) {
-      int tile;
-      const int li = u_layer<SINGLE>(M, t, tile);
-      const int lend = SINGLE ? ut1 : min(ut1, layer_u_end(M, li));
-      const int nt = min(LB_MAXT, lend - t);
-      yo = u_group(SINGLE ? V0 : layer_view(A.L[li]), li, batch, tile, nt, pre, hpre, tag, check, sync, sc, S, u_lds,
-                   red);
-      t += nt;
     }
-    while (t < ut1) {
-      int tile;
-      const int li = u_layer<SINGLE>(M, t, tile);
+    // Groups of up to LB_MAXT tiles of one layer from registers.  A group's
+    // sign words and row scales are loaded while the group before it runs
+    // (the single launch's first group: during phase A), so no group waits
+    // a memory round trip for them.  The loads are unconditional (the group
+    // after the last repeats the last group's tiles, never used), which
+    // keeps the compiler's wait counts exact.
+    auto group_of = [&](int tg, int& tile, int& nt) {
+      const int li = u_layer<SINGLE>(M, tg, tile);
       const int lend = SINGLE ? ut1 : min(ut1, layer_u_end(M, li));
-      const int nt = min(LB_MAXT, lend - t);
+      nt = min(LB_MAXT, lend - tg);
+      return li;
+    };
+    auto load_group = [&](int tg, UTilePre<NPW> (&p)[LB_MAXT], HPre& h) {
+      int tile, nt;
+      const int li = group_of(tg, tile, nt);
       const LayerView L = SINGLE ? V0 : layer_view(A.L[li]);
-      UTilePre<NPW> p[LB_MAXT];
 #pragma unroll
       for (int k = 0; k < LB_MAXT; ++k) u_prefetch(L, tile + min(k, nt - 1), p[k]);
-      HPre h;
 #pragma unroll
       for (int j = 0; j < 2; ++j) load_h(L, tile + min((wave_id() >> 2) + 2 * j, nt - 1), h, j);
+    };
+    UTilePre<NPW> cur[LB_MAXT];
+    HPre hc;
+    if (MODE == 2 && !UPRE) {
+#pragma unroll
+      for (int k = 0; k < LB_MAXT; ++k) cur[k] = pre[k];
+      hc = hpre;
+    } else if (t < ut1) {
+      load_group(t, cur, hc);
+    }
+    bool first_group = true;
+    while (t < ut1) {
+      int tile, nt;
+      const int li = group_of(t, tile, nt);
+      UTilePre<NPW> nxt[LB_MAXT];
+      HPre hn;
+      load_group(min(t + nt, ut1 - 1), nxt, hn);
       store_y(yo);
-      yo = u_group(L, li, batch, tile, nt, p, h, tag, check, sync, sc, S, u_lds, red);
+      yo = u_group(SINGLE ? V0 : layer_view(A.L[li]), li, batch, tile, nt, cur, hc, tag, check, sync, sc, S, u_lds,
+                   red);
+      if (first_group) LB_MSTAMP(5);
+      first_group = false;
       t += nt;
+#pragma unroll
+      for (int k = 0; k < LB_MAXT; ++k) cur[k] = nxt[k];
+      hc = hn;
     }
     store_y(yo);
   }
+  LB_MSTAMP(6);
   // this workgroup's call is done: the next call's tag is one higher
   if (MODE == 2 && threadIdx.x == 0) add64c_noret(sync + LB_SYNC_CTR + 8 * wg, 1ull);
 }

@@ -435,6 +435,24 @@ __device__ __forceinline__ void v_load_words(const VTile& v, int pc, VWords& w) 
     }
 }
 
+// A unit's first two batches of sign words.  Both are loaded before the
+// workgroup issues any later load (the first U block's copy above all):
+// loads complete in issue order, so a second batch loaded at its use would
+// wait for everything issued before it.
+struct VWords2 {
+  VWords b0, b1;
+};
+
+// The second batch's first group of four pairs is loaded even when the share
+// has no second batch (v_load_words clamps it to the share's last pair, and
+// its words are then never used): a load under a branch would make the
+// compiler keep the words in memory.
+template <int TPU>
+__device__ __forceinline__ void v_load_first(const VTile& v, VWords2& w) {
+  v_load_words<TPU>(v, v.pa, w.b0);
+  v_load_words<TPU>(v, v.pa + DK_VPW, w.b1);
+}
+
 // V activations through a row broadcast.  Every lane of a 16-lane row (one
 // lane group) needs the same 8 activations for an instruction; rather than
 // each lane reading them (16 bytes per lane per instruction), lane r of each
@@ -495,25 +513,31 @@ __device__ __forceinline__ void v_group(const VTile& v, int pc, const u32x4& q, 
 }
 
 // Returns this lane's partial sums (rows 4 (lane / 16) + q of column
-// lane % 16: tile T0 in column 0, T1 in column 1); `w` holds the first
-// batch's words on entry.
+// lane % 16: tile T0 in column 0, T1 in column 1); `w` holds the first two
+// batches' words on entry.
 template <int TPU>
-__device__ __forceinline__ f32x4 v_tile_sums(const VTile& v, const uint16_t* up, const f16x16& B, VWords& w) {
+__device__ __forceinline__ f32x4 v_tile_sums(const VTile& v, const uint16_t* up, const f16x16& B, const VWords2& w) {
   static_assert(DK_VPW == 8, "two activation groups per batch");
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   const int plast = max(v.pb - 1, 0);
-  // The first batch stands outside the loop.  Inside it, a batch's words are
-  // loaded at the top and used at once, and the compiler's wait for them is
-  // counted from there; had the first batch been an iteration, its words
-  // (loaded much earlier) would get that same wait, i.e. for all but the last
-  // few loads issued since: the first U block's copy among them.  (Pairs
-  // beyond an empty share are skipped by v_pair.)
-  v_group<TPU, 0>(v, v.pa, load_act_group(up, v.pa, plast, v.nu), w, B, acc0, acc1);
-  v_group<TPU, 1>(v, v.pa, load_act_group(up, v.pa + 4, plast, v.nu), w, B, acc0, acc1);
-  for (int pc = v.pa + DK_VPW; pc < v.pb; pc += DK_VPW) {
-    v_load_words<TPU>(v, pc, w);
-    v_group<TPU, 0>(v, pc, load_act_group(up, pc, plast, v.nu), w, B, acc0, acc1);
-    v_group<TPU, 1>(v, pc, load_act_group(up, pc + 4, plast, v.nu), w, B, acc0, acc1);
+  // The first two batches stand outside the loop.  Inside it, a batch's
+  // words are loaded at the top and used at once, and the compiler's wait for
+  // them is counted from there; had the first batches been iterations, their
+  // words (loaded much earlier) would get that same wait, i.e. for all but
+  // the last few loads issued since: the first U block's copy among them.
+  // (Pairs beyond the share are skipped by v_pair.)
+  v_group<TPU, 0>(v, v.pa, load_act_group(up, v.pa, plast, v.nu), w.b0, B, acc0, acc1);
+  v_group<TPU, 1>(v, v.pa, load_act_group(up, v.pa + 4, plast, v.nu), w.b0, B, acc0, acc1);
+  if (v.pa + DK_VPW < v.pb) {
+    const int pc = v.pa + DK_VPW;
+    v_group<TPU, 0>(v, pc, load_act_group(up, pc, plast, v.nu), w.b1, B, acc0, acc1);
+    v_group<TPU, 1>(v, pc, load_act_group(up, pc + 4, plast, v.nu), w.b1, B, acc0, acc1);
+  }
+  for (int pc = v.pa + 2 * DK_VPW; pc < v.pb; pc += DK_VPW) {
+    VWords wl;
+    v_load_words<TPU>(v, pc, wl);
+    v_group<TPU, 0>(v, pc, load_act_group(up, pc, plast, v.nu), wl, B, acc0, acc1);
+    v_group<TPU, 1>(v, pc, load_act_group(up, pc + 4, plast, v.nu), wl, B, acc0, acc1);
   }
   return acc0 + acc1;
 }
@@ -786,7 +810,7 @@ __global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* p
   int vt0 = 0, vt1 = 0;
   int k = 0, T0 = 0, T1 = 0;
   VTile v;
-  VWords w;
+  VWords2 w;
   const int n1 = pre_n & 0xFFFF;  // the single layer's n, and its branches' V tile counts
   const int ntv0 = (int)((uint32_t)pre_n >> 16), ntv1 = (int)(pre_misc >> 17);
   const int vsplit = (ntv0 + TPU - 1) / TPU;  // V units of branch 0
@@ -796,7 +820,7 @@ __global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* p
       k = vt0 >= vsplit ? 1 : 0;
       v_pair_tiles(vt0 - (k ? vsplit : 0), k ? ntv1 : ntv0, TPU, T0, T1);
       v = v_tile_geom(k ? pre_vb1 : pre_vb0, n1, T0, T1);
-      v_load_words<TPU>(v, v.pa, w);
+      v_load_first<TPU>(v, w);
     }
   }
   u32x4 acopy = {0u, 0u, 0u, 0u};
@@ -844,7 +868,7 @@ __global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* p
     if (!SINGLE) {
       v_pair_tiles(u, (L.r(k & 1) + 15) >> 4, TPU, T0, T1);
       v = v_tile_geom(L.vb(k & 1), L.n, T0, T1);
-      v_load_words<TPU>(v, v.pa, w);
+      v_load_first<TPU>(v, w);
     }
     lcur = l_of(L, k & 1, T0, T1);
   }
@@ -926,7 +950,7 @@ __global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* p
     // the next unit's sign words and latent scales
     int kn = k, Tn0 = T0, Tn1 = T1;
     VTile vn = v;
-    VWords wn;
+    VWords2 wn;
     uint32_t lnext = 0;
     if (t + 1 < vt1) {
       int un = 0;
@@ -934,7 +958,7 @@ __global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* p
       const SL Ln = layer_rec(kn >> 1);
       v_pair_tiles(un, (Ln.r(kn & 1) + 15) >> 4, TPU, Tn0, Tn1);
       vn = v_tile_geom(Ln.vb(kn & 1), Ln.n, Tn0, Tn1);
-      v_load_words<TPU>(vn, vn.pa, wn);
+      v_load_first<TPU>(vn, wn);
       lnext = l_of(Ln, kn & 1, Tn0, Tn1);
     }
     if (t == vt0) LB_STAMP(14);

@@ -1,14 +1,14 @@
-"""Phase timeline of the one-token decode kernel, from the instrumented
-library (``python -m binary_rank_gemv_amd.build --phase-stamps``).
+"""Phase timeline of the decode kernels, from the instrumented library
+(``python -m binary_rank_gemv_amd.build --phase-stamps``).
 
-    python -m binary_rank_gemv_amd.phase_timeline up70b_b1 up7b_b1 block13b_0.55_b1
+    python -m binary_rank_gemv_amd.phase_timeline up70b_b1 up7b_b1 block13b_0.55_b1 up70b_b16
 
-For each configuration (bench.py's decode configurations at batch 1): one
-call per layer copy to warm nothing but the code path, then 24 single calls,
-each on a different copy; per call the percentiles over workgroups of each
-phase point, in microseconds from the first workgroup's start, and the
-median of those over the calls.  The points are the ones decode1.hip
-records under LB_PHASE_STAMPS.
+For each configuration (bench.py's decode configurations): one call per
+layer copy to warm nothing but the code path, then 24 single calls, each on
+a different copy; per call the percentiles over workgroups of each phase
+point, in microseconds from the first workgroup's start, and the median of
+those over the calls.  The points are the ones decode1.hip (one token) and
+decode.hip (several tokens) record under LB_PHASE_STAMPS.
 """
 
 import os
@@ -22,6 +22,11 @@ POINTS = [(0, "start"), (1, "arguments + first u staged"), (7, "multi-layer tile
           (9, "last V unit's z stored"), (4, "first z copied"), (10, "last z copy done"),
           (5, "first U group products done"), (6, "end")]
 COUNTS = (11, 12)  # u stagings, z copies of a workgroup
+MPOINTS = [(0, "start"), (10, "V chunk 0 begun"), (13, "V chunk 0 staged"), (1, "phase-B loads issued"),
+           (11, "V chunk 1 begun"), (14, "V chunk 1 staged"), (12, "V chunk 2 begun"), (15, "V chunk 2 staged"),
+           (3, "V products done"), (2, "first V tile done"), (9, "last V tile done"), (4, "z copy done"),
+           (5, "first U group done"), (8, "last U group begun"), (7, "last U group products issued"),
+           (6, "end")]
 
 
 def main(configs):
@@ -39,8 +44,12 @@ def main(configs):
     stamps = torch.zeros(nwg * 16, dtype=torch.int64, device="cuda")
     if lib.littlebit_phase_stamps_set(ctypes.c_void_p(stamps.data_ptr())) != 0:
         raise RuntimeError("littlebit_phase_stamps_set failed")
+    if lib.littlebit_phase_stamps_multi_set(ctypes.c_void_p(stamps.data_ptr())) != 0:
+        raise RuntimeError("littlebit_phase_stamps_multi_set failed")
     for cfg in configs:
         w = bench.DecodeWorkload(lb, torch, synth, cfg, 1.0)
+        multi = w.batch > 1
+        points = MPOINTS if multi else POINTS
         for c in w.calls:
             c()
         torch.cuda.synchronize()
@@ -64,7 +73,7 @@ def main(configs):
         print(f"== {cfg}: {a.shape[1]} workgroups; us from the first workgroup's start "
               f"(median over 24 calls of the per-call percentile over workgroups)")
         print(f"  {'point':30s} {'n':>4s} {'min':>7s} {'p10':>7s} {'p50':>7s} {'p90':>7s} {'max':>7s}")
-        for j, name in POINTS:
+        for j, name in points:
             col = a[:, :, j]
             n = int(np.sum(~np.isnan(col[0])))
             if n == 0:
@@ -72,7 +81,9 @@ def main(configs):
             v = [np.nanmedian(np.nanpercentile(col, q, axis=1)) for q in (0, 10, 50, 90, 100)]
             print(f"  {name:30s} {n:4d} " + " ".join(f"{x:7.2f}" for x in v))
         wa = np.stack(wrows)  # call, region, workgroup, wave
-        for R, name in ((0, "first V products done"), (1, "first U group products done")):
+        wnames = (((0, "z copy done"),) if multi else
+                  ((0, "first V products done"), (1, "first U group products done")))
+        for R, name in wnames:
             x = wa[:, R]
             if np.all(np.isnan(x)):
                 continue
@@ -84,8 +95,9 @@ def main(configs):
                   + " ".join(f"{np.nanmedian(x[:, :, k]):.2f}" for k in range(8)))
         # workgroups grouped by their counts of u stagings and z copies:
         # how many, and the median over calls of their median end
-        keys = sorted({(int(a[0, i, 11]), int(a[0, i, 12])) for i in range(a.shape[1])})
-        print("  by (u stagings, z copies): workgroups, median last z stored / last z copy done / end")
+        keys = [] if multi else sorted({(int(a[0, i, 11]), int(a[0, i, 12])) for i in range(a.shape[1])})
+        if keys:
+            print("  by (u stagings, z copies): workgroups, median last z stored / last z copy done / end")
         for key in keys:
             sel = (a[0, :, 11] == key[0]) & (a[0, :, 12] == key[1])
             med = [np.nanmedian(np.nanmedian(a[:, sel, j], axis=1)) for j in (9, 10, 6)]
