@@ -27,6 +27,7 @@
 #include "lb_common.h"
 #include "lb_sync.h"
 
+#include <type_traits>
 #include <vector>
 
 // Phase timestamps, in an instrumented build only (-DLB_PHASE_STAMPS; the
@@ -84,7 +85,6 @@ struct LbDecodeKernargs {
   int pre_n, pre_ldx, pre_vsplit;
   uint32_t pre_misc;
   LbDecodeArgs A;
-  int chunk_pairs;
   uint8_t* sync;
 };
 
@@ -200,18 +200,16 @@ __device__ inline void u_role(const LayerView& L, int wave, int& b, int& p0, int
 }
 
 // ------------------------------------------------------------------ phase A
-// One 16-row tile of sign(V)^T of branch b of layer L: t, then
-// z = fp16(l*t), stored as tagged words.
-// The sign words are loaded in batches of LB_WAVES * LB_MAXPV pairs (128
-// inputs each; one batch covers n <= 8192): wave w holds pairs
-// w, w + 8, w + 16, ... of the batch in registers.  The reduction runs over
-// LDS chunks of `chunk_pairs` pairs (a multiple of 8 unless one chunk covers
-// the tile), so each wave has the same number of pairs in every chunk and a
-// batch's words are waited for once, whatever the number of chunks.
-// With HOOK, `hook` runs after the first chunk's matrix steps are issued, i.e.
-// once this tile's sign words have arrived, so its loads do not compete with
-// them for memory.  The first chunk is its
-// own copy of the code, so every wait count in it is exact.
+// One 16-row tile of sign(V)^T of branch b of layer L: t = sum_k s_k g_k x_k
+// per token, then z = fp16(l*t), stored as tagged words.  The matrix core
+// forms each product g_k x_k exactly: its A operand is +-g_k (g's fp16 sign
+// bit flipped by the weight's sign bit, as in the prefill GEMMs) and its B
+// operand the token's x, so no scaled copy of x is made.  Wave w sums pairs
+// w, w + 8, w + 16, ... (128 inputs each, four 32-input matrix steps), in
+// order; the sign words of a batch of LB_WAVES * LB_MAXPV pairs are loaded
+// together.  Every lane loads its own token's x (and a share of g) of a pair
+// straight into the operand registers, two pairs ahead of the products: x
+// is read once per workgroup and nothing is staged in LDS.
 template <bool B>
 struct BoolTag {
   static constexpr bool value = B;
@@ -225,7 +223,6 @@ struct VGeom {
   const uint8_t* tile_ptr;  // the tile's packed sign words
   long ldx;
   int n, nu, np;
-  bool fast;                // 16-byte loads of x and g
 };
 
 // Reads only the fields a caller may know before the rest of the arguments:
@@ -237,45 +234,88 @@ __device__ __forceinline__ VGeom v_geom(const LayerView& L, int b, int tile) {
   G.nu = lb16_units(G.n);
   G.np = (G.nu + 1) >> 1;
   G.tile_ptr = (b ? L.vb1 : L.vb0) + (long)tile * lb16_tile_bytes(G.n);
-  // 16-byte loads of x and g when aligned and n % 8 == 0 (then a group of 8
-  // inputs is either wholly below n or wholly at/after it)
-  G.fast = ((((uintptr_t)L.x) & 15) == 0) && ((L.ldx & 7) == 0) && ((G.n & 7) == 0);
   G.x = L.x;
   G.ldx = L.ldx;
   return G;
 }
 
-// Inputs k..k+7 of a row of x or of g: with 16-byte loads (fast) from an
-// always-valid address, zeroed by the caller when k >= n; else one by one,
-// zero at and beyond n.
+// Inputs k..k+7 of a row of x or of g: with 16-byte loads (FAST: x 16-byte
+// aligned, ldx and n multiples of 8, so a group of 8 inputs lies wholly below
+// n or wholly at/after it) from an always-valid address, zeroed by the
+// caller when k >= n; else one by one, zero at and beyond n.  FAST is a
+// template argument of the kernel, chosen by the host: as a run-time flag
+// both forms sat around every load, and the compiler's waits at their joins
+// took no account of the loads issued ahead.
+template <bool FAST>
 __device__ __forceinline__ uint4 v_load8(const VGeom& G, const uint16_t* row, int k) {
-  if (G.fast) return *reinterpret_cast<const uint4*>(row + min(k, G.n - 8));
+  if (FAST) return *reinterpret_cast<const uint4*>(row + min(k, G.n - 8));
   uint16_t e8[8];
   for (int e = 0; e < 8; ++e) e8[e] = (k + e < G.n) ? row[k + e] : (uint16_t)0;
   return *reinterpret_cast<uint4*>(e8);
 }
 
-// The loads that open the batch of V pairs starting at pair wb of a tile:
-// this thread's first group of inputs of the batch's first chunk (token 0's
-// x and g), then
-// the wave's sign words, pair wb + wave + 8 i in slot i (the activations come
-// first, so waiting for them leaves the words in flight).
-struct VLoads {
-  uint4 xv0, gv0;
-  uint32_t words[LB_MAXPV];
+// One pair's operands of this lane: its token's x (B operands of the four
+// steps, inputs 128 p + 32 s + 8 grp .. + 7 of step s) and one 32-bit pair
+// of g.  Lane r of row grp holds g of inputs 128 p + 32 (r / 4) + 8 grp +
+// 2 (r % 4) and + 1, i.e. dword r % 4 of step r / 4 of its row's operand, so
+// each g value is loaded once per wave and reaches the lanes of its row by
+// a row broadcast (v_pair_g); loading every lane's operand would move 16
+// times the bytes of g through the L1 cache, as much as x itself.
+struct VPairAct {
+  uint4 x[4];
+  uint32_t g;
 };
 
-__device__ __forceinline__ void v_issue(const VGeom& G, int wb, int chunk_pairs, VLoads& R) {
+// Loads pair p's operands (token row `trow`).  Unconditional (a pair past
+// the share is loaded from the clamped pair, never used), so wait counts stay
+// exact; g at and beyond n reads as zero.
+template <bool FAST>
+__device__ __forceinline__ void v_load_pair(const VGeom& G, int p, int trow, VPairAct& a) {
+  const int lane = threadIdx.x & 63, grp = lane >> 4, r = lane & 15;
+  const uint16_t* xr = G.x + (long)trow * G.ldx;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) a.x[s] = v_load8<FAST>(G, xr, 128 * p + 32 * s + 8 * grp);
+  const int kg = 128 * p + 32 * (r >> 2) + 8 * grp + 2 * (r & 3);
+  if (FAST) {
+    // n % 8 == 0: both inputs of the pair lie below n or neither does
+    const uint32_t v = *reinterpret_cast<const uint32_t*>(G.g + min(kg, G.n - 2));
+    a.g = kg < G.n ? v : 0u;
+  } else {
+    const uint32_t lo = kg < G.n ? G.g[kg] : 0u, hi = kg + 1 < G.n ? G.g[kg + 1] : 0u;
+    a.g = lo | (hi << 16);
+  }
+}
+
+// Dword dd (inputs 2 dd, 2 dd + 1 of the lane's 8) of step S's g operand:
+// from lane 4 S + dd of the row (every lane of the row is written, so the
+// move needs no prior value).
+template <int S>
+__device__ __forceinline__ u32x4 v_pair_g(uint32_t gw) {
+  u32x4 q;
+  q[0] = (uint32_t)__builtin_amdgcn_mov_dpp((int)gw, 0x150 + 4 * S + 0, 0xF, 0xF, false);
+  q[1] = (uint32_t)__builtin_amdgcn_mov_dpp((int)gw, 0x150 + 4 * S + 1, 0xF, 0xF, false);
+  q[2] = (uint32_t)__builtin_amdgcn_mov_dpp((int)gw, 0x150 + 4 * S + 2, 0xF, 0xF, false);
+  q[3] = (uint32_t)__builtin_amdgcn_mov_dpp((int)gw, 0x150 + 4 * S + 3, 0xF, 0xF, false);
+  return q;
+}
+
+// The loads that open a batch of V pairs starting at pair wb of a tile: the
+// wave's sign words (pair wb + wave + 8 i in slot i), then its first pair's
+// operands.
+struct VLoads {
+  uint32_t words[LB_MAXPV];
+  VPairAct act;
+};
+
+template <bool FAST>
+__device__ __forceinline__ void v_issue(const VGeom& G, int wb, int batch, VLoads& R) {
   const int lane = threadIdx.x & 63, wave = wave_id();
-  const int cn = min(G.np - wb, chunk_pairs);
-  const int k = 128 * wb + 8 * min((int)threadIdx.x, 16 * cn - 1);
-  R.xv0 = v_load8(G, G.x, k);  // token 0
-  R.gv0 = v_load8(G, G.g, k);
   // unconditional loads (clamped to the tile's last pair) keep the wait
   // counts exact; slots beyond the tile are never used
 #pragma unroll
   for (int i = 0; i < LB_MAXPV; ++i)
     R.words[i] = lb16_load_pair(G.tile_ptr, min(wb + wave + 8 * i, G.np - 1), lane, G.nu);
+  v_load_pair<FAST>(G, min(wb + wave, G.np - 1), min(lane & 15, batch - 1), R.act);
 }
 
 // Stores one V tile's z (zstage: [token][16 rows] fp16, in LDS) as tagged
@@ -304,22 +344,18 @@ __device__ __forceinline__ void v_store_z(const LayerView& L, int batch, int b, 
   }
 }
 
-// V pass over one 16-row tile of branch b of layer L (all its pairs, in
-// chunks of chunk_pairs whose u = g*x is staged in u_lds), then z = l*t of
-// the tile's rows stored as tagged words.  HOOK: hook() runs once the first
-// chunk's loads have landed, before its matrix steps.  EARLY: the first
-// chunk's loads were issued by the caller (`early`, from v_issue with the
-// same geometry).  reuse_u: u_lds already holds this tile's u (the previous
-// tile had the same layer and branch, and one chunk covers the reduction).
-// DEFER: z is left in zstage for the caller to store (v_store_z).  MAXB:
-// the most tokens a call may have (1, or LB_MAX_BATCH).
-template <int MAXB, bool HOOK, bool EARLY, bool DEFER = false, class Hook>
-__device__ __forceinline__ void v_tile(const LayerView& L, int batch, int b, int tile, int chunk_pairs,
-                                       const uint32_t& tag, const LbSignConsts& sc, uint16_t* u_lds,
-                                       float (*red)[256], uint32_t* zstage, Hook&& hook, const VLoads& early,
-                                       bool reuse_u = false) {
+// V pass over one 16-row tile of branch b of layer L, then z = l*t of the
+// tile's rows stored as tagged words.  R holds the first batch's loads
+// (v_issue with this geometry, issued by the caller: EARLY, or here).
+// HOOK: hook() runs after the last pair's loads are issued (its loads then
+// queue behind this tile's, which complete first).  DEFER: z is left in
+// zstage for the caller to store (v_store_z).
+template <int MAXB, bool FAST, bool HOOK, bool EARLY, bool DEFER = false, class Hook>
+__device__ __forceinline__ void v_tile(const LayerView& L, int batch, int b, int tile, const uint32_t& tag,
+                                       const LbSignConsts& sc, float (*red)[256], uint32_t* zstage, Hook&& hook,
+                                       const VLoads& early) {
   const VGeom G = v_geom(L, b, tile);
-  const int n = G.n, nu = G.nu, np = G.np;
+  const int np = G.np, nu = G.nu;
   const int r = b ? L.r1 : L.r0;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
@@ -327,127 +363,58 @@ __device__ __forceinline__ void v_tile(const LayerView& L, int batch, int b, int
   const int trow = min(tok, batch - 1);      // operand row read by this lane
   const int rho = tid & 15, tk = (tid >> 4) & 15;  // epilogue role (threads < 256)
   const int j = 16 * tile + rho;
-  uint32_t lj_raw = 0;  // fp16 bits of l[j]
+  // l[j] (from an always-valid index; converted at use in the epilogue)
+  const uint32_t lj_raw = (b ? L.l1 : L.l0)[min(j, r - 1)];
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  // u = fp16(g*x) of inputs k0 + 8 k8 .. + 7 of this thread's token, to LDS
-  // (an fp16 product rounds the exact product once, as fp32 then fp16 would)
-  auto u_put = [&](int t, int k0, int rowh, int k8, uint4 xv, uint4 gv) {
-    if (G.fast && k0 + 8 * k8 >= n) xv = gv = make_uint4(0u, 0u, 0u, 0u);
-    const f16x8 u = __builtin_bit_cast(f16x8, xv) * __builtin_bit_cast(f16x8, gv);
-    *reinterpret_cast<f16x8*>(u_lds + t * rowh + 8 * k8) = u;
+  // the products of one pair: A = +-g (sign bit of the weight xor that of
+  // g), B = x, four steps alternating between two accumulators
+  auto step = [&](auto S, uint32_t reg, const uint4& x, uint32_t gw) {
+    constexpr int s = decltype(S)::value;
+    const u32x4 gq = v_pair_g<s>(gw);
+    u32x4 d;
+#pragma unroll
+    for (int dd = 0; dd < 4; ++dd) d[dd] = ((reg << (4 * s + dd)) & sc.sign_mask) ^ gq[dd];
+    f32x4& ac = (s & 1) ? acc1 : acc;
+    ac = mfma16(__builtin_bit_cast(f16x8, d), __builtin_bit_cast(f16x8, x), ac);
   };
-  // chunk of pairs [cb, cb + cn) of the batch that starts at wb (cb - wb is a
-  // multiple of 8); first: R.xv0/gv0 hold this thread's first group of
-  // token 0.  Thread i builds groups i, i + 512, ... of every token (one load
-  // of g serves all tokens; all of a group's loads are issued before use).
+  auto pair_products = [&](uint32_t word, int p, const VPairAct& a) {
+    // Inputs at and beyond n: g reads as zero there, so their A operands are
+    // +-0 and their products vanish (x itself came from a clamped, valid
+    // address: finite activations, as the layer's inputs are).
+    // late(): the expansion is not hoisted above this point (it would hold
+    // registers and wait for the load early)
+    const uint32_t reg = lb16_reg_word(late(word), lb16_pair_sel(p, lane, nu));
+    const uint32_t gw = late(a.g);
+    step(std::integral_constant<int, 0>(), reg, a.x[0], gw);
+    step(std::integral_constant<int, 1>(), reg, a.x[1], gw);
+    step(std::integral_constant<int, 2>(), reg, a.x[2], gw);
+    step(std::integral_constant<int, 3>(), reg, a.x[3], gw);
+  };
   constexpr int WB = LB_WAVES * LB_MAXPV;
-  int nchunk = 0;  // (phase stamps only)
-  auto chunk = [&](int wb, int cb, const VLoads& R, bool first, auto with_hook) {
-    const int cn = min(min(np, wb + WB) - cb, chunk_pairs);
-    const int k0 = 128 * cb, kc = 128 * cn, ng = kc >> 3;
-    const int rowh = kc + 8;
-    if (nchunk < 3) LB_MSTAMP(10 + nchunk);
-    if (!reuse_u) {
-      __syncthreads();  // previous users of u_lds are done
-      int k8 = tid;
-      if (first && batch == 1 && k8 < ng) {
-        u_put(0, k0, rowh, k8, R.xv0, R.gv0);
-        k8 += LB_THREADS;
-      }
-      if (G.fast) {
-        for (; k8 < ng; k8 += LB_THREADS) {
-          const int k = k0 + 8 * k8;
-          const uint4 gv = v_load8(G, G.g, k);
-          uint4 xs[MAXB];
-#pragma unroll
-          for (int t = 0; t < MAXB; ++t)
-            xs[t] = t < batch ? v_load8(G, G.x + t * G.ldx, k) : make_uint4(0u, 0u, 0u, 0u);
-#pragma unroll
-          for (int t = 0; t < MAXB; ++t)
-            if (t < batch) u_put(t, k0, rowh, k8, xs[t], gv);
-        }
-      } else {
-        for (; k8 < ng; k8 += LB_THREADS) {
-          const int k = k0 + 8 * k8;
-          const uint4 gv = v_load8(G, G.g, k);
-#pragma unroll 1
-          for (int t = 0; t < batch; ++t) u_put(t, k0, rowh, k8, v_load8(G, G.x + t * G.ldx, k), gv);
-        }
-      }
-      __syncthreads();
-    }
-    if (nchunk < 3) LB_MSTAMP(13 + nchunk);
-    ++nchunk;
-
-    // the phase-B loads (hook) go out once this chunk's sign words are in, so
-    // they do not compete with them, and arrive while the matrix steps run
-    if constexpr (decltype(with_hook)::value) {
-      __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
-      hook();
-      LB_MSTAMP(1);
-    }
-    // l[j] (from an always-valid index; converted at use in the epilogue) is
-    // loaded after the hook's wait, which would otherwise wait for it too
-    if (cb == 0) lj_raw = (b ? L.l1 : L.l0)[min(j, r - 1)];
-    // inputs beyond n are zero in LDS, so the odd last unit's two missing
-    // steps contribute nothing and every pair runs all 4 steps; the next
-    // pair's operands are read from LDS while the current pair computes
-    // this wave's pairs in the chunk: slots i0, i0 + 1, ... while below pe
-    const int i0 = (cb - wb) >> 3, pe = cb + cn;
-    const uint16_t* ub = u_lds + trow * rowh + 8 * grp - k0;
-    f16x8 bv[4];
-    const int pf = min(wb + wave + 8 * i0, pe - 1);
-#pragma unroll
-    for (int st = 0; st < 4; ++st) bv[st] = *reinterpret_cast<const f16x8*>(ub + 32 * (4 * pf + st));
+  VLoads R;
+  if constexpr (EARLY) R = early;
+  else v_issue<FAST>(G, 0, batch, R);
+  for (int wb = 0; wb < np; wb += WB) {
+    if (wb != 0) v_issue<FAST>(G, wb, batch, R);
+    // operands two pairs ahead of the products (8 KB per wave in flight)
+    VPairAct cur = R.act, nx1;
+    v_load_pair<FAST>(G, min(wb + wave + 8, np - 1), trow, nx1);
+    const int pend = min(np, wb + WB);
 #pragma unroll
     for (int i = 0; i < LB_MAXPV; ++i) {
       const int p = wb + wave + 8 * i;
-      if (i >= i0 && p < pe) {
-        f16x8 bn[4];
-        const int pn = (p + 8 < pe) ? p + 8 : p;
-#pragma unroll
-        for (int st = 0; st < 4; ++st) bn[st] = *reinterpret_cast<const f16x8*>(ub + 32 * (4 * pn + st));
-        // late(): the expansion is not hoisted above this point (it would hold
-        // registers and wait for the load early)
-        const uint32_t reg = lb16_reg_word(late(R.words[i]), lb16_pair_sel(p, lane, nu));
-        acc = mfma16(lb16_step_operand_val(reg, 0, sc.sign_mask, sc.one_pair), bv[0], acc);
-        acc1 = mfma16(lb16_step_operand_val(reg, 1, sc.sign_mask, sc.one_pair), bv[1], acc1);
-        acc = mfma16(lb16_step_operand_val(reg, 2, sc.sign_mask, sc.one_pair), bv[2], acc);
-        acc1 = mfma16(lb16_step_operand_val(reg, 3, sc.sign_mask, sc.one_pair), bv[3], acc1);
-#pragma unroll
-        for (int st = 0; st < 4; ++st) bv[st] = bn[st];
-      }
+      // the operands of the pair after next first (clamped: always issued)
+      VPairAct nx2;
+      v_load_pair<FAST>(G, min(p + 16, np - 1), trow, nx2);
+      if (p < pend) pair_products(R.words[i], p, cur);
+      cur = nx1;
+      nx1 = nx2;
     }
-  };
-  // with a hook or early loads the first chunk is its own copy of the code;
-  // the rest run in one loop, which issues a batch's loads at its first chunk
-  VLoads R;
-  int wb = 0, cb = 0;
-  auto advance = [&]() {
-    cb += chunk_pairs;
-    if (cb >= min(np, wb + WB)) cb = wb = wb + WB;
-  };
-  // With several chunks the hook runs after the last one instead: its loads
-  // (sign words of phase B, from memory) would otherwise sit in front of the
-  // next chunks' activation loads, which complete after them.
-  const bool one_chunk = np <= chunk_pairs;
-  if constexpr (EARLY || HOOK) {
-    if constexpr (EARLY) R = early;
-    else v_issue(G, 0, chunk_pairs, R);
-    if (one_chunk) chunk(0, 0, R, true, BoolTag<HOOK>());
-    else chunk(0, 0, R, true, BoolTag<false>());
-    advance();
-  }
-  for (; cb < np; advance()) {
-    if (cb == wb) v_issue(G, wb, chunk_pairs, R);
-    chunk(wb, cb, R, false, BoolTag<false>());
   }
   if constexpr (HOOK) {
-    if (!one_chunk) {
-      hook();
-      LB_MSTAMP(1);
-    }
+    hook();
+    LB_MSTAMP(1);
   }
   acc += acc1;
   LB_MSTAMP(3);
@@ -938,13 +905,13 @@ __device__ __forceinline__ void u_span_lds(const LayerView& L, int li, int batch
 // (kernel-argument preloading), so a single-layer kernel issues its first
 // sign-word and activation loads without waiting for a kernel-argument fetch.
 // They repeat fields of A.L[0]; the multi-layer kernel ignores them.
-//   misc = vq | vr << 8 | batch << 16 | chunk_pairs << 21  (V tiles of
+//   misc = vq | vr << 8 | batch << 16  (V tiles of
 //          workgroup w: vq + (w < vr), contiguous)
-template <int MODE, bool SINGLE, bool UPRE, int MAXB = 1>
+template <int MODE, bool SINGLE, bool UPRE, int MAXB = 1, bool FAST = true>
 __global__ __launch_bounds__(LB_THREADS) void lb_decode_kernel(
     const uint8_t* pre_vb0, const uint8_t* pre_vb1, const uint16_t* pre_x, const uint16_t* pre_g0,
     const uint16_t* pre_g1, int pre_n, int pre_ldx, int pre_vsplit, uint32_t pre_misc,
-    LbDecodeArgs, int chunk_pairs_arg, uint8_t* sync) {
+    LbDecodeArgs, uint8_t* sync) {
   extern __shared__ __align__(16) uint16_t u_lds[];
   __shared__ __align__(16) float red[LB_MAXT][LB_WAVES][256];  // cross-wave partial sums
   // z of a V tile (16 tokens x 16 rows of fp16); two, so a multi-layer
@@ -974,15 +941,13 @@ __global__ __launch_bounds__(LB_THREADS) void lb_decode_kernel(
       P.n = pre_n;
       P.ldx = pre_ldx;
       const int b = vt0 >= pre_vsplit ? 1 : 0;
-      v_issue(v_geom(P, b, vt0 - (b ? pre_vsplit : 0)), 0, (int)(pre_misc >> 21),
-              early);
+      v_issue<FAST>(v_geom(P, b, vt0 - (b ? pre_vsplit : 0)), 0, (int)((pre_misc >> 16) & 31u), early);
     }
   }
   // the remaining arguments are read from here on (their loads, and register
   // spills that wait for them, stay behind the loads above)
   const LbDecodeArgs& A = kernarg_barrier();
   const int batch = SINGLE ? (int)((pre_misc >> 16) & 31u) : A.batch;
-  const int chunk_pairs = SINGLE ? (int)(pre_misc >> 21) : chunk_pairs_arg;
   const LbSignConsts sc = lb16_sign_consts();
   TileMap M;
   load_map(A, M);
@@ -1066,43 +1031,39 @@ __global__ __launch_bounds__(LB_THREADS) void lb_decode_kernel(
       load_ctr();
       prefetch();
     };
-    v_tile<MAXB, MODE == 2, EARLY>(V0, batch, k & 1, tile, chunk_pairs, tag, sc, u_lds, red[0], zstage, first_hook, early);
+    v_tile<MAXB, FAST, MODE == 2, EARLY>(V0, batch, k & 1, tile, tag, sc, red[0], zstage, first_hook, early);
     __syncthreads();
     LB_MSTAMP(2);
     for (int t = vt0 + 1; t < vt1; ++t) {
       const int kt = v_slot<SINGLE>(M, pre_vsplit, t, tile);
-      v_tile<MAXB, false, false>(V0, batch, kt & 1, tile, chunk_pairs, tag, sc, u_lds, red[0], zstage, prefetch, early);
+      v_tile<MAXB, FAST, false, false>(V0, batch, kt & 1, tile, tag, sc, red[0], zstage, prefetch, early);
       __syncthreads();
     }
     LB_MSTAMP(9);
   } else if (vt0 < vt1) {
-    // several layers: a tile's first loads are issued during the previous
-    // tile, once that tile's own sign words have landed, and the previous
-    // tile's z is stored then (so no wait for a tile's words also waits for
-    // the stores before them).  The phase-B loads go out with the last
-    // tile's hook, after every V word.  A tile of the same layer and branch
-    // as the previous one reuses u from LDS when one chunk covers the
-    // reduction.
+    // several layers: a tile's first loads are issued at the end of the
+    // previous tile's products, and the previous tile's z is stored then (so
+    // no wait for a tile's words also waits for the stores before them).
+    // The phase-B loads go out with the last tile's hook, after every V
+    // word.
     int tile;
     int k = v_slot<SINGLE>(M, pre_vsplit, vt0, tile);
     VLoads cur;
-    v_issue(v_geom(layer_view(A.L[k >> 1]), k & 1, tile), 0, chunk_pairs, cur);
+    v_issue<FAST>(v_geom(layer_view(A.L[k >> 1]), k & 1, tile), 0, batch, cur);
     int prev_k = -1, prev_tile = 0;
     for (int t = vt0; t < vt1; ++t) {
       int ntile = 0;
       const int nk = t + 1 < vt1 ? v_slot<SINGLE>(M, pre_vsplit, t + 1, ntile) : -1;
       VLoads nxt;
       auto hook = [&]() {
-        if (nk >= 0) v_issue(v_geom(layer_view(A.L[nk >> 1]), nk & 1, ntile), 0, chunk_pairs, nxt);
+        if (nk >= 0) v_issue<FAST>(v_geom(layer_view(A.L[nk >> 1]), nk & 1, ntile), 0, batch, nxt);
         if (t == vt0) load_ctr();
         if (prev_k >= 0)
           v_store_z(layer_view(A.L[prev_k >> 1]), batch, prev_k & 1, prev_tile, late(tag), zst[(t - vt0 + 1) & 1]);
         if (MODE == 2 && t == vt1 - 1) prefetch();
       };
       const LayerView L = layer_view(A.L[k >> 1]);
-      const bool reuse_u = k == prev_k && ((lb16_units(L.n) + 1) >> 1) <= chunk_pairs;
-      v_tile<MAXB, true, true, true>(L, batch, k & 1, tile, chunk_pairs, tag, sc, u_lds, red[0], zst[(t - vt0) & 1], hook,
-                               cur, reuse_u);
+      v_tile<MAXB, FAST, true, true, true>(L, batch, k & 1, tile, tag, sc, red[0], zst[(t - vt0) & 1], hook, cur);
       __syncthreads();
       if (t == vt0) LB_MSTAMP(2);
       prev_k = k;
@@ -1228,14 +1189,12 @@ hipError_t lb_launch_take_error(void* sync, uint32_t* out, hipStream_t stream) {
 
 static int g_fused_grid[64];  // per device: workgroups of the single-launch kernel (0: unknown, -1: none)
 
-// Dynamic LDS of a decode launch: phase A stages g*x (chunks of 128*chunk_pairs
-// inputs per token), phase B stages z (zs + 8 halves per token) in the same
-// space.
-size_t lb_decode_lds_bytes(const LbDecodeArgs& a, int chunk_pairs) {
+// Dynamic LDS of a decode launch: phase B stages z (zs + 8 halves per token)
+// of the largest layer (phase A keeps its operands in registers).
+size_t lb_decode_lds_bytes(const LbDecodeArgs& a) {
   int zs = 0;
   for (int i = 0; i < a.nlayers; ++i) zs = a.L[i].zs > zs ? a.L[i].zs : zs;
-  const size_t pa = (size_t)a.batch * (128 * chunk_pairs + 8), pb = (size_t)a.batch * (zs + 8);
-  return (pa > pb ? pa : pb) * sizeof(uint16_t);
+  return (size_t)a.batch * (zs + 8) * sizeof(uint16_t);
 }
 
 // Splits costs c[0..n) into G contiguous ranges, begin[0..G], whose largest
@@ -1295,24 +1254,47 @@ static void cost_split(LbDecodeArgs& a, int G, int vrows = 16) {
   balanced_split(c.data(), (int)c.size(), G, a.ut_begin);
 }
 
-// Smallest per-CU occupancy of the single-launch kernels of one token limit.
-template <int MAXB>
-static hipError_t fused_occupancy(int& occ) {
+// Smallest per-CU occupancy of the single-launch kernels of one token limit
+// and one form of the activation loads.
+template <int MAXB, bool FAST>
+static hipError_t fused_occupancy_f(int& occ) {
   int o[4] = {0, 0, 0, 0};
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o[0], lb_decode_kernel<2, true, false, MAXB>,
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o[0], lb_decode_kernel<2, true, false, MAXB, FAST>,
                                                               LB_THREADS, LB_DECODE_LDS_MAX);
   if (e == hipSuccess)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o[1], lb_decode_kernel<2, false, false, MAXB>, LB_THREADS,
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o[1], lb_decode_kernel<2, false, false, MAXB, FAST>, LB_THREADS,
                                                      LB_DECODE_LDS_MAX);
   if (e == hipSuccess)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o[2], lb_decode_kernel<2, true, true, MAXB>, LB_THREADS,
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o[2], lb_decode_kernel<2, true, true, MAXB, FAST>, LB_THREADS,
                                                      LB_UPRE_DYN_MAX);
   if (e == hipSuccess)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o[3], lb_decode_kernel<2, false, true, MAXB>, LB_THREADS,
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o[3], lb_decode_kernel<2, false, true, MAXB, FAST>, LB_THREADS,
                                                      LB_UPRE_DYN_MAX);
   occ = o[0];
   for (int i = 1; i < 4; ++i) occ = o[i] < occ ? o[i] : occ;
   return e;
+}
+
+// Smallest per-CU occupancy of the single-launch kernels of one token limit
+// (both forms of the activation loads).
+template <int MAXB>
+static hipError_t fused_occupancy(int& occ) {
+  int a = 0, b = 0;
+  hipError_t e = fused_occupancy_f<MAXB, true>(a);
+  if (e == hipSuccess) e = fused_occupancy_f<MAXB, false>(b);
+  occ = a < b ? a : b;
+  return e;
+}
+
+// The multi-token V pass takes 16-byte loads of x and g when every layer's x
+// is 16-byte aligned with ldx and n multiples of 8 (g is 16-byte aligned by
+// contract).
+static bool decode_fast_loads(const LbDecodeArgs& a) {
+  for (int i = 0; i < a.nlayers; ++i) {
+    const LbLayerArgs& L = a.L[i];
+    if ((((uintptr_t)L.x) & 15) != 0 || (L.ldx & 7) != 0 || (L.n & 7) != 0) return false;
+  }
+  return true;
 }
 
 hipError_t lb_decode1_occupancy(bool single, size_t lds, int& occ);
@@ -1347,10 +1329,10 @@ static hipError_t fused_grid(int& G) {
   return hipSuccess;
 }
 
-template <bool SINGLE, int MAXB>
-static hipError_t launch_decode_t(const LbDecodeArgs& args, int chunk_pairs, void* sync, int allow_fused,
+template <bool SINGLE, int MAXB, bool FAST>
+static hipError_t launch_decode_f(const LbDecodeArgs& args, void* sync, int allow_fused,
                                   hipStream_t stream) {
-  const size_t lds = lb_decode_lds_bytes(args, chunk_pairs);
+  const size_t lds = lb_decode_lds_bytes(args);
   if (lds > LB_DECODE_LDS_MAX) return hipErrorInvalidValue;  // the host routes such calls elsewhere
   hipError_t e = hipSuccess;
   // preloaded copies of layer 0's phase-A fields (single-layer kernels)
@@ -1362,7 +1344,7 @@ static hipError_t launch_decode_t(const LbDecodeArgs& args, int chunk_pairs, voi
   const uint16_t* g1 = SINGLE ? L0.br[1].g : nullptr;
   const int pn = SINGLE ? L0.n : 0, pldx = SINGLE ? (int)L0.ldx : 0, vsplit = SINGLE ? args.vt_end[0] : 0;
   auto misc = [&](const LbDecodeArgs& a) {
-    return (uint32_t)a.vq | ((uint32_t)a.vr << 8) | ((uint32_t)a.batch << 16) | ((uint32_t)chunk_pairs << 21);
+    return (uint32_t)a.vq | ((uint32_t)a.vr << 8) | ((uint32_t)a.batch << 16);
   };
   if (allow_fused) {
     int G = 0;
@@ -1384,28 +1366,35 @@ static hipError_t launch_decode_t(const LbDecodeArgs& args, int chunk_pairs, voi
         regs_hold = (np + (args.L[0].nb == 2 ? 3 : 7)) / (args.L[0].nb == 2 ? 4 : 8) <= LB_MAXPW;
       }
       if (lds <= LB_UPRE_DYN_MAX && !regs_hold)
-        hipLaunchKernelGGL((lb_decode_kernel<2, SINGLE, true, MAXB>), dim3(G), dim3(LB_THREADS), lds, stream, vb0, vb1, px,
-                           g0, g1, pn, pldx, vsplit, misc(a), a, chunk_pairs, (uint8_t*)sync);
+        hipLaunchKernelGGL((lb_decode_kernel<2, SINGLE, true, MAXB, FAST>), dim3(G), dim3(LB_THREADS), lds, stream, vb0, vb1, px,
+                           g0, g1, pn, pldx, vsplit, misc(a), a, (uint8_t*)sync);
       else
-        hipLaunchKernelGGL((lb_decode_kernel<2, SINGLE, false, MAXB>), dim3(G), dim3(LB_THREADS), lds, stream, vb0, vb1, px,
-                           g0, g1, pn, pldx, vsplit, misc(a), a, chunk_pairs, (uint8_t*)sync);
+        hipLaunchKernelGGL((lb_decode_kernel<2, SINGLE, false, MAXB, FAST>), dim3(G), dim3(LB_THREADS), lds, stream, vb0, vb1, px,
+                           g0, g1, pn, pldx, vsplit, misc(a), a, (uint8_t*)sync);
       return hipGetLastError();
     }
   }
   LbDecodeArgs a = args;
   a.vq = 1; a.vr = 0;
-  hipLaunchKernelGGL((lb_decode_kernel<0, SINGLE, false, MAXB>), dim3(a.nvt), dim3(LB_THREADS), lds, stream, vb0, vb1, px, g0,
-                     g1, pn, pldx, vsplit, misc(a), a, chunk_pairs, (uint8_t*)sync);
+  hipLaunchKernelGGL((lb_decode_kernel<0, SINGLE, false, MAXB, FAST>), dim3(a.nvt), dim3(LB_THREADS), lds, stream, vb0, vb1, px, g0,
+                     g1, pn, pldx, vsplit, misc(a), a, (uint8_t*)sync);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int gb = a.nut < 1024 ? a.nut : 1024;
   a.uq = a.nut / gb; a.ur = a.nut % gb;
   hipLaunchKernelGGL((lb_decode_kernel<1, SINGLE, false>), dim3(gb), dim3(LB_THREADS), lds, stream, vb0, vb1, px, g0, g1,
-                     pn, pldx, vsplit, misc(a), a, chunk_pairs, (uint8_t*)sync);
+                     pn, pldx, vsplit, misc(a), a, (uint8_t*)sync);
   return hipGetLastError();
 }
 
-hipError_t lb_launch_decode(const LbDecodeArgs& args, int chunk_pairs, void* sync, int allow_fused,
+template <bool SINGLE, int MAXB>
+static hipError_t launch_decode_t(const LbDecodeArgs& args, void* sync, int allow_fused,
+                                  hipStream_t stream) {
+  return decode_fast_loads(args) ? launch_decode_f<SINGLE, MAXB, true>(args, sync, allow_fused, stream)
+                                 : launch_decode_f<SINGLE, MAXB, false>(args, sync, allow_fused, stream);
+}
+
+hipError_t lb_launch_decode(const LbDecodeArgs& args, void* sync, int allow_fused,
                             hipStream_t stream) {
   if (args.batch == 1) {
     // one token: the sparse-instruction kernels of decode1.hip
@@ -1434,6 +1423,6 @@ hipError_t lb_launch_decode(const LbDecodeArgs& args, int chunk_pairs, void* syn
     if (G > 0 && a.nlayers > 1) cost_split(a, G, 16 * a.vtpu);
     return lb_launch_decode1(a, G, sync, stream);
   }
-  return args.nlayers == 1 ? launch_decode_t<true, LB_MAX_BATCH>(args, chunk_pairs, sync, allow_fused, stream)
-                           : launch_decode_t<false, LB_MAX_BATCH>(args, chunk_pairs, sync, allow_fused, stream);
+  return args.nlayers == 1 ? launch_decode_t<true, LB_MAX_BATCH>(args, sync, allow_fused, stream)
+                           : launch_decode_t<false, LB_MAX_BATCH>(args, sync, allow_fused, stream);
 }

@@ -14,7 +14,7 @@ hipError_t lb_launch_pack(const void* latent, int is_f16, long ld, int transpose
                           void* dst, hipStream_t stream);
 hipError_t lb_launch_prefill(const LbPrefillArgs& args, hipStream_t stream);
 hipError_t lb_launch_transpose_packed(const void* src, int R, int K, void* dst, hipStream_t stream);
-hipError_t lb_launch_decode(const LbDecodeArgs& args, int chunk_pairs, void* sync, int allow_fused,
+hipError_t lb_launch_decode(const LbDecodeArgs& args, void* sync, int allow_fused,
                             hipStream_t stream);
 hipError_t lb_launch_take_error(void* sync, uint32_t* out, hipStream_t stream);
 
@@ -39,8 +39,6 @@ lb_status hip_fail(hipError_t e, const char* what) {
 constexpr int kMaxRank = 4096;
 constexpr int kMaxN = 32768;
 constexpr int kDecodeMaxBatch = 16;
-constexpr size_t kDecodeLdsBudget = 56 * 1024;
-constexpr int kDecodeMaxChunkPairs = 64;  // 8 waves x 8 register-held pairs
 
 inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -120,22 +118,6 @@ lb_status check_layer(const lb_layer* L, uint32_t mask, int* sel, int* nsel, con
   return LB_OK;
 }
 
-// Pairs (128 inputs each) of the decode V pass staged in LDS at once: a
-// multiple of 8 (every wave gets the same number of pairs per chunk), or all
-// the tile's pairs.  The budget is the larger of a fixed share and what phase
-// B's z takes (zs + 8 halves per token) in the same space anyway.
-int decode_chunk_pairs(int64_t batch, int n, int zs) {
-  const int np = (lb16_units(n) + 1) / 2;
-  size_t budget = (size_t)batch * (zs + 8) * sizeof(uint16_t);
-  if (budget < kDecodeLdsBudget) budget = kDecodeLdsBudget;
-  if (budget > LB_DECODE_LDS_MAX) budget = LB_DECODE_LDS_MAX;
-  int cp = (int)((budget / sizeof(uint16_t) / batch - 8) / 128);
-  cp = cp / 8 * 8;
-  if (cp > kDecodeMaxChunkPairs) cp = kDecodeMaxChunkPairs;
-  if (cp < 8) cp = 8;
-  return cp >= np ? np : cp;
-}
-
 void fill_layer_args(LbLayerArgs& a, const lb_layer& L, const int* sel, int nsel, const LayerWs& w,
                      uint8_t* base, const uint16_t* x, long ldx, uint16_t* y, long ldy) {
   memset(&a, 0, sizeof a);
@@ -191,22 +173,19 @@ lb_status run_decode(LbLayerArgs* layers, int nl, int batch, void* sync, int all
   memset(&args, 0, sizeof args);
   args.nlayers = nl;
   args.batch = batch;
-  int vt = 0, ut = 0, maxn = 1, maxzs = 0;
+  int vt = 0, ut = 0;
   for (int i = 0; i < nl; ++i) {
     args.L[i] = layers[i];
-    if (layers[i].zs > maxzs) maxzs = layers[i].zs;
     for (int b = 0; b < 2; ++b) {
       if (b < layers[i].nb) vt += (layers[i].br[b].r + 15) / 16;
       args.vt_end[2 * i + b] = vt;
     }
     ut += (layers[i].m + 15) / 16;
     args.ut_end[i] = ut;
-    if (layers[i].n > maxn) maxn = layers[i].n;
   }
   args.nvt = vt;
   args.nut = ut;
-  const int cp = decode_chunk_pairs(batch, maxn, maxzs);
-  hipError_t e = lb_launch_decode(args, cp, sync, allow_fused, stream);
+  hipError_t e = lb_launch_decode(args, sync, allow_fused, stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return LB_OK;
 }
