@@ -34,8 +34,8 @@
 // regular library has none of this): thread 0 of each workgroup stores the
 // 100 MHz real-time counter at fixed points of a call to the device buffer
 // given to littlebit_phase_stamps_multi_set, slot 16 w + i for workgroup w
-// and point i (0 start, 10 + c / 13 + c chunk c < 3 of a V tile begun /
-// staged, 1 phase-B loads issued, 3 V products done, 2 first V tile done,
+// and point i (0 start, 10 / 13 / 14 pair slot 0 / 3 / 7 of the first V
+// batch done, 1 phase-B loads issued, 3 V products done, 2 first V tile done,
 // 9 last V tile done, 4 z copy done (the last layer entered), 5 first U
 // group done, 8 / 7 a U group begun / its products issued, 6 end; each
 // stamp holds its last time); lane 0 of every wave
@@ -408,6 +408,9 @@ __device__ __forceinline__ void v_tile(const LayerView& L, int batch, int b, int
       VPairAct nx2;
       v_load_pair<FAST>(G, min(p + 16, np - 1), trow, nx2);
       if (p < pend) pair_products(R.words[i], p, cur);
+      if (wb == 0 && i == 0) LB_MSTAMP(10);
+      if (wb == 0 && i == 3) LB_MSTAMP(13);
+      if (wb == 0 && i == 7) LB_MSTAMP(14);
       cur = nx1;
       nx1 = nx2;
     }

@@ -22,9 +22,8 @@ POINTS = [(0, "start"), (1, "arguments + first u staged"), (7, "multi-layer tile
           (9, "last V unit's z stored"), (4, "first z copied"), (10, "last z copy done"),
           (5, "first U group products done"), (6, "end")]
 COUNTS = (11, 12)  # u stagings, z copies of a workgroup
-MPOINTS = [(0, "start"), (10, "V chunk 0 begun"), (13, "V chunk 0 staged"), (1, "phase-B loads issued"),
-           (11, "V chunk 1 begun"), (14, "V chunk 1 staged"), (12, "V chunk 2 begun"), (15, "V chunk 2 staged"),
-           (3, "V products done"), (2, "first V tile done"), (9, "last V tile done"), (4, "z copy done"),
+MPOINTS = [(0, "start"), (10, "V pair slot 0 done"), (13, "V pair slot 3 done"), (14, "V pair slot 7 done"),
+           (1, "phase-B loads issued"), (3, "V products done"), (2, "first V tile done"), (9, "last V tile done"), (4, "z copy done"),
            (5, "first U group done"), (8, "last U group begun"), (7, "last U group products issued"),
            (6, "end")]
 
