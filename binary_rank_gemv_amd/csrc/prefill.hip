@@ -416,108 +416,135 @@ lb_prefill2_kernel(LbPrefillArgs A) {
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt) acc[rt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // this wave's two matrix steps (2kh, 2kh+1) of chunk c from stage S; the
-  // second half of a pair made of one unit has none.  The B fragments of the
-  // second step are read while the first step's products run.
-  // The matrix steps of chunk c from stage S: steps 2kh and 2kh+1, or, for
-  // a pair made of one unit (2 steps), step kh alone.  The loads of chunk
-  // c + 2 into stage `ahead` are issued between the first step's products,
-  // where a wave stalled on a full memory queue leaves the matrix core to
-  // the other wave of its SIMD; no branch separates them from the waits
-  // that guard their stage.
-  auto compute = [&](int c, const uint8_t* S, uint8_t* ahead, auto loads) __attribute__((always_inline)) {
-    constexpr bool LOADS = decltype(loads)::value;
-    const int sg = c >= np0 ? 1 : 0;
-    const int p = c - (sg ? np0 : 0);
-    const bool full = 2 * p + 1 < (sg ? nu1 : nu0);
+  // Per chunk c (stage S) a wave runs its two matrix steps, 2kh and 2kh+1, or,
+  // for a pair made of one unit (2 steps), step kh alone.  The barrier that
+  // makes chunk c + 1 visible sits between the two steps: after it the wave
+  // reads chunk c + 1's first-step B fragments and sign words, which land
+  // while its second step of chunk c runs, so no chunk opens with the matrix
+  // core waiting for LDS.  Everything a wave reads of stage S (both steps' B
+  // fragments and g) is read before that barrier and waited for, so the
+  // stage may be refilled once every wave has passed it.  The loads of chunk
+  // c + 2 into stage `ahead` (the stage of chunk c - 1, free since the
+  // barrier before) are issued between the first step's products, where a
+  // wave stalled on a full memory queue leaves the matrix core to the other
+  // wave of its SIMD.
+  auto pair_of = [&](int c, int& sg, int& p, bool& full) {
+    sg = c >= np0 ? 1 : 0;
+    p = c - (sg ? np0 : 0);
+    full = 2 * p + 1 < (sg ? nu1 : nu0);
+  };
+  // the lane's column, opaque here so that the fragment addresses are formed
+  // per chunk instead of being held in registers across the loop
+  auto read_b = [&](const uint8_t* S, int st, f16x8* dst) {
+    int colx = col;
+    __asm__ volatile("" : "+v"(colx));
+    const int q = 4 * st + grp;
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt)
+      dst[tt] = *reinterpret_cast<const f16x8*>(S + 16 * (16 * (16 * tt + colx) + (q ^ colx)));
+  };
+  // GEMM 2 operand values +-h_b[i]: the sign is folded into the word here,
+  // the magnitude pair is formed at each use
+  auto hbits = [&](int sg, int rt) { return sg ? hraw[rt] >> 16 : hraw[rt] & 0xFFFFu; };
+  // chunk c's first-step B fragments and its sign words, from stage S
+  auto head = [&](int c, const uint8_t* S, f16x8* b0, uint32_t* reg) {
+    int sg, p;
+    bool full;
+    pair_of(c, sg, p, full);
     const int st0 = full ? 2 * kh : kh;
     const uint32_t sel = lb16_pair_sel(p, lane, sg ? nu1 : nu0);
     const uint32_t* words = reinterpret_cast<const uint32_t*>(S + P2_WORDS_OFF) + rg * 256 + (full ? lane : lane >> 1);
-    f16x8 b[2][8];
-    // the lane's column, opaque here so that the fragment addresses are
-    // formed per chunk instead of being held in registers across the loop
-    int colx = col;
-    __asm__ volatile("" : "+v"(colx));
-    auto read_b = [&](int st, f16x8* dst) {
-      const int q = 4 * st + grp;
-#pragma unroll
-      for (int tt = 0; tt < 8; ++tt)
-        dst[tt] = *reinterpret_cast<const f16x8*>(S + 16 * (16 * (16 * tt + colx) + (q ^ colx)));
-    };
-    read_b(st0, b[0]);
-    // GEMM 2 operand values +-h_b[i]: the sign is folded into the word here,
-    // the magnitude pair is formed at each use
-    auto hbits = [&](int rt) { return sg ? hraw[rt] >> 16 : hraw[rt] & 0xFFFFu; };
-    uint32_t reg[4];
+    read_b(S, st0, b0);
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
-      reg[rt] = lb16_reg_word(words[64 * rt], sel) ^ (MODE == 2 && (hbits(rt) & 0x8000u) ? 0xFFFFFFFFu : 0u);
-    auto mstep = [&](int st, const f16x8* bb, bool with_loads) {
-      if (with_loads) issue(min(c + P2_STAGES - 1, C - 1), ahead);
-      u32x4 gq = u32x4{0u, 0u, 0u, 0u};
-      if (MODE == 1) gq = *reinterpret_cast<const u32x4*>(S + P2_G_OFF + 2 * (32 * st + 8 * grp));
+      reg[rt] = lb16_reg_word(words[64 * rt], sel) ^ (MODE == 2 && (hbits(sg, rt) & 0x8000u) ? 0xFFFFFFFFu : 0u);
+  };
+  auto mstep = [&](int c, int sg, int st, const f16x8* bb, const uint32_t* reg, const u32x4& gq, uint8_t* ahead,
+                   bool with_loads) {
+    if (with_loads) issue(min(c + P2_STAGES - 1, C - 1), ahead);
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        f16x8 a;
-        if (MODE == 1) {
-          u32x4 d;
+    for (int rt = 0; rt < 4; ++rt) {
+      f16x8 a;
+      if (MODE == 1) {
+        u32x4 d;
 #pragma unroll
-          for (int dd = 0; dd < 4; ++dd) d[dd] = ((reg[rt] << (4 * st + dd)) & sc.sign_mask) ^ gq[dd];
-          a = __builtin_bit_cast(f16x8, d);
-        } else {
-          a = lb16_step_operand_val(reg[rt], st, sc.sign_mask, (hbits(rt) & 0x7FFFu) * 0x10001u);
-        }
-#pragma unroll
-        for (int tt = 0; tt < 8; ++tt) acc[rt][tt] = mfma16(a, bb[tt], acc[rt][tt]);
+        for (int dd = 0; dd < 4; ++dd) d[dd] = ((reg[rt] << (4 * st + dd)) & sc.sign_mask) ^ gq[dd];
+        a = __builtin_bit_cast(f16x8, d);
+      } else {
+        a = lb16_step_operand_val(reg[rt], st, sc.sign_mask, (hbits(sg, rt) & 0x7FFFu) * 0x10001u);
       }
-      // issue order: the first operand, then each later operand's ALU work
-      // (and the loads) spread between the products of the one before
-      __builtin_amdgcn_sched_group_barrier(0x2, 8, 0);
 #pragma unroll
-      for (int i = 0; i < 24; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x8, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x2, 1, 0);
-        if (with_loads && (i & 3) == 3 && i < 20) __builtin_amdgcn_sched_group_barrier(0x10, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x8, 8, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    read_b(st0 + 1, b[1]);
-    __builtin_amdgcn_sched_barrier(0);  // keep those reads ahead of the first step's products
-    mstep(st0, b[0], LOADS);
-    if (full) mstep(st0 + 1, b[1], false);
+      for (int tt = 0; tt < 8; ++tt) acc[rt][tt] = mfma16(a, bb[tt], acc[rt][tt]);
+    }
+    // issue order: the first operand, then each later operand's ALU work
+    // (and the loads) spread between the products of the one before
+    __builtin_amdgcn_sched_group_barrier(0x2, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 24; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x8, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x2, 1, 0);
+      if (with_loads && (i & 3) == 3 && i < 20) __builtin_amdgcn_sched_group_barrier(0x10, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x8, 8, 0);
+    __builtin_amdgcn_sched_barrier(0);
   };
 
-  // chunk c: a loading wave waits until its loads of it have landed (those
-  // of chunk c + 1 may still be in flight), then every wave waits until all
-  // have (a plain barrier; the empty asm keeps LDS reads below it).  The
-  // stage of chunk c - 1 is then free for chunk c + 2: every wave has
-  // consumed its reads.  Every step of a loading wave issues loads, past the
-  // end as repeats of the last chunk into a stage nobody reads again, so the
-  // wait count is a constant; the loading and the other waves run separate
-  // copies of the loop, so that no branch separates a load from its waits.
+  // A loading wave waits until its loads of the next chunk have landed (those
+  // of the chunk after may still be in flight), every wave until its LDS
+  // reads have; then all meet (the empty asm keeps LDS reads below the
+  // barrier).  Every first step of a loading wave issues loads, past the end
+  // as repeats of the last chunk into a stage nobody reads again, so the wait
+  // count is a constant; the loading and the other waves run separate copies
+  // of the loop, so that no branch separates a load from its waits.
   auto run = [&](auto loads) __attribute__((always_inline)) {
     constexpr bool LOADS = decltype(loads)::value;
-    auto step = [&](int c, const uint8_t* cur, uint8_t* ahead) __attribute__((always_inline)) {
-      // vmcnt(kOps * (P2_STAGES - 2)): the loads of the next stages may still be in flight
-      constexpr int kWait = kOps * (P2_STAGES - 2);
-      if (LOADS) __builtin_amdgcn_s_waitcnt((kWait & 15) | ((kWait >> 4) << 14) | (7 << 4) | (15 << 8));
+    constexpr int kWait = kOps * (P2_STAGES - 2);
+    auto sync = [&]() __attribute__((always_inline)) {
+      if (LOADS)
+        __builtin_amdgcn_s_waitcnt((kWait & 15) | ((kWait >> 4) << 14) | (7 << 4));
+      else
+        __builtin_amdgcn_s_waitcnt((15 | (3 << 14)) | (7 << 4));
       __builtin_amdgcn_s_barrier();
       __asm__ volatile("" ::: "memory");
-      compute(c, cur, ahead, loads);
+    };
+    f16x8 b0[8], b1[8];
+    uint32_t reg[4], regn[4] = {0u, 0u, 0u, 0u};
+    auto body = [&](int c, const uint8_t* S, const uint8_t* Snext, uint8_t* ahead) __attribute__((always_inline)) {
+      int sg, p;
+      bool full;
+      pair_of(c, sg, p, full);
+      const int st0 = full ? 2 * kh : kh;
+      read_b(S, st0 + 1, b1);
+      u32x4 gq0 = u32x4{0u, 0u, 0u, 0u}, gq1 = gq0;
+      if (MODE == 1) {
+        gq0 = *reinterpret_cast<const u32x4*>(S + P2_G_OFF + 2 * (32 * st0 + 8 * grp));
+        gq1 = *reinterpret_cast<const u32x4*>(S + P2_G_OFF + 2 * (32 * (st0 + 1) + 8 * grp));
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keep those reads ahead of the first step's products
+      mstep(c, sg, st0, b0, reg, gq0, ahead, LOADS);
+      // unconditional (after the last chunk it rereads that chunk's copy in
+      // a stage nobody needs), so that every path to a read of a stage has
+      // passed the same waits
+      sync();
+      head(min(c + 1, C - 1), Snext, b0, regn);
+      if (full) mstep(c, sg, st0 + 1, b1, reg, gq1, ahead, false);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) reg[rt] = regn[rt];
     };
     if (LOADS) {
       issue(0, stage0);
       issue(min(1, C - 1), stage1);
     }
+    sync();
+    head(0, stage0, b0, reg);
     int c = 0;
     for (; c + P2_STAGES <= C; c += P2_STAGES) {
-      step(c, stage0, stage2);
-      step(c + 1, stage1, stage0);
-      step(c + 2, stage2, stage1);
+      body(c, stage0, stage1, stage2);
+      body(c + 1, stage1, stage2, stage0);
+      body(c + 2, stage2, stage0, stage1);
     }
-    if (c < C) step(c, stage0, stage2);
-    if (c + 1 < C) step(c + 1, stage1, stage0);
+    if (c < C) body(c, stage0, stage1, stage2);
+    if (c + 1 < C) body(c + 1, stage1, stage2, stage0);
   };
   if (kh == 0)
     run(std::integral_constant<bool, true>());
