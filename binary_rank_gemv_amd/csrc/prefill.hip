@@ -313,18 +313,27 @@ __device__ __forceinline__ P2Tile p2_tile(int rb, int tb, int nbz) {
   return t;
 }
 
-__host__ __device__ inline int p2_row_blocks(const LbPrefillArgs& a, int mode) {
+// Row tiles of GEMM `mode` (the largest branch's for GEMM 1), and the
+// 64 * rowt-row blocks that cover them.
+__host__ __device__ inline int p2_row_tiles(const LbPrefillArgs& a, int mode) {
   int t = 0;
   if (mode == 1)
     for (int b = 0; b < a.nb; ++b) t = max(t, (a.br[b].r + 15) >> 4);
   else
     t = (a.m + 15) >> 4;
-  return (t + 15) / 16;
+  return t;
 }
 
-template <int MODE>
+__host__ __device__ inline int p2_row_blocks(const LbPrefillArgs& a, int mode, int rowt) {
+  return (p2_row_tiles(a, mode) + 4 * rowt - 1) / (4 * rowt);
+}
+
+// ROWT: row tiles per wave (4, or 3 where 192-row blocks fill the machine
+// in fewer rounds of workgroups).
+template <int MODE, int ROWT>
 __global__ __launch_bounds__(64 * P2_WAVES, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 lb_prefill2_kernel(LbPrefillArgs A) {
+  static_assert(ROWT == 3 || ROWT == 4, "3 or 4 row tiles per wave");
   // global-to-LDS loads per chunk of a loading (first-half) wave: 8 x 1 KB
   // of activations, the sign bytes of its row group, (GEMM 1) g
   constexpr int kOps = MODE == 1 ? 10 : 9;
@@ -335,9 +344,9 @@ lb_prefill2_kernel(LbPrefillArgs A) {
   const int rg = wave & 3, kh = wave >> 2;  // row group, half of each chunk
   const int grp = lane >> 4, col = lane & 15;
   const int M = A.M;
-  const P2Tile bt = p2_tile(p2_row_blocks(A, MODE), (M + PF_BN - 1) / PF_BN, MODE == 1 ? A.nb : 1);
+  const P2Tile bt = p2_tile(p2_row_blocks(A, MODE, ROWT), (M + PF_BN - 1) / PF_BN, MODE == 1 ? A.nb : 1);
   const int tok0 = bt.by * PF_BN;
-  const int tile0 = 16 * bt.bx + 4 * rg;  // first row tile of this wave
+  const int tile0 = 4 * ROWT * bt.bx + ROWT * rg;  // first row tile of this wave
   const LbSignConsts sc = lb16_sign_consts();
 
   // the reduction as a sequence of 128-input chunks over one or two segments
@@ -345,7 +354,7 @@ lb_prefill2_kernel(LbPrefillArgs A) {
   const LbBranchArgs& B0 = A.br[b1];
   const LbBranchArgs& B1 = A.br[MODE == 2 && A.nb == 2 ? 1 : b1];
   const int ntiles = MODE == 1 ? (B0.r + 15) >> 4 : (A.m + 15) >> 4;
-  if (16 * bt.bx >= ntiles) return;  // rows beyond this branch (uniform)
+  if (4 * ROWT * bt.bx >= ntiles) return;  // rows beyond this branch (uniform)
   const int K0 = MODE == 1 ? A.n : B0.r, K1 = MODE == 1 ? A.n : B1.r;
   const int nu0 = lb16_units(K0), nu1 = lb16_units(K1);
   const int np0 = MODE == 1 ? A.n / 128 : (nu0 + 1) >> 1;
@@ -360,9 +369,9 @@ lb_prefill2_kernel(LbPrefillArgs A) {
 
   // GEMM 2: h_b[i] of the lane's row i of each tile, branch 0 in the low and
   // branch 1 in the high half
-  uint32_t hraw[4];
+  uint32_t hraw[ROWT];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
+  for (int rt = 0; rt < ROWT; ++rt) {
     hraw[rt] = 0u;
     if (MODE == 2) {
       const int i = min(16 * (tile0 + rt) + col, A.m - 1);
@@ -372,7 +381,8 @@ lb_prefill2_kernel(LbPrefillArgs A) {
 
   // per-lane byte offsets of the loads, the same for every chunk (the launch
   // guarantees that they fit 32 bits): activation slot i; sign bytes of row
-  // tile lane/16 of the row group for segment sg, 16 per lane, for a full
+  // tile lane/16 of the row group for segment sg (with 3 tiles per wave,
+  // lanes 48.. load a tile nobody reads), 16 per lane, for a full
   // pair (256 bytes per tile) and for a pair of one unit (128 bytes, each
   // half-row loaded twice so that the LDS copy keeps the full pair's
   // addressing: byte 4j of a lane's word sits at 4*(lane/2)); g
@@ -410,9 +420,9 @@ lb_prefill2_kernel(LbPrefillArgs A) {
                                        (__attribute__((address_space(3))) void*)(S + P2_G_OFF), 16, 0, 0);
   };
 
-  f32x4 acc[4][8];
+  f32x4 acc[ROWT][8];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
+  for (int rt = 0; rt < ROWT; ++rt)
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt) acc[rt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -443,9 +453,12 @@ lb_prefill2_kernel(LbPrefillArgs A) {
     for (int tt = 0; tt < 8; ++tt)
       dst[tt] = *reinterpret_cast<const f16x8*>(S + 16 * (16 * (16 * tt + colx) + (q ^ colx)));
   };
-  // GEMM 2 operand values +-h_b[i]: the sign is folded into the word here,
-  // the magnitude pair is formed at each use
-  auto hbits = [&](int sg, int rt) { return sg ? hraw[rt] >> 16 : hraw[rt] & 0xFFFFu; };
+  // GEMM 2: h_b[i] of segment (branch) sg in both halves of a word, for the
+  // lane's row of each tile
+  auto hpairs = [&](int sg, uint32_t* hp) {
+#pragma unroll
+    for (int rt = 0; rt < ROWT; ++rt) hp[rt] = __builtin_amdgcn_perm(hraw[rt], hraw[rt], sg ? 0x03020302u : 0x01000100u);
+  };
   // chunk c's first-step B fragments and its sign words, from stage S
   auto head = [&](int c, const uint8_t* S, f16x8* b0, uint32_t* reg) {
     int sg, p;
@@ -456,23 +469,20 @@ lb_prefill2_kernel(LbPrefillArgs A) {
     const uint32_t* words = reinterpret_cast<const uint32_t*>(S + P2_WORDS_OFF) + rg * 256 + (full ? lane : lane >> 1);
     read_b(S, st0, b0);
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-      reg[rt] = lb16_reg_word(words[64 * rt], sel) ^ (MODE == 2 && (hbits(sg, rt) & 0x8000u) ? 0xFFFFFFFFu : 0u);
+    for (int rt = 0; rt < ROWT; ++rt)
+      reg[rt] = lb16_reg_word(words[64 * rt], sel);
   };
-  auto mstep = [&](int c, int sg, int st, const f16x8* bb, const uint32_t* reg, const u32x4& gq, uint8_t* ahead,
-                   bool with_loads) {
+  // The A operand of step st: the weight's sign bit XORed into the scale's
+  // fp16 bits, +-g_k (GEMM 1: gq, per input) or +-h_i (GEMM 2: hp, per row).
+  auto mstep = [&](int c, int st, const f16x8* bb, const uint32_t* reg, const u32x4& gq, const uint32_t* hp,
+                   uint8_t* ahead, bool with_loads) {
     if (with_loads) issue(min(c + P2_STAGES - 1, C - 1), ahead);
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      f16x8 a;
-      if (MODE == 1) {
-        u32x4 d;
+    for (int rt = 0; rt < ROWT; ++rt) {
+      u32x4 d;
 #pragma unroll
-        for (int dd = 0; dd < 4; ++dd) d[dd] = ((reg[rt] << (4 * st + dd)) & sc.sign_mask) ^ gq[dd];
-        a = __builtin_bit_cast(f16x8, d);
-      } else {
-        a = lb16_step_operand_val(reg[rt], st, sc.sign_mask, (hbits(sg, rt) & 0x7FFFu) * 0x10001u);
-      }
+      for (int dd = 0; dd < 4; ++dd) d[dd] = ((reg[rt] << (4 * st + dd)) & sc.sign_mask) ^ (MODE == 1 ? gq[dd] : hp[rt]);
+      const f16x8 a = __builtin_bit_cast(f16x8, d);
 #pragma unroll
       for (int tt = 0; tt < 8; ++tt) acc[rt][tt] = mfma16(a, bb[tt], acc[rt][tt]);
     }
@@ -480,7 +490,7 @@ lb_prefill2_kernel(LbPrefillArgs A) {
     // (and the loads) spread between the products of the one before
     __builtin_amdgcn_sched_group_barrier(0x2, 8, 0);
 #pragma unroll
-    for (int i = 0; i < 24; ++i) {
+    for (int i = 0; i < 8 * (ROWT - 1); ++i) {
       __builtin_amdgcn_sched_group_barrier(0x8, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x2, 1, 0);
       if (with_loads && (i & 3) == 3 && i < 20) __builtin_amdgcn_sched_group_barrier(0x10, 1, 0);
@@ -508,7 +518,7 @@ lb_prefill2_kernel(LbPrefillArgs A) {
       __asm__ volatile("" ::: "memory");
     };
     f16x8 b0[8], b1[8];
-    uint32_t reg[4], regn[4] = {0u, 0u, 0u, 0u};
+    uint32_t reg[ROWT], regn[ROWT] = {};
     auto body = [&](int c, const uint8_t* S, const uint8_t* Snext, uint8_t* ahead) __attribute__((always_inline)) {
       int sg, p;
       bool full;
@@ -520,16 +530,18 @@ lb_prefill2_kernel(LbPrefillArgs A) {
         gq0 = *reinterpret_cast<const u32x4*>(S + P2_G_OFF + 2 * (32 * st0 + 8 * grp));
         gq1 = *reinterpret_cast<const u32x4*>(S + P2_G_OFF + 2 * (32 * (st0 + 1) + 8 * grp));
       }
+      uint32_t hp[ROWT];
+      if (MODE == 2) hpairs(sg, hp);
       __builtin_amdgcn_sched_barrier(0);  // keep those reads ahead of the first step's products
-      mstep(c, sg, st0, b0, reg, gq0, ahead, LOADS);
+      mstep(c, st0, b0, reg, gq0, hp, ahead, LOADS);
       // unconditional (after the last chunk it rereads that chunk's copy in
       // a stage nobody needs), so that every path to a read of a stage has
       // passed the same waits
       sync();
       head(min(c + 1, C - 1), Snext, b0, regn);
-      if (full) mstep(c, sg, st0 + 1, b1, reg, gq1, ahead, false);
+      if (full) mstep(c, st0 + 1, b1, reg, gq1, hp, ahead, false);
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) reg[rt] = regn[rt];
+      for (int rt = 0; rt < ROWT; ++rt) reg[rt] = regn[rt];
     };
     if (LOADS) {
       issue(0, stage0);
@@ -555,7 +567,8 @@ lb_prefill2_kernel(LbPrefillArgs A) {
   __syncthreads();
 
   // the second-half waves hand their sums to the first-half waves: row tiles
-  // 0..2 through the three stages, then row tile 3 through the first
+  // 0..2 through the three stages, then (4 tiles per wave) row tile 3
+  // through the first
   {
     f32x4* red0 = reinterpret_cast<f32x4*>(stage0) + rg * 512 + lane;
     f32x4* red1 = reinterpret_cast<f32x4*>(stage1) + rg * 512 + lane;
@@ -577,15 +590,17 @@ lb_prefill2_kernel(LbPrefillArgs A) {
         acc[2][tt] += red2[64 * tt];
       }
     }
-    __syncthreads();
-    if (kh == 1) {
+    if constexpr (ROWT == 4) {
+      __syncthreads();
+      if (kh == 1) {
 #pragma unroll
-      for (int tt = 0; tt < 8; ++tt) red0[64 * tt] = acc[3][tt];
-    }
-    __syncthreads();
-    if (kh == 0) {
+        for (int tt = 0; tt < 8; ++tt) red0[64 * tt] = acc[ROWT - 1][tt];
+      }
+      __syncthreads();
+      if (kh == 0) {
 #pragma unroll
-      for (int tt = 0; tt < 8; ++tt) acc[3][tt] += red0[64 * tt];
+        for (int tt = 0; tt < 8; ++tt) acc[ROWT - 1][tt] += red0[64 * tt];
+      }
     }
   }
 
@@ -593,7 +608,7 @@ lb_prefill2_kernel(LbPrefillArgs A) {
     const LbBranchArgs& B = B0;
     if (kh == 0) {
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
+      for (int rt = 0; rt < ROWT; ++rt) {
         const int tile = tile0 + rt;
         if (tile >= ntiles) continue;
         const int j0 = 16 * tile + 4 * grp;
@@ -613,7 +628,7 @@ lb_prefill2_kernel(LbPrefillArgs A) {
     }
     // the block holding the last row tile also zeroes this token block's
     // z entries between 16*ceil(r/16) and 128*ceil(r/128)
-    if (bt.bx == (ntiles - 1) >> 4) {
+    if (bt.bx == (ntiles - 1) / (4 * ROWT)) {
       const int j0 = 16 * ntiles, nz = 128 * ((B.r + 127) / 128) - j0;
       const int per_tok = nz >> 2;
       for (int e = threadIdx.x; e < per_tok * PF_BN; e += 64 * P2_WAVES) {
@@ -624,7 +639,7 @@ lb_prefill2_kernel(LbPrefillArgs A) {
     }
   } else if (kh == 0) {
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
+    for (int rt = 0; rt < ROWT; ++rt) {
       const int tile = tile0 + rt;
       if (tile >= ntiles) continue;
       const int i0 = 16 * tile + 4 * grp;
@@ -647,6 +662,24 @@ lb_prefill2_kernel(LbPrefillArgs A) {
   }
 }
 
+// Row tiles per wave of lb_prefill2_kernel for GEMM `mode`: 3 when 192-row
+// blocks take fewer rounds of one workgroup per compute unit times rows per
+// block than 256-row blocks (e.g. 2 x 92 tiles of the 7B layer's GEMM 1 at
+// 16 token blocks: 256 workgroups, one round of 3, instead of 192, one round
+// of 4), else 4.
+static int p2_rowt(const LbPrefillArgs& a, int mode, unsigned tb) {
+  int dev = 0, ncu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0)
+    return 4;
+  const long nz = mode == 1 ? a.nb : 1;
+  auto cost = [&](int rowt) {
+    const long wgs = (long)p2_row_blocks(a, mode, rowt) * tb * nz;
+    return (wgs + ncu - 1) / ncu * rowt;
+  };
+  return cost(3) < cost(4) ? 3 : 4;
+}
+
 hipError_t lb_launch_prefill(const LbPrefillArgs& a, hipStream_t stream) {
   const unsigned tb = (unsigned)((a.M + PF_BN - 1) / PF_BN);
   int maxt = 0;
@@ -659,8 +692,12 @@ hipError_t lb_launch_prefill(const LbPrefillArgs& a, hipStream_t stream) {
   hipError_t e;
   if (aligned_x && a.n % 128 == 0 && fits32(a.ldx, a.n)) {
     // v2: GEMM 1 over both branches, then GEMM 2 (one-dimensional grids, see p2_tile)
-    hipLaunchKernelGGL((lb_prefill2_kernel<1>), dim3((unsigned)(p2_row_blocks(a, 1) * tb * a.nb)),
-                       dim3(64 * P2_WAVES), 0, stream, a);
+    if (p2_rowt(a, 1, tb) == 3)
+      hipLaunchKernelGGL((lb_prefill2_kernel<1, 3>), dim3((unsigned)(p2_row_blocks(a, 1, 3) * tb * a.nb)),
+                         dim3(64 * P2_WAVES), 0, stream, a);
+    else
+      hipLaunchKernelGGL((lb_prefill2_kernel<1, 4>), dim3((unsigned)(p2_row_blocks(a, 1, 4) * tb * a.nb)),
+                         dim3(64 * P2_WAVES), 0, stream, a);
   } else {
     const dim3 g1((unsigned)((maxt + 7) / 8), tb, (unsigned)a.nb);
     if (a.n % 8 == 0 && aligned_x)
@@ -672,9 +709,12 @@ hipError_t lb_launch_prefill(const LbPrefillArgs& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   // GEMM 2 reads z (always 16-byte aligned, zero-padded to whole chunks)
   const int mt = (a.m + 15) >> 4;
-  if (fits32(a.zs, a.zs))
-    hipLaunchKernelGGL((lb_prefill2_kernel<2>), dim3((unsigned)(p2_row_blocks(a, 2) * tb)), dim3(64 * P2_WAVES), 0,
-                       stream, a);
+  if (fits32(a.zs, a.zs) && p2_rowt(a, 2, tb) == 3)
+    hipLaunchKernelGGL((lb_prefill2_kernel<2, 3>), dim3((unsigned)(p2_row_blocks(a, 2, 3) * tb)), dim3(64 * P2_WAVES),
+                       0, stream, a);
+  else if (fits32(a.zs, a.zs))
+    hipLaunchKernelGGL((lb_prefill2_kernel<2, 4>), dim3((unsigned)(p2_row_blocks(a, 2, 4) * tb)), dim3(64 * P2_WAVES),
+                       0, stream, a);
   else
     hipLaunchKernelGGL((lb_prefill_kernel<2, true>), dim3((unsigned)((mt + 7) / 8), tb, 1), dim3(PF_THREADS), 0,
                        stream, a);

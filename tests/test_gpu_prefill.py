@@ -133,6 +133,19 @@ def test_prefill_matches_decode(lb):
     _assert_parity(yp, yd.float().cpu().numpy().astype(np.float64), "prefill vs decode")
 
 
+@pytest.mark.parametrize("m,ranks,batch", [
+    (256, (1728, 1728), 2048),  # GEMM 1 in 256-row blocks (224 workgroups), GEMM 2 in 192-row blocks
+    (4000, (200, 1000), 300),   # both GEMMs in 192-row blocks, ragged last block and token block
+])
+def test_prefill_block_geometries(lb, m, ranks, batch):
+    """Both row-block heights of the main prefill kernels (the library picks
+    the one that fills the compute units in fewer rounds of rows)."""
+    print(f"[case] prefill geometry m={m} r={ranks} batch={batch}", flush=True)
+    br, x = synth.make_layer(synth.LayerShape("geometry", m, 256, ranks), batch=batch, seed=m + batch)
+    y = lb.littlebit_linear_fwd(_layer(lb, br), torch.from_numpy(x).cuda(), path=lb.LB_PATH_PREFILL)
+    _assert_parity(y, oracle.factored_forward(x, br), f"prefill geometry m={m} r={ranks} b={batch}")
+
+
 def test_prefill_chunked_beyond_8192_tokens(lb):
     print("[case] prefill 8200 tokens", flush=True)
     br, x = synth.make_layer(synth.LayerShape("long", 96, 128, (16, 16)), batch=8200, seed=4)
