@@ -329,10 +329,12 @@ __host__ __device__ inline int p2_row_blocks(const LbPrefillArgs& a, int mode, i
 }
 
 // ROWT: row tiles per wave (4, or 3 where 192-row blocks fill the machine
-// in fewer rounds of workgroups).
+// in fewer rounds of workgroups).  The launch covers row tiles tile_base..
+// in row_blocks blocks of 4 * ROWT tiles (a GEMM may be split into a launch
+// of 256-row blocks and one of 192-row blocks for the last round).
 template <int MODE, int ROWT>
 __global__ __launch_bounds__(64 * P2_WAVES, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void
-lb_prefill2_kernel(LbPrefillArgs A) {
+lb_prefill2_kernel(LbPrefillArgs A, int tile_base, int row_blocks) {
   static_assert(ROWT == 3 || ROWT == 4, "3 or 4 row tiles per wave");
   // global-to-LDS loads per chunk of a loading (first-half) wave: 8 x 1 KB
   // of activations, the sign bytes of its row group, (GEMM 1) g
@@ -344,9 +346,10 @@ lb_prefill2_kernel(LbPrefillArgs A) {
   const int rg = wave & 3, kh = wave >> 2;  // row group, half of each chunk
   const int grp = lane >> 4, col = lane & 15;
   const int M = A.M;
-  const P2Tile bt = p2_tile(p2_row_blocks(A, MODE, ROWT), (M + PF_BN - 1) / PF_BN, MODE == 1 ? A.nb : 1);
+  const P2Tile bt = p2_tile(row_blocks, (M + PF_BN - 1) / PF_BN, MODE == 1 ? A.nb : 1);
   const int tok0 = bt.by * PF_BN;
-  const int tile0 = 4 * ROWT * bt.bx + ROWT * rg;  // first row tile of this wave
+  const int blk0 = tile_base + 4 * ROWT * bt.bx;  // first row tile of this workgroup
+  const int tile0 = blk0 + ROWT * rg;             // first row tile of this wave
   const LbSignConsts sc = lb16_sign_consts();
 
   // the reduction as a sequence of 128-input chunks over one or two segments
@@ -354,7 +357,7 @@ lb_prefill2_kernel(LbPrefillArgs A) {
   const LbBranchArgs& B0 = A.br[b1];
   const LbBranchArgs& B1 = A.br[MODE == 2 && A.nb == 2 ? 1 : b1];
   const int ntiles = MODE == 1 ? (B0.r + 15) >> 4 : (A.m + 15) >> 4;
-  if (4 * ROWT * bt.bx >= ntiles) return;  // rows beyond this branch (uniform)
+  if (blk0 >= ntiles) return;  // rows beyond this branch (uniform)
   const int K0 = MODE == 1 ? A.n : B0.r, K1 = MODE == 1 ? A.n : B1.r;
   const int nu0 = lb16_units(K0), nu1 = lb16_units(K1);
   const int np0 = MODE == 1 ? A.n / 128 : (nu0 + 1) >> 1;
@@ -628,7 +631,7 @@ lb_prefill2_kernel(LbPrefillArgs A) {
     }
     // the block holding the last row tile also zeroes this token block's
     // z entries between 16*ceil(r/16) and 128*ceil(r/128)
-    if (bt.bx == (ntiles - 1) / (4 * ROWT)) {
+    if (blk0 <= ntiles - 1 && ntiles - 1 < blk0 + 4 * ROWT) {
       const int j0 = 16 * ntiles, nz = 128 * ((B.r + 127) / 128) - j0;
       const int per_tok = nz >> 2;
       for (int e = threadIdx.x; e < per_tok * PF_BN; e += 64 * P2_WAVES) {
@@ -662,22 +665,41 @@ lb_prefill2_kernel(LbPrefillArgs A) {
   }
 }
 
-// Row tiles per wave of lb_prefill2_kernel for GEMM `mode`: 3 when 192-row
-// blocks take fewer rounds of one workgroup per compute unit times rows per
-// block than 256-row blocks (e.g. 2 x 92 tiles of the 7B layer's GEMM 1 at
-// 16 token blocks: 256 workgroups, one round of 3, instead of 192, one round
-// of 4), else 4.
-static int p2_rowt(const LbPrefillArgs& a, int mode, unsigned tb) {
+static int p2_cu_count() {
   int dev = 0, ncu = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0)
-    return 4;
+    return 0;
+  return ncu;
+}
+
+// Row geometry of lb_prefill2_kernel for GEMM `mode`: the first `split`
+// row tiles (a multiple of 16) in 256-row blocks (4 tiles per wave), the
+// rest in 192-row blocks (3 tiles per wave), chosen to minimise the rounds
+// of one workgroup per compute unit weighted by rows per block.  Workgroups
+// of the same height take about the same time, and each launch's
+// workgroups start together, so a launch costs rounds x height.  E.g. the
+// 7B layer's GEMM 1 (2 x 92 tiles, 16 token blocks): all in 192-row blocks,
+// 256 workgroups, one round of 3 (against 192 workgroups, one round of 4);
+// its GEMM 2 (688 tiles): 512 tiles in 256-row blocks (2 rounds of 4), 176
+// in 192-row blocks (240 workgroups, 1 round of 3), against 3 rounds of 4.
+// GEMM 1 is never split (its last block also clears z's padding).
+static int p2_split(const LbPrefillArgs& a, int mode, unsigned tb) {
+  const int T = p2_row_tiles(a, mode), ncu = p2_cu_count();
   const long nz = mode == 1 ? a.nb : 1;
-  auto cost = [&](int rowt) {
-    const long wgs = (long)p2_row_blocks(a, mode, rowt) * tb * nz;
-    return (wgs + ncu - 1) / ncu * rowt;
+  if (ncu == 0) return T;
+  auto rounds = [&](long wgs) { return (wgs + ncu - 1) / ncu; };
+  auto cost = [&](int split) {
+    const long b4 = (split + 15) / 16, b3 = (T - split + 11) / 12;
+    return rounds(b4 * tb * nz) * 4 + rounds(b3 * tb * nz) * 3;
   };
-  return cost(3) < cost(4) ? 3 : 4;
+  int best = T;  // all in 256-row blocks
+  long bc = cost(T);
+  if (cost(0) < bc) best = 0, bc = cost(0);
+  if (mode == 2)
+    for (int sp = 16; sp < T; sp += 16)
+      if (cost(sp) < bc) best = sp, bc = cost(sp);
+  return best;
 }
 
 hipError_t lb_launch_prefill(const LbPrefillArgs& a, hipStream_t stream) {
@@ -692,12 +714,15 @@ hipError_t lb_launch_prefill(const LbPrefillArgs& a, hipStream_t stream) {
   hipError_t e;
   if (aligned_x && a.n % 128 == 0 && fits32(a.ldx, a.n)) {
     // v2: GEMM 1 over both branches, then GEMM 2 (one-dimensional grids, see p2_tile)
-    if (p2_rowt(a, 1, tb) == 3)
-      hipLaunchKernelGGL((lb_prefill2_kernel<1, 3>), dim3((unsigned)(p2_row_blocks(a, 1, 3) * tb * a.nb)),
-                         dim3(64 * P2_WAVES), 0, stream, a);
-    else
-      hipLaunchKernelGGL((lb_prefill2_kernel<1, 4>), dim3((unsigned)(p2_row_blocks(a, 1, 4) * tb * a.nb)),
-                         dim3(64 * P2_WAVES), 0, stream, a);
+    if (p2_split(a, 1, tb) == 0) {
+      const int rb = p2_row_blocks(a, 1, 3);
+      hipLaunchKernelGGL((lb_prefill2_kernel<1, 3>), dim3((unsigned)(rb * tb * a.nb)), dim3(64 * P2_WAVES), 0, stream,
+                         a, 0, rb);
+    } else {
+      const int rb = p2_row_blocks(a, 1, 4);
+      hipLaunchKernelGGL((lb_prefill2_kernel<1, 4>), dim3((unsigned)(rb * tb * a.nb)), dim3(64 * P2_WAVES), 0, stream,
+                         a, 0, rb);
+    }
   } else {
     const dim3 g1((unsigned)((maxt + 7) / 8), tb, (unsigned)a.nb);
     if (a.n % 8 == 0 && aligned_x)
@@ -709,13 +734,21 @@ hipError_t lb_launch_prefill(const LbPrefillArgs& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   // GEMM 2 reads z (always 16-byte aligned, zero-padded to whole chunks)
   const int mt = (a.m + 15) >> 4;
-  if (fits32(a.zs, a.zs) && p2_rowt(a, 2, tb) == 3)
-    hipLaunchKernelGGL((lb_prefill2_kernel<2, 3>), dim3((unsigned)(p2_row_blocks(a, 2, 3) * tb)), dim3(64 * P2_WAVES),
-                       0, stream, a);
-  else if (fits32(a.zs, a.zs))
-    hipLaunchKernelGGL((lb_prefill2_kernel<2, 4>), dim3((unsigned)(p2_row_blocks(a, 2, 4) * tb)), dim3(64 * P2_WAVES),
-                       0, stream, a);
-  else
+  if (fits32(a.zs, a.zs)) {
+    const int T = p2_row_tiles(a, 2), split = p2_split(a, 2, tb);
+    if (split > 0) {
+      const int rb = (split + 15) / 16;
+      hipLaunchKernelGGL((lb_prefill2_kernel<2, 4>), dim3((unsigned)(rb * tb)), dim3(64 * P2_WAVES), 0, stream, a, 0,
+                         rb);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    if (split < T) {
+      const int rb = (T - split + 11) / 12;
+      hipLaunchKernelGGL((lb_prefill2_kernel<2, 3>), dim3((unsigned)(rb * tb)), dim3(64 * P2_WAVES), 0, stream, a,
+                         split, rb);
+    }
+  } else
     hipLaunchKernelGGL((lb_prefill_kernel<2, true>), dim3((unsigned)((mt + 7) / 8), tb, 1), dim3(PF_THREADS), 0,
                        stream, a);
   return hipGetLastError();

@@ -136,12 +136,14 @@ def test_prefill_matches_decode(lb):
 @pytest.mark.parametrize("m,ranks,batch", [
     (256, (1728, 1728), 2048),  # GEMM 1 in 256-row blocks (224 workgroups), GEMM 2 in 192-row blocks
     (4000, (200, 1000), 300),   # both GEMMs in 192-row blocks, ragged last block and token block
+    (11008, (32, 32), 2048),    # GEMM 2 split: 512 row tiles in 256-row blocks, 176 in 192-row blocks
 ])
 def test_prefill_block_geometries(lb, m, ranks, batch):
     """Both row-block heights of the main prefill kernels (the library picks
     the one that fills the compute units in fewer rounds of rows)."""
     print(f"[case] prefill geometry m={m} r={ranks} batch={batch}", flush=True)
-    br, x = synth.make_layer(synth.LayerShape("geometry", m, 256, ranks), batch=batch, seed=m + batch)
+    n = 128 if m > 10000 else 256
+    br, x = synth.make_layer(synth.LayerShape("geometry", m, n, ranks), batch=batch, seed=m + batch)
     y = lb.littlebit_linear_fwd(_layer(lb, br), torch.from_numpy(x).cuda(), path=lb.LB_PATH_PREFILL)
     _assert_parity(y, oracle.factored_forward(x, br), f"prefill geometry m={m} r={ranks} b={batch}")
 
