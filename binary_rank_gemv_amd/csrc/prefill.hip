@@ -336,9 +336,6 @@ template <int MODE, int ROWT>
 __global__ __launch_bounds__(64 * P2_WAVES, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 lb_prefill2_kernel(LbPrefillArgs A, int tile_base, int row_blocks) {
   static_assert(ROWT == 3 || ROWT == 4, "3 or 4 row tiles per wave");
-  // global-to-LDS loads per chunk of a loading (first-half) wave: 8 x 1 KB
-  // of activations, the sign bytes of its row group, (GEMM 1) g
-  constexpr int kOps = MODE == 1 ? 10 : 9;
   __shared__ __align__(16) uint8_t stage0[P2_STAGE_BYTES];
   __shared__ __align__(16) uint8_t stage1[P2_STAGE_BYTES];
   __shared__ __align__(16) uint8_t stage2[P2_STAGE_BYTES];
@@ -388,39 +385,42 @@ lb_prefill2_kernel(LbPrefillArgs A, int tile_base, int row_blocks) {
   // lanes 48.. load a tile nobody reads), 16 per lane, for a full
   // pair (256 bytes per tile) and for a pair of one unit (128 bytes, each
   // half-row loaded twice so that the LDS copy keeps the full pair's
-  // addressing: byte 4j of a lane's word sits at 4*(lane/2)); g
-  // (slot i + 4 is 16 tokens further than slot i; past the last token it
-  // repeats slot i)
+  // addressing: byte 4j of a lane's word sits at 4*(lane/2)); g.  Wave
+  // (rg, kh) loads activation slots 8 rg + 4 kh + i (i < 4), tokens
+  // 32 rg + 16 kh .. + 15 of the block (past the last token: the last token)
   uint32_t aoff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int u = (rg * 8 + i) * 64 + lane;
+    const int u = (rg * 8 + 4 * kh + i) * 64 + lane;
     const int t = u >> 4, q = (u & 15) ^ (t & 15);
     aoff[i] = (uint32_t)(((long)min(tok0 + t, M - 1) * ld + 8 * q) * 2);
   }
-  const uint32_t aoff_step = (uint32_t)(32 * ld), aoff_end = (uint32_t)((long)M * ld * 2);
   const uint32_t row0 = (uint32_t)(min(tile0 + (lane >> 4), ntiles - 1) * lb16_tile_bytes(K0));
   const uint32_t row1 = (uint32_t)(min(tile0 + (lane >> 4), ntiles - 1) * lb16_tile_bytes(K1));
 
-  // loads of chunk c into stage S (all global-to-LDS), by the first-half
-  // waves only, so that while one wave of a SIMD waits on a full memory
-  // queue the other keeps the matrix core busy: activation slots
-  // 8rg..8rg+7, the sign bytes of row group rg, and (GEMM 1) g (lanes 16..
-  // repeat lanes 0..15; every loading wave writes the same bytes)
-  auto issue = [&](int c, uint8_t* S) {
+  // loads of chunk c into stage S (all global-to-LDS), shared by all waves
+  // so that no wave's matrix steps wait much longer on the memory queue
+  // than its partner's on the SIMD: 4 KB of activations each, the sign bytes
+  // of row group rg (first-half waves) and (GEMM 1, second-half waves) g
+  // (lanes 16.. repeat lanes 0..15; four waves write the same bytes).
+  auto issue = [&](auto khc, int c, uint8_t* S) {
+    constexpr int KH = decltype(khc)::value;
     const int sg = c >= np0 ? 1 : 0;
     const int p = c - (sg ? np0 : 0);
     const uint8_t* src = reinterpret_cast<const uint8_t*>(sg ? src1 : src0) + 256 * p;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      __builtin_amdgcn_global_load_lds(src + (i < 4 ? aoff[i] : aoff[i - 4] + aoff_step < aoff_end ? aoff[i - 4] + aoff_step : aoff[i - 4]),
-                                       (__attribute__((address_space(3))) void*)(S + (rg * 8 + i) * 1024), 16, 0, 0);
-    const bool full = 2 * p + 1 < (sg ? nu1 : nu0);
-    const uint8_t* wsrc = (sg ? bits1 : bits0) + 256 * p + (sg ? row1 : row0) + 16 * (lane & (full ? 15 : 7));
-    __builtin_amdgcn_global_load_lds(wsrc, (__attribute__((address_space(3))) void*)(S + P2_WORDS_OFF + rg * 1024), 16, 0, 0);
-    if (MODE == 1)
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds(src + aoff[i], (__attribute__((address_space(3))) void*)(S + (rg * 8 + 4 * KH + i) * 1024),
+                                       16, 0, 0);
+    if (KH == 0) {
+      const bool full = 2 * p + 1 < (sg ? nu1 : nu0);
+      const uint8_t* wsrc = (sg ? bits1 : bits0) + 256 * p + (sg ? row1 : row0) + 16 * (lane & (full ? 15 : 7));
+      __builtin_amdgcn_global_load_lds(wsrc, (__attribute__((address_space(3))) void*)(S + P2_WORDS_OFF + rg * 1024), 16,
+                                       0, 0);
+    } else if (MODE == 1) {
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(gsrc) + 256 * p + 16 * (lane & 15),
                                        (__attribute__((address_space(3))) void*)(S + P2_G_OFF), 16, 0, 0);
+    }
   };
 
   f32x4 acc[ROWT][8];
@@ -477,9 +477,9 @@ lb_prefill2_kernel(LbPrefillArgs A, int tile_base, int row_blocks) {
   };
   // The A operand of step st: the weight's sign bit XORed into the scale's
   // fp16 bits, +-g_k (GEMM 1: gq, per input) or +-h_i (GEMM 2: hp, per row).
-  auto mstep = [&](int c, int st, const f16x8* bb, const uint32_t* reg, const u32x4& gq, const uint32_t* hp,
+  auto mstep = [&](auto khc, int c, int st, const f16x8* bb, const uint32_t* reg, const u32x4& gq, const uint32_t* hp,
                    uint8_t* ahead, bool with_loads) {
-    if (with_loads) issue(min(c + P2_STAGES - 1, C - 1), ahead);
+    if (with_loads) issue(khc, min(c + P2_STAGES - 1, C - 1), ahead);
 #pragma unroll
     for (int rt = 0; rt < ROWT; ++rt) {
       u32x4 d;
@@ -502,21 +502,21 @@ lb_prefill2_kernel(LbPrefillArgs A, int tile_base, int row_blocks) {
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // A loading wave waits until its loads of the next chunk have landed (those
-  // of the chunk after may still be in flight), every wave until its LDS
-  // reads have; then all meet (the empty asm keeps LDS reads below the
-  // barrier).  Every first step of a loading wave issues loads, past the end
-  // as repeats of the last chunk into a stage nobody reads again, so the wait
-  // count is a constant; the loading and the other waves run separate copies
-  // of the loop, so that no branch separates a load from its waits.
-  auto run = [&](auto loads) __attribute__((always_inline)) {
-    constexpr bool LOADS = decltype(loads)::value;
+  // A wave waits until its loads of the next chunk and its LDS reads have
+  // landed (its loads of the chunk after may still be in flight); then all
+  // meet (the empty asm keeps LDS reads below the barrier).  Every first step
+  // issues loads, past the end as repeats of the last chunk into a stage
+  // nobody reads again, so the wait count is a constant; the two halves'
+  // waves (different loads) run separate copies of the loop, so that no
+  // branch separates a load from its waits.
+  auto run = [&](auto khc) __attribute__((always_inline)) {
+    constexpr int KH = decltype(khc)::value;
+    // global-to-LDS loads per chunk of this wave: 4 of activations, the sign
+    // bytes (first half) or g (second half, GEMM 1)
+    constexpr int kOps = 4 + (KH == 0 || MODE == 1 ? 1 : 0);
     constexpr int kWait = kOps * (P2_STAGES - 2);
     auto sync = [&]() __attribute__((always_inline)) {
-      if (LOADS)
-        __builtin_amdgcn_s_waitcnt((kWait & 15) | ((kWait >> 4) << 14) | (7 << 4));
-      else
-        __builtin_amdgcn_s_waitcnt((15 | (3 << 14)) | (7 << 4));
+      __builtin_amdgcn_s_waitcnt((kWait & 15) | ((kWait >> 4) << 14) | (7 << 4));
       __builtin_amdgcn_s_barrier();
       __asm__ volatile("" ::: "memory");
     };
@@ -536,20 +536,18 @@ lb_prefill2_kernel(LbPrefillArgs A, int tile_base, int row_blocks) {
       uint32_t hp[ROWT];
       if (MODE == 2) hpairs(sg, hp);
       __builtin_amdgcn_sched_barrier(0);  // keep those reads ahead of the first step's products
-      mstep(c, st0, b0, reg, gq0, hp, ahead, LOADS);
+      mstep(khc, c, st0, b0, reg, gq0, hp, ahead, true);
       // unconditional (after the last chunk it rereads that chunk's copy in
       // a stage nobody needs), so that every path to a read of a stage has
       // passed the same waits
       sync();
       head(min(c + 1, C - 1), Snext, b0, regn);
-      if (full) mstep(c, st0 + 1, b1, reg, gq1, hp, ahead, false);
+      if (full) mstep(khc, c, st0 + 1, b1, reg, gq1, hp, ahead, false);
 #pragma unroll
       for (int rt = 0; rt < ROWT; ++rt) reg[rt] = regn[rt];
     };
-    if (LOADS) {
-      issue(0, stage0);
-      issue(min(1, C - 1), stage1);
-    }
+    issue(khc, 0, stage0);
+    issue(khc, min(1, C - 1), stage1);
     sync();
     head(0, stage0, b0, reg);
     int c = 0;
@@ -562,9 +560,9 @@ lb_prefill2_kernel(LbPrefillArgs A, int tile_base, int row_blocks) {
     if (c + 1 < C) body(c + 1, stage1, stage2, stage0);
   };
   if (kh == 0)
-    run(std::integral_constant<bool, true>());
+    run(std::integral_constant<int, 0>());
   else
-    run(std::integral_constant<bool, false>());
+    run(std::integral_constant<int, 1>());
   // every load has landed and every wave is past its reads: the stages are free
   __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
   __syncthreads();
