@@ -294,6 +294,38 @@ def test_llama2_13b_block_several_tokens(lb, setting, batch):
         assert torch.equal(ys[i], y2), f"13B {setting} b={batch} {shape.name}: block and two-launch differ"
 
 
+@pytest.mark.parametrize("ranks", [
+    # gate/up with 12 pairs per branch (3 per wave in phase B), the others 6-8
+    {"attn": (688, 112), "mlp": (1472, 168), "down": (1008, 1008)},
+    # one-branch layers among the two-branch ones
+    {"attn": (688,), "mlp": (1008, 168), "down": (256,)},
+])
+def test_block_one_token_mixed_ranks(lb, ranks):
+    """A seven-projection call at one token on smaller dimensions with mixed
+    ranks and branch counts: every projection against the oracle, and equal
+    bit for bit to the same projection's two-launch call."""
+    print(f"[case] block one token ranks {ranks}", flush=True)
+    d, f = 1024, 2816
+    shapes = [synth.LayerShape(nm, mm, nn, ranks[key]) for nm, mm, nn, key in (
+        ("q", d, d, "attn"), ("k", d, d, "attn"), ("v", d, d, "attn"), ("o", d, d, "attn"),
+        ("gate", f, d, "mlp"), ("up", f, d, "mlp"), ("down", d, f, "down"))]
+    rng = np.random.default_rng(11)
+    layers = [synth.make_branches(sh, rng) for sh in shapes]
+    xs = (synth.make_tokens(1, d, rng), synth.make_tokens(1, d, rng), synth.make_tokens(1, d, rng),
+          synth.make_tokens(1, f, rng))
+    dev_layers = [_layer(lb, br) for br in layers]
+    xt = [torch.from_numpy(a).cuda() for a in xs]
+    ws = torch.zeros((lb.littlebit_block_workspace_bytes(dev_layers, 1),), dtype=torch.uint8, device="cuda")
+    ys = lb.littlebit_block_fwd(dev_layers, *xt, workspace=ws)
+    torch.cuda.synchronize()
+    assert int(ws[2048:2052].cpu().view(torch.int32)) == 0, "z poll spin limit hit"
+    for i, (shape, br) in enumerate(zip(shapes, layers)):
+        xi = synth.block_inputs_for(i, xs)
+        _assert_parity(ys[i], oracle.factored_forward(xi, br), f"block {shape.name} {ranks}")
+        y2 = lb.littlebit_linear_fwd(dev_layers[i], torch.from_numpy(xi).cuda(), path=lb.LB_DECODE_TWO_LAUNCHES)
+        assert torch.equal(ys[i], y2), f"block {shape.name} {ranks}: block and two-launch differ"
+
+
 @pytest.mark.parametrize("setting", ["0.55", "0.1"])
 def test_llama2_13b_block(lb, setting):
     print(f"[case] 13b block {setting}", flush=True)
