@@ -605,9 +605,51 @@ lb_prefill2_kernel(LbPrefillArgs A, int tile_base, int row_blocks) {
     }
   }
 
+  // Blocks wholly inside the rows (m, or the branch's r in GEMM 1), with the
+  // output and its row pitch 16-byte aligned, store through LDS
+  // (workgroup-uniform): the first-half waves place their rows of every
+  // token (fp16) in a token-major tile, tokens 0..63 in stage 0 and 64..127
+  // in stage 1, then all waves store whole 16-byte pieces of each token's
+  // contiguous run of rows, instead of 8-byte pieces 16 tokens apart.
+  uint16_t* const out = MODE == 1 ? A.z + B0.zoff : A.y;
+  const long ldo = MODE == 1 ? A.zs : A.ldy;
+  const bool whole_rows = blk0 + 4 * ROWT <= ntiles && 16 * blk0 + 64 * ROWT <= (MODE == 1 ? B0.r : A.m) &&
+                          (ldo & 7) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0;
+  constexpr int RS = 64 * ROWT + 8;  // halves per staged token (16 more: banks staggered)
+  static_assert(64 * RS * 2 <= P2_STAGE_BYTES, "half the staged tile fits a stage");
+  auto store_staged = [&](auto value) {
+    __syncthreads();  // every reader of the reduction buffers is done
+    if (kh == 0) {
+#pragma unroll
+      for (int rt = 0; rt < ROWT; ++rt) {
+        const int lr = 16 * (ROWT * rg + rt) + 4 * grp;
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt) {
+          uint16_t v[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] = value(rt, tt, q);
+          uint8_t* st = tt < 4 ? stage0 : stage1;
+          *reinterpret_cast<uint2*>(st + 2 * ((16 * (tt & 3) + col) * RS + lr)) = *reinterpret_cast<uint2*>(v);
+        }
+      }
+    }
+    __syncthreads();
+    constexpr int CPT = 8 * ROWT;  // 16-byte pieces per token
+    const int row0 = 16 * blk0;
+    for (int e = threadIdx.x; e < PF_BN * CPT; e += 64 * P2_WAVES) {
+      const int t = e / CPT, j = e - t * CPT;
+      if (tok0 + t < M) {
+        const uint8_t* st = t < 64 ? stage0 : stage1;
+        *reinterpret_cast<uint4*>(out + (long)(tok0 + t) * ldo + row0 + 8 * j) =
+            *reinterpret_cast<const uint4*>(st + 2 * ((t & 63) * RS + 8 * j));
+      }
+    }
+  };
+  if (MODE == 1 && whole_rows)
+    store_staged([&](int rt, int tt, int q) { return f2h(h2f(B0.l[16 * (tile0 + rt) + 4 * grp + q]) * acc[rt][tt][q]); });
   if (MODE == 1) {
     const LbBranchArgs& B = B0;
-    if (kh == 0) {
+    if (kh == 0 && !whole_rows) {
 #pragma unroll
       for (int rt = 0; rt < ROWT; ++rt) {
         const int tile = tile0 + rt;
@@ -638,6 +680,8 @@ lb_prefill2_kernel(LbPrefillArgs A, int tile_base, int row_blocks) {
           *reinterpret_cast<uint2*>(A.z + (long)tok * A.zs + B.zoff + j0 + 4 * (e % per_tok)) = make_uint2(0u, 0u);
       }
     }
+  } else if (whole_rows) {
+    store_staged([&](int rt, int tt, int q) { return f2h(acc[rt][tt][q]); });
   } else if (kh == 0) {
 #pragma unroll
     for (int rt = 0; rt < ROWT; ++rt) {
