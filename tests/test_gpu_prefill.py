@@ -86,6 +86,22 @@ def test_prefill_strided_unaligned_rows(lb):
     assert (ybig[:, :3] == 7.0).all() and (ybig[:, 259:] == 7.0).all()
 
 
+@pytest.mark.parametrize("col0,width", [(8, 528), (3, 517)])
+def test_prefill_output_views(lb, col0, width):
+    """The main prefill kernels writing into a view of a wider output: a
+    16-byte aligned start and row pitch (rows stored through LDS as whole
+    16-byte pieces), and an odd start and pitch (direct stores).  Every value
+    matches the oracle and nothing outside the view is written."""
+    print(f"[case] prefill output view col0={col0} width={width}", flush=True)
+    m, n, batch = 512, 256, 200
+    br, x = synth.make_layer(synth.LayerShape("view", m, n, (64, 96)), batch=batch, seed=col0 + width)
+    ybig = torch.full((batch, width), 7.0, dtype=torch.float16, device="cuda")
+    lb.littlebit_linear_fwd(_layer(lb, br), torch.from_numpy(x).cuda(), out=ybig[:, col0:col0 + m],
+                            path=lb.LB_PATH_PREFILL)
+    _assert_parity(ybig[:, col0:col0 + m], oracle.linear_forward(x, br), f"prefill view col0={col0}")
+    assert (ybig[:, :col0] == 7.0).all() and (ybig[:, col0 + m:] == 7.0).all()
+
+
 def test_prefill_branch_masks(lb):
     print("[case] prefill branch masks", flush=True)
     br, x = synth.make_layer(synth.LayerShape("mask", 300, 512, (48, 72)), batch=33, seed=3)
