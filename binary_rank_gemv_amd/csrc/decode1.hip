@@ -79,7 +79,8 @@ extern "C" int littlebit_phase_stamps_set(void* p) {
 #define DK_WAVES 8
 #define DK_THREADS (64 * DK_WAVES)
 #define DK_VPW 8   // V-pass pairs per wave per batch of sign words
-#define DK_UTG 8   // U tiles per group (one epilogue)
+#define DK_UTG 8   // U tiles per group (one epilogue), at most; launches whose
+                   // workgroups hold at most 4 U tiles use groups of 4
 #define DK_UPW 4   // U-pass pairs per wave per block of sign words
 
 namespace {
@@ -649,23 +650,26 @@ __device__ __forceinline__ void u_role1(const SL& L, int wave, int& b, int& p0, 
   }
 }
 
-// A block of U sign words: tiles [t0, t0 + nt) of one layer, this wave's pairs
-// [pc, pc + DK_UPW) of its range (clamped loads keep the wait counts static).
+// A block of U sign words: tiles [t0, t0 + nt) of one layer (nt <= UTG),
+// this wave's pairs [pc, pc + DK_UPW) of its range (clamped loads keep the
+// wait counts static).
+template <int UTG>
 struct UBlock {
-  uint32_t w[DK_UTG][DK_UPW];
+  uint32_t w[UTG][DK_UPW];
 };
 
 // Row scales (fp16 bits) of this thread's epilogue entry of a group of tiles
-// [t0, t0 + nt): tile (tid / 16) % DK_UTG, row tid % 16, clamped to a valid
+// [t0, t0 + nt): tile (tid / 16) % UTG, row tid % 16, clamped to a valid
 // row (threads beyond the group's entries never store).  Unconditional loads,
 // so no wait is placed at a branch join.
 struct HPair {
   uint32_t h0, h1;
 };
 
+template <int UTG>
 __device__ __forceinline__ HPair load_group_h(const SL& L, int t0, int nt) {
   const int tid = threadIdx.x;
-  const int row = min(16 * (t0 + min((tid >> 4) % DK_UTG, nt - 1)) + (tid & 15), L.m - 1);
+  const int row = min(16 * (t0 + min((tid >> 4) % UTG, nt - 1)) + (tid & 15), L.m - 1);
   const uint16_t* h1p = L.nb == 2 ? L.h1 : L.h0;
   HPair h;
   h.h0 = L.h0[row];
@@ -684,9 +688,10 @@ __device__ __forceinline__ void load_utile(const SL& L, int b, int t0, int nt, i
   for (int i = 0; i < DK_UPW; ++i) w[i] = pair_word(tile, min(pc + i, plast), nu);
 }
 
-__device__ __forceinline__ void load_ublock(const SL& L, int b, int t0, int nt, int pc, int p1, UBlock& U) {
+template <int UTG>
+__device__ __forceinline__ void load_ublock(const SL& L, int b, int t0, int nt, int pc, int p1, UBlock<UTG>& U) {
 #pragma unroll
-  for (int k = 0; k < DK_UTG; ++k) load_utile(L, b, t0, nt, pc, p1, k, U.w[k]);
+  for (int k = 0; k < UTG; ++k) load_utile(L, b, t0, nt, pc, p1, k, U.w[k]);
 }
 
 // The same block straight into LDS (no registers held while it is in
@@ -694,38 +699,43 @@ __device__ __forceinline__ void load_ublock(const SL& L, int b, int t0, int nt, 
 // layout, to dst + 64 DK_UPW k with one 16-byte load per lane, bounded by
 // the tile (lanes beyond it read zeros).  Word (k, i) of a lane is then
 // dst[64 (DK_UPW k + i) + lane] (lane / 2 for an odd last unit), as
-// pair_word reads it from memory.
+// pair_word reads it from memory.  The copy's cost grows with its tiles
+// (UTG of them, a group's last tile repeated past nt): a launch whose
+// workgroups hold at most 4 U tiles copies 4, not 8.
+template <int UTG>
 __device__ __forceinline__ void dma_ublock(const SL& L, int b, int t0, int nt, int pc, uint32_t* dst) {
   static_assert(DK_UPW == 4, "one 16-byte load per lane and tile");
   const int r = L.r(b), lane = threadIdx.x & 63;
   const long tb = lb16_tile_bytes(r);
 #pragma unroll
-  for (int k = 0; k < DK_UTG; ++k) {
+  for (int k = 0; k < UTG; ++k) {
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(L.ub(b) + (long)(t0 + min(k, nt - 1)) * tb, (int)tb);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + 64 * DK_UPW * k),
                                              16, 256 * pc + 16 * lane, 0, 0, 0);
   }
 }
 
-__device__ __forceinline__ void lds_ublock(const uint32_t* src, int pc, int nu, UBlock& U) {
+template <int UTG>
+__device__ __forceinline__ void lds_ublock(const uint32_t* src, int pc, int nu, UBlock<UTG>& U) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int i = 0; i < DK_UPW; ++i) {
     const int li = 2 * (pc + i) + 1 < nu ? lane : lane >> 1;
 #pragma unroll
-    for (int k = 0; k < DK_UTG; ++k) U.w[k][i] = src[64 * (DK_UPW * k + i) + li];
+    for (int k = 0; k < UTG; ++k) U.w[k][i] = src[64 * (DK_UPW * k + i) + li];
   }
 }
 
 // The h epilogue of a group: cross-wave sums in wave order, y = h0 s0 + h1 s1.
 // acc[j] holds tiles 2j (column 0) and 2j + 1 (column 1).
-__device__ __forceinline__ void u_epilogue(const SL& L, int t0, int nt, const f32x4 (&acc)[DK_UTG / 2],
+template <int UTG>
+__device__ __forceinline__ void u_epilogue(const SL& L, int t0, int nt, const f32x4 (&acc)[UTG / 2],
                                            float (*red)[DK_WAVES][16], uint32_t h0raw, uint32_t h1raw) {
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int col = lane & 15;
   if (col < 2) {
 #pragma unroll
-    for (int j = 0; j < DK_UTG / 2; ++j)
+    for (int j = 0; j < UTG / 2; ++j)
       if (2 * j + col < nt)
 #pragma unroll
         for (int q = 0; q < 4; ++q) red[2 * j + col][wave][4 * (lane >> 4) + q] = acc[j][q];
@@ -783,7 +793,7 @@ __device__ __forceinline__ const LbDecodeArgs* dk1_kernarg_args() {
 // ranges vt_begin / ut_begin of the argument block (two launches: vq/vr,
 // uq/ur).  TPU: 16-rank tiles per unit of V work (1, or 2 on one
 // instruction: the host takes 2 when there are more tiles than workgroups).
-template <int MODE, bool SINGLE, int TPU>
+template <int MODE, bool SINGLE, int TPU, int UTG = DK_UTG>
 __global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* pre_vb0, const uint8_t* pre_vb1,
                                                                 const uint16_t* pre_x, const uint16_t* pre_g0,
                                                                 const uint16_t* pre_g1, uint8_t* sync, int pre_n,
@@ -881,7 +891,7 @@ __global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* p
     GroupInfo g;
     g.li = u_layer1<SINGLE>(A, t, g.tile);
     const int lend = SINGLE ? ut1 : min(ut1, rfl(A.ut_end[g.li]));
-    g.nt = min(DK_UTG, lend - t);
+    g.nt = min(UTG, lend - t);
     u_role1(L, wave, g.b, g.p0, g.p1);
     g.nch = max(1, (g.p1 - g.p0 + DK_UPW - 1) / DK_UPW);
     return g;
@@ -897,7 +907,7 @@ __global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* p
   // workgroup without U tiles copies a stand-in (the start of the workspace
   // header, as one 16-row tile of one unit) instead: the loads stay
   // unconditional, which keeps the compiler's waits for earlier loads exact.
-  UBlock cur;
+  UBlock<UTG> cur;
   const bool have_u = ut0 < ut1;
   SL uL = {};
   GroupInfo ug = {};
@@ -914,8 +924,8 @@ __global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* p
   auto issue_first_u = [&]() {
     if (MODE != 0) {
       compiler_memory_barrier();
-      dma_ublock(uL, ug.b, ug.tile, ug.nt, ug.p0, ublk[wave]);
-      hcur = load_group_h(uL, ug.tile, ug.nt);
+      dma_ublock<UTG>(uL, ug.b, ug.tile, ug.nt, ug.p0, ublk[wave]);
+      hcur = load_group_h<UTG>(uL, ug.tile, ug.nt);
       compiler_memory_barrier();
     }
   };
@@ -1000,7 +1010,7 @@ __global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* p
   for (int t = vt0 + 1; t < vt1; ++t) v_step(t);
 
   // ---------------- phase B
-  // Groups of up to DK_UTG tiles of one layer; each wave runs its pair range
+  // Groups of up to UTG tiles of one layer; each wave runs its pair range
   // [p0, p1) of its branch in blocks of DK_UPW pairs, whose sign words are
   // loaded one block ahead, with the group's row scales.
   //
@@ -1041,12 +1051,12 @@ __global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* p
     }
     const uint16_t* zb = dyn + L.zoff(g.b);
     const HPair hg = hcur;  // this group's row scales (loaded with its first block)
-    f32x4 acc[DK_UTG / 2], acc1[DK_UTG / 2];  // tile pairs (2j, 2j + 1)
+    f32x4 acc[UTG / 2], acc1[UTG / 2];  // tile pairs (2j, 2j + 1)
 #pragma unroll
-    for (int j = 0; j < DK_UTG / 2; ++j) acc[j] = acc1[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < UTG / 2; ++j) acc[j] = acc1[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int c = 0; c < g.nch; ++c) {
       // the next block's words: this group's next chunk, or the next group's first
-      UBlock nxt;
+      UBlock<UTG> nxt;
       bool more = false;
       if (c + 1 < g.nch) {
         load_ublock(L, g.b, g.tile, g.nt, g.p0 + (c + 1) * DK_UPW, g.p1, nxt);
@@ -1055,7 +1065,7 @@ __global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* p
         const SL Ln = layer_rec(layer_of_u(t + g.nt));
         const GroupInfo h = group_at(t + g.nt, Ln);
         load_ublock(Ln, h.b, h.tile, h.nt, h.p0, h.p1, nxt);
-        hcur = load_group_h(Ln, h.tile, h.nt);  // the next group's
+        hcur = load_group_h<UTG>(Ln, h.tile, h.nt);  // the next group's
         more = true;
       }
       const int pc = g.p0 + c * DK_UPW;
@@ -1066,7 +1076,7 @@ __global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* p
           const bool two = 2 * p + 1 < nu;
           const PairAct za = load_pair_act(zb + 128 * p, two);
 #pragma unroll
-          for (int j = 0; j < DK_UTG / 2; ++j)
+          for (int j = 0; j < UTG / 2; ++j)
             if (2 * j < g.nt)  // (for an odd count the last tile pairs with itself: load_ublock clamps)
               pair_products2(za, pair_bits(late(cur.w[2 * j][i]), two), pair_bits(late(cur.w[2 * j + 1][i]), two), two,
                              B, acc[j], acc1[j]);
@@ -1075,10 +1085,10 @@ __global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* p
       if (more) cur = nxt;
     }
 #pragma unroll
-    for (int j = 0; j < DK_UTG / 2; ++j) acc[j] += acc1[j];
+    for (int j = 0; j < UTG / 2; ++j) acc[j] += acc1[j];
     if (t == ut0) LB_STAMP(5);
     if (t == ut0) LB_WSTAMP(1);
-    u_epilogue(L, g.tile, g.nt, acc, ured[grp & 1], late(hg.h0), late(hg.h1));
+    u_epilogue<UTG>(L, g.tile, g.nt, acc, ured[grp & 1], late(hg.h0), late(hg.h1));
     ++grp;
     t += g.nt;
   }
@@ -1104,21 +1114,37 @@ typedef void (*Decode1Kernel)(const uint8_t*, const uint8_t*, const uint16_t*, c
                              uint8_t*, int, uint32_t, LbDecodeArgs);
 
 // The instantiation for a launch: one or several layers, one or two V tiles
-// per unit.
+// per unit, U groups of 4 tiles (small: no workgroup holds more than 4 U
+// tiles) or 8.
 template <int MODE>
-Decode1Kernel decode1_variant(bool single, bool one) {
+Decode1Kernel decode1_variant(bool single, bool one, bool small = false) {
+  if constexpr (MODE != 0) {
+    if (small && single) return one ? lb_decode1_kernel<MODE, true, 1, 4> : lb_decode1_kernel<MODE, true, 2, 4>;
+    if (small) return one ? lb_decode1_kernel<MODE, false, 1, 4> : lb_decode1_kernel<MODE, false, 2, 4>;
+  }
   if (single) return one ? lb_decode1_kernel<MODE, true, 1> : lb_decode1_kernel<MODE, true, 2>;
   return one ? lb_decode1_kernel<MODE, false, 1> : lb_decode1_kernel<MODE, false, 2>;
+}
+
+// Whether every workgroup's U tiles fit one group of 4: q + (r > 0) per
+// workgroup for an even split, or the largest range of a cost-balanced one.
+static bool decode1_small_groups(const LbDecodeArgs& a, int G, bool single) {
+  if (single || G == 0) return a.uq + (a.ur > 0 ? 1 : 0) <= 4;
+  int mx = 0;
+  for (int w = 0; w < G; ++w) mx = a.ut_begin[w + 1] - a.ut_begin[w] > mx ? a.ut_begin[w + 1] - a.ut_begin[w] : mx;
+  return mx <= 4;
 }
 
 // Workgroups of a single launch that fit at once, for the given dynamic LDS
 // (the lower count of the two V unit sizes).
 hipError_t lb_decode1_occupancy(bool single, size_t lds, int& occ) {
-  int o1 = 0, o2 = 0;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o1, decode1_variant<2>(single, true), DK_THREADS, lds);
-  if (e == hipSuccess)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o2, decode1_variant<2>(single, false), DK_THREADS, lds);
-  occ = o1 < o2 ? o1 : o2;
+  int o[4] = {0, 0, 0, 0};
+  hipError_t e = hipSuccess;
+  for (int i = 0; i < 4 && e == hipSuccess; ++i)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o[i], decode1_variant<2>(single, (i & 1) != 0, i >= 2),
+                                                     DK_THREADS, lds);
+  occ = o[0];
+  for (int i = 1; i < 4; ++i) occ = o[i] < occ ? o[i] : occ;
   return e;
 }
 
@@ -1153,8 +1179,8 @@ hipError_t lb_launch_decode1(const LbDecodeArgs& args, int G, void* sync, hipStr
     a.uq = a.nut / G;
     a.ur = a.nut % G;
     if (a.vq > 255 || a.vr > 255) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(decode1_variant<2>(single, one), dim3(G), dim3(DK_THREADS), lds, stream, vb0, vb1, px, g0, g1,
-                       sy, pn, single ? misc(a.vq, a.vr) : 0u, a);
+    hipLaunchKernelGGL(decode1_variant<2>(single, one, decode1_small_groups(a, G, single)), dim3(G), dim3(DK_THREADS),
+                       lds, stream, vb0, vb1, px, g0, g1, sy, pn, single ? misc(a.vq, a.vr) : 0u, a);
     return hipGetLastError();
   }
   a.vq = 1;
@@ -1171,7 +1197,8 @@ hipError_t lb_launch_decode1(const LbDecodeArgs& args, int G, void* sync, hipStr
   a.uq = a.nut / gb;
   a.ur = a.nut % gb;
   // (the U launch does no V work: one instantiation per layer count)
-  hipLaunchKernelGGL(decode1_variant<1>(single, false), dim3(gb), dim3(DK_THREADS), lds, stream, vb0, vb1, px, g0, g1,
+  hipLaunchKernelGGL(decode1_variant<1>(single, false, decode1_small_groups(a, 0, true)), dim3(gb), dim3(DK_THREADS),
+                     lds, stream, vb0, vb1, px, g0, g1,
                      sy, pn, single ? misc(0, 0) : 0u, a);
   return hipGetLastError();
 }
