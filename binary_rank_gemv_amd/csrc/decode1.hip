@@ -695,34 +695,41 @@ __device__ __forceinline__ void load_ublock(const SL& L, int b, int t0, int nt, 
 }
 
 // The same block straight into LDS (no registers held while it is in
-// flight): tile k's pairs [pc, pc + DK_UPW), 1 KB contiguous in the LB16
-// layout, to dst + 64 DK_UPW k with one 16-byte load per lane, bounded by
-// the tile (lanes beyond it read zeros).  Word (k, i) of a lane is then
-// dst[64 (DK_UPW k + i) + lane] (lane / 2 for an odd last unit), as
-// pair_word reads it from memory.  The copy's cost grows with its tiles
-// (UTG of them, a group's last tile repeated past nt): a launch whose
-// workgroups hold at most 4 U tiles copies 4, not 8.
-template <int UTG>
+// flight): tile k's pairs [pc, pc + PPT), contiguous in the LB16 layout, to
+// dst + 64 PPT k with one 16-byte load per lane, 4 / PPT tiles per load
+// (lanes 16 PPT j .. take tile k + j).  Word (k, i) of a lane is then
+// dst[64 (PPT k + i) + lane] (lane / 2 for an odd last unit), as pair_word
+// reads it from memory.  The copy costs in proportion to its bytes, so it
+// takes UTG tiles (a group's last tile repeated past nt; groups of 4 where no
+// workgroup holds more) and PPT pairs of each (2 where no wave's range is
+// longer, else 4).  Reads are bounded by the end of the factor.
+template <int UTG, int PPT>
 __device__ __forceinline__ void dma_ublock(const SL& L, int b, int t0, int nt, int pc, uint32_t* dst) {
-  static_assert(DK_UPW == 4, "one 16-byte load per lane and tile");
+  static_assert(PPT == 2 || PPT == 4, "2 or 4 pairs per tile");
+  constexpr int TPL = 4 / PPT;  // tiles per load
   const int r = L.r(b), lane = threadIdx.x & 63;
   const long tb = lb16_tile_bytes(r);
+  const int ntf = (L.m + 15) >> 4;
 #pragma unroll
-  for (int k = 0; k < UTG; ++k) {
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(L.ub(b) + (long)(t0 + min(k, nt - 1)) * tb, (int)tb);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + 64 * DK_UPW * k),
-                                             16, 256 * pc + 16 * lane, 0, 0, 0);
+  for (int k = 0; k < UTG; k += TPL) {
+    const int ta = t0 + min(k, nt - 1), tl = t0 + min(k + lane / (16 * PPT), nt - 1);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(L.ub(b) + (long)ta * tb, (int)((ntf - ta) * tb));
+    const int off = (int)((tl - ta) * tb) + 256 * pc + 16 * (lane & (16 * PPT - 1));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + 64 * PPT * k), 16, off,
+                                             0, 0, 0);
   }
 }
 
-template <int UTG>
+// A block's words from its LDS copy; pairs past PPT (past every wave's
+// range) are zero.
+template <int UTG, int PPT>
 __device__ __forceinline__ void lds_ublock(const uint32_t* src, int pc, int nu, UBlock<UTG>& U) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int i = 0; i < DK_UPW; ++i) {
     const int li = 2 * (pc + i) + 1 < nu ? lane : lane >> 1;
 #pragma unroll
-    for (int k = 0; k < UTG; ++k) U.w[k][i] = src[64 * (DK_UPW * k + i) + li];
+    for (int k = 0; k < UTG; ++k) U.w[k][i] = i < PPT ? src[64 * (PPT * k + i) + li] : 0u;
   }
 }
 
@@ -793,7 +800,7 @@ __device__ __forceinline__ const LbDecodeArgs* dk1_kernarg_args() {
 // ranges vt_begin / ut_begin of the argument block (two launches: vq/vr,
 // uq/ur).  TPU: 16-rank tiles per unit of V work (1, or 2 on one
 // instruction: the host takes 2 when there are more tiles than workgroups).
-template <int MODE, bool SINGLE, int TPU, int UTG = DK_UTG>
+template <int MODE, bool SINGLE, int TPU, int UTG = DK_UTG, int PPT = DK_UPW>
 __global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* pre_vb0, const uint8_t* pre_vb1,
                                                                 const uint16_t* pre_x, const uint16_t* pre_g0,
                                                                 const uint16_t* pre_g1, uint8_t* sync, int pre_n,
@@ -924,7 +931,7 @@ __global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* p
   auto issue_first_u = [&]() {
     if (MODE != 0) {
       compiler_memory_barrier();
-      dma_ublock<UTG>(uL, ug.b, ug.tile, ug.nt, ug.p0, ublk[wave]);
+      dma_ublock<UTG, PPT>(uL, ug.b, ug.tile, ug.nt, ug.p0, ublk[wave]);
       hcur = load_group_h<UTG>(uL, ug.tile, ug.nt);
       compiler_memory_barrier();
     }
@@ -1031,7 +1038,7 @@ __global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* p
     LB_STAMP(4);
     LB_STAMP(10);
     LB_COUNT(12);
-    lds_ublock(ublk[wave], ug.p0, nu0, cur);
+    lds_ublock<UTG, PPT>(ublk[wave], ug.p0, nu0, cur);
   }
   get_tag();
   for (int t = ut0; t < ut1;) {
@@ -1116,14 +1123,34 @@ typedef void (*Decode1Kernel)(const uint8_t*, const uint8_t*, const uint16_t*, c
 // The instantiation for a launch: one or several layers, one or two V tiles
 // per unit, U groups of 4 tiles (small: no workgroup holds more than 4 U
 // tiles) or 8.
+template <int MODE, int UTG, int PPT>
+Decode1Kernel decode1_pick(bool single, bool one) {
+  if (single) return one ? lb_decode1_kernel<MODE, true, 1, UTG, PPT> : lb_decode1_kernel<MODE, true, 2, UTG, PPT>;
+  return one ? lb_decode1_kernel<MODE, false, 1, UTG, PPT> : lb_decode1_kernel<MODE, false, 2, UTG, PPT>;
+}
+
+// The instantiation for a launch: one or several layers, one or two V tiles
+// per unit, U groups of 4 tiles (small: no workgroup holds more than 4 U
+// tiles) or 8, first-block copies of 2 pairs per tile (narrow: no wave's
+// range is longer) or 4.
 template <int MODE>
-Decode1Kernel decode1_variant(bool single, bool one, bool small = false) {
+Decode1Kernel decode1_variant(bool single, bool one, bool small = false, bool narrow = false) {
   if constexpr (MODE != 0) {
-    if (small && single) return one ? lb_decode1_kernel<MODE, true, 1, 4> : lb_decode1_kernel<MODE, true, 2, 4>;
-    if (small) return one ? lb_decode1_kernel<MODE, false, 1, 4> : lb_decode1_kernel<MODE, false, 2, 4>;
+    if (small) return narrow ? decode1_pick<MODE, 4, 2>(single, one) : decode1_pick<MODE, 4, DK_UPW>(single, one);
+    if (narrow) return decode1_pick<MODE, DK_UTG, 2>(single, one);
   }
-  if (single) return one ? lb_decode1_kernel<MODE, true, 1> : lb_decode1_kernel<MODE, true, 2>;
-  return one ? lb_decode1_kernel<MODE, false, 1> : lb_decode1_kernel<MODE, false, 2>;
+  return decode1_pick<MODE, DK_UTG, DK_UPW>(single, one);
+}
+
+// Whether no wave's phase-B pair range exceeds 2 pairs in any layer
+// (u_role1: quarters of a branch's pairs with two branches, eighths with one).
+static bool decode1_narrow(const LbDecodeArgs& a) {
+  for (int i = 0; i < a.nlayers; ++i)
+    for (int b = 0; b < a.L[i].nb; ++b) {
+      const int np = (nunits(a.L[i].br[b].r) + 1) >> 1;
+      if (np > (a.L[i].nb == 2 ? 8 : 16)) return false;
+    }
+  return true;
 }
 
 // Whether every workgroup's U tiles fit one group of 4: q + (r > 0) per
@@ -1138,13 +1165,13 @@ static bool decode1_small_groups(const LbDecodeArgs& a, int G, bool single) {
 // Workgroups of a single launch that fit at once, for the given dynamic LDS
 // (the lower count of the two V unit sizes).
 hipError_t lb_decode1_occupancy(bool single, size_t lds, int& occ) {
-  int o[4] = {0, 0, 0, 0};
+  int o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   hipError_t e = hipSuccess;
-  for (int i = 0; i < 4 && e == hipSuccess; ++i)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o[i], decode1_variant<2>(single, (i & 1) != 0, i >= 2),
+  for (int i = 0; i < 8 && e == hipSuccess; ++i)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o[i], decode1_variant<2>(single, (i & 1) != 0, (i & 2) != 0, i >= 4),
                                                      DK_THREADS, lds);
   occ = o[0];
-  for (int i = 1; i < 4; ++i) occ = o[i] < occ ? o[i] : occ;
+  for (int i = 1; i < 8; ++i) occ = o[i] < occ ? o[i] : occ;
   return e;
 }
 
@@ -1179,7 +1206,7 @@ hipError_t lb_launch_decode1(const LbDecodeArgs& args, int G, void* sync, hipStr
     a.uq = a.nut / G;
     a.ur = a.nut % G;
     if (a.vq > 255 || a.vr > 255) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(decode1_variant<2>(single, one, decode1_small_groups(a, G, single)), dim3(G), dim3(DK_THREADS),
+    hipLaunchKernelGGL(decode1_variant<2>(single, one, decode1_small_groups(a, G, single), decode1_narrow(a)), dim3(G), dim3(DK_THREADS),
                        lds, stream, vb0, vb1, px, g0, g1, sy, pn, single ? misc(a.vq, a.vr) : 0u, a);
     return hipGetLastError();
   }
@@ -1197,7 +1224,7 @@ hipError_t lb_launch_decode1(const LbDecodeArgs& args, int G, void* sync, hipStr
   a.uq = a.nut / gb;
   a.ur = a.nut % gb;
   // (the U launch does no V work: one instantiation per layer count)
-  hipLaunchKernelGGL(decode1_variant<1>(single, false, decode1_small_groups(a, 0, true)), dim3(gb), dim3(DK_THREADS),
+  hipLaunchKernelGGL(decode1_variant<1>(single, false, decode1_small_groups(a, 0, true), decode1_narrow(a)), dim3(gb), dim3(DK_THREADS),
                      lds, stream, vb0, vb1, px, g0, g1,
                      sy, pn, single ? misc(0, 0) : 0u, a);
   return hipGetLastError();
