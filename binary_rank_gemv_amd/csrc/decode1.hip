@@ -700,18 +700,21 @@ __device__ __forceinline__ void load_ublock(const SL& L, int b, int t0, int nt, 
 // (lanes 16 PPT j .. take tile k + j).  Word (k, i) of a lane is then
 // dst[64 (PPT k + i) + lane] (lane / 2 for an odd last unit), as pair_word
 // reads it from memory.  The copy costs in proportion to its bytes, so it
-// takes UTG tiles (a group's last tile repeated past nt; groups of 4 where no
-// workgroup holds more) and PPT pairs of each (2 where no wave's range is
+// takes CT tiles (a group's last tile repeated past nt; groups of 4 where no
+// workgroup holds more, 7 of a group of 8 where none holds 8: the eighth
+// slot is then never a tile of the group, and its column of the last tile
+// pair is discarded) and PPT pairs of each (2 where no wave's range is
 // longer, else 4).  Reads are bounded by the end of the factor.
-template <int UTG, int PPT>
+template <int UTG, int PPT, int CT = UTG>
 __device__ __forceinline__ void dma_ublock(const SL& L, int b, int t0, int nt, int pc, uint32_t* dst) {
   static_assert(PPT == 2 || PPT == 4, "2 or 4 pairs per tile");
   constexpr int TPL = 4 / PPT;  // tiles per load
   const int r = L.r(b), lane = threadIdx.x & 63;
   const long tb = lb16_tile_bytes(r);
   const int ntf = (L.m + 15) >> 4;
+  static_assert(CT == UTG || (CT <= UTG && CT % TPL == 0), "whole loads");
 #pragma unroll
-  for (int k = 0; k < UTG; k += TPL) {
+  for (int k = 0; k < CT; k += TPL) {
     const int ta = t0 + min(k, nt - 1), tl = t0 + min(k + lane / (16 * PPT), nt - 1);
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(L.ub(b) + (long)ta * tb, (int)((ntf - ta) * tb));
     const int off = (int)((tl - ta) * tb) + 256 * pc + 16 * (lane & (16 * PPT - 1));
@@ -800,7 +803,7 @@ __device__ __forceinline__ const LbDecodeArgs* dk1_kernarg_args() {
 // ranges vt_begin / ut_begin of the argument block (two launches: vq/vr,
 // uq/ur).  TPU: 16-rank tiles per unit of V work (1, or 2 on one
 // instruction: the host takes 2 when there are more tiles than workgroups).
-template <int MODE, bool SINGLE, int TPU, int UTG = DK_UTG, int PPT = DK_UPW>
+template <int MODE, bool SINGLE, int TPU, int UTG = DK_UTG, int PPT = DK_UPW, int CT = UTG>
 __global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* pre_vb0, const uint8_t* pre_vb1,
                                                                 const uint16_t* pre_x, const uint16_t* pre_g0,
                                                                 const uint16_t* pre_g1, uint8_t* sync, int pre_n,
@@ -931,7 +934,7 @@ __global__ __launch_bounds__(DK_THREADS) void lb_decode1_kernel(const uint8_t* p
   auto issue_first_u = [&]() {
     if (MODE != 0) {
       compiler_memory_barrier();
-      dma_ublock<UTG, PPT>(uL, ug.b, ug.tile, ug.nt, ug.p0, ublk[wave]);
+      dma_ublock<UTG, PPT, CT>(uL, ug.b, ug.tile, ug.nt, ug.p0, ublk[wave]);
       hcur = load_group_h<UTG>(uL, ug.tile, ug.nt);
       compiler_memory_barrier();
     }
@@ -1123,21 +1126,24 @@ typedef void (*Decode1Kernel)(const uint8_t*, const uint8_t*, const uint16_t*, c
 // The instantiation for a launch: one or several layers, one or two V tiles
 // per unit, U groups of 4 tiles (small: no workgroup holds more than 4 U
 // tiles) or 8.
-template <int MODE, int UTG, int PPT>
+template <int MODE, int UTG, int PPT, int CT = UTG>
 Decode1Kernel decode1_pick(bool single, bool one) {
-  if (single) return one ? lb_decode1_kernel<MODE, true, 1, UTG, PPT> : lb_decode1_kernel<MODE, true, 2, UTG, PPT>;
-  return one ? lb_decode1_kernel<MODE, false, 1, UTG, PPT> : lb_decode1_kernel<MODE, false, 2, UTG, PPT>;
+  if (single)
+    return one ? lb_decode1_kernel<MODE, true, 1, UTG, PPT, CT> : lb_decode1_kernel<MODE, true, 2, UTG, PPT, CT>;
+  return one ? lb_decode1_kernel<MODE, false, 1, UTG, PPT, CT> : lb_decode1_kernel<MODE, false, 2, UTG, PPT, CT>;
 }
 
 // The instantiation for a launch: one or several layers, one or two V tiles
 // per unit, U groups of 4 tiles (small: no workgroup holds more than 4 U
 // tiles) or 8, first-block copies of 2 pairs per tile (narrow: no wave's
-// range is longer) or 4.
+// range is longer) or 4, of 7 tiles of a group of 8 (seven: no workgroup
+// holds 8 U tiles).
 template <int MODE>
-Decode1Kernel decode1_variant(bool single, bool one, bool small = false, bool narrow = false) {
+Decode1Kernel decode1_variant(bool single, bool one, bool small = false, bool narrow = false, bool seven = false) {
   if constexpr (MODE != 0) {
     if (small) return narrow ? decode1_pick<MODE, 4, 2>(single, one) : decode1_pick<MODE, 4, DK_UPW>(single, one);
     if (narrow) return decode1_pick<MODE, DK_UTG, 2>(single, one);
+    if (seven) return decode1_pick<MODE, DK_UTG, DK_UPW, DK_UTG - 1>(single, one);
   }
   return decode1_pick<MODE, DK_UTG, DK_UPW>(single, one);
 }
@@ -1153,25 +1159,26 @@ static bool decode1_narrow(const LbDecodeArgs& a) {
   return true;
 }
 
-// Whether every workgroup's U tiles fit one group of 4: q + (r > 0) per
-// workgroup for an even split, or the largest range of a cost-balanced one.
-static bool decode1_small_groups(const LbDecodeArgs& a, int G, bool single) {
-  if (single || G == 0) return a.uq + (a.ur > 0 ? 1 : 0) <= 4;
+// The most U tiles a workgroup holds: q + (r > 0) for an even split, or the
+// largest range of a cost-balanced one.
+static int decode1_max_utiles(const LbDecodeArgs& a, int G, bool single) {
+  if (single || G == 0) return a.uq + (a.ur > 0 ? 1 : 0);
   int mx = 0;
   for (int w = 0; w < G; ++w) mx = a.ut_begin[w + 1] - a.ut_begin[w] > mx ? a.ut_begin[w + 1] - a.ut_begin[w] : mx;
-  return mx <= 4;
+  return mx;
 }
 
 // Workgroups of a single launch that fit at once, for the given dynamic LDS
 // (the lower count of the two V unit sizes).
 hipError_t lb_decode1_occupancy(bool single, size_t lds, int& occ) {
-  int o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  int o[10] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
   hipError_t e = hipSuccess;
-  for (int i = 0; i < 8 && e == hipSuccess; ++i)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o[i], decode1_variant<2>(single, (i & 1) != 0, (i & 2) != 0, i >= 4),
-                                                     DK_THREADS, lds);
+  for (int i = 0; i < 10 && e == hipSuccess; ++i)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &o[i], decode1_variant<2>(single, (i & 1) != 0, i < 8 && (i & 2) != 0, i < 8 && (i & 4) != 0, i >= 8),
+        DK_THREADS, lds);
   occ = o[0];
-  for (int i = 1; i < 8; ++i) occ = o[i] < occ ? o[i] : occ;
+  for (int i = 1; i < 10; ++i) occ = o[i] < occ ? o[i] : occ;
   return e;
 }
 
@@ -1206,7 +1213,8 @@ hipError_t lb_launch_decode1(const LbDecodeArgs& args, int G, void* sync, hipStr
     a.uq = a.nut / G;
     a.ur = a.nut % G;
     if (a.vq > 255 || a.vr > 255) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(decode1_variant<2>(single, one, decode1_small_groups(a, G, single), decode1_narrow(a)), dim3(G), dim3(DK_THREADS),
+    hipLaunchKernelGGL(decode1_variant<2>(single, one, decode1_max_utiles(a, G, single) <= 4, decode1_narrow(a),
+                                          decode1_max_utiles(a, G, single) <= DK_UTG - 1), dim3(G), dim3(DK_THREADS),
                        lds, stream, vb0, vb1, px, g0, g1, sy, pn, single ? misc(a.vq, a.vr) : 0u, a);
     return hipGetLastError();
   }
@@ -1224,7 +1232,8 @@ hipError_t lb_launch_decode1(const LbDecodeArgs& args, int G, void* sync, hipStr
   a.uq = a.nut / gb;
   a.ur = a.nut % gb;
   // (the U launch does no V work: one instantiation per layer count)
-  hipLaunchKernelGGL(decode1_variant<1>(single, false, decode1_small_groups(a, 0, true), decode1_narrow(a)), dim3(gb), dim3(DK_THREADS),
+  hipLaunchKernelGGL(decode1_variant<1>(single, false, decode1_max_utiles(a, 0, true) <= 4, decode1_narrow(a),
+                                        decode1_max_utiles(a, 0, true) <= DK_UTG - 1), dim3(gb), dim3(DK_THREADS),
                      lds, stream, vb0, vb1, px, g0, g1,
                      sy, pn, single ? misc(0, 0) : 0u, a);
   return hipGetLastError();
